@@ -1,0 +1,360 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention-input epilogue on one MI355X.
+
+A step is one launch of the epilogue over one batch of synthetic input.  The
+headline workload is the 14B-shape prefill: 4096 tokens at positions 0..4095,
+40 query heads and 8 kv heads of 128, f32 q/k/v, f16 KV cache.  The value is
+achieved HBM bandwidth in GB/s = algorithmic bytes per launch / mean launch
+time, where the algorithmic bytes are
+
+    per token : 2*(nqt + 2*nkt)*4   read and write back q, k, v
+              + 2*nkt*cb            the K and V cache rows (cb = 2 for f16)
+              + 4                   the position (+4 for a slot index)
+    per launch: (nqt + 2*nkt)*4     the three biases
+
+Input sets are rotated (each set has its own q/k/v and caches, together well
+over the 256 MB last-level cache) so every launch reads its inputs from HBM.
+Timing: HIP events on the launch stream around the timed launches.
+
+Extra figures in the same line: the 256-sequence batched decode (f16 and f32
+caches) in GB/s, and decode microseconds per layer for the 7B and 14B decode
+steps (stream loop and HIP-graph replay).  The CPU baseline is the oracle of
+the unfused chain, single-threaded, timed on a bounded sample of the headline
+workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "fused QKV epilogue achieved HBM GB/s (14B shape) + decode µs/layer"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algo_bytes(w, nt, cache_bytes, slot=False):
+    per_tok = 2 * (w.nqt + 2 * w.nkt) * 4 + 2 * w.nkt * cache_bytes + 4 + (4 if slot else 0)
+    return per_tok * nt + (w.nqt + 2 * w.nkt) * 4
+
+
+def kernel_source_hash():
+    p = os.path.join(ROOT, "qkv_bias_rope_amd", "csrc", "qkv_epilogue.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM traffic per launch from a committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", f"pmc_qkv_epilogue_{workload}.txt")
+    if not os.path.exists(p):
+        return None
+    vals = {}
+    for line in open(p):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Sets:
+    """R independent input sets of one workload on the device."""
+
+    def __init__(self, w, R, cache_dtype, nt=None, share_cache=False):
+        import numpy as np
+        import torch
+        from qkv_bias_rope_amd import workloads as wl
+        self.w = w
+        self.nt = w.nt if nt is None else nt
+        d = wl.draw_layer(w, 0, nt=self.nt)
+        dev = "cuda:0"
+        self.bq, self.bk, self.bv = (torch.from_numpy(d[n]).to(dev) for n in ("bq", "bk", "bv"))
+        cdt = torch.float16 if cache_dtype == wl.CACHE_F16 else torch.float32
+        rows = w.n_slots * w.n_ctx
+        self.sets = []
+        base = {n: torch.from_numpy(d[n]).to(dev) for n in ("q", "k", "v")}
+        shared = None
+        for r in range(R):
+            s = {}
+            for n in ("q", "k", "v"):
+                s[n] = base[n].clone() if r else base[n]
+            if w.pos_mode == "uniform":
+                rng = np.random.default_rng(w.seed * 7919 + r)
+                s["pos"] = torch.from_numpy(
+                    rng.integers(0, w.n_ctx, size=self.nt, dtype=np.int32)).to(dev)
+            else:
+                s["pos"] = torch.from_numpy(d["pos"]).to(dev)
+            s["slot"] = None if d["slot"] is None else torch.from_numpy(d["slot"]).to(dev)
+            if share_cache and shared is not None:
+                s["kc"], s["vc"] = shared
+            else:
+                s["kc"] = torch.empty((rows, w.nkt), dtype=cdt, device=dev)
+                s["vc"] = torch.empty((rows, w.nkt), dtype=cdt, device=dev)
+                shared = (s["kc"], s["vc"])
+            self.sets.append(s)
+        self.cache_dtype = cache_dtype
+
+    def args(self, r, stream):
+        from qkv_bias_rope_amd import binding as B
+        s = self.sets[r % len(self.sets)]
+        w = self.w
+        return B.make_args(s["q"], s["k"], s["v"], self.bq, self.bk, self.bv, s["pos"], s["kc"],
+                           s["vc"], n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim,
+                           theta=w.theta, cache_dtype=self.cache_dtype, slot=s["slot"],
+                           n_ctx=w.n_ctx, n_slots=w.n_slots, stream=stream, use_stream=True,
+                           nt=self.nt)
+
+
+def time_launches(h, arg_list, steps, warmup, stream):
+    """Mean time per launch (ms) over `steps` launches cycling through
+    arg_list, HIP events recorded on the launch stream."""
+    import torch
+    from qkv_bias_rope_amd import binding as B
+    for i in range(warmup):
+        rc = B.qkv_epilogue_run_ex(h, arg_list[i % len(arg_list)])
+        assert rc == 0, B.qkv_epilogue_last_error(h)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        B.qkv_epilogue_run_ex(h, arg_list[i % len(arg_list)])
+    e1.record(stream)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    assert B.qkv_epilogue_status(h) == 0, B.qkv_epilogue_last_error(h)
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_bandwidth(h, w, cache_dtype, steps, warmup, stream, min_set_bytes=1.5e9, slot=False):
+    from qkv_bias_rope_amd import workloads as wl
+    cb = 2 if cache_dtype == wl.CACHE_F16 else 4
+    nbytes = algo_bytes(w, w.nt, cb, slot=slot)
+    per_set = w.nt * (w.nqt + 2 * w.nkt) * 4 * 2
+    R = max(2, int(-(-min_set_bytes // per_set)))
+    # big caches (batched decode) are shared by the sets: their rows are written
+    # at random positions, so a shared cache gets no reuse anyway
+    share = w.n_slots > 1
+    sets = Sets(w, R, cache_dtype, share_cache=share)
+    args = [sets.args(r, stream) for r in range(R)]
+    ms = time_launches(h, args, steps, warmup, stream)
+    return dict(ms=ms, bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9, sets=R), sets
+
+
+def bench_decode(h, w, steps, warmup, stream):
+    """One decode step = one launch per layer.  Returns microseconds per layer
+    for a plain stream loop and for a HIP-graph replay of the whole step."""
+    import torch
+    from qkv_bias_rope_amd import binding as B
+    from qkv_bias_rope_amd import workloads as wl
+    layers = []
+    for layer in range(w.layers):
+        s = Sets(w, 1, w.cache_dtypes[0])
+        if w.concat_even_layers and layer % 2 == 0:
+            # one [nqt + 2*nkt] row holding the three sections
+            buf = torch.cat([s.sets[0]["q"], s.sets[0]["k"], s.sets[0]["v"]], dim=1).contiguous()
+            s.sets[0]["q"] = buf[:, :w.nqt]
+            s.sets[0]["k"] = buf[:, w.nqt:w.nqt + w.nkt]
+            s.sets[0]["v"] = buf[:, w.nqt + w.nkt:]
+            s.buf = buf
+        layers.append(s)
+    args = [s.args(0, stream) for s in layers]
+    n_loops = max(1, steps)
+    # stream loop
+    ms_step = time_launches(h, args, n_loops * w.layers, warmup * w.layers, stream) * w.layers
+    # graph replay of one step
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for a in args:
+            a.stream = torch.cuda.current_stream().cuda_stream
+            assert B.qkv_epilogue_run_ex(h, a) == 0
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    e0.record(cur)
+    for _ in range(n_loops):
+        g.replay()
+    e1.record(cur)
+    e1.synchronize()
+    ms_graph = e0.elapsed_time(e1) / n_loops
+    assert B.qkv_epilogue_status(h) == 0
+    cb = 2 if w.cache_dtypes[0] == wl.CACHE_F16 else 4
+    return dict(us_per_layer_stream=ms_step * 1e3 / w.layers,
+                us_per_layer_graph=ms_graph * 1e3 / w.layers,
+                bytes_per_layer=algo_bytes(w, 1, cb), layers=w.layers)
+
+
+def cpu_baseline(w, cache_dtype, budget_s=10.0):
+    """The oracle (single-threaded C, unfused chain) on the headline workload,
+    repeated over whole launches until about budget_s seconds have passed."""
+    import numpy as np
+    import oracle
+    from qkv_bias_rope_amd import workloads as wl
+    d = wl.draw_layer(w, 0)
+    cb = 2 if cache_dtype == wl.CACHE_F16 else 4
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        q, k, v = (d[x].copy() for x in ("q", "k", "v"))
+        ts = time.perf_counter()
+        oracle.qkv_epilogue(q.ravel(), k.ravel(), v.ravel(), d["bq"], d["bk"], d["bv"], d["pos"],
+                            n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim,
+                            theta=w.theta, n_ctx=w.n_ctx, cache_dtype=cache_dtype,
+                            slot=d["slot"], n_slots=w.n_slots)
+        n += 1
+        if n == 1:
+            spent = time.perf_counter() - ts
+        else:
+            spent += time.perf_counter() - ts
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    s_per = spent / n
+    return dict(value=algo_bytes(w, w.nt, cb) / s_per / 1e9, unit="GB/s", cores=1, kind="oracle",
+                sample=f"{n} full launch(es) of {w.name} ({w.nt} tokens, f16 cache) on 1 host "
+                       f"thread, {s_per:.3f} s each")
+
+
+def copy_calibration(steps):
+    """A plain device copy of known size (for scaling FETCH_SIZE/WRITE_SIZE)."""
+    import torch
+    n = 256 * 1024 * 1024  # float32 elements = 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                      "launches": steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="run only a 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the epilogue needs no collective: each GPU would run its own shard of tokens "
+              "or heads, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from qkv_bias_rope_amd import build as _b
+    if not os.path.exists(_b.LIB):
+        _b.build()
+    from qkv_bias_rope_amd import binding as B
+    from qkv_bias_rope_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calib:
+        copy_calibration(args.steps)
+        return
+
+    rc, h = B.qkv_epilogue_create(0, 4096)
+    assert rc == 0, rc
+    # all work on one non-default stream (a HIP graph cannot capture the null stream)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        line = run_all(args, h, stream)
+    B.qkv_epilogue_destroy(h)
+    print(json.dumps(line), flush=True)
+
+
+def run_all(args, h, stream):
+    import torch
+    from qkv_bias_rope_amd import workloads as wl
+
+    w = wl.PREFILL_14B
+    log(f"[bench] {w.name}: {args.warmup} warmup + {args.steps} timed launches")
+    main_res, sets = bench_bandwidth(h, w, wl.CACHE_F16, args.steps, args.warmup, stream)
+    del sets
+    torch.cuda.empty_cache()
+    log(f"[bench] {w.name}: {main_res['ms'] * 1e3:.2f} us/launch, {main_res['gbs']:.1f} GB/s")
+
+    extra = {}
+    if not args.no_extra:
+        wb = wl.BATCHED_DECODE_14B
+        for cd, tag in ((wl.CACHE_F16, "f16"), (wl.CACHE_F32, "f32")):
+            log(f"[bench] {wb.name} {tag}")
+            r, sets = bench_bandwidth(h, wb, cd, args.steps, args.warmup, stream,
+                                      min_set_bytes=1.0e9, slot=True)
+            del sets
+            torch.cuda.empty_cache()
+            extra[f"{wb.name}_{tag}"] = dict(
+                gbs=round(r["gbs"], 1), us_per_launch=round(r["ms"] * 1e3, 3),
+                bytes_per_launch=r["bytes"], frac_of_peak=round(r["gbs"] / PEAK_HBM_GBS, 4),
+                input_sets=r["sets"])
+            log(f"[bench]   {r['ms'] * 1e3:.2f} us/launch, {r['gbs']:.1f} GB/s")
+        for wd in (wl.DECODE_7B, wl.DECODE_14B):
+            log(f"[bench] {wd.name}")
+            r = bench_decode(h, wd, max(10, args.steps // 10), max(2, args.warmup // 10), stream)
+            extra[wd.name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
+            log(f"[bench]   {r['us_per_layer_stream']:.2f} us/layer (stream), "
+                f"{r['us_per_layer_graph']:.2f} us/layer (graph)")
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_baseline(w, wl.CACHE_F16)
+        cpu["value"] = round(cpu["value"], 4)
+        log(f"[bench]   {cpu['value']} GB/s")
+
+    traffic = read_traffic(w.name)
+    achieved = main_res["gbs"]
+    line = {
+        "metric": METRIC,
+        "value": round(achieved, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) q/k/v, N(0,0.1) biases)",
+        "config": {"workload": w.name, "n_head": w.n_head, "n_kv_head": w.n_kv_head,
+                   "head_dim": w.head_dim, "tokens": w.nt, "positions": "0..4095",
+                   "cache": "f16", "theta": w.theta, "input_sets_rotated": main_res["sets"],
+                   "bytes_per_launch": main_res["bytes"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    return line
+
+
+if __name__ == "__main__":
+    main()

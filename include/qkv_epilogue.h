@@ -1,0 +1,214 @@
+/*
+ * qkv_epilogue.h -- C ABI of the fused attention-input epilogue for MI355X
+ * (gfx950).
+ *
+ * The operation (page "73 · D3-8 — G4 FusedQKV ported to CUDA", minfer CUDA
+ * optimization steps, §2 and §3.2 Excerpt A): for every token t of a launch
+ *
+ *   1. add the biases:  q[t][j] += bq[j], k[t][j] += bk[j], v[t][j] += bv[j]
+ *      (one f32 add each);
+ *   2. rotate q and k with NeoX-paired rotary embedding: inside every head of
+ *      head_dim elements, element i pairs with element i + head_dim/2 and the
+ *      pair turns by the angle pos[t] * theta^(-2i/head_dim);
+ *   3. write k and v back in place, and store them into the layer's KV cache
+ *      at row pos[t] (page "07 · The allocator", §2.5: each per-layer region is
+ *      n_ctx rows of n_kv_head*head_dim elements, the element of token t at
+ *      dst[pos*nkt + j]), as f32 or as f16 rounded to nearest even.
+ *
+ * It is one kernel launch per call.  q, k and v are section base pointers, so
+ * one concat q|k|v buffer and three separate buffers use the same entry point
+ * (page 73, §2 "pointer-form").
+ *
+ * Numerics:
+ *   - the inverse frequencies are the correctly rounded f32 of
+ *     theta^(-2i/head_dim), computed once per (theta, head_dim) on the host in
+ *     double precision;
+ *   - the angle is the f32 product pos * inv[i];
+ *   - cos and sin are evaluated in double precision and rounded to f32;
+ *   - each rotated value is the f32 rounding of x0*c - x1*s (or x0*s + x1*c)
+ *     evaluated in double (the products of two f32 values are exact there);
+ *   - f16 cache values are IEEE binary16 round-to-nearest-even, subnormals
+ *     kept, overflow to infinity.
+ *
+ * Conventions common to every call:
+ *   - All tensor pointers are caller-owned DEVICE pointers on the handle's
+ *     device.  The library never allocates, frees or copies tensor memory.
+ *   - Calls that launch work are asynchronous on the given HIP stream: they
+ *     never synchronize and may be captured into a HIP graph.
+ *   - Every function returns 0 on success or a negative QKV_ERR_* code; the
+ *     text of the last failure is available from qkv_epilogue_last_error.
+ *     There is no fallback path: an unsupported request is an error (page
+ *     "06 · Assign + fusion", §2.1: a violated kernel invariant aborts rather
+ *     than falling back).
+ *   - A handle is not thread-safe: use one handle per host thread.
+ */
+#ifndef QKV_EPILOGUE_H
+#define QKV_EPILOGUE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ------------------------------------------------------- */
+#define QKV_OK 0
+#define QKV_ERR_INVALID_ARG   (-1) /* bad pointer, size, stride, dtype or theta */
+#define QKV_ERR_ALIAS         (-2) /* output ranges overlap each other or an input */
+#define QKV_ERR_UNSUPPORTED   (-3) /* a rotary style other than NeoX pairing */
+#define QKV_ERR_HIP           (-4) /* a HIP runtime call or launch failed */
+#define QKV_ERR_POSITION_RANGE (-5) /* (status only) a pos/slot was out of range */
+
+/* ---- cache element types ------------------------------------------------ */
+#define QKV_CACHE_F32 0
+#define QKV_CACHE_F16 1
+
+/* ---- rotary styles ------------------------------------------------------ */
+#define QKV_ROPE_NEOX 0         /* pair i with i + head_dim/2: the only one */
+#define QKV_ROPE_INTERLEAVED 1  /* pair 2i with 2i+1: rejected, QKV_ERR_UNSUPPORTED */
+
+/* Largest supported head_dim (the inverse-frequency table travels with the
+ * launch and holds head_dim/2 values). */
+#define QKV_MAX_HEAD_DIM 512
+
+typedef struct qkv_epilogue qkv_epilogue_t;
+
+typedef struct qkv_epilogue_config {
+    int device;   /* HIP device ordinal the tensors live on */
+    int64_t n_ctx;  /* positions per cache slot (rows of a one-sequence cache) */
+    void *stream; /* hipStream_t used by qkv_epilogue_run; NULL = null stream */
+} qkv_epilogue_config_t;
+
+/*
+ * Create a handle.  Allocates the handle and a 16-byte device error word on
+ * cfg->device (that word is the only device memory the library owns).
+ * Returns QKV_ERR_INVALID_ARG for a NULL out/cfg, n_ctx < 1 or a bad device
+ * ordinal, QKV_ERR_HIP if the device cannot be used.  *out is NULL on error.
+ */
+int qkv_epilogue_create(qkv_epilogue_t **out, const qkv_epilogue_config_t *cfg);
+
+/*
+ * The epilogue over nt tokens of one layer, on the handle's stream.
+ *
+ *   q      [nt][n_head*head_dim]     f32, dense rows, biased + roped in place
+ *   k      [nt][n_kv_head*head_dim]  f32, dense rows, biased + roped in place
+ *   v      [nt][n_kv_head*head_dim]  f32, dense rows, biased in place
+ *   bq     [n_head*head_dim]         f32 bias of q (read only)
+ *   bk, bv [n_kv_head*head_dim]      f32 biases of k and v (read only)
+ *   pos    [nt]                      int32 positions, read on the device
+ *   kcache, vcache [n_ctx][n_kv_head*head_dim] of f32 (cache_dtype 0) or f16
+ *          (cache_dtype 1): row pos[t] receives token t's k and v; no other
+ *          row is touched.
+ *   theta  rotary base (> 0, finite), e.g. 1e6.
+ *
+ * Dense rows only: for a concat q|k|v buffer with nt > 1 use
+ * qkv_epilogue_run_ex and pass the concat row stride.  nt == 0 does nothing
+ * and returns 0.  Equivalent to qkv_epilogue_run_ex with slot = NULL,
+ * n_slots = 1, rope_style = NEOX, dense strides, the handle's n_ctx and
+ * stream.
+ *
+ * A position outside [0, n_ctx) is reported by qkv_epilogue_status (that
+ * token's q/k/v are still computed, its cache rows are not written); page
+ * "07 · The allocator", §3.2 Excerpt 8: a position beyond the cache is a
+ * hard error, never a silent overflow.
+ */
+int qkv_epilogue_run(qkv_epilogue_t *h, float *q, float *k, float *v,
+                     const float *bq, const float *bk, const float *bv,
+                     const int32_t *pos, void *kcache, void *vcache, int nt,
+                     int n_head, int n_kv_head, int head_dim, float theta,
+                     int cache_dtype);
+
+typedef struct qkv_epilogue_args {
+    float *q, *k, *v;               /* section bases (device) */
+    const float *bq, *bk, *bv;      /* biases (device) */
+    const int32_t *pos;             /* [nt] positions (device) */
+    const int32_t *slot;            /* [nt] cache slot per token, or NULL = 0 */
+    void *kcache, *vcache;          /* [n_slots][n_ctx][nkt] (device) */
+    int64_t ld_q, ld_k, ld_v;       /* row strides in elements; 0 = dense */
+    int64_t n_ctx;                  /* positions per slot; 0 = the handle's */
+    int64_t n_slots;                /* slots in each cache; 0 = 1 */
+    int nt, n_head, n_kv_head, head_dim;
+    float theta;
+    int cache_dtype;                /* QKV_CACHE_F32 / QKV_CACHE_F16 */
+    int rope_style;                 /* QKV_ROPE_NEOX only */
+    void *stream;                   /* hipStream_t; NULL = the handle's */
+    int use_stream;                 /* nonzero: launch on `stream` even if NULL */
+} qkv_epilogue_args_t;
+
+/*
+ * The general form.  Token t's cache row is slot[t]*n_ctx + pos[t] (slot 0
+ * without a slot array); the multi-sequence reading of the page's single
+ * region dst[pos*nkt + j].  Row strides let q, k and v be the sections of a
+ * concat [nt][nqt + 2*nkt] buffer: q = base, k = base + nqt,
+ * v = base + nqt + nkt, all with ld = nqt + 2*nkt.
+ *
+ * Errors (returned synchronously, nothing is launched):
+ *   QKV_ERR_INVALID_ARG  NULL handle/args; a NULL tensor pointer when nt > 0;
+ *                        nt < 0; n_head or n_kv_head < 1; head_dim <= 0, odd
+ *                        or > QKV_MAX_HEAD_DIM; theta <= 0 or not finite; an
+ *                        unknown cache_dtype; a stride below its row width;
+ *                        n_ctx or n_slots < 0; a cache pointer not aligned to
+ *                        its element size; more than 2^31 work units.
+ *   QKV_ERR_ALIAS        two of q, k, v, kcache, vcache share an element, or
+ *                        a read-only input (bias, pos, slot) overlaps one.
+ *   QKV_ERR_UNSUPPORTED  rope_style is not QKV_ROPE_NEOX (page "06 · Assign +
+ *                        fusion", §3.2: a backend claims only the rotary
+ *                        style its kernel implements).
+ *   QKV_ERR_HIP          the launch failed (text from the HIP runtime).
+ * Duplicate cache rows within one call are a caller error: the row then holds
+ * one of the colliding tokens' values.
+ */
+int qkv_epilogue_run_ex(qkv_epilogue_t *h, const qkv_epilogue_args_t *a);
+
+/*
+ * Blocking: synchronize the stream of the handle's last launch, read and
+ * clear the device error word.  Returns QKV_ERR_POSITION_RANGE if any token
+ * launched since the last status call had pos outside [0, n_ctx) or slot
+ * outside [0, n_slots), QKV_ERR_HIP on a runtime failure, else 0.
+ */
+int qkv_epilogue_status(qkv_epilogue_t *h);
+
+/* Text of the last non-zero return on this handle ("" if none).  The pointer
+ * stays valid until the next call on the handle. */
+const char *qkv_epilogue_last_error(const qkv_epilogue_t *h);
+
+/* Free the handle and its error word.  NULL is a no-op. */
+void qkv_epilogue_destroy(qkv_epilogue_t *h);
+
+/* ---- host-only helpers (no device needed) ------------------------------- */
+
+/*
+ * The f32 inverse-frequency table the kernels use: out[i] = correctly rounded
+ * theta^(-2i/head_dim), i < head_dim/2.  Returns QKV_ERR_INVALID_ARG for a
+ * bad theta/head_dim or NULL out.
+ */
+int qkv_epilogue_inv_freq(float theta, int head_dim, float *out);
+
+/*
+ * Validate a request exactly as qkv_epilogue_run_ex does, without a handle
+ * or a device.  n_ctx must be given (> 0) in *a.  Writes the reason to msg
+ * (NUL-terminated, truncated to msg_len) and returns the code run_ex would.
+ */
+int qkv_epilogue_check_args(const qkv_epilogue_args_t *a, char *msg, size_t msg_len);
+
+/*
+ * The launch plan run_ex would use for *a (host-only): vector width of the
+ * kernel variant (4 = 16-byte vector path, 1 = scalar path), work units per
+ * token, units per thread, workgroup size, workgroup count and dynamic LDS
+ * bytes.  Returns the check_args code.
+ */
+typedef struct qkv_epilogue_plan {
+    int vec_width;
+    int units_per_token;
+    int units_per_thread;
+    int block;
+    int64_t grid;
+    int lds_bytes;
+} qkv_epilogue_plan_t;
+int qkv_epilogue_plan(const qkv_epilogue_args_t *a, qkv_epilogue_plan_t *plan);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QKV_EPILOGUE_H */

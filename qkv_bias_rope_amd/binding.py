@@ -1,0 +1,277 @@
+"""ctypes binding of libqkv_epilogue.so (the C ABI in include/qkv_epilogue.h).
+
+Argument marshalling only: every step of the epilogue runs in the HIP kernels
+of the library.  The functions keep the C names and return the C codes; the
+``Epilogue`` class wraps them for torch tensors and raises on errors.  PyTorch
+is used for nothing but device memory (``data_ptr``) and the current stream.
+
+If the library is not built this module raises at import time: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+# Load torch first: its wheel bundles the HIP runtime (SONAME libamdhip64.so.7)
+# and this library must bind to that same runtime instance, not load a second
+# copy from /opt/rocm (two runtimes in one process do not share device state).
+import torch  # noqa: F401
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqkv_epilogue.so")
+
+QKV_OK = 0
+QKV_ERR_INVALID_ARG = -1
+QKV_ERR_ALIAS = -2
+QKV_ERR_UNSUPPORTED = -3
+QKV_ERR_HIP = -4
+QKV_ERR_POSITION_RANGE = -5
+ERR_NAMES = {0: "QKV_OK", -1: "QKV_ERR_INVALID_ARG", -2: "QKV_ERR_ALIAS",
+             -3: "QKV_ERR_UNSUPPORTED", -4: "QKV_ERR_HIP", -5: "QKV_ERR_POSITION_RANGE"}
+QKV_CACHE_F32 = 0
+QKV_CACHE_F16 = 1
+QKV_ROPE_NEOX = 0
+QKV_ROPE_INTERLEAVED = 1
+QKV_MAX_HEAD_DIM = 512
+
+EXPORTS = ("qkv_epilogue_create", "qkv_epilogue_run", "qkv_epilogue_run_ex",
+           "qkv_epilogue_status", "qkv_epilogue_last_error", "qkv_epilogue_destroy",
+           "qkv_epilogue_inv_freq", "qkv_epilogue_check_args", "qkv_epilogue_plan")
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+
+
+class QkvEpilogueConfig(ctypes.Structure):
+    _fields_ = [("device", _I), ("n_ctx", _I64), ("stream", _P)]
+
+
+class QkvEpilogueArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", _P), ("k", _P), ("v", _P),
+        ("bq", _P), ("bk", _P), ("bv", _P),
+        ("pos", _P), ("slot", _P),
+        ("kcache", _P), ("vcache", _P),
+        ("ld_q", _I64), ("ld_k", _I64), ("ld_v", _I64),
+        ("n_ctx", _I64), ("n_slots", _I64),
+        ("nt", _I), ("n_head", _I), ("n_kv_head", _I), ("head_dim", _I),
+        ("theta", _F),
+        ("cache_dtype", _I), ("rope_style", _I),
+        ("stream", _P), ("use_stream", _I),
+    ]
+
+
+class QkvEpiloguePlan(ctypes.Structure):
+    _fields_ = [("vec_width", _I), ("units_per_token", _I), ("units_per_thread", _I),
+                ("block", _I), ("grid", _I64), ("lds_bytes", _I)]
+
+
+class QkvError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{ERR_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc --offload-arch=gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.qkv_epilogue_create.argtypes = [ctypes.POINTER(_P), ctypes.POINTER(QkvEpilogueConfig)]
+    lib.qkv_epilogue_create.restype = _I
+    lib.qkv_epilogue_run.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     _I, _I, _I, _I, _F, _I]
+    lib.qkv_epilogue_run.restype = _I
+    lib.qkv_epilogue_run_ex.argtypes = [_P, ctypes.POINTER(QkvEpilogueArgs)]
+    lib.qkv_epilogue_run_ex.restype = _I
+    lib.qkv_epilogue_status.argtypes = [_P]
+    lib.qkv_epilogue_status.restype = _I
+    lib.qkv_epilogue_last_error.argtypes = [_P]
+    lib.qkv_epilogue_last_error.restype = ctypes.c_char_p
+    lib.qkv_epilogue_destroy.argtypes = [_P]
+    lib.qkv_epilogue_destroy.restype = None
+    lib.qkv_epilogue_inv_freq.argtypes = [_F, _I, _P]
+    lib.qkv_epilogue_inv_freq.restype = _I
+    lib.qkv_epilogue_check_args.argtypes = [ctypes.POINTER(QkvEpilogueArgs), ctypes.c_char_p,
+                                            ctypes.c_size_t]
+    lib.qkv_epilogue_check_args.restype = _I
+    lib.qkv_epilogue_plan.argtypes = [ctypes.POINTER(QkvEpilogueArgs),
+                                      ctypes.POINTER(QkvEpiloguePlan)]
+    lib.qkv_epilogue_plan.restype = _I
+    return lib
+
+
+lib = _load()
+
+
+def _addr(x):
+    """Device address of a tensor (data_ptr) or a raw integer address."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+# ---- the C entry points, same names ----------------------------------------
+
+def qkv_epilogue_create(device: int = 0, n_ctx: int = 4096, stream=None):
+    """Returns (rc, handle); handle is an opaque integer (0 on failure)."""
+    h = _P()
+    cfg = QkvEpilogueConfig(device, n_ctx, _stream_addr(stream))
+    rc = lib.qkv_epilogue_create(ctypes.byref(h), ctypes.byref(cfg))
+    return rc, (h.value or 0)
+
+
+def qkv_epilogue_run(h, q, k, v, bq, bk, bv, pos, kcache, vcache, nt, n_head, n_kv_head,
+                     head_dim, theta, cache_dtype) -> int:
+    return lib.qkv_epilogue_run(h, _addr(q), _addr(k), _addr(v), _addr(bq), _addr(bk),
+                                _addr(bv), _addr(pos), _addr(kcache), _addr(vcache),
+                                nt, n_head, n_kv_head, head_dim, theta, cache_dtype)
+
+
+def qkv_epilogue_run_ex(h, args: QkvEpilogueArgs) -> int:
+    return lib.qkv_epilogue_run_ex(h, ctypes.byref(args))
+
+
+def qkv_epilogue_status(h) -> int:
+    return lib.qkv_epilogue_status(h)
+
+
+def qkv_epilogue_last_error(h) -> str:
+    r = lib.qkv_epilogue_last_error(h)
+    return r.decode() if r else ""
+
+
+def qkv_epilogue_destroy(h) -> None:
+    lib.qkv_epilogue_destroy(h)
+
+
+def qkv_epilogue_inv_freq(theta: float, head_dim: int, out_addr: int) -> int:
+    return lib.qkv_epilogue_inv_freq(theta, head_dim, out_addr)
+
+
+def qkv_epilogue_check_args(args: QkvEpilogueArgs):
+    """Returns (rc, message)."""
+    buf = ctypes.create_string_buffer(512)
+    rc = lib.qkv_epilogue_check_args(ctypes.byref(args), buf, len(buf))
+    return rc, buf.value.decode()
+
+
+def qkv_epilogue_plan(args: QkvEpilogueArgs):
+    """Returns (rc, QkvEpiloguePlan)."""
+    p = QkvEpiloguePlan()
+    rc = lib.qkv_epilogue_plan(ctypes.byref(args), ctypes.byref(p))
+    return rc, p
+
+
+# ---- torch convenience ------------------------------------------------------
+
+def _stream_addr(stream):
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _row_stride(t, width, name):
+    """Row stride (elements) of a [nt][width] section view, 0 when dense."""
+    if t.dim() == 1:
+        return 0
+    if t.dim() != 2 or t.stride(-1) != 1:
+        raise ValueError(f"{name}: need a 1-D tensor or a 2-D view with unit column stride")
+    if t.shape[-1] != width:
+        raise ValueError(f"{name}: rows hold {t.shape[-1]} elements, expected {width}")
+    return 0 if t.shape[0] <= 1 else t.stride(0)
+
+
+def make_args(q, k, v, bq, bk, bv, pos, kcache, vcache, *, n_head, n_kv_head, head_dim,
+              theta, cache_dtype, nt=None, slot=None, n_ctx=0, n_slots=0, ld_q=None,
+              ld_k=None, ld_v=None, rope_style=QKV_ROPE_NEOX, stream=None,
+              use_stream=False) -> QkvEpilogueArgs:
+    """Build the run_ex argument block.  Tensors (or raw addresses) are taken as
+    they are; strides come from 2-D tensor views unless given."""
+    nqt, nkt = n_head * head_dim, n_kv_head * head_dim
+    if nt is None:
+        nt = int(pos.numel())
+    if ld_q is None:
+        ld_q = 0 if (q is None or isinstance(q, int)) else _row_stride(q, nqt, "q")
+    if ld_k is None:
+        ld_k = 0 if (k is None or isinstance(k, int)) else _row_stride(k, nkt, "k")
+    if ld_v is None:
+        ld_v = 0 if (v is None or isinstance(v, int)) else _row_stride(v, nkt, "v")
+    a = QkvEpilogueArgs()
+    a.q, a.k, a.v = _addr(q), _addr(k), _addr(v)
+    a.bq, a.bk, a.bv = _addr(bq), _addr(bk), _addr(bv)
+    a.pos, a.slot = _addr(pos), _addr(slot)
+    a.kcache, a.vcache = _addr(kcache), _addr(vcache)
+    a.ld_q, a.ld_k, a.ld_v = ld_q, ld_k, ld_v
+    a.n_ctx, a.n_slots = n_ctx, n_slots
+    a.nt, a.n_head, a.n_kv_head, a.head_dim = nt, n_head, n_kv_head, head_dim
+    a.theta = theta
+    a.cache_dtype = cache_dtype
+    a.rope_style = rope_style
+    a.stream = _stream_addr(stream)
+    a.use_stream = 1 if use_stream else 0
+    return a
+
+
+class Epilogue:
+    """A handle bound to one device.  ``run`` launches on torch's current
+    stream and raises QkvError on a non-zero return."""
+
+    def __init__(self, device: int = 0, n_ctx: int = 4096):
+        rc, h = qkv_epilogue_create(device, n_ctx, None)
+        if rc != QKV_OK:
+            raise QkvError(rc, f"qkv_epilogue_create(device={device}, n_ctx={n_ctx}) failed")
+        self.h = h
+        self.device = device
+        self.n_ctx = n_ctx
+
+    def run(self, q, k, v, bq, bk, bv, pos, kcache, vcache, *, n_head, n_kv_head, head_dim,
+            theta=1.0e6, slot=None, n_ctx=None, n_slots=None, stream=None, **kw):
+        import torch
+        if kcache.dtype == torch.float32:
+            cd = QKV_CACHE_F32
+        elif kcache.dtype == torch.float16:
+            cd = QKV_CACHE_F16
+        else:
+            raise TypeError(f"cache dtype must be float32 or float16, got {kcache.dtype}")
+        if vcache.dtype != kcache.dtype:
+            raise TypeError("kcache and vcache must share a dtype")
+        for name, t in (("q", q), ("k", k), ("v", v), ("bq", bq), ("bk", bk), ("bv", bv)):
+            if t.dtype != torch.float32 or not t.is_cuda:
+                raise TypeError(f"{name} must be a float32 device tensor")
+        for name, t in (("pos", pos), ("slot", slot)):
+            if t is not None and (t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous()):
+                raise TypeError(f"{name} must be a contiguous int32 device tensor")
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        a = make_args(q, k, v, bq, bk, bv, pos, kcache, vcache, n_head=n_head,
+                      n_kv_head=n_kv_head, head_dim=head_dim, theta=theta, cache_dtype=cd,
+                      slot=slot, n_ctx=n_ctx or 0, n_slots=n_slots or 0, stream=stream,
+                      use_stream=True, **kw)
+        rc = qkv_epilogue_run_ex(self.h, a)
+        if rc != QKV_OK:
+            raise QkvError(rc, qkv_epilogue_last_error(self.h))
+
+    def status(self) -> int:
+        return qkv_epilogue_status(self.h)
+
+    def last_error(self) -> str:
+        return qkv_epilogue_last_error(self.h)
+
+    def close(self):
+        if self.h:
+            qkv_epilogue_destroy(self.h)
+            self.h = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,338 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle on the
+same seeded inputs, for the five workloads of the op and its edge cases.
+
+Workloads (shapes from the pages' 0.5B/7B/14B attention geometry):
+  tiny decode (14/2/64, pos 5, f32 cache of 32), 7B decode (28/4/128, 28
+  layers), 14B decode (40/8/128, 48 layers, even layers concat q|k|v, odd
+  layers separate), 14B prefill (4096 tokens), 14B batched decode (256
+  sequences, slot per sequence, 32768 positions, f16 and f32 caches).
+"""
+import numpy as np
+import pytest
+import torch
+
+from parity_helpers import DEV, Case, changed_rows, new_cache, say
+from qkv_bias_rope_amd import binding as B
+from qkv_bias_rope_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def handle():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rc, h = B.qkv_epilogue_create(0, 4096)
+    assert rc == 0, rc
+    yield h
+    B.qkv_epilogue_destroy(h)
+
+
+def run_case(h, c, entry="run_ex", check_untouched=True, label=""):
+    say(f"[case] {label} nt={c.nt} form={c.form} cache={'f16' if c.cd else 'f32'} entry={entry}")
+    c.run_oracle().upload()
+    rc = c.run_gpu(h, entry)
+    assert rc == 0, B.qkv_epilogue_last_error(h)
+    st = B.qkv_epilogue_status(h)
+    assert st == (B.QKV_ERR_POSITION_RANGE if c.o_bad else 0), (st, B.qkv_epilogue_last_error(h))
+    c.download()
+    return c.check(check_untouched=check_untouched, label=label)
+
+
+# ---- the five workloads -----------------------------------------------------
+
+@pytest.mark.parametrize("form", ["separate", "concat"])
+@pytest.mark.parametrize("entry", ["run", "run_ex"])
+def test_tiny_decode(handle, form, entry):
+    if entry == "run" and form == "concat":
+        pytest.skip("run takes dense rows; nt=1 concat sections go through run_ex")
+    w = wl.TINY_DECODE
+    c = Case(w, form=form)
+    # the plain entry point uses the handle's n_ctx; give it a matching handle
+    if entry == "run":
+        rc, h = B.qkv_epilogue_create(0, w.n_ctx)
+        assert rc == 0
+        try:
+            run_case(h, c, entry=entry, label="tiny")
+        finally:
+            B.qkv_epilogue_destroy(h)
+    else:
+        run_case(handle, c, entry=entry, label="tiny")
+
+
+def _decode_steps(handle, w, steps):
+    """Several decode steps over every layer; each layer has its own caches
+    and biases, every step one position shared by all layers."""
+    caches = [(new_cache(w.n_ctx, w.nkt, w.cache_dtypes[0]),
+               new_cache(w.n_ctx, w.nkt, w.cache_dtypes[0])) for _ in range(w.layers)]
+    positions = wl.step_positions(w, steps)
+    written = [set() for _ in range(w.layers)]
+    for s, p in enumerate(positions):
+        for layer in range(w.layers):
+            form = "concat" if (w.concat_even_layers and layer % 2 == 0) else "separate"
+            d = wl.draw_layer(w, layer)
+            # a fresh activation per step, the layer's own bias
+            rng = np.random.default_rng(w.seed * 100000 + s * 1000 + layer)
+            for n in ("q", "k", "v"):
+                d[n] = rng.standard_normal(d[n].shape, dtype=np.float32)
+            c = Case(w, inputs=d, pos=[p], form=form)
+            c.run_oracle().upload(kcache=caches[layer][0], vcache=caches[layer][1])
+            assert c.run_gpu(handle) == 0, B.qkv_epilogue_last_error(handle)
+            c.download()
+            c.check(check_untouched=False, label=f"{w.name} step {s} layer {layer} {form}")
+            written[layer].add(int(p))
+        assert B.qkv_epilogue_status(handle) == 0
+    for layer, (kc, vc) in enumerate(caches):
+        for cache in (kc, vc):
+            ch = changed_rows(cache, w.cache_dtypes[0])
+            assert set(ch.tolist()) == written[layer], (layer, ch, written[layer])
+
+
+def test_decode_7b(handle):
+    say("[case] decode_7b 28 layers x 3 steps")
+    _decode_steps(handle, wl.DECODE_7B, steps=3)
+
+
+def test_decode_14b_both_pointer_forms(handle):
+    say("[case] decode_14b 48 layers x 2 steps, even concat / odd separate")
+    _decode_steps(handle, wl.DECODE_14B, steps=2)
+
+
+def test_prefill_14b_full(handle):
+    res = run_case(handle, Case(wl.PREFILL_14B), label="prefill_14b_4096")
+    say(f"  q/k max abs, max rel, #not-bit-exact: {res}")
+
+
+@pytest.mark.parametrize("cd", [wl.CACHE_F16, wl.CACHE_F32])
+def test_batched_decode_14b_full(handle, cd):
+    """256 sequences, one token each, caches of 256 slots x 32768 positions
+    (17 GB per f16 cache, 34 GB per f32 cache); every unwritten row checked."""
+    res = run_case(handle, Case(wl.BATCHED_DECODE_14B, cache_dtype=cd),
+                   label=f"batched_decode_14b cache={'f16' if cd else 'f32'}")
+    say(f"  {res}")
+    torch.cuda.empty_cache()
+
+
+# ---- scaled-down cases spanning several tiles with ragged tails -------------
+
+@pytest.mark.parametrize("nt", [2, 3, 37, 255, 1000])
+@pytest.mark.parametrize("cd", [wl.CACHE_F16, wl.CACHE_F32])
+def test_prefill_ragged(handle, nt, cd):
+    w = wl.PREFILL_14B
+    run_case(handle, Case(w, nt=nt, cache_dtype=cd, pos=np.arange(nt) * 3 % 4096),
+             label=f"prefill nt={nt}")
+
+
+@pytest.mark.parametrize("nt", [5, 129])
+def test_prefill_concat_rows(handle, nt):
+    """nt > 1 concat q|k|v rows: sections with the concat row stride."""
+    w = wl.PREFILL_14B
+    run_case(handle, Case(w, nt=nt, form="concat", pos=(np.arange(nt) * 7) % 4096),
+             label=f"prefill concat nt={nt}")
+
+
+@pytest.mark.parametrize("nt", [1, 7, 64])
+def test_batched_slots_small(handle, nt):
+    w = wl.Workload("batched_small", 40, 8, 128, nt=nt, n_ctx=64, n_slots=nt + 3, layers=1,
+                    seed=11, cache_dtypes=(wl.CACHE_F16,))
+    rng = np.random.default_rng(5)
+    slot = rng.permutation(nt + 3)[:nt]
+    run_case(handle, Case(w, slot=slot), label=f"slots nt={nt}")
+
+
+# ---- geometry edge cases ----------------------------------------------------
+
+@pytest.mark.parametrize("geom", [(14, 2, 64), (8, 8, 96), (3, 1, 256), (2, 1, 512), (5, 3, 8),
+                                  (4, 2, 6), (3, 3, 2), (7, 1, 18)])
+@pytest.mark.parametrize("cd", [wl.CACHE_F16, wl.CACHE_F32])
+def test_head_geometries(handle, geom, cd):
+    nh, nkv, hd = geom
+    w = wl.Workload(f"geom{nh}x{nkv}x{hd}", nh, nkv, hd, nt=19, n_ctx=97, n_slots=1, layers=1,
+                    seed=21, cache_dtypes=(cd,))
+    run_case(handle, Case(w), label=f"geom {geom}")
+
+
+@pytest.mark.parametrize("form", ["separate", "concat"])
+def test_misaligned_sections_use_scalar_path(handle, form):
+    w = wl.Workload("misaligned", 40, 8, 128, nt=9, n_ctx=4096, n_slots=1, layers=1, seed=31)
+    c = Case(w, form=form, misalign=1)
+    c.run_oracle().upload()
+    a = B.make_args(c.g_q, c.g_k, c.g_v, c.g_bq, c.g_bk, c.g_bv, c.g_pos, c.kc, c.vc,
+                    n_head=40, n_kv_head=8, head_dim=128, theta=w.theta, cache_dtype=c.cd,
+                    n_ctx=w.n_ctx)
+    rc, plan = B.qkv_epilogue_plan(a)
+    assert rc == 0 and plan.vec_width == 1
+    run_case(handle, c, label=f"misaligned {form}")
+
+
+def test_nt_zero_is_noop(handle):
+    w = wl.TINY_DECODE
+    kc = new_cache(w.n_ctx, w.nkt, wl.CACHE_F32)
+    before = kc.clone()
+    x = torch.zeros(16, device=DEV)
+    assert B.qkv_epilogue_run(handle, x, x, x, x, x, x, None, kc, kc, 0, 14, 2, 64, 1e6, 0) == 0
+    # null pointers are fine with nt == 0 through run_ex as well
+    a = B.make_args(None, None, None, None, None, None, None, None, None, n_head=14, n_kv_head=2,
+                    head_dim=64, theta=1e6, cache_dtype=0, nt=0, n_ctx=32)
+    assert B.qkv_epilogue_run_ex(handle, a) == 0
+    assert B.qkv_epilogue_status(handle) == 0
+    assert torch.equal(kc.view(torch.int32), before.view(torch.int32))
+
+
+def test_invalid_requests_rejected(handle):
+    c = Case(wl.TINY_DECODE).run_oracle().upload()
+    w = c.w
+    def args(**kw):
+        base = dict(n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim, theta=w.theta,
+                    cache_dtype=c.cd, n_ctx=w.n_ctx, ld_q=0, ld_k=0, ld_v=0)
+        base.update(kw)
+        return B.make_args(c.g_q, c.g_k, c.g_v, c.g_bq, c.g_bk, c.g_bv, c.g_pos, c.kc, c.vc,
+                           **base)
+    assert B.qkv_epilogue_run_ex(handle, args(head_dim=63, n_head=1, n_kv_head=1)) == \
+        B.QKV_ERR_INVALID_ARG
+    assert "head_dim" in B.qkv_epilogue_last_error(handle)
+    assert B.qkv_epilogue_run_ex(handle, args(rope_style=B.QKV_ROPE_INTERLEAVED)) == \
+        B.QKV_ERR_UNSUPPORTED
+    assert B.qkv_epilogue_run_ex(handle, args(theta=0.0)) == B.QKV_ERR_INVALID_ARG
+    a = args()
+    a.vcache = a.kcache
+    assert B.qkv_epilogue_run_ex(handle, a) == B.QKV_ERR_ALIAS
+    torch.cuda.synchronize()
+    # nothing was launched: inputs and caches unchanged
+    assert np.array_equal(c.g_q.cpu().numpy(), c.d["q"])
+    assert changed_rows(c.kc, c.cd).size == 0
+
+
+def test_out_of_range_positions_flagged_and_not_stored(handle):
+    w = wl.Workload("range", 40, 8, 128, nt=6, n_ctx=100, n_slots=1, layers=1, seed=41,
+                    cache_dtypes=(wl.CACHE_F32,))
+    c = Case(w, pos=[0, 99, 100, -1, 50, 1 << 30])
+    res = run_case(handle, c, label="out-of-range positions")
+    assert c.o_bad == 3
+    # the status word was cleared by the read
+    assert B.qkv_epilogue_status(handle) == 0
+
+
+def test_out_of_range_slots_flagged(handle):
+    w = wl.Workload("slotrange", 8, 8, 64, nt=5, n_ctx=16, n_slots=4, layers=1, seed=42,
+                    cache_dtypes=(wl.CACHE_F16,))
+    run_case(handle, Case(w, pos=[1, 2, 3, 4, 5], slot=[0, 3, 4, -1, 2]), label="slot range")
+
+
+def test_f16_ties_subnormals_and_overflow(handle):
+    """k and v values sitting exactly on binary16 rounding ties, in the
+    subnormal range and past the largest finite value, at position 0 with zero
+    bias so they reach the cache unchanged."""
+    w = wl.Workload("f16edge", 4, 4, 64, nt=8, n_ctx=8, n_slots=1, layers=1, seed=51,
+                    cache_dtypes=(wl.CACHE_F16,))
+    rng = np.random.default_rng(3)
+    nkt = w.nkt
+    h = rng.integers(0, 0x7bfe, size=(8, nkt)).astype(np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    ties = ((lo + hi) / 2).astype(np.float32)
+    ties[0, :8] = np.array([65504, 65519, 65520, 70000, 2**-24, 2**-25, 3 * 2**-26, 2**-14],
+                           np.float32)
+    ties[1] = (rng.standard_normal(nkt) * 2**-20).astype(np.float32)   # subnormal f16 range
+    sign = np.where(rng.random((8, nkt)) < 0.5, -1, 1).astype(np.float32)
+    k = ties * sign
+    v = ties[::-1].copy() * sign
+    d = wl.draw_layer(w, 0)
+    d["k"], d["v"] = k, v
+    d["bk"] = np.zeros(nkt, np.float32)
+    d["bv"] = np.zeros(nkt, np.float32)
+    d["pos"] = np.zeros(8, np.int32) + np.arange(8, dtype=np.int32)
+    # position t != 0 would rotate k; keep k unrotated by using position 0 for
+    # a second launch below, and check v (never rotated) at every row here
+    c = Case(w, inputs=d)
+    run_case(handle, c, label="f16 edges (v at all rows)")
+    d2 = dict(d)
+    d2["pos"] = np.zeros(1, np.int32)
+    for n in ("q", "k", "v"):
+        d2[n] = d[n][:1].copy()
+    run_case(handle, Case(w, inputs=d2), label="f16 edges (k at pos 0)")
+
+
+def test_large_angles(handle):
+    w = wl.Workload("angles", 40, 8, 128, nt=12, n_ctx=1 << 20, n_slots=1, layers=1, seed=61,
+                    cache_dtypes=(wl.CACHE_F32,))
+    pos = [32767, 32766, 65535, 1 << 19, (1 << 20) - 1, 1, 0, 2, 4095, 12345, 99999, 777777]
+    run_case(handle, Case(w, pos=pos), label="large angles")
+
+
+def test_duplicate_positions_hold_one_writer(handle):
+    """Two tokens at the same position write the same row: either token's
+    values are a correct result (the op leaves the order unspecified)."""
+    w = wl.Workload("dups", 40, 8, 128, nt=24, n_ctx=8, n_slots=1, layers=1, seed=71)
+    c = Case(w, pos=np.arange(24) % 8)
+    run_case(handle, c, label="duplicate positions")
+
+
+def test_deterministic(handle):
+    w = wl.PREFILL_14B
+    outs = []
+    for _ in range(2):
+        c = Case(w, nt=300, pos=np.arange(300) * 11 % 4096).run_oracle().upload()
+        assert c.run_gpu(handle) == 0
+        torch.cuda.synchronize()
+        c.download()
+        outs.append((c.r_q.copy(), c.r_k.copy(), c.kc.cpu().numpy().copy()))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_nondefault_stream(handle):
+    s = torch.cuda.Stream()
+    w = wl.PREFILL_14B
+    c = Case(w, nt=64, pos=np.arange(64)).run_oracle().upload()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        assert c.run_gpu(handle, stream=s) == 0
+    s.synchronize()
+    assert B.qkv_epilogue_status(handle) == 0
+    c.download()
+    c.check(label="side stream")
+
+
+def test_graph_capture_replay_48_layers(handle):
+    """48 decode layers captured into one HIP graph; replays with new positions
+    and new activations written into the same buffers match the oracle."""
+    w = wl.DECODE_14B
+    L = w.layers
+    layers = []
+    for layer in range(L):
+        d = wl.draw_layer(w, layer)
+        c = Case(w, inputs=d, pos=[0], form="concat" if layer % 2 == 0 else "separate")
+        c.upload()
+        layers.append(c)
+    pos = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for c in layers:
+        c.g_pos = pos
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):           # warm-up outside capture
+        for c in layers:
+            assert c.run_gpu(handle, stream=s) == 0
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for c in layers:
+            assert c.run_gpu(handle, stream=torch.cuda.current_stream()) == 0
+    torch.cuda.synchronize()
+    for rep, p in enumerate([17, 4095, 1234]):
+        # fresh activations and a new position in the captured buffers
+        for li, c in enumerate(layers):
+            rng = np.random.default_rng(1000 * rep + li)
+            for n in ("q", "k", "v"):
+                c.d[n] = rng.standard_normal(c.d[n].shape, dtype=np.float32)
+                getattr(c, "g_" + n).copy_(torch.from_numpy(c.d[n]).to(DEV))
+            c.d["pos"] = np.array([p], np.int32)
+        pos.fill_(p)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert B.qkv_epilogue_status(handle) == 0
+        for li, c in enumerate(layers):
+            c.run_oracle()
+            c.download()
+            c.check(check_untouched=False, label=f"graph replay {rep} layer {li}")

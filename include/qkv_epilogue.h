@@ -149,7 +149,8 @@ typedef struct qkv_epilogue_args {
  *                        or > QKV_MAX_HEAD_DIM; theta <= 0 or not finite; an
  *                        unknown cache_dtype; a stride below its row width;
  *                        n_ctx or n_slots < 0; a cache pointer not aligned to
- *                        its element size; more than 2^31 work units.
+ *                        its element size; more than 2^28 work units per
+ *                        token or 2^31-1 workgroups.
  *   QKV_ERR_ALIAS        two of q, k, v, kcache, vcache share an element, or
  *                        a read-only input (bias, pos, slot) overlaps one.
  *   QKV_ERR_UNSUPPORTED  rope_style is not QKV_ROPE_NEOX (page "06 · Assign +
@@ -195,14 +196,17 @@ int qkv_epilogue_check_args(const qkv_epilogue_args_t *a, char *msg, size_t msg_
 /*
  * The launch plan run_ex would use for *a (host-only): vector width of the
  * kernel variant (4 = 16-byte vector path, 1 = scalar path), work units per
- * token, units per thread, workgroup size, workgroup count and dynamic LDS
- * bytes.  Returns the check_args code.
+ * token (a unit is two vector slots of one token's row), units per thread,
+ * workgroup size, column blocks per token, tokens per workgroup, workgroup
+ * count and dynamic LDS bytes.  Returns the check_args code.
  */
 typedef struct qkv_epilogue_plan {
     int vec_width;
     int units_per_token;
     int units_per_thread;
     int block;
+    int col_blocks;
+    int tokens_per_block;
     int64_t grid;
     int lds_bytes;
 } qkv_epilogue_plan_t;

@@ -66,7 +66,8 @@ class QkvEpilogueArgs(ctypes.Structure):
 
 class QkvEpiloguePlan(ctypes.Structure):
     _fields_ = [("vec_width", _I), ("units_per_token", _I), ("units_per_thread", _I),
-                ("block", _I), ("grid", _I64), ("lds_bytes", _I)]
+                ("block", _I), ("col_blocks", _I), ("tokens_per_block", _I), ("grid", _I64),
+                ("lds_bytes", _I)]
 
 
 class QkvError(RuntimeError):

@@ -14,18 +14,25 @@
 //    unit is W rotary pairs of one head: elements [i0, i0+W) and
 //    [i0+half, i0+half+W), so both halves of a pair arrive in the same lane
 //    from two 16-byte loads and no cross-lane exchange is needed.  For v a
-//    unit is 2W consecutive elements.  Units of a token are laid out q, k, v;
-//    the launch walks the flat range [0, nt*units_per_token) so tokens and
-//    sequences (prefill, batched decode) fill the chip the same way.
-//  * Each thread owns UPT units strided by the workgroup size, so a wave's
-//    loads cover whole 128-byte lines; every load of a thread is issued before
-//    any arithmetic.
+//    unit is [c, c+W) and [c+nkt/2, c+nkt/2+W), so that, like the rope
+//    units, consecutive lanes touch consecutive 16 bytes and every store
+//    instruction writes whole 128-byte lines.  Units of a token are ordered
+//    q, k, v.
+//  * Grid.  A workgroup owns a column block (a fixed range of units) and a
+//    token block.  Each thread decodes its units once, keeps their biases in
+//    registers and walks the tokens of its block, issuing the next token's
+//    loads before it computes the current one.  Prefill and batched decode
+//    pick few, wide column blocks and several tokens per block; a one-token
+//    decode spreads the token over many small column blocks.
 //  * cos/sin are computed once per (token, pair index) per workgroup, in double
 //    precision, rounded to f32 and kept in LDS; the inverse frequencies ride in
 //    the kernel arguments (computed on the host once per theta/head_dim).
 //  * The rotation is evaluated in double: the products of two f32 values are
 //    exact in double, so x0*c - x1*s is rounded once there and once to f32
 //    whether or not the compiler fuses it into an FMA.
+//  * q/k/v and the cache rows are touched exactly once per launch, so their
+//    loads and stores carry the nontemporal hint; the biases (reused by every
+//    workgroup) do not.
 //  * f16 stores convert each element with the round-to-nearest-even conversion
 //    and store W halves per instruction; the round-toward-zero pack
 //    conversion is never used.
@@ -51,7 +58,7 @@
 namespace {
 
 constexpr int kMaxHalf = QKV_MAX_HEAD_DIM / 2;
-constexpr int kBlock = 256;
+constexpr int kMaxBlock = 1024;
 
 // Inverse-frequency table passed by value in the kernel arguments.
 struct InvTable {
@@ -69,15 +76,17 @@ struct KParams {
     int64_t n_ctx;
     int64_t n_slots;
     int64_t nkt;
-    uint32_t total;       // nt * U
     int nt;
     int hd;
     int half;
     int uph;              // rope units per head = half / W
     int qu;               // q rope units per token
     int qku;              // q + k rope units per token
+    int vhalf;            // nkt / 2: distance between the two slots of a v unit
     int U;                // units per token
-    int max_tok;          // tokens one workgroup may touch (LDS sizing)
+    int cbu;              // units per column block = blockDim.x
+    int ncb;              // column blocks per token
+    int tb;               // tokens per token block
 };
 
 template <int W>
@@ -90,19 +99,54 @@ struct alignas(2 * W) HVec {
     _Float16 e[W];
 };
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Plain load (biases, LDS).
 template <int W>
 __device__ __forceinline__ FVec<W> ld_vec(const float *p)
 {
     return *reinterpret_cast<const FVec<W> *>(p);
 }
 
-template <int W>
-__device__ __forceinline__ void st_vec(float *p, const FVec<W> &v)
+// Load / store of q, k, v and the cache rows.  With STREAM (large launches,
+// whose data is touched once and far exceeds the caches) they carry the
+// nontemporal hint; small launches (decode) keep the default policy so data
+// the producer just wrote, or the consumer reads next, stays cached.
+template <int W, bool STREAM>
+__device__ __forceinline__ FVec<W> ld_data(const float *p)
 {
-    *reinterpret_cast<FVec<W> *>(p) = v;
+    if constexpr (!STREAM) {
+        return ld_vec<W>(p);
+    } else {
+        FVec<W> r;
+        if constexpr (W == 4) {
+            const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+            r.e[0] = v.x;
+            r.e[1] = v.y;
+            r.e[2] = v.z;
+            r.e[3] = v.w;
+        } else {
+            r.e[0] = __builtin_nontemporal_load(p);
+        }
+        return r;
+    }
 }
 
-template <int W, bool F16>
+template <int W, bool STREAM>
+__device__ __forceinline__ void st_data(float *p, const FVec<W> &v)
+{
+    if constexpr (!STREAM) {
+        *reinterpret_cast<FVec<W> *>(p) = v;
+    } else if constexpr (W == 4) {
+        const f32x4 x = {v.e[0], v.e[1], v.e[2], v.e[3]};
+        __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(p));
+    } else {
+        __builtin_nontemporal_store(v.e[0], p);
+    }
+}
+
+template <int W, bool F16, bool STREAM>
 __device__ __forceinline__ void st_cache(void *cache, int64_t off, const FVec<W> &v)
 {
     if constexpr (F16) {
@@ -110,114 +154,149 @@ __device__ __forceinline__ void st_cache(void *cache, int64_t off, const FVec<W>
 #pragma unroll
         for (int e = 0; e < W; ++e)
             h.e[e] = static_cast<_Float16>(v.e[e]);  // v_cvt_f16_f32: RNE
-        *reinterpret_cast<HVec<W> *>(static_cast<_Float16 *>(cache) + off) = h;
+        _Float16 *dst = static_cast<_Float16 *>(cache) + off;
+        if constexpr (!STREAM) {
+            *reinterpret_cast<HVec<W> *>(dst) = h;
+        } else if constexpr (W == 4) {
+            const f16x4 x = {h.e[0], h.e[1], h.e[2], h.e[3]};
+            __builtin_nontemporal_store(x, reinterpret_cast<f16x4 *>(dst));
+        } else {
+            __builtin_nontemporal_store(h.e[0], dst);
+        }
     } else {
-        *reinterpret_cast<FVec<W> *>(static_cast<float *>(cache) + off) = v;
+        st_data<W, STREAM>(static_cast<float *>(cache) + off, v);
     }
 }
 
-// LDS layout: int64 row[max_tok] | float cos[max_tok*half] | float sin[...]
-__host__ __device__ inline int lds_row_bytes(int max_tok)
+// LDS layout: int64 row[tb] | float cos[tb*half] | float sin[tb*half]
+__host__ __device__ inline int lds_row_bytes(int tb)
 {
-    return ((max_tok * 8) + 15) & ~15;
+    return ((tb * 8) + 15) & ~15;
 }
 
-template <int W, bool F16, int UPT>
-__global__ __launch_bounds__(kBlock) void qkv_epilogue_kernel(KParams p, InvTable inv)
+// Unit r of a token (0 <= r < U): section, column of the first slot, first
+// pair index (rope units) and distance from the first slot to the second.
+template <int W>
+__device__ __forceinline__ void decode_unit(const KParams &p, int r, int &sec, int &col, int &i0,
+                                            int &d1)
+{
+    if (r < p.qku) {
+        sec = r < p.qu ? 0 : 1;
+        if (sec)
+            r -= p.qu;
+        const int h = r / p.uph;
+        i0 = (r - h * p.uph) * W;
+        col = h * p.hd + i0;
+        d1 = p.half;
+    } else {
+        sec = 2;
+        i0 = 0;
+        col = (r - p.qku) * W;
+        d1 = p.vhalf;
+    }
+}
+
+// Section operands picked with selects on wave-uniform kernel arguments (an
+// indexed read of the argument array would become a per-lane memory load in
+// front of every data load).
+template <typename T>
+__device__ __forceinline__ T pick3(int s, T a, T b, T c)
+{
+    return s == 0 ? a : (s == 1 ? b : c);
+}
+
+template <int W, bool F16, int TPB, bool STREAM>
+__global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvTable inv)
 {
     extern __shared__ __align__(16) unsigned char lds_raw[];
     int64_t *s_row = reinterpret_cast<int64_t *>(lds_raw);
-    float *s_cos = reinterpret_cast<float *>(lds_raw + lds_row_bytes(p.max_tok));
-    float *s_sin = s_cos + p.max_tok * p.half;
+    float *s_cos = reinterpret_cast<float *>(lds_raw + lds_row_bytes(TPB));
+    float *s_sin = s_cos + TPB * p.half;
 
-    const uint32_t tid = threadIdx.x;
-    const uint32_t g0 = blockIdx.x * (uint32_t)(kBlock * UPT);
-    const uint32_t g_last = min(g0 + (uint32_t)(kBlock * UPT), p.total) - 1u;
-    const int t_lo = (int)(g0 / (uint32_t)p.U);
-    const int ntok = (int)(g_last / (uint32_t)p.U) - t_lo + 1;
+    const int tid = (int)threadIdx.x;
+    const int nthr = (int)blockDim.x;
+    const int cb = (int)blockIdx.x % p.ncb;
+    const int t0 = ((int)blockIdx.x / p.ncb) * TPB;
+    const int ntok = min(TPB, p.nt - t0);
+    const int ent = ntok * p.half;
 
-    // ---- phase 1: decode this thread's units and issue every load ---------
-    int sec[UPT];        // 0 q, 1 k, 2 v, -1 none
-    int tl[UPT];         // token index local to the workgroup
-    int col[UPT];        // column of the first slot inside the section row
-    int i0[UPT];         // first pair index (rope units)
-    FVec<W> xa[UPT], xb[UPT], ba[UPT], bb[UPT];
+    // Every load below is unconditional (out-of-range lanes read a clamped,
+    // valid address and discard it) so that each wait covers exactly the
+    // loads it needs: the cos/sin inputs are loaded first and their wait does
+    // not hold up the data loads issued after them.
 
+    // ---- cos/sin input of this thread's first entry, row input per token ---
+    const int ec = min(tid, ent - 1);
+    const int e_tk = ec / p.half;
+    const int e_i = ec - e_tk * p.half;
+    const int32_t e_pos = p.pos[t0 + e_tk];
+    const float e_inv = inv.v[e_i];
+    const int rc = min(tid, ntok - 1);
+    const int32_t r_pos = p.pos[t0 + rc];
+    const int32_t r_slot = (p.slot ? p.slot : p.pos)[t0 + rc];
+
+    // ---- this thread's unit, its biases and its data for every token -------
+    const int r = cb * p.cbu + tid;
+    const bool live = r < p.U;
+    int sec, col, i0, d1;
+    decode_unit<W>(p, min(r, p.U - 1), sec, col, i0, d1);
+    float *const xs = pick3(sec, p.x[0], p.x[1], p.x[2]) + col;
+    const int64_t ldx = pick3(sec, p.ld[0], p.ld[1], p.ld[2]);
+    const float *const bp = pick3(sec, p.b[0], p.b[1], p.b[2]) + col;
+    const FVec<W> ba = ld_vec<W>(bp);
+    const FVec<W> bb = ld_vec<W>(bp + d1);
+    FVec<W> xa[TPB], xb[TPB];
 #pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-        const uint32_t g = g0 + (uint32_t)u * kBlock + tid;
-        sec[u] = -1;
-        if (g < p.total) {
-            const int t = (int)(g / (uint32_t)p.U);
-            int r = (int)(g - (uint32_t)t * (uint32_t)p.U);
-            int s, c, i, d1;
-            if (r < p.qku) {
-                s = r < p.qu ? 0 : 1;
-                if (s) r -= p.qu;
-                const int h = r / p.uph;
-                i = (r - h * p.uph) * W;
-                c = h * p.hd + i;
-                d1 = p.half;
-            } else {
-                s = 2;
-                i = 0;
-                c = (r - p.qku) * (2 * W);
-                d1 = W;
-            }
-            sec[u] = s;
-            tl[u] = t - t_lo;
-            col[u] = c;
-            i0[u] = i;
-            const float *xp = p.x[s] + (int64_t)t * p.ld[s] + c;
-            const float *bp = p.b[s] + c;
-            xa[u] = ld_vec<W>(xp);
-            xb[u] = ld_vec<W>(xp + d1);
-            ba[u] = ld_vec<W>(bp);
-            bb[u] = ld_vec<W>(bp + d1);
-        }
+    for (int tt = 0; tt < TPB; ++tt) {
+        const float *xp = xs + (int64_t)(t0 + min(tt, ntok - 1)) * ldx;
+        xa[tt] = ld_data<W, STREAM>(xp);
+        xb[tt] = ld_data<W, STREAM>(xp + d1);
     }
 
-    // ---- phase 2: per (token, pair) cos/sin and per-token cache rows -------
-    const int ent = ntok * p.half;
-    for (int e = (int)tid; e < ent; e += kBlock) {
+    // ---- cos/sin per (token, pair index) and cache row per token -----------
+    if (tid < ent) {
+        const float a = (float)e_pos * e_inv;   // f32 angle
+        double sd, cd;
+        sincos((double)a, &sd, &cd);
+        s_cos[tid] = (float)cd;
+        s_sin[tid] = (float)sd;
+    }
+    for (int e = tid + nthr; e < ent; e += nthr) {  // only when TPB*half > nthr
         const int tk = e / p.half;
         const int i = e - tk * p.half;
-        const float a = (float)p.pos[t_lo + tk] * inv.v[i];   // f32 angle
+        const float a = (float)p.pos[t0 + tk] * inv.v[i];
         double sd, cd;
         sincos((double)a, &sd, &cd);
         s_cos[e] = (float)cd;
         s_sin[e] = (float)sd;
     }
-    for (int e = (int)tid; e < ntok; e += kBlock) {
-        const int t = t_lo + e;
-        const int64_t ps = p.pos[t];
-        const int64_t sl = p.slot ? (int64_t)p.slot[t] : 0;
+    if (tid < ntok) {
+        const int64_t sl = p.slot ? (int64_t)r_slot : 0;
         int64_t row = -1;
-        if (ps >= 0 && ps < p.n_ctx && sl >= 0 && sl < p.n_slots)
-            row = sl * p.n_ctx + ps;
+        if (r_pos >= 0 && (int64_t)r_pos < p.n_ctx && sl >= 0 && sl < p.n_slots)
+            row = sl * p.n_ctx + r_pos;
         else
             atomicOr(p.err, 1u);
-        s_row[e] = row;
+        s_row[tid] = row;
     }
     __syncthreads();
+    if (!live)
+        return;
 
-    // ---- phase 3: bias, rotate, write back, store cache rows ---------------
+    // ---- bias, rotate, write back, store the cache rows --------------------
+    void *const cache = sec == 1 ? p.cache[0] : p.cache[1];
 #pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-        const int s = sec[u];
-        if (s < 0)
-            continue;
-        const int t = t_lo + tl[u];
+    for (int tt = 0; tt < TPB; ++tt) {
+        if (tt >= ntok)
+            break;
         FVec<W> ra, rb;
 #pragma unroll
         for (int e = 0; e < W; ++e) {
-            ra.e[e] = xa[u].e[e] + ba[u].e[e];
-            rb.e[e] = xb[u].e[e] + bb[u].e[e];
+            ra.e[e] = xa[tt].e[e] + ba.e[e];
+            rb.e[e] = xb[tt].e[e] + bb.e[e];
         }
-        int d1 = W;
-        if (s < 2) {
-            d1 = p.half;
-            const int ci = tl[u] * p.half + i0[u];
+        if (sec < 2) {
+            const int ci = tt * p.half + i0;
             const FVec<W> cs = ld_vec<W>(s_cos + ci);
             const FVec<W> sn = ld_vec<W>(s_sin + ci);
 #pragma unroll
@@ -230,16 +309,14 @@ __global__ __launch_bounds__(kBlock) void qkv_epilogue_kernel(KParams p, InvTabl
                 rb.e[e] = (float)(x0 * sv + x1 * c);
             }
         }
-        float *xp = p.x[s] + (int64_t)t * p.ld[s] + col[u];
-        st_vec<W>(xp, ra);
-        st_vec<W>(xp + d1, rb);
-        if (s > 0) {
-            const int64_t row = s_row[tl[u]];
-            if (row >= 0) {
-                const int64_t off = row * p.nkt + col[u];
-                st_cache<W, F16>(p.cache[s - 1], off, ra);
-                st_cache<W, F16>(p.cache[s - 1], off + d1, rb);
-            }
+        float *xp = xs + (int64_t)(t0 + tt) * ldx;
+        st_data<W, STREAM>(xp, ra);
+        st_data<W, STREAM>(xp + d1, rb);
+        const int64_t row = s_row[tt];
+        if (sec > 0 && row >= 0) {
+            const int64_t off = row * p.nkt + col;
+            st_cache<W, F16, STREAM>(cache, off, ra);
+            st_cache<W, F16, STREAM>(cache, off + d1, rb);
         }
     }
 }
@@ -249,17 +326,54 @@ __global__ __launch_bounds__(kBlock) void qkv_epilogue_kernel(KParams p, InvTabl
 // ---------------------------------------------------------------------------
 
 struct Plan {
-    int W;
-    int U;
-    int UPT;
+    int W;        // vector width: 4 (16-byte slots) or 1 (scalar slots)
+    int U;        // units per token
+    int nthr;     // threads per workgroup (one unit each)
+    int ncb;      // column blocks per token
+    int tb;       // tokens per workgroup (1 or 2)
+    bool stream;  // nontemporal hints on the data
     int64_t grid;
     int lds;
-    int max_tok;
     int half;
     int64_t nqt, nkt;
     int64_t ld[3];
     int64_t n_ctx, n_slots;
 };
+
+int ceil_div(int64_t a, int64_t b)
+{
+    return (int)((a + b - 1) / b);
+}
+
+// Tiling of the (token x unit) space, one unit per thread.  Measured on
+// MI355X (14B shape, 896 units per token):
+//  * thousands of tokens (prefill): 128-thread column blocks, one token per
+//    workgroup, nontemporal data (the launch streams far more than the
+//    caches hold) -- the per-workgroup cos/sin (64 values) rides under the
+//    load latency;
+//  * hundreds of tokens (batched decode): wider blocks holding two tokens, so
+//    fewer, fuller workgroups carry the launch;
+//  * a few tokens (decode): 64-thread blocks spread one token over many
+//    workgroups, default cache policy (the data is cache-resident).
+void choose_tiling(int64_t nt, int U, Plan *pl)
+{
+    if (nt >= 1024) {
+        pl->nthr = 128;
+        pl->tb = 1;
+        pl->stream = true;
+    } else if (nt >= 64) {
+        pl->nthr = ceil_div(ceil_div(U, 2), 64) * 64;
+        if (pl->nthr > kMaxBlock)
+            pl->nthr = kMaxBlock;
+        pl->tb = 2;
+        pl->stream = true;
+    } else {
+        pl->nthr = 64;
+        pl->tb = 1;
+        pl->stream = false;
+    }
+    pl->ncb = ceil_div(U, pl->nthr);
+}
 
 void set_msg(char *msg, size_t len, const char *fmt, ...)
 {
@@ -393,10 +507,12 @@ int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl
     pl->n_slots = n_slots;
     pl->W = 1;
     pl->U = 0;
-    pl->UPT = 1;
+    pl->stream = false;
+    pl->nthr = 64;
+    pl->ncb = 1;
+    pl->tb = 1;
     pl->grid = 0;
     pl->lds = 0;
-    pl->max_tok = 0;
 
     if (a->nt == 0)
         return QKV_OK;
@@ -466,29 +582,20 @@ int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl
     const int W = vec ? 4 : 1;
     const int half = a->head_dim / 2;
     const int64_t U = (int64_t)(a->n_head + a->n_kv_head) * (half / W) + nkt / (2 * W);
-    const int64_t total = U * nt;
-    if (total > (int64_t)INT32_MAX - (int64_t)kBlock * 8) {
-        set_msg(msg, mlen, "launch too large: %lld work units (split the tokens)", (long long)total);
+    if (U > (1 << 28)) {
+        set_msg(msg, mlen, "rows too wide: %lld work units per token", (long long)U);
         return QKV_ERR_INVALID_ARG;
     }
-    // Units per thread: keep >= 1024 workgroups (4 per CU) when possible.
-    int upt = 1;
-    while (upt < 4 && total / ((int64_t)kBlock * upt * 2) >= 1024)
-        upt *= 2;
-    const int64_t span = (int64_t)kBlock * upt;
-    int64_t max_tok = (span + U - 1) / U + 1;
-    if (max_tok > nt)
-        max_tok = nt;
     pl->W = W;
     pl->U = (int)U;
-    pl->UPT = upt;
-    pl->grid = (total + span - 1) / span;
-    pl->max_tok = (int)max_tok;
-    pl->lds = lds_row_bytes((int)max_tok) + (int)(2 * max_tok * half * 4);
-    if (pl->lds > 64 * 1024) {
-        set_msg(msg, mlen, "internal: LDS plan %d bytes too large", pl->lds);
+    choose_tiling(nt, (int)U, pl);
+    const int64_t ntb = (nt + pl->tb - 1) / pl->tb;
+    pl->grid = ntb * pl->ncb;
+    if (pl->grid > INT32_MAX) {
+        set_msg(msg, mlen, "launch too large: %lld workgroups (split the tokens)", (long long)pl->grid);
         return QKV_ERR_INVALID_ARG;
     }
+    pl->lds = lds_row_bytes(pl->tb) + 2 * pl->tb * half * 4;  // tb <= 2: <= 4 KB + 16
     return QKV_OK;
 }
 
@@ -499,23 +606,22 @@ void host_inv_freq(float theta, int head_dim, float *out)
         out[i] = (float)std::pow((double)theta, -(double)(2 * i) / (double)head_dim);
 }
 
-template <int W, bool F16, int UPT>
-hipError_t launch_t(const KParams &kp, const InvTable &inv, int64_t grid, int lds, hipStream_t st)
+template <int W, bool F16, int TPB, bool STREAM>
+hipError_t launch_t(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
 {
-    hipLaunchKernelGGL((qkv_epilogue_kernel<W, F16, UPT>), dim3((unsigned)grid), dim3(kBlock),
-                       (unsigned)lds, st, kp, inv);
+    hipLaunchKernelGGL((qkv_epilogue_kernel<W, F16, TPB, STREAM>), dim3((unsigned)pl.grid),
+                       dim3((unsigned)pl.nthr), (unsigned)pl.lds, st, kp, inv);
     return hipGetLastError();
 }
 
 template <int W, bool F16>
-hipError_t launch_w(const KParams &kp, const InvTable &inv, int upt, int64_t grid, int lds,
-                    hipStream_t st)
+hipError_t launch_w(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
 {
-    switch (upt) {
-    case 1: return launch_t<W, F16, 1>(kp, inv, grid, lds, st);
-    case 2: return launch_t<W, F16, 2>(kp, inv, grid, lds, st);
-    default: return launch_t<W, F16, 4>(kp, inv, grid, lds, st);
-    }
+    if (pl.tb == 1)
+        return pl.stream ? launch_t<W, F16, 1, true>(kp, inv, pl, st)
+                         : launch_t<W, F16, 1, false>(kp, inv, pl, st);
+    return pl.stream ? launch_t<W, F16, 2, true>(kp, inv, pl, st)
+                     : launch_t<W, F16, 2, false>(kp, inv, pl, st);
 }
 
 }  // namespace
@@ -644,15 +750,17 @@ int qkv_epilogue_run_ex(qkv_epilogue_t *h, const qkv_epilogue_args_t *a)
     kp.n_ctx = pl.n_ctx;
     kp.n_slots = pl.n_slots;
     kp.nkt = pl.nkt;
-    kp.total = (uint32_t)((int64_t)pl.U * a->nt);
     kp.nt = a->nt;
     kp.hd = a->head_dim;
     kp.half = pl.half;
     kp.uph = pl.half / pl.W;
     kp.qu = a->n_head * kp.uph;
     kp.qku = (a->n_head + a->n_kv_head) * kp.uph;
+    kp.vhalf = (int)(pl.nkt / 2);
     kp.U = pl.U;
-    kp.max_tok = pl.max_tok;
+    kp.cbu = pl.nthr;
+    kp.ncb = pl.ncb;
+    kp.tb = pl.tb;
 
     hipStream_t st = (a->stream || a->use_stream) ? static_cast<hipStream_t>(a->stream) : h->stream;
     DeviceGuard g;
@@ -661,11 +769,9 @@ int qkv_epilogue_run_ex(qkv_epilogue_t *h, const qkv_epilogue_args_t *a)
         return fail(h, QKV_ERR_HIP, "hipSetDevice(%d): %s", h->device, hipGetErrorString(e));
     const bool f16 = a->cache_dtype == QKV_CACHE_F16;
     if (pl.W == 4)
-        e = f16 ? launch_w<4, true>(kp, h->inv, pl.UPT, pl.grid, pl.lds, st)
-                : launch_w<4, false>(kp, h->inv, pl.UPT, pl.grid, pl.lds, st);
+        e = f16 ? launch_w<4, true>(kp, h->inv, pl, st) : launch_w<4, false>(kp, h->inv, pl, st);
     else
-        e = f16 ? launch_w<1, true>(kp, h->inv, pl.UPT, pl.grid, pl.lds, st)
-                : launch_w<1, false>(kp, h->inv, pl.UPT, pl.grid, pl.lds, st);
+        e = f16 ? launch_w<1, true>(kp, h->inv, pl, st) : launch_w<1, false>(kp, h->inv, pl, st);
     if (e != hipSuccess)
         return fail(h, QKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     h->last_stream = st;
@@ -760,8 +866,10 @@ int qkv_epilogue_plan(const qkv_epilogue_args_t *a, qkv_epilogue_plan_t *plan)
     if (plan) {
         plan->vec_width = pl.W;
         plan->units_per_token = pl.U;
-        plan->units_per_thread = pl.UPT;
-        plan->block = kBlock;
+        plan->units_per_thread = 1;
+        plan->block = pl.nthr;
+        plan->col_blocks = pl.ncb;
+        plan->tokens_per_block = pl.tb;
         plan->grid = pl.grid;
         plan->lds_bytes = pl.lds;
     }

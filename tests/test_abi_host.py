@@ -196,11 +196,15 @@ def test_plan_vector_path_and_units():
     p = plan_of(base_args(nt=4096))
     assert p.vec_width == 4
     assert p.units_per_token == (40 + 8) * 16 + 1024 // 8   # 896
-    assert p.block == 256
-    span = p.block * p.units_per_thread
-    assert p.grid == -(-4096 * 896 // span)
+    assert p.block % 64 == 0 and p.block <= 1024
+    # the column blocks of a token cover its units
+    assert p.col_blocks * p.block * p.units_per_thread >= 896
+    assert (p.col_blocks - 1) * p.block * p.units_per_thread < 896
+    assert p.grid == p.col_blocks * -(-4096 // p.tokens_per_block)
     p = plan_of(base_args(nt=256))
     assert p.vec_width == 4 and p.grid >= 256
+    p = plan_of(base_args(nt=1))
+    assert p.tokens_per_block == 1 and p.grid == p.col_blocks >= 4
 
 
 def test_plan_scalar_path_for_misaligned_or_small_heads():

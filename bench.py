@@ -51,8 +51,11 @@ def algo_bytes(w, nt, cache_bytes, slot=False):
 
 
 def kernel_source_hash():
-    p = os.path.join(ROOT, "qkv_bias_rope_amd", "csrc", "qkv_epilogue.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Hash of the fused kernel's sources (its file and the shared internals)."""
+    h = hashlib.sha256()
+    for f in ("qkv_epilogue.hip", "qkv_internal.h"):
+        h.update(open(os.path.join(ROOT, "qkv_bias_rope_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(workload):
@@ -122,30 +125,31 @@ class Sets:
                            nt=self.nt)
 
 
-def time_launches(h, arg_list, steps, warmup, stream, settle_s=0.3):
+def time_launches(h, arg_list, steps, warmup, stream, settle_s=0.3, fn=None):
     """Mean time per launch (ms) over `steps` launches cycling through
     arg_list, HIP events recorded on the launch stream.  Before the `warmup`
     untimed launches, the same launches run untimed for about settle_s
     seconds so the GPU clocks have ramped up when timing starts."""
     import torch
     from qkv_bias_rope_amd import binding as B
+    run = fn or B.qkv_epilogue_run_ex
     t_end = time.perf_counter() + settle_s
     i = 0
     while time.perf_counter() < t_end:
         for _ in range(len(arg_list)):
-            rc = B.qkv_epilogue_run_ex(h, arg_list[i % len(arg_list)])
+            rc = run(h, arg_list[i % len(arg_list)])
             assert rc == 0, B.qkv_epilogue_last_error(h)
             i += 1
         torch.cuda.synchronize()
     for i in range(warmup):
-        rc = B.qkv_epilogue_run_ex(h, arg_list[i % len(arg_list)])
+        rc = run(h, arg_list[i % len(arg_list)])
         assert rc == 0, B.qkv_epilogue_last_error(h)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(steps):
-        B.qkv_epilogue_run_ex(h, arg_list[i % len(arg_list)])
+        run(h, arg_list[i % len(arg_list)])
     e1.record(stream)
     e1.synchronize()
     torch.cuda.synchronize()
@@ -153,7 +157,8 @@ def time_launches(h, arg_list, steps, warmup, stream, settle_s=0.3):
     return e0.elapsed_time(e1) / steps
 
 
-def bench_bandwidth(h, w, cache_dtype, steps, warmup, stream, min_set_bytes=1.5e9, slot=False):
+def bench_bandwidth(h, w, cache_dtype, steps, warmup, stream, min_set_bytes=1.5e9, slot=False,
+                    fn=None):
     from qkv_bias_rope_amd import workloads as wl
     cb = 2 if cache_dtype == wl.CACHE_F16 else 4
     nbytes = algo_bytes(w, w.nt, cb, slot=slot)
@@ -164,13 +169,14 @@ def bench_bandwidth(h, w, cache_dtype, steps, warmup, stream, min_set_bytes=1.5e
     share = w.n_slots > 1
     sets = Sets(w, R, cache_dtype, share_cache=share)
     args = [sets.args(r, stream) for r in range(R)]
-    ms = time_launches(h, args, steps, warmup, stream)
+    ms = time_launches(h, args, steps, warmup, stream, fn=fn)
     return dict(ms=ms, bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9, sets=R), sets
 
 
-def bench_decode(h, w, steps, warmup, stream):
-    """One decode step = one launch per layer.  Returns microseconds per layer
-    for a plain stream loop and for a HIP-graph replay of the whole step."""
+def bench_decode(h, w, steps, warmup, stream, unfused=False):
+    """One decode step = one fused launch per layer (or, with unfused=True, the
+    seven-launch unfused chain per layer).  Returns microseconds per layer for a
+    plain stream loop and for a HIP-graph replay of the whole step."""
     import torch
     from qkv_bias_rope_amd import binding as B
     from qkv_bias_rope_amd import workloads as wl
@@ -186,15 +192,17 @@ def bench_decode(h, w, steps, warmup, stream):
             s.buf = buf
         layers.append(s)
     args = [s.args(0, stream) for s in layers]
+    run = B.qkv_epilogue_run_unfused if unfused else B.qkv_epilogue_run_ex
     n_loops = max(1, steps)
     # stream loop
-    ms_step = time_launches(h, args, n_loops * w.layers, warmup * w.layers, stream) * w.layers
+    ms_step = time_launches(h, args, n_loops * w.layers, warmup * w.layers, stream,
+                            fn=run) * w.layers
     # graph replay of one step
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         for a in args:
             a.stream = torch.cuda.current_stream().cuda_stream
-            assert B.qkv_epilogue_run_ex(h, a) == 0
+            assert run(h, a) == 0
     t_end = time.perf_counter() + 0.2
     while time.perf_counter() < t_end:
         g.replay()
@@ -215,6 +223,7 @@ def bench_decode(h, w, steps, warmup, stream):
     cb = 2 if w.cache_dtypes[0] == wl.CACHE_F16 else 4
     return dict(us_per_layer_stream=ms_step * 1e3 / w.layers,
                 us_per_layer_graph=ms_graph * 1e3 / w.layers,
+                launches_per_layer=7 if unfused else 1,
                 bytes_per_layer=algo_bytes(w, 1, cb), layers=w.layers)
 
 
@@ -304,6 +313,7 @@ def main():
 
 def run_all(args, h, stream):
     import torch
+    from qkv_bias_rope_amd import binding as B
     from qkv_bias_rope_amd import workloads as wl
 
     w = wl.PREFILL_14B
@@ -334,6 +344,25 @@ def run_all(args, h, stream):
             log(f"[bench]   {r['us_per_layer_stream']:.2f} us/layer (stream), "
                 f"{r['us_per_layer_graph']:.2f} us/layer (graph)")
             torch.cuda.empty_cache()
+        # same-binary A/B of the fusion: the unfused seven-launch chain
+        wd = wl.DECODE_14B
+        log(f"[bench] {wd.name} unfused chain")
+        r = bench_decode(h, wd, max(10, args.steps // 10), max(2, args.warmup // 10), stream,
+                         unfused=True)
+        extra[wd.name + "_unfused"] = {k: (round(v, 3) if isinstance(v, float) else v)
+                                       for k, v in r.items()}
+        log(f"[bench]   {r['us_per_layer_stream']:.2f} us/layer (stream), "
+            f"{r['us_per_layer_graph']:.2f} us/layer (graph)")
+        torch.cuda.empty_cache()
+        log(f"[bench] {w.name} unfused chain")
+        r, sets = bench_bandwidth(h, w, wl.CACHE_F16, max(20, args.steps // 4),
+                                  max(2, args.warmup // 4), stream, fn=B.qkv_epilogue_run_unfused)
+        del sets
+        torch.cuda.empty_cache()
+        extra[w.name + "_unfused"] = dict(gbs=round(r["gbs"], 1),
+                                          us_per_launch_chain=round(r["ms"] * 1e3, 3),
+                                          launches=7)
+        log(f"[bench]   {r['ms'] * 1e3:.2f} us per 7-launch chain, {r['gbs']:.1f} GB/s")
 
     cpu = None
     if not args.no_cpu:

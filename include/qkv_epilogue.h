@@ -163,6 +163,18 @@ typedef struct qkv_epilogue_args {
 int qkv_epilogue_run_ex(qkv_epilogue_t *h, const qkv_epilogue_args_t *a);
 
 /*
+ * The same operation as qkv_epilogue_run_ex, computed by the UNFUSED chain the
+ * fused kernel replaces: three bias-add launches (q, k, v), two rope launches
+ * (q, k) and two store launches (K, V), seven kernels in that order (page "73 ·
+ * D3-8 — G4 FusedQKV ported to CUDA", §1-§2: add_bias x3 + rope x2 +
+ * store_kv x2 per layer).  Same arguments, validation, errors and numerics as
+ * qkv_epilogue_run_ex (the rope launches evaluate cos/sin per pair instead of
+ * once per token); results are bit-identical to the fused kernel.  For
+ * same-binary A/B measurements of the fusion.
+ */
+int qkv_epilogue_run_unfused(qkv_epilogue_t *h, const qkv_epilogue_args_t *a);
+
+/*
  * Blocking: synchronize the stream of the handle's last launch, read and
  * clear the device error word.  Returns QKV_ERR_POSITION_RANGE if any token
  * launched since the last status call had pos outside [0, n_ctx) or slot

@@ -36,6 +36,7 @@ QKV_ROPE_INTERLEAVED = 1
 QKV_MAX_HEAD_DIM = 512
 
 EXPORTS = ("qkv_epilogue_create", "qkv_epilogue_run", "qkv_epilogue_run_ex",
+           "qkv_epilogue_run_unfused",
            "qkv_epilogue_status", "qkv_epilogue_last_error", "qkv_epilogue_destroy",
            "qkv_epilogue_inv_freq", "qkv_epilogue_check_args", "qkv_epilogue_plan")
 
@@ -88,6 +89,8 @@ def _load():
     lib.qkv_epilogue_run.restype = _I
     lib.qkv_epilogue_run_ex.argtypes = [_P, ctypes.POINTER(QkvEpilogueArgs)]
     lib.qkv_epilogue_run_ex.restype = _I
+    lib.qkv_epilogue_run_unfused.argtypes = [_P, ctypes.POINTER(QkvEpilogueArgs)]
+    lib.qkv_epilogue_run_unfused.restype = _I
     lib.qkv_epilogue_status.argtypes = [_P]
     lib.qkv_epilogue_status.restype = _I
     lib.qkv_epilogue_last_error.argtypes = [_P]
@@ -136,6 +139,10 @@ def qkv_epilogue_run(h, q, k, v, bq, bk, bv, pos, kcache, vcache, nt, n_head, n_
 
 def qkv_epilogue_run_ex(h, args: QkvEpilogueArgs) -> int:
     return lib.qkv_epilogue_run_ex(h, ctypes.byref(args))
+
+
+def qkv_epilogue_run_unfused(h, args: QkvEpilogueArgs) -> int:
+    return lib.qkv_epilogue_run_unfused(h, ctypes.byref(args))
 
 
 def qkv_epilogue_status(h) -> int:

@@ -1,4 +1,4 @@
-"""Compile the HIP library in-tree: csrc/qkv_epilogue.hip -> libqkv_epilogue.so.
+"""Compile the HIP library in-tree: csrc/*.hip -> libqkv_epilogue.so.
 
 hipcc cross-compiles for gfx950 without a GPU.  Flags: -O3, no fast-math
 (denormals and IEEE rounding stay as HIP's defaults), packed FP32 ops off.
@@ -11,8 +11,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "qkv_epilogue.hip")
-HDR = os.path.join(ROOT, "include", "qkv_epilogue.h")
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("qkv_epilogue.hip", "qkv_unfused.hip")]
+HDRS = [os.path.join(ROOT, "include", "qkv_epilogue.h"), os.path.join(PKG, "csrc", "qkv_internal.h")]
 LIB = os.path.join(PKG, "libqkv_epilogue.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -26,7 +26,7 @@ FLAGS = [
 def build(verbose: bool = False) -> str:
     """Always recompile (the build check must compile), atomically replace."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), SRC, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *SRCS, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
@@ -42,7 +42,7 @@ def is_stale() -> bool:
     if not os.path.exists(LIB):
         return True
     t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(p) > t for p in (SRC, HDR))
+    return any(os.path.getmtime(p) > t for p in (*SRCS, *HDRS))
 
 
 if __name__ == "__main__":

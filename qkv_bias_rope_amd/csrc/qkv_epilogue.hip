@@ -53,17 +53,11 @@
 #include <cstring>
 #include <new>
 
-#include "qkv_epilogue.h"
+#include "qkv_internal.h"
+
+using namespace qkv_detail;
 
 namespace {
-
-constexpr int kMaxHalf = QKV_MAX_HEAD_DIM / 2;
-constexpr int kMaxBlock = 1024;
-
-// Inverse-frequency table passed by value in the kernel arguments.
-struct InvTable {
-    float v[kMaxHalf];
-};
 
 struct KParams {
     float *x[3];          // q, k, v section bases
@@ -88,91 +82,6 @@ struct KParams {
     int ncb;              // column blocks per token
     int tb;               // tokens per token block
 };
-
-template <int W>
-struct alignas(4 * W) FVec {
-    float e[W];
-};
-
-template <int W>
-struct alignas(2 * W) HVec {
-    _Float16 e[W];
-};
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-
-// Plain load (biases, LDS).
-template <int W>
-__device__ __forceinline__ FVec<W> ld_vec(const float *p)
-{
-    return *reinterpret_cast<const FVec<W> *>(p);
-}
-
-// Load / store of q, k, v and the cache rows.  With STREAM (large launches,
-// whose data is touched once and far exceeds the caches) they carry the
-// nontemporal hint; small launches (decode) keep the default policy so data
-// the producer just wrote, or the consumer reads next, stays cached.
-template <int W, bool STREAM>
-__device__ __forceinline__ FVec<W> ld_data(const float *p)
-{
-    if constexpr (!STREAM) {
-        return ld_vec<W>(p);
-    } else {
-        FVec<W> r;
-        if constexpr (W == 4) {
-            const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
-            r.e[0] = v.x;
-            r.e[1] = v.y;
-            r.e[2] = v.z;
-            r.e[3] = v.w;
-        } else {
-            r.e[0] = __builtin_nontemporal_load(p);
-        }
-        return r;
-    }
-}
-
-template <int W, bool STREAM>
-__device__ __forceinline__ void st_data(float *p, const FVec<W> &v)
-{
-    if constexpr (!STREAM) {
-        *reinterpret_cast<FVec<W> *>(p) = v;
-    } else if constexpr (W == 4) {
-        const f32x4 x = {v.e[0], v.e[1], v.e[2], v.e[3]};
-        __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(p));
-    } else {
-        __builtin_nontemporal_store(v.e[0], p);
-    }
-}
-
-template <int W, bool F16, bool STREAM>
-__device__ __forceinline__ void st_cache(void *cache, int64_t off, const FVec<W> &v)
-{
-    if constexpr (F16) {
-        HVec<W> h;
-#pragma unroll
-        for (int e = 0; e < W; ++e)
-            h.e[e] = static_cast<_Float16>(v.e[e]);  // v_cvt_f16_f32: RNE
-        _Float16 *dst = static_cast<_Float16 *>(cache) + off;
-        if constexpr (!STREAM) {
-            *reinterpret_cast<HVec<W> *>(dst) = h;
-        } else if constexpr (W == 4) {
-            const f16x4 x = {h.e[0], h.e[1], h.e[2], h.e[3]};
-            __builtin_nontemporal_store(x, reinterpret_cast<f16x4 *>(dst));
-        } else {
-            __builtin_nontemporal_store(h.e[0], dst);
-        }
-    } else {
-        st_data<W, STREAM>(static_cast<float *>(cache) + off, v);
-    }
-}
-
-// LDS layout: int64 row[tb] | float cos[tb*half] | float sin[tb*half]
-__host__ __device__ inline int lds_row_bytes(int tb)
-{
-    return ((tb * 8) + 15) & ~15;
-}
 
 // Unit r of a token (0 <= r < U): section, column of the first slot, first
 // pair index (rope units) and distance from the first slot to the second.
@@ -321,24 +230,27 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
     }
 }
 
-// ---------------------------------------------------------------------------
-// host side
-// ---------------------------------------------------------------------------
+template <int W, bool F16, int TPB, bool STREAM>
+hipError_t launch_t(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
+{
+    hipLaunchKernelGGL((qkv_epilogue_kernel<W, F16, TPB, STREAM>), dim3((unsigned)pl.grid),
+                       dim3((unsigned)pl.nthr), (unsigned)pl.lds, st, kp, inv);
+    return hipGetLastError();
+}
 
-struct Plan {
-    int W;        // vector width: 4 (16-byte slots) or 1 (scalar slots)
-    int U;        // units per token
-    int nthr;     // threads per workgroup (one unit each)
-    int ncb;      // column blocks per token
-    int tb;       // tokens per workgroup (1 or 2)
-    bool stream;  // nontemporal hints on the data
-    int64_t grid;
-    int lds;
-    int half;
-    int64_t nqt, nkt;
-    int64_t ld[3];
-    int64_t n_ctx, n_slots;
-};
+template <int W, bool F16>
+hipError_t launch_w(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
+{
+    if (pl.tb == 1)
+        return pl.stream ? launch_t<W, F16, 1, true>(kp, inv, pl, st)
+                         : launch_t<W, F16, 1, false>(kp, inv, pl, st);
+    return pl.stream ? launch_t<W, F16, 2, true>(kp, inv, pl, st)
+                     : launch_t<W, F16, 2, false>(kp, inv, pl, st);
+}
+
+}  // namespace
+
+namespace qkv_detail {
 
 int ceil_div(int64_t a, int64_t b)
 {
@@ -606,40 +518,6 @@ void host_inv_freq(float theta, int head_dim, float *out)
         out[i] = (float)std::pow((double)theta, -(double)(2 * i) / (double)head_dim);
 }
 
-template <int W, bool F16, int TPB, bool STREAM>
-hipError_t launch_t(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
-{
-    hipLaunchKernelGGL((qkv_epilogue_kernel<W, F16, TPB, STREAM>), dim3((unsigned)pl.grid),
-                       dim3((unsigned)pl.nthr), (unsigned)pl.lds, st, kp, inv);
-    return hipGetLastError();
-}
-
-template <int W, bool F16>
-hipError_t launch_w(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
-{
-    if (pl.tb == 1)
-        return pl.stream ? launch_t<W, F16, 1, true>(kp, inv, pl, st)
-                         : launch_t<W, F16, 1, false>(kp, inv, pl, st);
-    return pl.stream ? launch_t<W, F16, 2, true>(kp, inv, pl, st)
-                     : launch_t<W, F16, 2, false>(kp, inv, pl, st);
-}
-
-}  // namespace
-
-struct qkv_epilogue {
-    int device;
-    int64_t n_ctx;
-    hipStream_t stream;
-    hipStream_t last_stream;
-    unsigned int *d_err;
-    float inv_theta;
-    int inv_hd;
-    InvTable inv;
-    char msg[512];
-};
-
-namespace {
-
 int fail(qkv_epilogue *h, int code, const char *fmt, ...)
 {
     if (h) {
@@ -651,28 +529,17 @@ int fail(qkv_epilogue *h, int code, const char *fmt, ...)
     return code;
 }
 
-struct DeviceGuard {
-    int prev = -1;
-    bool changed = false;
-    hipError_t set(int dev)
-    {
-        hipError_t e = hipGetDevice(&prev);
-        if (e != hipSuccess)
-            return e;
-        if (prev != dev) {
-            changed = true;
-            return hipSetDevice(dev);
-        }
-        return hipSuccess;
+const InvTable &handle_inv(qkv_epilogue *h, float theta, int head_dim)
+{
+    if (h->inv_hd != head_dim || h->inv_theta != theta) {
+        host_inv_freq(theta, head_dim, h->inv.v);
+        h->inv_hd = head_dim;
+        h->inv_theta = theta;
     }
-    ~DeviceGuard()
-    {
-        if (changed)
-            (void)hipSetDevice(prev);
-    }
-};
+    return h->inv;
+}
 
-}  // namespace
+}  // namespace qkv_detail
 
 extern "C" {
 
@@ -726,11 +593,7 @@ int qkv_epilogue_run_ex(qkv_epilogue_t *h, const qkv_epilogue_args_t *a)
     if (a->nt == 0)
         return QKV_OK;
 
-    if (h->inv_hd != a->head_dim || h->inv_theta != a->theta) {
-        host_inv_freq(a->theta, a->head_dim, h->inv.v);
-        h->inv_hd = a->head_dim;
-        h->inv_theta = a->theta;
-    }
+    const InvTable &inv = handle_inv(h, a->theta, a->head_dim);
 
     KParams kp;
     kp.x[0] = a->q;
@@ -769,9 +632,9 @@ int qkv_epilogue_run_ex(qkv_epilogue_t *h, const qkv_epilogue_args_t *a)
         return fail(h, QKV_ERR_HIP, "hipSetDevice(%d): %s", h->device, hipGetErrorString(e));
     const bool f16 = a->cache_dtype == QKV_CACHE_F16;
     if (pl.W == 4)
-        e = f16 ? launch_w<4, true>(kp, h->inv, pl, st) : launch_w<4, false>(kp, h->inv, pl, st);
+        e = f16 ? launch_w<4, true>(kp, inv, pl, st) : launch_w<4, false>(kp, inv, pl, st);
     else
-        e = f16 ? launch_w<1, true>(kp, h->inv, pl, st) : launch_w<1, false>(kp, h->inv, pl, st);
+        e = f16 ? launch_w<1, true>(kp, inv, pl, st) : launch_w<1, false>(kp, inv, pl, st);
     if (e != hipSuccess)
         return fail(h, QKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     h->last_stream = st;

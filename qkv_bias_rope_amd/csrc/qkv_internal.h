@@ -1,0 +1,181 @@
+// qkv_internal.h -- internals shared by the translation units of
+// libqkv_epilogue.so (fused kernel, unfused chain): vector slot types, the
+// load/store policies, argument validation and planning, the handle.
+// Not part of the public interface (that is include/qkv_epilogue.h).
+#ifndef QKV_INTERNAL_H
+#define QKV_INTERNAL_H
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "qkv_epilogue.h"
+
+namespace qkv_detail {
+
+constexpr int kMaxHalf = QKV_MAX_HEAD_DIM / 2;
+constexpr int kMaxBlock = 1024;
+
+// Inverse-frequency table passed by value in the kernel arguments.
+struct InvTable {
+    float v[kMaxHalf];
+};
+
+template <int W>
+struct alignas(4 * W) FVec {
+    float e[W];
+};
+
+template <int W>
+struct alignas(2 * W) HVec {
+    _Float16 e[W];
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Plain load (biases, LDS).
+template <int W>
+__device__ __forceinline__ FVec<W> ld_vec(const float *p)
+{
+    return *reinterpret_cast<const FVec<W> *>(p);
+}
+
+// Load / store of q, k, v and the cache rows.  With STREAM (large launches,
+// whose data is touched once and far exceeds the caches) they carry the
+// nontemporal hint; small launches (decode) keep the default policy so data
+// the producer just wrote, or the consumer reads next, stays cached.
+template <int W, bool STREAM>
+__device__ __forceinline__ FVec<W> ld_data(const float *p)
+{
+    if constexpr (!STREAM) {
+        return ld_vec<W>(p);
+    } else {
+        FVec<W> r;
+        if constexpr (W == 4) {
+            const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+            r.e[0] = v.x;
+            r.e[1] = v.y;
+            r.e[2] = v.z;
+            r.e[3] = v.w;
+        } else {
+            r.e[0] = __builtin_nontemporal_load(p);
+        }
+        return r;
+    }
+}
+
+template <int W, bool STREAM>
+__device__ __forceinline__ void st_data(float *p, const FVec<W> &v)
+{
+    if constexpr (!STREAM) {
+        *reinterpret_cast<FVec<W> *>(p) = v;
+    } else if constexpr (W == 4) {
+        const f32x4 x = {v.e[0], v.e[1], v.e[2], v.e[3]};
+        __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(p));
+    } else {
+        __builtin_nontemporal_store(v.e[0], p);
+    }
+}
+
+template <int W, bool F16, bool STREAM>
+__device__ __forceinline__ void st_cache(void *cache, int64_t off, const FVec<W> &v)
+{
+    if constexpr (F16) {
+        HVec<W> h;
+#pragma unroll
+        for (int e = 0; e < W; ++e)
+            h.e[e] = static_cast<_Float16>(v.e[e]);  // v_cvt_f16_f32: RNE
+        _Float16 *dst = static_cast<_Float16 *>(cache) + off;
+        if constexpr (!STREAM) {
+            *reinterpret_cast<HVec<W> *>(dst) = h;
+        } else if constexpr (W == 4) {
+            const f16x4 x = {h.e[0], h.e[1], h.e[2], h.e[3]};
+            __builtin_nontemporal_store(x, reinterpret_cast<f16x4 *>(dst));
+        } else {
+            __builtin_nontemporal_store(h.e[0], dst);
+        }
+    } else {
+        st_data<W, STREAM>(static_cast<float *>(cache) + off, v);
+    }
+}
+
+// LDS layout: int64 row[tb] | float cos[tb*half] | float sin[tb*half]
+__host__ __device__ inline int lds_row_bytes(int tb)
+{
+    return ((tb * 8) + 15) & ~15;
+}
+
+struct Plan {
+    int W;        // vector width: 4 (16-byte slots) or 1 (scalar slots)
+    int U;        // units per token
+    int nthr;     // threads per workgroup (one unit each)
+    int ncb;      // column blocks per token
+    int tb;       // tokens per workgroup (1 or 2)
+    bool stream;  // nontemporal hints on the data
+    int64_t grid;
+    int lds;
+    int half;
+    int64_t nqt, nkt;
+    int64_t ld[3];
+    int64_t n_ctx, n_slots;
+};
+
+int ceil_div(int64_t a, int64_t b);
+void set_msg(char *msg, size_t len, const char *fmt, ...);
+
+// Validate a request (the checks run_ex documents) and plan the fused launch.
+int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl, char *msg,
+                   size_t mlen);
+
+// inv[i] = f32(theta^(-2i/head_dim)), computed in double and rounded once.
+void host_inv_freq(float theta, int head_dim, float *out);
+
+struct DeviceGuard {
+    int prev = -1;
+    bool changed = false;
+    hipError_t set(int dev)
+    {
+        hipError_t e = hipGetDevice(&prev);
+        if (e != hipSuccess)
+            return e;
+        if (prev != dev) {
+            changed = true;
+            return hipSetDevice(dev);
+        }
+        return hipSuccess;
+    }
+    ~DeviceGuard()
+    {
+        if (changed)
+            (void)hipSetDevice(prev);
+    }
+};
+
+
+}  // namespace qkv_detail
+
+struct qkv_epilogue {
+    int device;
+    int64_t n_ctx;
+    hipStream_t stream;
+    hipStream_t last_stream;
+    unsigned int *d_err;
+    float inv_theta;
+    int inv_hd;
+    qkv_detail::InvTable inv;
+    char msg[512];
+};
+
+namespace qkv_detail {
+
+int fail(qkv_epilogue *h, int code, const char *fmt, ...);
+
+// The handle's table for (theta, head_dim), recomputed only when they change.
+const InvTable &handle_inv(qkv_epilogue *h, float theta, int head_dim);
+
+}  // namespace qkv_detail
+
+#endif  // QKV_INTERNAL_H

@@ -66,6 +66,18 @@ def changed_rows(cache, cd, chunk_rows=1 << 16):
     return np.concatenate(out) if out else np.zeros(0, np.int64)
 
 
+def tensors_bitwise_equal(a, b, chunk=1 << 28):
+    """Byte equality of two same-shaped device tensors, chunked on the device."""
+    ia = a.reshape(-1).view(torch.uint8)
+    ib = b.reshape(-1).view(torch.uint8)
+    if ia.numel() != ib.numel():
+        return False
+    for i in range(0, ia.numel(), chunk):
+        if not torch.equal(ia[i:i + chunk], ib[i:i + chunk]):
+            return False
+    return True
+
+
 def qk_close(got, want):
     got = got.astype(np.float64)
     want = want.astype(np.float64)
@@ -154,14 +166,18 @@ class Case:
                                     self.g_bv, self.g_pos, self.kc, self.vc, self.nt, w.n_head,
                                     w.n_kv_head, w.head_dim, w.theta, self.cd)
         else:
-            a = B.make_args(self.g_q, self.g_k, self.g_v, self.g_bq, self.g_bk, self.g_bv,
-                            self.g_pos, self.kc, self.vc, n_head=w.n_head, n_kv_head=w.n_kv_head,
-                            head_dim=w.head_dim, theta=w.theta, cache_dtype=self.cd,
-                            slot=self.g_slot, n_ctx=self.n_ctx, n_slots=self.n_slots,
-                            stream=stream if stream is not None else torch.cuda.current_stream(),
-                            use_stream=True, nt=self.nt)
-            rc = B.qkv_epilogue_run_ex(h, a)
+            a = self.args(stream)
+            rc = (B.qkv_epilogue_run_unfused if entry == "unfused" else B.qkv_epilogue_run_ex)(h, a)
         return rc
+
+    def args(self, stream=None):
+        w = self.w
+        return B.make_args(self.g_q, self.g_k, self.g_v, self.g_bq, self.g_bk, self.g_bv,
+                           self.g_pos, self.kc, self.vc, n_head=w.n_head, n_kv_head=w.n_kv_head,
+                           head_dim=w.head_dim, theta=w.theta, cache_dtype=self.cd,
+                           slot=self.g_slot, n_ctx=self.n_ctx, n_slots=self.n_slots,
+                           stream=stream if stream is not None else torch.cuda.current_stream(),
+                           use_stream=True, nt=self.nt)
 
     def download(self):
         self.r_q = self.g_q.cpu().numpy().reshape(self.nt, -1)

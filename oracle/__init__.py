@@ -40,30 +40,53 @@ def build(force: bool = False) -> str:
 _lib = None
 
 
+def _bind(lib):
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I = ctypes.c_int
+    F = ctypes.c_float
+    lib.oracle_add_bias.argtypes = [P, P, I64, I64, I64]
+    lib.oracle_add_bias.restype = None
+    lib.oracle_inv_freq.argtypes = [F, I, P]
+    lib.oracle_inv_freq.restype = None
+    lib.oracle_rope_neox.argtypes = [P, I64, I64, I, I, P, P]
+    lib.oracle_rope_neox.restype = None
+    lib.oracle_f32_to_f16.argtypes = [F]
+    lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+    lib.oracle_store_rows.argtypes = [P, I64, I64, I64, P, P, I64, I64, I, P, P]
+    lib.oracle_store_rows.restype = I64
+    lib.oracle_scatter_rows.argtypes = [P, I64, I64, I, I64, P, P]
+    lib.oracle_scatter_rows.restype = None
+    lib.oracle_qkv_epilogue.argtypes = [
+        P, P, P, I64, I64, I64, P, P, P, P, P, I64, I, I, I, F, I64, I64, I, P, P, P]
+    lib.oracle_qkv_epilogue.restype = I64
+    return lib
+
+
+class using_library:
+    """Context manager: route every oracle call to another build of the C file
+    (used by the tests that plant mistakes in a copy of the oracle)."""
+
+    def __init__(self, path):
+        self.lib = _bind(ctypes.CDLL(path))
+
+    def __enter__(self):
+        global _lib
+        self.saved = _load()
+        _lib = self.lib
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
 def _load():
     global _lib
     if _lib is None:
         build()
-        lib = ctypes.CDLL(_LIB)
-        P = ctypes.c_void_p
-        I64 = ctypes.c_int64
-        I = ctypes.c_int
-        F = ctypes.c_float
-        lib.oracle_add_bias.argtypes = [P, P, I64, I64, I64]
-        lib.oracle_add_bias.restype = None
-        lib.oracle_inv_freq.argtypes = [F, I, P]
-        lib.oracle_inv_freq.restype = None
-        lib.oracle_rope_neox.argtypes = [P, I64, I64, I, I, P, P]
-        lib.oracle_rope_neox.restype = None
-        lib.oracle_f32_to_f16.argtypes = [F]
-        lib.oracle_f32_to_f16.restype = ctypes.c_uint16
-        lib.oracle_store_rows.argtypes = [P, I64, I64, I64, P, P, I64, I64, I, P, P]
-        lib.oracle_store_rows.restype = I64
-        lib.oracle_scatter_rows.argtypes = [P, I64, I64, I, I64, P, P]
-        lib.oracle_scatter_rows.restype = None
-        lib.oracle_qkv_epilogue.argtypes = [
-            P, P, P, I64, I64, I64, P, P, P, P, P, I64, I, I, I, F, I64, I64, I, P, P, P]
-        lib.oracle_qkv_epilogue.restype = I64
+        lib = _bind(ctypes.CDLL(_LIB))
         _lib = lib
     return _lib
 

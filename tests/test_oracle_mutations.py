@@ -1,0 +1,113 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in a copy of oracle/qkv_oracle.c (on the CPU, in a
+temporary directory), builds it with the oracle's flags, routes the oracle's
+Python front end to that build and runs the pins of test_oracle_pins.py.  At
+least one pin must fail for every planted mistake; the pins that caught it are
+listed in the assertion message of a survivor.
+"""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+from qkv_bias_rope_amd import workloads as wl
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "qkv_oracle.c")
+
+# (name, [(old, new), ...]): every `old` must occur exactly once in the source.
+MUTATIONS = [
+    ("drop q bias", [("    oracle_add_bias(q, bq, nt, nqt, ld_q);\n", "")]),
+    ("drop v bias", [("    oracle_add_bias(v, bv, nt, nkt, ld_v);\n", "")]),
+    ("bias subtracted", [("x[t * ld + j] = x[t * ld + j] + b[j];", "x[t * ld + j] = x[t * ld + j] - b[j];")]),
+    ("rotation sign flipped", [("(float)((double)x0 * c - (double)x1 * s)", "(float)((double)x0 * c + (double)x1 * s)")]),
+    ("reverse rotation", [("(float)((double)x0 * c - (double)x1 * s)", "(float)((double)x0 * c + (double)x1 * s)"),
+                          ("(float)((double)x0 * s + (double)x1 * c)", "(float)(-(double)x0 * s + (double)x1 * c)")]),
+    ("cos and sin swapped", [("float c = (float)cos((double)a);", "float c = (float)sin((double)a);"),
+                             ("float s = (float)sin((double)a);", "float s = (float)cos((double)a);")]),
+    ("interleaved pairing", [("float x0 = row[i];", "float x0 = row[2 * i];"),
+                             ("float x1 = row[i + half];", "float x1 = row[2 * i + 1];"),
+                             ("row[i]        = (float)", "row[2 * i]    = (float)"),
+                             ("row[i + half] = (float)", "row[2 * i + 1] = (float)")]),
+    ("exponent 1i/hd", [("-(2.0 * (double)i) / (double)head_dim", "-(1.0 * (double)i) / (double)head_dim")]),
+    ("inverse frequency not inverted", [("-(2.0 * (double)i) / (double)head_dim", "(2.0 * (double)i) / (double)head_dim")]),
+    ("first token's position for all", [("float a = (float)pos[t] * inv[i];", "float a = (float)pos[0] * inv[i];")]),
+    ("position off by one", [("float a = (float)pos[t] * inv[i];", "float a = (float)(pos[t] + 1) * inv[i];")]),
+    ("k not rotated", [("    oracle_rope_neox(k, nt, ld_k, n_kv_head, head_dim, pos, inv);\n", "")]),
+    ("v rotated too", [("    oracle_rope_neox(k, nt, ld_k, n_kv_head, head_dim, pos, inv);\n",
+                        "    oracle_rope_neox(k, nt, ld_k, n_kv_head, head_dim, pos, inv);\n"
+                        "    oracle_rope_neox(v, nt, ld_v, n_kv_head, head_dim, pos, inv);\n")]),
+    ("V row from k", [("    oracle_store_rows(v, nt, ld_v, nkt, pos, slot, n_ctx, n_slots,",
+                       "    oracle_store_rows(k, nt, ld_k, nkt, pos, slot, n_ctx, n_slots,")]),
+    ("f16 truncates", [("    if (rem > 0x1000u || (rem == 0x1000u && (h & 1u)))", "    if (0)")]),
+    ("f16 ties away from zero", [("(rem == 0x1000u && (h & 1u))", "(rem == 0x1000u)")]),
+    ("f16 subnormals flushed", [("if (exp < 102)", "if (exp < 113)")]),
+    ("f16 overflow saturates", [("        return (uint16_t)(sign | 0x7c00u);\n\n    if (e16 <= 0)",
+                                 "        return (uint16_t)(sign | 0x7bffu);\n\n    if (e16 <= 0)")]),
+    ("slot ignored", [("return s * n_ctx + p;", "return p;")]),
+    ("position bound off by one", [("if (p < 0 || p >= n_ctx)", "if (p < 0 || p > n_ctx)")]),
+    ("slot bound missing", [("if (s < 0 || s >= n_slots)", "if (s < 0)")]),
+    ("row stride ignored", [("float *row = x + t * ld + (int64_t)h * head_dim;",
+                             "float *row = x + t * (int64_t)n_heads * head_dim + (int64_t)h * head_dim;")]),
+]
+
+
+def _pin_calls():
+    """Every pin, with fixed parameters, as (name, zero-argument callable)."""
+    return [
+        ("inv_freq decimal 1e6/128", lambda: pins.test_inv_freq_matches_decimal(1.0e6, 128)),
+        ("inv_freq decimal 1e4/64", lambda: pins.test_inv_freq_matches_decimal(1.0e4, 64)),
+        ("inv_freq closed forms", pins.test_inv_freq_closed_forms),
+        ("f16 golden table", pins.test_f16_golden_table),
+        ("f16 vs numpy", pins.test_f16_matches_numpy_over_ranges),
+        ("f16 nan", pins.test_f16_nan_stays_nan),
+        ("hand-worked 1h4d", pins.test_handworked_1h4d),
+        ("pos0 bias only (tiny)", lambda: pins.test_pos0_is_bias_only(wl.TINY_DECODE)),
+        ("pos0 bias only (7B)", lambda: pins.test_pos0_is_bias_only(wl.DECODE_7B)),
+        ("v bias only", pins.test_v_is_bias_only_at_any_position),
+        ("norm preserved", lambda: pins.test_norm_preserved(wl.DECODE_14B)),
+        ("complex multiply", pins.test_matches_complex_multiply_large_angles),
+        ("decimal sin/cos", pins.test_cos_sin_match_decimal_at_large_positions),
+        ("composition", pins.test_rotations_compose_additively),
+        ("store brute force", pins.test_store_bruteforce_tiny),
+        ("store f16 rows", pins.test_store_f16_rows_are_rne_of_outputs),
+        ("slot rows and range", pins.test_slot_rows_and_range_errors),
+        ("tokens independent", pins.test_tokens_are_independent),
+        ("concat equals separate", pins.test_concat_rows_equal_separate_buffers),
+    ]
+
+
+def _build_mutant(edits, workdir):
+    src = open(SRC).read()
+    for old, new in edits:
+        assert src.count(old) == 1, f"mutation anchor not unique or missing: {old!r}"
+        src = src.replace(old, new)
+    c = os.path.join(workdir, "mutant.c")
+    so = os.path.join(workdir, "libmutant.so")
+    open(c, "w").write(src)
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+                           "-shared", "-fPIC", "-o", so, c, "-lm"])
+    return so
+
+
+def test_unmutated_copy_passes_every_pin(tmp_path):
+    so = _build_mutant([], str(tmp_path))
+    with oracle.using_library(so):
+        for name, call in _pin_calls():
+            call()
+
+
+@pytest.mark.parametrize("name,edits", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, edits, tmp_path):
+    so = _build_mutant(edits, str(tmp_path))
+    caught = []
+    with oracle.using_library(so):
+        for pin, call in _pin_calls():
+            try:
+                call()
+            except (AssertionError, ValueError):
+                caught.append(pin)
+    assert caught, f"planted mistake '{name}' survived every pin"

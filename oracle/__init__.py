@@ -60,6 +60,11 @@ def _bind(lib):
     lib.oracle_qkv_epilogue.argtypes = [
         P, P, P, I64, I64, I64, P, P, P, P, P, I64, I, I, I, F, I64, I64, I, P, P, P]
     lib.oracle_qkv_epilogue.restype = I64
+    lib.oracle_rms_norm_heads.argtypes = [P, I64, I64, I, I, P, F]
+    lib.oracle_rms_norm_heads.restype = None
+    lib.oracle_qkv_norm_epilogue.argtypes = [
+        P, P, P, I64, I64, I64, P, P, P, P, P, F, P, P, I64, I, I, I, F, I64, I64, I, P, P, P]
+    lib.oracle_qkv_norm_epilogue.restype = I64
     return lib
 
 
@@ -130,6 +135,15 @@ def rope_neox(x, nt, ld, n_heads, head_dim, pos, inv):
     if nt:
         assert x.size >= (nt - 1) * ld + n_heads * head_dim
     _load().oracle_rope_neox(_ptr(x), nt, ld, n_heads, head_dim, _ptr(pos), _ptr(inv))
+
+
+def rms_norm_heads(x, nt, ld, n_heads, head_dim, w, eps):
+    """Step N (per-head RMS norm) in place on x."""
+    _f32(x, "x"), _f32(w, "w")
+    assert w.size >= head_dim
+    if nt:
+        assert x.size >= (nt - 1) * ld + n_heads * head_dim
+    _load().oracle_rms_norm_heads(_ptr(x), nt, ld, n_heads, head_dim, _ptr(w), eps)
 
 
 def f32_to_f16_bits(values) -> np.ndarray:
@@ -203,6 +217,46 @@ def qkv_epilogue(q, k, v, bq, bk, bv, pos, *, n_head, n_kv_head, head_dim, theta
     bad = _load().oracle_qkv_epilogue(
         base(q, ld_q, nqt, "q"), base(k, ld_k, nkt, "k"), base(v, ld_v, nkt, "v"), ld_q, ld_k, ld_v,
         _ptr(bq), _ptr(bk), _ptr(bv), _ptr(pos), _ptr(slot), nt,
+        n_head, n_kv_head, head_dim, theta, n_ctx, n_slots, cache_dtype,
+        _ptr(row_ids), _ptr(krows), _ptr(vrows))
+    if bad < 0:
+        raise ValueError("oracle: head_dim must be positive and even")
+    return row_ids, krows, vrows, int(bad)
+
+
+def qkv_norm_epilogue(q, k, v, bq, bk, bv, wq, wk, eps, pos, *, n_head, n_kv_head, head_dim,
+                      theta, n_ctx, cache_dtype, slot=None, n_slots=1, ld_q=None, ld_k=None,
+                      ld_v=None):
+    """The q/k-norm variant of the chain (biases may be None).  Same returns as
+    qkv_epilogue."""
+    nt = int(pos.size)
+    nqt = n_head * head_dim
+    nkt = n_kv_head * head_dim
+    ld_q = nqt if ld_q is None else ld_q
+    ld_k = nkt if ld_k is None else ld_k
+    ld_v = nkt if ld_v is None else ld_v
+    for name, a in (("q", q), ("k", k), ("v", v), ("wq", wq), ("wk", wk)):
+        if not (isinstance(a, np.ndarray) and a.dtype == np.float32):
+            raise TypeError(f"{name} must be float32")
+    for name, a in (("bq", bq), ("bk", bk), ("bv", bv)):
+        if a is not None and not (isinstance(a, np.ndarray) and a.dtype == np.float32):
+            raise TypeError(f"{name} must be float32 or None")
+    _i32(pos, "pos")
+    if slot is not None:
+        _i32(slot, "slot")
+    assert wq.size >= head_dim and wk.size >= head_dim
+    row_ids = np.zeros(nt, dtype=np.int64)
+    rdt = np.float32 if cache_dtype == CACHE_F32 else np.uint16
+    krows = np.zeros((nt, nkt), dtype=rdt)
+    vrows = np.zeros((nt, nkt), dtype=rdt)
+    for name, a, ld, width in (("q", q, ld_q, nqt), ("k", k, ld_k, nkt), ("v", v, ld_v, nkt)):
+        if a.ndim != 1 or not a.flags.c_contiguous:
+            raise TypeError(f"{name} must be a 1-D contiguous float32 view")
+        if nt and a.size < (nt - 1) * ld + width:
+            raise ValueError(f"{name} holds {a.size} elements, needs {(nt - 1) * ld + width}")
+    bad = _load().oracle_qkv_norm_epilogue(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, ld_q, ld_k, ld_v,
+        _ptr(bq), _ptr(bk), _ptr(bv), _ptr(wq), _ptr(wk), eps, _ptr(pos), _ptr(slot), nt,
         n_head, n_kv_head, head_dim, theta, n_ctx, n_slots, cache_dtype,
         _ptr(row_ids), _ptr(krows), _ptr(vrows))
     if bad < 0:

@@ -14,6 +14,9 @@
  *   rope on q, then rope on k            (NeoX pairing: element i with i+half)
  *   store K, then store V into the cache (row = position, dst[pos*nkt + j])
  *
+ * and the q/k-norm variant (per-head RMS norm of q and k between the bias add
+ * and the rope, see oracle_rms_norm_heads).
+ *
  * Each step is its own plain loop, in that order, written for a reader to check
  * against the page by eye.  The per-pair cos/sin are recomputed inside the rope
  * loop exactly as the unfused rope kernel does (nothing is hoisted or blocked).
@@ -93,6 +96,31 @@ void oracle_rope_neox(float *x, int64_t nt, int64_t ld, int n_heads,
                 row[i]        = (float)((double)x0 * c - (double)x1 * s);
                 row[i + half] = (float)((double)x0 * s + (double)x1 * c);
             }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Step N -- per-head RMS norm (the q/k norm of the Qwen3-style variant).
+ * Page "06 · Assign + fusion" §3.2 lists a per-head q/k norm op (QkNorm) and
+ * the fused FusedQkvNorm, "the Qwen3 per-head-norm variant", without a
+ * formula.  Reading: over each head's head_dim values,
+ *   y[j] = x[j] / sqrt(mean_j(x[j]^2) + eps) * w[j]
+ * with one [head_dim] weight shared by the heads of the section, evaluated in
+ * double (the squares of f32 values are exact there) and rounded once to f32.
+ * ------------------------------------------------------------------------- */
+void oracle_rms_norm_heads(float *x, int64_t nt, int64_t ld, int n_heads,
+                           int head_dim, const float *w, float eps)
+{
+    for (int64_t t = 0; t < nt; ++t) {
+        for (int h = 0; h < n_heads; ++h) {
+            float *row = x + t * ld + (int64_t)h * head_dim;
+            double ss = 0.0;
+            for (int j = 0; j < head_dim; ++j)
+                ss += (double)row[j] * (double)row[j];
+            double r = 1.0 / sqrt(ss / (double)head_dim + (double)eps);
+            for (int j = 0; j < head_dim; ++j)
+                row[j] = (float)((double)row[j] * r * (double)w[j]);
         }
     }
 }
@@ -228,6 +256,49 @@ int64_t oracle_qkv_epilogue(float *q, float *k, float *v,
     oracle_add_bias(q, bq, nt, nqt, ld_q);
     oracle_add_bias(k, bk, nt, nkt, ld_k);
     oracle_add_bias(v, bv, nt, nkt, ld_v);
+
+    oracle_inv_freq(theta, head_dim, inv);
+    oracle_rope_neox(q, nt, ld_q, n_head, head_dim, pos, inv);
+    oracle_rope_neox(k, nt, ld_k, n_kv_head, head_dim, pos, inv);
+
+    int64_t bad = oracle_store_rows(k, nt, ld_k, nkt, pos, slot, n_ctx,
+                                    n_slots, cache_dtype, row_ids, krows);
+    oracle_store_rows(v, nt, ld_v, nkt, pos, slot, n_ctx, n_slots,
+                      cache_dtype, row_ids, vrows);
+    return bad;
+}
+
+/* ---------------------------------------------------------------------------
+ * The q/k-norm variant of the chain: optional add_bias (NULL bias = none, as
+ * in the Qwen3 attention), per-head RMS norm of q (weight wq) and of k (weight
+ * wk), then rope on q and k, then store K and V.  v is never normalised.
+ * Returns as oracle_qkv_epilogue.
+ * ------------------------------------------------------------------------- */
+int64_t oracle_qkv_norm_epilogue(float *q, float *k, float *v,
+                                 int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                                 const float *bq, const float *bk, const float *bv,
+                                 const float *wq, const float *wk, float eps,
+                                 const int32_t *pos, const int32_t *slot,
+                                 int64_t nt, int n_head, int n_kv_head,
+                                 int head_dim, float theta,
+                                 int64_t n_ctx, int64_t n_slots, int cache_dtype,
+                                 int64_t *row_ids, void *krows, void *vrows)
+{
+    int64_t nqt = (int64_t)n_head * head_dim;
+    int64_t nkt = (int64_t)n_kv_head * head_dim;
+    float inv[4096];
+    if (head_dim <= 0 || head_dim % 2 != 0 || head_dim / 2 > 4096)
+        return -1;
+
+    if (bq)
+        oracle_add_bias(q, bq, nt, nqt, ld_q);
+    if (bk)
+        oracle_add_bias(k, bk, nt, nkt, ld_k);
+    if (bv)
+        oracle_add_bias(v, bv, nt, nkt, ld_v);
+
+    oracle_rms_norm_heads(q, nt, ld_q, n_head, head_dim, wq, eps);
+    oracle_rms_norm_heads(k, nt, ld_k, n_kv_head, head_dim, wk, eps);
 
     oracle_inv_freq(theta, head_dim, inv);
     oracle_rope_neox(q, nt, ld_q, n_head, head_dim, pos, inv);

@@ -106,6 +106,18 @@ def draw_layer(w: Workload, layer: int = 0, nt: int | None = None) -> dict:
     return dict(q=q, k=k, v=v, bq=bq, bk=bk, bv=bv, pos=pos, slot=slot)
 
 
+def draw_norm_weights(w: Workload, layer: int = 0) -> dict:
+    """Per-head q/k norm weights of one layer ([head_dim] each), drawn as
+    1 + 0.1*N(0,1) in float32 from the stream seed*1000 + 500 + layer."""
+    rng = np.random.default_rng(w.seed * 1000 + 500 + layer)
+    wq = (np.float32(1.0) + rng.standard_normal(w.head_dim, dtype=np.float32) * np.float32(0.1))
+    wk = (np.float32(1.0) + rng.standard_normal(w.head_dim, dtype=np.float32) * np.float32(0.1))
+    return dict(wq=wq.astype(np.float32), wk=wk.astype(np.float32))
+
+
+QK_NORM_EPS = 1.0e-6
+
+
 def step_positions(w: Workload, steps: int) -> np.ndarray:
     """Decode positions for `steps` steps (one position per step, shared by all
     layers of that step), uniform in [0, n_ctx)."""

@@ -13,15 +13,19 @@ import tempfile
 import pytest
 
 import oracle
+import test_oracle_norm_pins as npins
 import test_oracle_pins as pins
 from qkv_bias_rope_amd import workloads as wl
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "qkv_oracle.c")
 
-# (name, [(old, new), ...]): every `old` must occur exactly once in the source.
+# (name, [(old, new), ...]): every occurrence of `old` is replaced (the same
+# mistake in both chains where they share a line); each `old` must occur.
 MUTATIONS = [
-    ("drop q bias", [("    oracle_add_bias(q, bq, nt, nqt, ld_q);\n", "")]),
-    ("drop v bias", [("    oracle_add_bias(v, bv, nt, nkt, ld_v);\n", "")]),
+    ("drop q bias", [("\n    oracle_add_bias(q, bq, nt, nqt, ld_q);\n", "\n"),
+                     ("        oracle_add_bias(q, bq, nt, nqt, ld_q);\n", "        ;\n")]),
+    ("drop v bias", [("\n    oracle_add_bias(v, bv, nt, nkt, ld_v);\n", "\n"),
+                     ("        oracle_add_bias(v, bv, nt, nkt, ld_v);\n", "        ;\n")]),
     ("bias subtracted", [("x[t * ld + j] = x[t * ld + j] + b[j];", "x[t * ld + j] = x[t * ld + j] - b[j];")]),
     ("rotation sign flipped", [("(float)((double)x0 * c - (double)x1 * s)", "(float)((double)x0 * c + (double)x1 * s)")]),
     ("reverse rotation", [("(float)((double)x0 * c - (double)x1 * s)", "(float)((double)x0 * c + (double)x1 * s)"),
@@ -50,8 +54,34 @@ MUTATIONS = [
     ("slot ignored", [("return s * n_ctx + p;", "return p;")]),
     ("position bound off by one", [("if (p < 0 || p >= n_ctx)", "if (p < 0 || p > n_ctx)")]),
     ("slot bound missing", [("if (s < 0 || s >= n_slots)", "if (s < 0)")]),
-    ("row stride ignored", [("float *row = x + t * ld + (int64_t)h * head_dim;",
-                             "float *row = x + t * (int64_t)n_heads * head_dim + (int64_t)h * head_dim;")]),
+    ("row stride ignored", [("            float *row = x + t * ld + (int64_t)h * head_dim;\n            for (int i = 0;",
+                             "            float *row = x + t * (int64_t)n_heads * head_dim + (int64_t)h * head_dim;\n            for (int i = 0;")]),
+    # q/k-norm variant
+    ("norm eps dropped", [("sqrt(ss / (double)head_dim + (double)eps)", "sqrt(ss / (double)head_dim)")]),
+    ("norm mean over hd-1", [("sqrt(ss / (double)head_dim + (double)eps)", "sqrt(ss / (double)(head_dim - 1) + (double)eps)")]),
+    ("norm without square root", [("1.0 / sqrt(ss / (double)head_dim + (double)eps)", "1.0 / (ss / (double)head_dim + (double)eps)")]),
+    ("norm weight dropped", [("row[j] = (float)((double)row[j] * r * (double)w[j]);", "row[j] = (float)((double)row[j] * r);")]),
+    ("norm stride ignored", [("            float *row = x + t * ld + (int64_t)h * head_dim;\n            double ss",
+                              "            float *row = x + t * (int64_t)n_heads * head_dim + (int64_t)h * head_dim;\n            double ss")]),
+    ("q norm uses k weight", [("oracle_rms_norm_heads(q, nt, ld_q, n_head, head_dim, wq, eps);", "oracle_rms_norm_heads(q, nt, ld_q, n_head, head_dim, wk, eps);")]),
+    ("k not normalised", [("    oracle_rms_norm_heads(k, nt, ld_k, n_kv_head, head_dim, wk, eps);\n", "")]),
+    ("v normalised too", [("    oracle_rms_norm_heads(k, nt, ld_k, n_kv_head, head_dim, wk, eps);\n",
+                           "    oracle_rms_norm_heads(k, nt, ld_k, n_kv_head, head_dim, wk, eps);\n"
+                           "    oracle_rms_norm_heads(v, nt, ld_v, n_kv_head, head_dim, wk, eps);\n")]),
+    ("norm after rope", [("    oracle_rms_norm_heads(q, nt, ld_q, n_head, head_dim, wq, eps);\n"
+                          "    oracle_rms_norm_heads(k, nt, ld_k, n_kv_head, head_dim, wk, eps);\n\n"
+                          "    oracle_inv_freq(theta, head_dim, inv);\n"
+                          "    oracle_rope_neox(q, nt, ld_q, n_head, head_dim, pos, inv);\n"
+                          "    oracle_rope_neox(k, nt, ld_k, n_kv_head, head_dim, pos, inv);\n",
+                          "    oracle_inv_freq(theta, head_dim, inv);\n"
+                          "    oracle_rope_neox(q, nt, ld_q, n_head, head_dim, pos, inv);\n"
+                          "    oracle_rope_neox(k, nt, ld_k, n_kv_head, head_dim, pos, inv);\n"
+                          "    oracle_rms_norm_heads(q, nt, ld_q, n_head, head_dim, wq, eps);\n"
+                          "    oracle_rms_norm_heads(k, nt, ld_k, n_kv_head, head_dim, wk, eps);\n")]),
+    ("bias after norm", [("    if (bq)\n        oracle_add_bias(q, bq, nt, nqt, ld_q);\n", ""),
+                         ("    oracle_rms_norm_heads(q, nt, ld_q, n_head, head_dim, wq, eps);\n",
+                          "    oracle_rms_norm_heads(q, nt, ld_q, n_head, head_dim, wq, eps);\n"
+                          "    if (bq)\n        oracle_add_bias(q, bq, nt, nqt, ld_q);\n")]),
 ]
 
 
@@ -77,13 +107,23 @@ def _pin_calls():
         ("slot rows and range", pins.test_slot_rows_and_range_errors),
         ("tokens independent", pins.test_tokens_are_independent),
         ("concat equals separate", pins.test_concat_rows_equal_separate_buffers),
+        ("norm hand-worked", npins.test_handworked_3_4),
+        ("norm constant vector", lambda: npins.test_constant_vector_closed_form(0.5, 1e-6)),
+        ("norm tiny constant", lambda: npins.test_constant_vector_closed_form(1e-3, 1e-6)),
+        ("norm scale invariance", npins.test_power_of_two_scale_invariance_is_exact),
+        ("norm mean square", npins.test_mean_square_invariant),
+        ("norm linalg", npins.test_matches_linalg_norm),
+        ("norm heads independent", npins.test_heads_are_independent_and_stride_respected),
+        ("variant pos0 (bias)", lambda: npins.test_variant_at_pos0_is_bias_then_norm(True)),
+        ("variant pos0 (no bias)", lambda: npins.test_variant_at_pos0_is_bias_then_norm(False)),
+        ("variant rotates after norm", npins.test_variant_rotates_after_norm),
     ]
 
 
 def _build_mutant(edits, workdir):
     src = open(SRC).read()
     for old, new in edits:
-        assert src.count(old) == 1, f"mutation anchor not unique or missing: {old!r}"
+        assert src.count(old) >= 1, f"mutation anchor missing: {old!r}"
         src = src.replace(old, new)
     c = os.path.join(workdir, "mutant.c")
     so = os.path.join(workdir, "libmutant.so")

@@ -80,7 +80,7 @@ def read_traffic(workload):
 class Sets:
     """R independent input sets of one workload on the device."""
 
-    def __init__(self, w, R, cache_dtype, nt=None, share_cache=False):
+    def __init__(self, w, R, cache_dtype, nt=None, share_cache=False, norm=False):
         import numpy as np
         import torch
         from qkv_bias_rope_amd import workloads as wl
@@ -89,6 +89,12 @@ class Sets:
         d = wl.draw_layer(w, 0, nt=self.nt)
         dev = "cuda:0"
         self.bq, self.bk, self.bv = (torch.from_numpy(d[n]).to(dev) for n in ("bq", "bk", "bv"))
+        self.norm = norm
+        if norm:   # the q/k-norm variant without biases (Qwen3-style attention)
+            nw = wl.draw_norm_weights(w, 0)
+            self.wq = torch.from_numpy(nw["wq"]).to(dev)
+            self.wk = torch.from_numpy(nw["wk"]).to(dev)
+            self.bq = self.bk = self.bv = None
         cdt = torch.float16 if cache_dtype == wl.CACHE_F16 else torch.float32
         rows = w.n_slots * w.n_ctx
         self.sets = []
@@ -125,6 +131,13 @@ class Sets:
                            nt=self.nt)
 
 
+def norm_runner(sets):
+    """run_ex-shaped callable for the q/k-norm variant of a Sets."""
+    from qkv_bias_rope_amd import binding as B
+    from qkv_bias_rope_amd import workloads as wl
+    return lambda h, a: B.qkv_epilogue_run_qk_norm(h, a, sets.wq, sets.wk, wl.QK_NORM_EPS)
+
+
 def time_launches(h, arg_list, steps, warmup, stream, settle_s=0.3, fn=None):
     """Mean time per launch (ms) over `steps` launches cycling through
     arg_list, HIP events recorded on the launch stream.  Before the `warmup`
@@ -158,17 +171,21 @@ def time_launches(h, arg_list, steps, warmup, stream, settle_s=0.3, fn=None):
 
 
 def bench_bandwidth(h, w, cache_dtype, steps, warmup, stream, min_set_bytes=1.5e9, slot=False,
-                    fn=None):
+                    fn=None, norm=False):
     from qkv_bias_rope_amd import workloads as wl
     cb = 2 if cache_dtype == wl.CACHE_F16 else 4
     nbytes = algo_bytes(w, w.nt, cb, slot=slot)
+    if norm:   # no biases; the two [head_dim] norm weights instead
+        nbytes += 2 * w.head_dim * 4 - (w.nqt + 2 * w.nkt) * 4
     per_set = w.nt * (w.nqt + 2 * w.nkt) * 4 * 2
     R = max(2, int(-(-min_set_bytes // per_set)))
     # big caches (batched decode) are shared by the sets: their rows are written
     # at random positions, so a shared cache gets no reuse anyway
     share = w.n_slots > 1
-    sets = Sets(w, R, cache_dtype, share_cache=share)
+    sets = Sets(w, R, cache_dtype, share_cache=share, norm=norm)
     args = [sets.args(r, stream) for r in range(R)]
+    if norm:
+        fn = norm_runner(sets)
     ms = time_launches(h, args, steps, warmup, stream, fn=fn)
     return dict(ms=ms, bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9, sets=R), sets
 
@@ -363,6 +380,16 @@ def run_all(args, h, stream):
                                           us_per_launch_chain=round(r["ms"] * 1e3, 3),
                                           launches=7)
         log(f"[bench]   {r['ms'] * 1e3:.2f} us per 7-launch chain, {r['gbs']:.1f} GB/s")
+        # the q/k-norm variant (no biases, per-head RMS norm before the rope)
+        log(f"[bench] {w.name} q/k-norm variant")
+        r, sets = bench_bandwidth(h, w, wl.CACHE_F16, max(20, args.steps // 2),
+                                  max(2, args.warmup // 2), stream, norm=True)
+        del sets
+        torch.cuda.empty_cache()
+        extra[w.name + "_qk_norm"] = dict(gbs=round(r["gbs"], 1), us_per_launch=round(r["ms"] * 1e3, 3),
+                                          bytes_per_launch=r["bytes"],
+                                          frac_of_peak=round(r["gbs"] / PEAK_HBM_GBS, 4))
+        log(f"[bench]   {r['ms'] * 1e3:.2f} us/launch, {r['gbs']:.1f} GB/s")
 
     cpu = None
     if not args.no_cpu:

@@ -163,6 +163,26 @@ typedef struct qkv_epilogue_args {
 int qkv_epilogue_run_ex(qkv_epilogue_t *h, const qkv_epilogue_args_t *a);
 
 /*
+ * The q/k-norm variant (page "06 · Assign + fusion", §3.2: a per-head q/k norm
+ * op and its fused form FusedQkvNorm, "the Qwen3 per-head-norm variant"; the
+ * page gives no formula).  Per token: the biases that are given (bq, bk, bv
+ * may each be NULL = no bias, as in the Qwen3 attention), then every q head
+ * and every k head of head_dim values is scaled as
+ *     y[j] = x[j] / sqrt(mean_j(x[j]^2) + eps) * w[j]
+ * with w = w_q for q heads and w_k for k heads (both [head_dim] f32 device
+ * arrays, shared by the heads of the section), then NeoX rotary embedding on q
+ * and k, then the K/V row store -- as qkv_epilogue_run_ex otherwise.  v is
+ * never normalised.  The sum of squares and the scaling are evaluated in
+ * double and rounded once to f32.  One launch.
+ *
+ * Errors: those of qkv_epilogue_run_ex, plus QKV_ERR_INVALID_ARG for a NULL
+ * or misaligned weight or eps < 0 / not finite, and QKV_ERR_ALIAS when a
+ * weight overlaps an output.
+ */
+int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
+                             const float *w_q, const float *w_k, float eps);
+
+/*
  * The same operation as qkv_epilogue_run_ex, computed by the UNFUSED chain the
  * fused kernel replaces: three bias-add launches (q, k, v), two rope launches
  * (q, k) and two store launches (K, V), seven kernels in that order (page "73 ·

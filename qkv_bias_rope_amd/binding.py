@@ -36,7 +36,7 @@ QKV_ROPE_INTERLEAVED = 1
 QKV_MAX_HEAD_DIM = 512
 
 EXPORTS = ("qkv_epilogue_create", "qkv_epilogue_run", "qkv_epilogue_run_ex",
-           "qkv_epilogue_run_unfused",
+           "qkv_epilogue_run_unfused", "qkv_epilogue_run_qk_norm",
            "qkv_epilogue_status", "qkv_epilogue_last_error", "qkv_epilogue_destroy",
            "qkv_epilogue_inv_freq", "qkv_epilogue_check_args", "qkv_epilogue_plan")
 
@@ -91,6 +91,8 @@ def _load():
     lib.qkv_epilogue_run_ex.restype = _I
     lib.qkv_epilogue_run_unfused.argtypes = [_P, ctypes.POINTER(QkvEpilogueArgs)]
     lib.qkv_epilogue_run_unfused.restype = _I
+    lib.qkv_epilogue_run_qk_norm.argtypes = [_P, ctypes.POINTER(QkvEpilogueArgs), _P, _P, _F]
+    lib.qkv_epilogue_run_qk_norm.restype = _I
     lib.qkv_epilogue_status.argtypes = [_P]
     lib.qkv_epilogue_status.restype = _I
     lib.qkv_epilogue_last_error.argtypes = [_P]
@@ -143,6 +145,10 @@ def qkv_epilogue_run_ex(h, args: QkvEpilogueArgs) -> int:
 
 def qkv_epilogue_run_unfused(h, args: QkvEpilogueArgs) -> int:
     return lib.qkv_epilogue_run_unfused(h, ctypes.byref(args))
+
+
+def qkv_epilogue_run_qk_norm(h, args: QkvEpilogueArgs, w_q, w_k, eps: float) -> int:
+    return lib.qkv_epilogue_run_qk_norm(h, ctypes.byref(args), _addr(w_q), _addr(w_k), eps)
 
 
 def qkv_epilogue_status(h) -> int:

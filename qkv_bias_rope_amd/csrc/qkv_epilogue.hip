@@ -81,6 +81,9 @@ struct KParams {
     int cbu;              // units per column block = blockDim.x
     int ncb;              // column blocks per token
     int tb;               // tokens per token block
+    unsigned has_bias;    // bit s: section s has a bias (all set for run/run_ex)
+    const float *nw[2];   // q/k norm weights [hd] (q/k-norm variant only)
+    double eps;           // q/k norm epsilon
 };
 
 // Unit r of a token (0 <= r < U): section, column of the first slot, first
@@ -114,13 +117,20 @@ __device__ __forceinline__ T pick3(int s, T a, T b, T c)
     return s == 0 ? a : (s == 1 ? b : c);
 }
 
-template <int W, bool F16, int TPB, bool STREAM>
+// NORM: the q/k-norm variant -- after the bias, every q and k head is scaled
+// by w / sqrt(mean(x^2) + eps) before the rotation.  The sum of squares is
+// taken in double (exact squares): each lane adds its 2W elements, writes the
+// partial to LDS, and after the barrier every lane of a head sums the head's
+// partials in the same order.  Column blocks hold whole heads (the planner
+// makes blockDim a multiple of the units per head).
+template <int W, bool F16, int TPB, bool STREAM, bool NORM>
 __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvTable inv)
 {
     extern __shared__ __align__(16) unsigned char lds_raw[];
     int64_t *s_row = reinterpret_cast<int64_t *>(lds_raw);
     float *s_cos = reinterpret_cast<float *>(lds_raw + lds_row_bytes(TPB));
     float *s_sin = s_cos + TPB * p.half;
+    double *s_ss = reinterpret_cast<double *>(s_sin + TPB * p.half);  // NORM: [TPB][nthr]
 
     const int tid = (int)threadIdx.x;
     const int nthr = (int)blockDim.x;
@@ -151,9 +161,20 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
     decode_unit<W>(p, min(r, p.U - 1), sec, col, i0, d1);
     float *const xs = pick3(sec, p.x[0], p.x[1], p.x[2]) + col;
     const int64_t ldx = pick3(sec, p.ld[0], p.ld[1], p.ld[2]);
-    const float *const bp = pick3(sec, p.b[0], p.b[1], p.b[2]) + col;
-    const FVec<W> ba = ld_vec<W>(bp);
-    const FVec<W> bb = ld_vec<W>(bp + d1);
+    // A section without a bias reads its own first row instead (a valid
+    // address; the values are replaced by zero below) -- no branch, so the
+    // waits stay exact.
+    const bool hb = (p.has_bias >> sec) & 1u;
+    const float *const bp = hb ? pick3(sec, p.b[0], p.b[1], p.b[2]) + col : xs;
+    FVec<W> ba = ld_vec<W>(bp);
+    FVec<W> bb = ld_vec<W>(bp + d1);
+    FVec<W> wa, wb;
+    if constexpr (NORM) {
+        // weights of the pair indices of this unit; v units read q's (unused)
+        const float *wp = (sec == 1 ? p.nw[1] : p.nw[0]) + i0;
+        wa = ld_vec<W>(wp);
+        wb = ld_vec<W>(wp + (sec < 2 ? d1 : 0));
+    }
     FVec<W> xa[TPB], xb[TPB];
 #pragma unroll
     for (int tt = 0; tt < TPB; ++tt) {
@@ -188,6 +209,26 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
             atomicOr(p.err, 1u);
         s_row[tid] = row;
     }
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+        ba.e[e] = hb ? ba.e[e] : 0.0f;
+        bb.e[e] = hb ? bb.e[e] : 0.0f;
+    }
+    if constexpr (NORM) {
+        // this lane's part of its head's sum of squares, per token
+#pragma unroll
+        for (int tt = 0; tt < TPB; ++tt) {
+            double ss = 0.0;
+#pragma unroll
+            for (int e = 0; e < W; ++e) {
+                const double xa0 = (double)(xa[tt].e[e] + ba.e[e]);
+                const double xb0 = (double)(xb[tt].e[e] + bb.e[e]);
+                ss += xa0 * xa0;
+                ss += xb0 * xb0;
+            }
+            s_ss[tt * nthr + tid] = ss;
+        }
+    }
     __syncthreads();
     if (!live)
         return;
@@ -205,6 +246,19 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
             rb.e[e] = xb[tt].e[e] + bb.e[e];
         }
         if (sec < 2) {
+            if constexpr (NORM) {
+                // sum of the head's partials, in unit order (same for every lane)
+                const double *hp = s_ss + tt * nthr + (tid - i0 / W);
+                double ss = 0.0;
+                for (int j = 0; j < p.uph; ++j)
+                    ss += hp[j];
+                const double rr = 1.0 / sqrt(ss / (double)p.hd + p.eps);
+#pragma unroll
+                for (int e = 0; e < W; ++e) {
+                    ra.e[e] = (float)((double)ra.e[e] * rr * (double)wa.e[e]);
+                    rb.e[e] = (float)((double)rb.e[e] * rr * (double)wb.e[e]);
+                }
+            }
             const int ci = tt * p.half + i0;
             const FVec<W> cs = ld_vec<W>(s_cos + ci);
             const FVec<W> sn = ld_vec<W>(s_sin + ci);
@@ -230,22 +284,33 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
     }
 }
 
-template <int W, bool F16, int TPB, bool STREAM>
+template <int W, bool F16, int TPB, bool STREAM, bool NORM>
 hipError_t launch_t(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
 {
-    hipLaunchKernelGGL((qkv_epilogue_kernel<W, F16, TPB, STREAM>), dim3((unsigned)pl.grid),
+    hipLaunchKernelGGL((qkv_epilogue_kernel<W, F16, TPB, STREAM, NORM>), dim3((unsigned)pl.grid),
                        dim3((unsigned)pl.nthr), (unsigned)pl.lds, st, kp, inv);
     return hipGetLastError();
 }
 
-template <int W, bool F16>
-hipError_t launch_w(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
+template <int W, bool F16, bool NORM>
+hipError_t launch_n(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
 {
     if (pl.tb == 1)
-        return pl.stream ? launch_t<W, F16, 1, true>(kp, inv, pl, st)
-                         : launch_t<W, F16, 1, false>(kp, inv, pl, st);
-    return pl.stream ? launch_t<W, F16, 2, true>(kp, inv, pl, st)
-                     : launch_t<W, F16, 2, false>(kp, inv, pl, st);
+        return pl.stream ? launch_t<W, F16, 1, true, NORM>(kp, inv, pl, st)
+                         : launch_t<W, F16, 1, false, NORM>(kp, inv, pl, st);
+    return pl.stream ? launch_t<W, F16, 2, true, NORM>(kp, inv, pl, st)
+                     : launch_t<W, F16, 2, false, NORM>(kp, inv, pl, st);
+}
+
+template <int W>
+hipError_t launch_w(const KParams &kp, const InvTable &inv, const Plan &pl, bool f16,
+                    hipStream_t st)
+{
+    if (pl.norm)
+        return f16 ? launch_n<W, true, true>(kp, inv, pl, st)
+                   : launch_n<W, false, true>(kp, inv, pl, st);
+    return f16 ? launch_n<W, true, false>(kp, inv, pl, st)
+               : launch_n<W, false, false>(kp, inv, pl, st);
 }
 
 }  // namespace
@@ -267,7 +332,7 @@ int ceil_div(int64_t a, int64_t b)
 //    fewer, fuller workgroups carry the launch;
 //  * a few tokens (decode): 64-thread blocks spread one token over many
 //    workgroups, default cache policy (the data is cache-resident).
-void choose_tiling(int64_t nt, int U, Plan *pl)
+void choose_tiling(int64_t nt, int U, int uph, Plan *pl)
 {
     if (nt >= 1024) {
         pl->nthr = 128;
@@ -283,6 +348,14 @@ void choose_tiling(int64_t nt, int U, Plan *pl)
         pl->nthr = 64;
         pl->tb = 1;
         pl->stream = false;
+    }
+    if (pl->norm) {
+        // whole heads per column block: a multiple of the units per head
+        int k = (pl->nthr + uph / 2) / uph;
+        k = k < 1 ? 1 : k;
+        while (k > 1 && k * uph > kMaxBlock)
+            --k;
+        pl->nthr = k * uph;
     }
     pl->ncb = ceil_div(U, pl->nthr);
 }
@@ -344,7 +417,7 @@ bool spans_overlap(Span a, Span b)
 }
 
 int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl, char *msg,
-                   size_t mlen)
+                   size_t mlen, unsigned flags, const float *wq, const float *wk, float eps)
 {
     if (!a) {
         set_msg(msg, mlen, "args is NULL");
@@ -420,6 +493,7 @@ int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl
     pl->W = 1;
     pl->U = 0;
     pl->stream = false;
+    pl->norm = (flags & kPlanNorm) != 0;
     pl->nthr = 64;
     pl->ncb = 1;
     pl->tb = 1;
@@ -429,13 +503,18 @@ int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl
     if (a->nt == 0)
         return QKV_OK;
 
+    const bool bias_opt = (flags & kPlanBiasOptional) != 0;
     struct {
         const void *p;
         const char *n;
-    } ptrs[] = {{a->q, "q"},   {a->k, "k"},   {a->v, "v"},   {a->bq, "bq"},         {a->bk, "bk"},
-                {a->bv, "bv"}, {a->pos, "pos"}, {a->kcache, "kcache"}, {a->vcache, "vcache"}};
+        bool optional;
+    } ptrs[] = {{a->q, "q", false},          {a->k, "k", false},
+                {a->v, "v", false},          {a->bq, "bq", bias_opt},
+                {a->bk, "bk", bias_opt},     {a->bv, "bv", bias_opt},
+                {a->pos, "pos", false},      {a->kcache, "kcache", false},
+                {a->vcache, "vcache", false}};
     for (auto &e : ptrs) {
-        if (!e.p) {
+        if (!e.p && !e.optional) {
             set_msg(msg, mlen, "%s is NULL", e.n);
             return QKV_ERR_INVALID_ARG;
         }
@@ -443,6 +522,20 @@ int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl
     for (const float *f : {(const float *)a->q, (const float *)a->k, (const float *)a->v, a->bq, a->bk, a->bv}) {
         if ((uintptr_t)f % 4) {
             set_msg(msg, mlen, "f32 tensor pointer not 4-byte aligned");
+            return QKV_ERR_INVALID_ARG;
+        }
+    }
+    if (flags & kPlanNorm) {
+        if (!wq || !wk) {
+            set_msg(msg, mlen, "%s is NULL", wq ? "w_k" : "w_q");
+            return QKV_ERR_INVALID_ARG;
+        }
+        if ((uintptr_t)wq % 4 || (uintptr_t)wk % 4) {
+            set_msg(msg, mlen, "norm weight pointer not 4-byte aligned");
+            return QKV_ERR_INVALID_ARG;
+        }
+        if (!(eps >= 0.0f) || !std::isfinite(eps)) {
+            set_msg(msg, mlen, "norm eps must be finite and >= 0, got %g", (double)eps);
             return QKV_ERR_INVALID_ARG;
         }
     }
@@ -471,12 +564,15 @@ int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl
                 set_msg(msg, mlen, "%s and %s overlap", outs[i].name, outs[j].name);
                 return QKV_ERR_ALIAS;
             }
-    Span ins[5] = {
-        {(uintptr_t)a->bq, 0, nqt * 4, 1, "bq"},
-        {(uintptr_t)a->bk, 0, nkt * 4, 1, "bk"},
-        {(uintptr_t)a->bv, 0, nkt * 4, 1, "bv"},
+    const int64_t wbytes = (flags & kPlanNorm) ? (int64_t)a->head_dim * 4 : 0;
+    Span ins[7] = {
+        {(uintptr_t)a->bq, 0, a->bq ? nqt * 4 : 0, 1, "bq"},
+        {(uintptr_t)a->bk, 0, a->bk ? nkt * 4 : 0, 1, "bk"},
+        {(uintptr_t)a->bv, 0, a->bv ? nkt * 4 : 0, 1, "bv"},
         {(uintptr_t)a->pos, 0, nt * 4, 1, "pos"},
         {(uintptr_t)a->slot, 0, a->slot ? nt * 4 : 0, 1, "slot"},
+        {(uintptr_t)wq, 0, wbytes, 1, "w_q"},
+        {(uintptr_t)wk, 0, wbytes, 1, "w_k"},
     };
     for (auto &in : ins)
         for (auto &o : outs)
@@ -488,7 +584,8 @@ int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl
     // kernel variant: 16-byte vectors when every slot is 16-byte aligned
     bool vec = (a->head_dim % 8) == 0;
     for (const float *f : {(const float *)a->q, (const float *)a->k, (const float *)a->v, a->bq, a->bk, a->bv})
-        vec = vec && ((uintptr_t)f % 16) == 0;
+        vec = vec && ((uintptr_t)f % 16) == 0;  // NULL (no bias) is aligned
+    vec = vec && ((uintptr_t)wq % 16) == 0 && ((uintptr_t)wk % 16) == 0;
     vec = vec && (ldq % 4) == 0 && (ldk % 4) == 0 && (ldv % 4) == 0;
     vec = vec && ((uintptr_t)a->kcache % (4 * cb)) == 0 && ((uintptr_t)a->vcache % (4 * cb)) == 0;
     const int W = vec ? 4 : 1;
@@ -500,7 +597,7 @@ int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl
     }
     pl->W = W;
     pl->U = (int)U;
-    choose_tiling(nt, (int)U, pl);
+    choose_tiling(nt, (int)U, half / W, pl);
     const int64_t ntb = (nt + pl->tb - 1) / pl->tb;
     pl->grid = ntb * pl->ncb;
     if (pl->grid > INT32_MAX) {
@@ -508,6 +605,8 @@ int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl
         return QKV_ERR_INVALID_ARG;
     }
     pl->lds = lds_row_bytes(pl->tb) + 2 * pl->tb * half * 4;  // tb <= 2: <= 4 KB + 16
+    if (pl->norm)
+        pl->lds += pl->tb * pl->nthr * 8;  // per-lane partial sums of squares
     return QKV_OK;
 }
 
@@ -537,6 +636,69 @@ const InvTable &handle_inv(qkv_epilogue *h, float theta, int head_dim)
         h->inv_theta = theta;
     }
     return h->inv;
+}
+
+// The fused launch behind run_ex (flags 0) and run_qk_norm.
+int launch_fused(qkv_epilogue_t *h, const qkv_epilogue_args_t *a, unsigned flags, const float *wq,
+                 const float *wk, float eps)
+{
+    if (!h)
+        return QKV_ERR_INVALID_ARG;
+    h->msg[0] = 0;
+    Plan pl;
+    int rc = check_and_plan(a, h->n_ctx, &pl, h->msg, sizeof h->msg, flags, wq, wk, eps);
+    if (rc != QKV_OK)
+        return rc;
+    if (a->nt == 0)
+        return QKV_OK;
+
+    const InvTable &inv = handle_inv(h, a->theta, a->head_dim);
+
+    KParams kp;
+    kp.x[0] = a->q;
+    kp.x[1] = a->k;
+    kp.x[2] = a->v;
+    kp.b[0] = a->bq;
+    kp.b[1] = a->bk;
+    kp.b[2] = a->bv;
+    kp.pos = a->pos;
+    kp.slot = a->slot;
+    kp.cache[0] = a->kcache;
+    kp.cache[1] = a->vcache;
+    kp.err = h->d_err;
+    kp.ld[0] = pl.ld[0];
+    kp.ld[1] = pl.ld[1];
+    kp.ld[2] = pl.ld[2];
+    kp.n_ctx = pl.n_ctx;
+    kp.n_slots = pl.n_slots;
+    kp.nkt = pl.nkt;
+    kp.nt = a->nt;
+    kp.hd = a->head_dim;
+    kp.half = pl.half;
+    kp.uph = pl.half / pl.W;
+    kp.qu = a->n_head * kp.uph;
+    kp.qku = (a->n_head + a->n_kv_head) * kp.uph;
+    kp.vhalf = (int)(pl.nkt / 2);
+    kp.U = pl.U;
+    kp.cbu = pl.nthr;
+    kp.ncb = pl.ncb;
+    kp.tb = pl.tb;
+    kp.has_bias = (a->bq ? 1u : 0u) | (a->bk ? 2u : 0u) | (a->bv ? 4u : 0u);
+    kp.nw[0] = wq;
+    kp.nw[1] = wk;
+    kp.eps = (double)eps;
+
+    hipStream_t st = (a->stream || a->use_stream) ? static_cast<hipStream_t>(a->stream) : h->stream;
+    DeviceGuard g;
+    hipError_t e = g.set(h->device);
+    if (e != hipSuccess)
+        return fail(h, QKV_ERR_HIP, "hipSetDevice(%d): %s", h->device, hipGetErrorString(e));
+    const bool f16 = a->cache_dtype == QKV_CACHE_F16;
+    e = pl.W == 4 ? launch_w<4>(kp, inv, pl, f16, st) : launch_w<1>(kp, inv, pl, f16, st);
+    if (e != hipSuccess)
+        return fail(h, QKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    h->last_stream = st;
+    return QKV_OK;
 }
 
 }  // namespace qkv_detail
@@ -583,62 +745,13 @@ int qkv_epilogue_create(qkv_epilogue_t **out, const qkv_epilogue_config_t *cfg)
 
 int qkv_epilogue_run_ex(qkv_epilogue_t *h, const qkv_epilogue_args_t *a)
 {
-    if (!h)
-        return QKV_ERR_INVALID_ARG;
-    h->msg[0] = 0;
-    Plan pl;
-    int rc = check_and_plan(a, h->n_ctx, &pl, h->msg, sizeof h->msg);
-    if (rc != QKV_OK)
-        return rc;
-    if (a->nt == 0)
-        return QKV_OK;
+    return launch_fused(h, a, 0u, nullptr, nullptr, 0.0f);
+}
 
-    const InvTable &inv = handle_inv(h, a->theta, a->head_dim);
-
-    KParams kp;
-    kp.x[0] = a->q;
-    kp.x[1] = a->k;
-    kp.x[2] = a->v;
-    kp.b[0] = a->bq;
-    kp.b[1] = a->bk;
-    kp.b[2] = a->bv;
-    kp.pos = a->pos;
-    kp.slot = a->slot;
-    kp.cache[0] = a->kcache;
-    kp.cache[1] = a->vcache;
-    kp.err = h->d_err;
-    kp.ld[0] = pl.ld[0];
-    kp.ld[1] = pl.ld[1];
-    kp.ld[2] = pl.ld[2];
-    kp.n_ctx = pl.n_ctx;
-    kp.n_slots = pl.n_slots;
-    kp.nkt = pl.nkt;
-    kp.nt = a->nt;
-    kp.hd = a->head_dim;
-    kp.half = pl.half;
-    kp.uph = pl.half / pl.W;
-    kp.qu = a->n_head * kp.uph;
-    kp.qku = (a->n_head + a->n_kv_head) * kp.uph;
-    kp.vhalf = (int)(pl.nkt / 2);
-    kp.U = pl.U;
-    kp.cbu = pl.nthr;
-    kp.ncb = pl.ncb;
-    kp.tb = pl.tb;
-
-    hipStream_t st = (a->stream || a->use_stream) ? static_cast<hipStream_t>(a->stream) : h->stream;
-    DeviceGuard g;
-    hipError_t e = g.set(h->device);
-    if (e != hipSuccess)
-        return fail(h, QKV_ERR_HIP, "hipSetDevice(%d): %s", h->device, hipGetErrorString(e));
-    const bool f16 = a->cache_dtype == QKV_CACHE_F16;
-    if (pl.W == 4)
-        e = f16 ? launch_w<4, true>(kp, inv, pl, st) : launch_w<4, false>(kp, inv, pl, st);
-    else
-        e = f16 ? launch_w<1, true>(kp, inv, pl, st) : launch_w<1, false>(kp, inv, pl, st);
-    if (e != hipSuccess)
-        return fail(h, QKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    h->last_stream = st;
-    return QKV_OK;
+int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a, const float *w_q,
+                             const float *w_k, float eps)
+{
+    return launch_fused(h, a, kPlanBiasOptional | kPlanNorm, w_q, w_k, eps);
 }
 
 int qkv_epilogue_run(qkv_epilogue_t *h, float *q, float *k, float *v, const float *bq,

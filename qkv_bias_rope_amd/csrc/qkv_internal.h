@@ -115,6 +115,7 @@ struct Plan {
     int ncb;      // column blocks per token
     int tb;       // tokens per workgroup (1 or 2)
     bool stream;  // nontemporal hints on the data
+    bool norm;    // q/k-norm variant (column blocks hold whole heads)
     int64_t grid;
     int lds;
     int half;
@@ -126,9 +127,16 @@ struct Plan {
 int ceil_div(int64_t a, int64_t b);
 void set_msg(char *msg, size_t len, const char *fmt, ...);
 
+// check_and_plan flags
+constexpr unsigned kPlanBiasOptional = 1u;  // NULL biases mean "no bias"
+constexpr unsigned kPlanNorm = 2u;          // plan the q/k-norm variant
+
 // Validate a request (the checks run_ex documents) and plan the fused launch.
+// With kPlanNorm, wq/wk are the [head_dim] norm weights (checked for NULL,
+// alignment and overlap with the outputs) and eps the norm epsilon.
 int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl, char *msg,
-                   size_t mlen);
+                   size_t mlen, unsigned flags = 0, const float *wq = nullptr,
+                   const float *wk = nullptr, float eps = 0.0f);
 
 // inv[i] = f32(theta^(-2i/head_dim)), computed in double and rounded once.
 void host_inv_freq(float theta, int head_dim, float *out);

@@ -101,8 +101,13 @@ class Case:
     """One launch: inputs drawn for workload w, run on the GPU and the oracle."""
 
     def __init__(self, w, layer=0, nt=None, pos=None, slot=None, cache_dtype=None, form="separate",
-                 n_ctx=None, n_slots=None, inputs=None, misalign=0):
+                 n_ctx=None, n_slots=None, inputs=None, misalign=0, norm=False, bias=True):
         self.w = w
+        self.norm = norm            # q/k-norm variant (run_qk_norm)
+        self.bias = bias            # False: no biases (NULL), only with norm
+        if norm:
+            self.nw = wl.draw_norm_weights(w, layer)
+            self.eps = wl.QK_NORM_EPS
         self.cd = w.cache_dtypes[0] if cache_dtype is None else cache_dtype
         d = wl.draw_layer(w, layer, nt=nt) if inputs is None else inputs
         if pos is not None:
@@ -120,10 +125,18 @@ class Case:
     def run_oracle(self):
         w, d = self.w, self.d
         q, k, v = (d[n].copy() for n in ("q", "k", "v"))
-        rid, kr, vr, bad = oracle.qkv_epilogue(
-            q.ravel(), k.ravel(), v.ravel(), d["bq"], d["bk"], d["bv"], d["pos"],
-            n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim, theta=w.theta,
-            n_ctx=self.n_ctx, cache_dtype=self.cd, slot=d["slot"], n_slots=self.n_slots)
+        if self.norm:
+            b = (d["bq"], d["bk"], d["bv"]) if self.bias else (None, None, None)
+            rid, kr, vr, bad = oracle.qkv_norm_epilogue(
+                q.ravel(), k.ravel(), v.ravel(), *b, self.nw["wq"], self.nw["wk"], self.eps,
+                d["pos"], n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim,
+                theta=w.theta, n_ctx=self.n_ctx, cache_dtype=self.cd, slot=d["slot"],
+                n_slots=self.n_slots)
+        else:
+            rid, kr, vr, bad = oracle.qkv_epilogue(
+                q.ravel(), k.ravel(), v.ravel(), d["bq"], d["bk"], d["bv"], d["pos"],
+                n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim, theta=w.theta,
+                n_ctx=self.n_ctx, cache_dtype=self.cd, slot=d["slot"], n_slots=self.n_slots)
         self.o_q, self.o_k, self.o_v = q, k, v
         self.o_rows, self.o_krows, self.o_vrows, self.o_bad = rid, kr, vr, bad
         return self
@@ -151,6 +164,11 @@ class Case:
             self._k, self.g_k = up(d["k"])
             self._v, self.g_v = up(d["v"])
         self.g_bq, self.g_bk, self.g_bv = (torch.from_numpy(d[n]).to(DEV) for n in ("bq", "bk", "bv"))
+        if not self.bias:
+            self.g_bq = self.g_bk = self.g_bv = None
+        if self.norm:
+            self.g_wq = torch.from_numpy(self.nw["wq"]).to(DEV)
+            self.g_wk = torch.from_numpy(self.nw["wk"]).to(DEV)
         self.g_pos = torch.from_numpy(d["pos"]).to(DEV)
         self.g_slot = None if d["slot"] is None else torch.from_numpy(d["slot"]).to(DEV)
         rows = self.n_slots * self.n_ctx
@@ -167,7 +185,10 @@ class Case:
                                     w.n_kv_head, w.head_dim, w.theta, self.cd)
         else:
             a = self.args(stream)
-            rc = (B.qkv_epilogue_run_unfused if entry == "unfused" else B.qkv_epilogue_run_ex)(h, a)
+            if self.norm:
+                rc = B.qkv_epilogue_run_qk_norm(h, a, self.g_wq, self.g_wk, self.eps)
+            else:
+                rc = (B.qkv_epilogue_run_unfused if entry == "unfused" else B.qkv_epilogue_run_ex)(h, a)
         return rc
 
     def args(self, stream=None):

@@ -119,11 +119,17 @@ __device__ __forceinline__ T pick3(int s, T a, T b, T c)
 
 // NORM: the q/k-norm variant -- after the bias, every q and k head is scaled
 // by w / sqrt(mean(x^2) + eps) before the rotation.  The sum of squares is
-// taken in double (exact squares): each lane adds its 2W elements, writes the
-// partial to LDS, and after the barrier every lane of a head sums the head's
-// partials in the same order.  Column blocks hold whole heads (the planner
-// makes blockDim a multiple of the units per head).
-template <int W, bool F16, int TPB, bool STREAM, bool NORM>
+// taken in double (exact squares), each lane adding its 2W elements first.
+//   NORM == 1: lanes write their partials to LDS before the barrier and every
+//              lane of a head sums the head's partials in the same order
+//              (any units-per-head count);
+//   NORM == 2: the units per head are a power of two dividing 64, so a head's
+//              lanes are aligned inside one wave and an xor butterfly gives
+//              every lane of the head the same sum (addition is commutative)
+//              with no LDS and no wait at the barrier.
+// Column blocks hold whole heads (the planner makes blockDim a multiple of the
+// units per head).
+template <int W, bool F16, int TPB, bool STREAM, int NORM>
 __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvTable inv)
 {
     extern __shared__ __align__(16) unsigned char lds_raw[];
@@ -169,7 +175,7 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
     FVec<W> ba = ld_vec<W>(bp);
     FVec<W> bb = ld_vec<W>(bp + d1);
     FVec<W> wa, wb;
-    if constexpr (NORM) {
+    if constexpr (NORM != 0) {
         // weights of the pair indices of this unit; v units read q's (unused)
         const float *wp = (sec == 1 ? p.nw[1] : p.nw[0]) + i0;
         wa = ld_vec<W>(wp);
@@ -214,7 +220,7 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
         ba.e[e] = hb ? ba.e[e] : 0.0f;
         bb.e[e] = hb ? bb.e[e] : 0.0f;
     }
-    if constexpr (NORM) {
+    if constexpr (NORM == 1) {
         // this lane's part of its head's sum of squares, per token
 #pragma unroll
         for (int tt = 0; tt < TPB; ++tt) {
@@ -245,8 +251,30 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
             ra.e[e] = xa[tt].e[e] + ba.e[e];
             rb.e[e] = xb[tt].e[e] + bb.e[e];
         }
+        if constexpr (NORM == 2) {
+            // butterfly over the head's lanes (all lanes take part: v lanes
+            // sit in groups of their own and their sums are not used)
+            double ss = 0.0;
+#pragma unroll
+            for (int e = 0; e < W; ++e) {
+                const double xa0 = (double)ra.e[e];
+                const double xb0 = (double)rb.e[e];
+                ss += xa0 * xa0;
+                ss += xb0 * xb0;
+            }
+            for (int m = p.uph >> 1; m >= 1; m >>= 1)
+                ss += __shfl_xor(ss, m, 64);
+            if (sec < 2) {
+                const double rr = 1.0 / sqrt(ss / (double)p.hd + p.eps);
+#pragma unroll
+                for (int e = 0; e < W; ++e) {
+                    ra.e[e] = (float)((double)ra.e[e] * rr * (double)wa.e[e]);
+                    rb.e[e] = (float)((double)rb.e[e] * rr * (double)wb.e[e]);
+                }
+            }
+        }
         if (sec < 2) {
-            if constexpr (NORM) {
+            if constexpr (NORM == 1) {
                 // sum of the head's partials, in unit order (same for every lane)
                 const double *hp = s_ss + tt * nthr + (tid - i0 / W);
                 double ss = 0.0;
@@ -284,7 +312,7 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
     }
 }
 
-template <int W, bool F16, int TPB, bool STREAM, bool NORM>
+template <int W, bool F16, int TPB, bool STREAM, int NORM>
 hipError_t launch_t(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
 {
     hipLaunchKernelGGL((qkv_epilogue_kernel<W, F16, TPB, STREAM, NORM>), dim3((unsigned)pl.grid),
@@ -292,7 +320,7 @@ hipError_t launch_t(const KParams &kp, const InvTable &inv, const Plan &pl, hipS
     return hipGetLastError();
 }
 
-template <int W, bool F16, bool NORM>
+template <int W, bool F16, int NORM>
 hipError_t launch_n(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
 {
     if (pl.tb == 1)
@@ -306,11 +334,13 @@ template <int W>
 hipError_t launch_w(const KParams &kp, const InvTable &inv, const Plan &pl, bool f16,
                     hipStream_t st)
 {
+    const int uph = pl.half / W;
+    const bool pow2 = uph <= 64 && (uph & (uph - 1)) == 0;
+    if (pl.norm && pow2)
+        return f16 ? launch_n<W, true, 2>(kp, inv, pl, st) : launch_n<W, false, 2>(kp, inv, pl, st);
     if (pl.norm)
-        return f16 ? launch_n<W, true, true>(kp, inv, pl, st)
-                   : launch_n<W, false, true>(kp, inv, pl, st);
-    return f16 ? launch_n<W, true, false>(kp, inv, pl, st)
-               : launch_n<W, false, false>(kp, inv, pl, st);
+        return f16 ? launch_n<W, true, 1>(kp, inv, pl, st) : launch_n<W, false, 1>(kp, inv, pl, st);
+    return f16 ? launch_n<W, true, 0>(kp, inv, pl, st) : launch_n<W, false, 0>(kp, inv, pl, st);
 }
 
 }  // namespace

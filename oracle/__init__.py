@@ -58,12 +58,16 @@ def _bind(lib):
     lib.oracle_scatter_rows.argtypes = [P, I64, I64, I, I64, P, P]
     lib.oracle_scatter_rows.restype = None
     lib.oracle_qkv_epilogue.argtypes = [
-        P, P, P, I64, I64, I64, P, P, P, P, P, I64, I, I, I, F, I64, I64, I, P, P, P]
+        P, P, P, I64, I64, I64, P, P, P, P, P, I64, I, I, I, F, I64, I64, I, I, F, P, P, P]
     lib.oracle_qkv_epilogue.restype = I64
     lib.oracle_rms_norm_heads.argtypes = [P, I64, I64, I, I, P, F]
     lib.oracle_rms_norm_heads.restype = None
     lib.oracle_qkv_norm_epilogue.argtypes = [
-        P, P, P, I64, I64, I64, P, P, P, P, P, F, P, P, I64, I, I, I, F, I64, I64, I, P, P, P]
+        P, P, P, I64, I64, I64, P, P, P, P, P, F, P, P, I64, I, I, I, F, I64, I64, I, I, F, P, P, P]
+    lib.oracle_inv_freq_scaled.argtypes = [F, F, I, P]
+    lib.oracle_inv_freq_scaled.restype = None
+    lib.oracle_rope_interleaved.argtypes = [P, I64, I64, I, I, P, P]
+    lib.oracle_rope_interleaved.restype = None
     lib.oracle_qkv_norm_epilogue.restype = I64
     return lib
 
@@ -128,6 +132,26 @@ def inv_freq(theta: float, head_dim: int) -> np.ndarray:
     return out
 
 
+ROPE_NEOX = 0
+ROPE_INTERLEAVED = 1
+
+
+def inv_freq_scaled(theta: float, freq_scale: float, head_dim: int) -> np.ndarray:
+    """Step O2 with a frequency scale: f32(freq_scale * theta^(-2i/hd))."""
+    out = np.zeros(head_dim // 2, dtype=np.float32)
+    _load().oracle_inv_freq_scaled(theta, freq_scale, head_dim, _ptr(out))
+    return out
+
+
+def rope_interleaved(x, nt, ld, n_heads, head_dim, pos, inv):
+    """Step O3' (pairs (2i, 2i+1)) in place on x."""
+    _f32(x, "x"), _i32(pos, "pos"), _f32(inv, "inv")
+    assert pos.size >= nt and inv.size >= head_dim // 2
+    if nt:
+        assert x.size >= (nt - 1) * ld + n_heads * head_dim
+    _load().oracle_rope_interleaved(_ptr(x), nt, ld, n_heads, head_dim, _ptr(pos), _ptr(inv))
+
+
 def rope_neox(x, nt, ld, n_heads, head_dim, pos, inv):
     """Step O3 in place on x."""
     _f32(x, "x"), _i32(pos, "pos"), _f32(inv, "inv")
@@ -178,7 +202,8 @@ def scatter_rows(cache, row_ids, rows):
 # ---- the whole chain --------------------------------------------------------
 
 def qkv_epilogue(q, k, v, bq, bk, bv, pos, *, n_head, n_kv_head, head_dim, theta,
-                 n_ctx, cache_dtype, slot=None, n_slots=1, ld_q=None, ld_k=None, ld_v=None):
+                 n_ctx, cache_dtype, slot=None, n_slots=1, ld_q=None, ld_k=None, ld_v=None,
+                 rope_style=ROPE_NEOX, freq_scale=1.0):
     """Run the unfused chain in place on q, k, v (float32 numpy arrays).
 
     q holds nt rows of stride ld_q (default n_head*head_dim), k and v rows of
@@ -217,7 +242,7 @@ def qkv_epilogue(q, k, v, bq, bk, bv, pos, *, n_head, n_kv_head, head_dim, theta
     bad = _load().oracle_qkv_epilogue(
         base(q, ld_q, nqt, "q"), base(k, ld_k, nkt, "k"), base(v, ld_v, nkt, "v"), ld_q, ld_k, ld_v,
         _ptr(bq), _ptr(bk), _ptr(bv), _ptr(pos), _ptr(slot), nt,
-        n_head, n_kv_head, head_dim, theta, n_ctx, n_slots, cache_dtype,
+        n_head, n_kv_head, head_dim, theta, n_ctx, n_slots, cache_dtype, rope_style, freq_scale,
         _ptr(row_ids), _ptr(krows), _ptr(vrows))
     if bad < 0:
         raise ValueError("oracle: head_dim must be positive and even")
@@ -226,7 +251,7 @@ def qkv_epilogue(q, k, v, bq, bk, bv, pos, *, n_head, n_kv_head, head_dim, theta
 
 def qkv_norm_epilogue(q, k, v, bq, bk, bv, wq, wk, eps, pos, *, n_head, n_kv_head, head_dim,
                       theta, n_ctx, cache_dtype, slot=None, n_slots=1, ld_q=None, ld_k=None,
-                      ld_v=None):
+                      ld_v=None, rope_style=ROPE_NEOX, freq_scale=1.0):
     """The q/k-norm variant of the chain (biases may be None).  Same returns as
     qkv_epilogue."""
     nt = int(pos.size)
@@ -257,7 +282,7 @@ def qkv_norm_epilogue(q, k, v, bq, bk, bv, wq, wk, eps, pos, *, n_head, n_kv_hea
     bad = _load().oracle_qkv_norm_epilogue(
         q.ctypes.data, k.ctypes.data, v.ctypes.data, ld_q, ld_k, ld_v,
         _ptr(bq), _ptr(bk), _ptr(bv), _ptr(wq), _ptr(wk), eps, _ptr(pos), _ptr(slot), nt,
-        n_head, n_kv_head, head_dim, theta, n_ctx, n_slots, cache_dtype,
+        n_head, n_kv_head, head_dim, theta, n_ctx, n_slots, cache_dtype, rope_style, freq_scale,
         _ptr(row_ids), _ptr(krows), _ptr(vrows))
     if bad < 0:
         raise ValueError("oracle: head_dim must be positive and even")

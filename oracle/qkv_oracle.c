@@ -15,7 +15,9 @@
  *   store K, then store V into the cache (row = position, dst[pos*nkt + j])
  *
  * and the q/k-norm variant (per-head RMS norm of q and k between the bias add
- * and the rope, see oracle_rms_norm_heads).
+ * and the rope, see oracle_rms_norm_heads).  The rope style (0 = NeoX,
+ * 1 = interleaved pairs (2i, 2i+1)) and a frequency scale are parameters of
+ * both chains.
  *
  * Each step is its own plain loop, in that order, written for a reader to check
  * against the page by eye.  The per-pair cos/sin are recomputed inside the rope
@@ -74,6 +76,18 @@ void oracle_inv_freq(float theta, int head_dim, float *inv)
     }
 }
 
+/* Step O2 with a frequency scale (the page's kernel multiplies by
+ * freq_scale, §3.2 Excerpt A): inv[i] = f32(freq_scale * theta^(-2i/hd)),
+ * the product taken in double and rounded once. */
+void oracle_inv_freq_scaled(float theta, float freq_scale, int head_dim, float *inv)
+{
+    int half = head_dim / 2;
+    for (int i = 0; i < half; ++i) {
+        double e = -(2.0 * (double)i) / (double)head_dim;
+        inv[i] = (float)((double)freq_scale * pow((double)theta, e));
+    }
+}
+
 /* ---------------------------------------------------------------------------
  * Step O3 -- rope, NeoX pairing, on one section holding n_heads heads of
  * head_dim elements per token row (row stride ld elements).
@@ -95,6 +109,32 @@ void oracle_rope_neox(float *x, int64_t nt, int64_t ld, int n_heads,
                 float x1 = row[i + half];
                 row[i]        = (float)((double)x0 * c - (double)x1 * s);
                 row[i + half] = (float)((double)x0 * s + (double)x1 * c);
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Step O3' -- rope with interleaved (GPT-J) pairing: inside each head, pair i
+ * is (x[2i], x[2i+1]) and turns by pos*inv[i].  Page "06 · Assign + fusion"
+ * §3.2 names the style (RopeStyle other than NonInterleaved); the rotation is
+ * the NeoX one applied to adjacent elements.
+ * ------------------------------------------------------------------------- */
+void oracle_rope_interleaved(float *x, int64_t nt, int64_t ld, int n_heads,
+                             int head_dim, const int32_t *pos, const float *inv)
+{
+    int half = head_dim / 2;
+    for (int64_t t = 0; t < nt; ++t) {
+        for (int h = 0; h < n_heads; ++h) {
+            float *row = x + t * ld + (int64_t)h * head_dim;
+            for (int i = 0; i < half; ++i) {
+                float a = (float)pos[t] * inv[i];
+                float c = (float)cos((double)a);
+                float s = (float)sin((double)a);
+                float x0 = row[2 * i];
+                float x1 = row[2 * i + 1];
+                row[2 * i]     = (float)((double)x0 * c - (double)x1 * s);
+                row[2 * i + 1] = (float)((double)x0 * s + (double)x1 * c);
             }
         }
     }
@@ -245,6 +285,7 @@ int64_t oracle_qkv_epilogue(float *q, float *k, float *v,
                             int64_t nt, int n_head, int n_kv_head,
                             int head_dim, float theta,
                             int64_t n_ctx, int64_t n_slots, int cache_dtype,
+                            int rope_style, float freq_scale,
                             int64_t *row_ids, void *krows, void *vrows)
 {
     int64_t nqt = (int64_t)n_head * head_dim;
@@ -257,9 +298,17 @@ int64_t oracle_qkv_epilogue(float *q, float *k, float *v,
     oracle_add_bias(k, bk, nt, nkt, ld_k);
     oracle_add_bias(v, bv, nt, nkt, ld_v);
 
-    oracle_inv_freq(theta, head_dim, inv);
-    oracle_rope_neox(q, nt, ld_q, n_head, head_dim, pos, inv);
-    oracle_rope_neox(k, nt, ld_k, n_kv_head, head_dim, pos, inv);
+    if (freq_scale == 1.0f)
+        oracle_inv_freq(theta, head_dim, inv);
+    else
+        oracle_inv_freq_scaled(theta, freq_scale, head_dim, inv);
+    if (rope_style == 0) {
+        oracle_rope_neox(q, nt, ld_q, n_head, head_dim, pos, inv);
+        oracle_rope_neox(k, nt, ld_k, n_kv_head, head_dim, pos, inv);
+    } else {
+        oracle_rope_interleaved(q, nt, ld_q, n_head, head_dim, pos, inv);
+        oracle_rope_interleaved(k, nt, ld_k, n_kv_head, head_dim, pos, inv);
+    }
 
     int64_t bad = oracle_store_rows(k, nt, ld_k, nkt, pos, slot, n_ctx,
                                     n_slots, cache_dtype, row_ids, krows);
@@ -282,6 +331,7 @@ int64_t oracle_qkv_norm_epilogue(float *q, float *k, float *v,
                                  int64_t nt, int n_head, int n_kv_head,
                                  int head_dim, float theta,
                                  int64_t n_ctx, int64_t n_slots, int cache_dtype,
+                                 int rope_style, float freq_scale,
                                  int64_t *row_ids, void *krows, void *vrows)
 {
     int64_t nqt = (int64_t)n_head * head_dim;
@@ -300,9 +350,17 @@ int64_t oracle_qkv_norm_epilogue(float *q, float *k, float *v,
     oracle_rms_norm_heads(q, nt, ld_q, n_head, head_dim, wq, eps);
     oracle_rms_norm_heads(k, nt, ld_k, n_kv_head, head_dim, wk, eps);
 
-    oracle_inv_freq(theta, head_dim, inv);
-    oracle_rope_neox(q, nt, ld_q, n_head, head_dim, pos, inv);
-    oracle_rope_neox(k, nt, ld_k, n_kv_head, head_dim, pos, inv);
+    if (freq_scale == 1.0f)
+        oracle_inv_freq(theta, head_dim, inv);
+    else
+        oracle_inv_freq_scaled(theta, freq_scale, head_dim, inv);
+    if (rope_style == 0) {
+        oracle_rope_neox(q, nt, ld_q, n_head, head_dim, pos, inv);
+        oracle_rope_neox(k, nt, ld_k, n_kv_head, head_dim, pos, inv);
+    } else {
+        oracle_rope_interleaved(q, nt, ld_q, n_head, head_dim, pos, inv);
+        oracle_rope_interleaved(k, nt, ld_k, n_kv_head, head_dim, pos, inv);
+    }
 
     int64_t bad = oracle_store_rows(k, nt, ld_k, nkt, pos, slot, n_ctx,
                                     n_slots, cache_dtype, row_ids, krows);

@@ -15,6 +15,7 @@ import pytest
 import oracle
 import test_oracle_norm_pins as npins
 import test_oracle_pins as pins
+import test_oracle_rope_variants as rpins
 from qkv_bias_rope_amd import workloads as wl
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "qkv_oracle.c")
@@ -68,16 +69,25 @@ MUTATIONS = [
     ("v normalised too", [("    oracle_rms_norm_heads(k, nt, ld_k, n_kv_head, head_dim, wk, eps);\n",
                            "    oracle_rms_norm_heads(k, nt, ld_k, n_kv_head, head_dim, wk, eps);\n"
                            "    oracle_rms_norm_heads(v, nt, ld_v, n_kv_head, head_dim, wk, eps);\n")]),
+    # norm after rope: the rope block is shared text in both chains, so a macro
+    # expands to nothing in the plain chain and to the norm calls in the
+    # q/k-norm chain (defined again just before that function)
     ("norm after rope", [("    oracle_rms_norm_heads(q, nt, ld_q, n_head, head_dim, wq, eps);\n"
-                          "    oracle_rms_norm_heads(k, nt, ld_k, n_kv_head, head_dim, wk, eps);\n\n"
-                          "    oracle_inv_freq(theta, head_dim, inv);\n"
-                          "    oracle_rope_neox(q, nt, ld_q, n_head, head_dim, pos, inv);\n"
-                          "    oracle_rope_neox(k, nt, ld_k, n_kv_head, head_dim, pos, inv);\n",
-                          "    oracle_inv_freq(theta, head_dim, inv);\n"
-                          "    oracle_rope_neox(q, nt, ld_q, n_head, head_dim, pos, inv);\n"
-                          "    oracle_rope_neox(k, nt, ld_k, n_kv_head, head_dim, pos, inv);\n"
-                          "    oracle_rms_norm_heads(q, nt, ld_q, n_head, head_dim, wq, eps);\n"
-                          "    oracle_rms_norm_heads(k, nt, ld_k, n_kv_head, head_dim, wk, eps);\n")]),
+                          "    oracle_rms_norm_heads(k, nt, ld_k, n_kv_head, head_dim, wk, eps);\n\n", ""),
+                         ("#include <string.h>\n", "#include <string.h>\n#define NORM_AFTER_ROPE (void)0\n"),
+                         ("int64_t oracle_qkv_norm_epilogue(",
+                          "#undef NORM_AFTER_ROPE\n#define NORM_AFTER_ROPE "
+                          "oracle_rms_norm_heads(q, nt, ld_q, n_head, head_dim, wq, eps); "
+                          "oracle_rms_norm_heads(k, nt, ld_k, n_kv_head, head_dim, wk, eps)\n"
+                          "int64_t oracle_qkv_norm_epilogue("),
+                         ("    int64_t bad = oracle_store_rows(k, nt, ld_k, nkt, pos, slot, n_ctx,\n",
+                          "    NORM_AFTER_ROPE;\n    int64_t bad = oracle_store_rows(k, nt, ld_k, nkt, pos, slot, n_ctx,\n")]),
+    # rope variants
+    ("interleaved reads the NeoX partner", [("float x1 = row[2 * i + 1];", "float x1 = row[i + half];")]),
+    ("interleaved writes the NeoX partner", [("row[2 * i + 1] = (float)((double)x0 * s", "row[i + half] = (float)((double)x0 * s")]),
+    ("frequency scale ignored", [("(float)((double)freq_scale * pow((double)theta, e))", "(float)(pow((double)theta, e))")]),
+    ("frequency scale divides", [("(float)((double)freq_scale * pow((double)theta, e))", "(float)(pow((double)theta, e) / (double)freq_scale)")]),
+    ("rope style ignored", [("    if (rope_style == 0) {", "    if (1) {")]),
     ("bias after norm", [("    if (bq)\n        oracle_add_bias(q, bq, nt, nqt, ld_q);\n", ""),
                          ("    oracle_rms_norm_heads(q, nt, ld_q, n_head, head_dim, wq, eps);\n",
                           "    oracle_rms_norm_heads(q, nt, ld_q, n_head, head_dim, wq, eps);\n"
@@ -117,6 +127,15 @@ def _pin_calls():
         ("variant pos0 (bias)", lambda: npins.test_variant_at_pos0_is_bias_then_norm(True)),
         ("variant pos0 (no bias)", lambda: npins.test_variant_at_pos0_is_bias_then_norm(False)),
         ("variant rotates after norm", npins.test_variant_rotates_after_norm),
+        ("interleaved hand-worked", rpins.test_interleaved_handworked_1h4d),
+        ("interleaved = permuted NeoX", lambda: rpins.test_interleaved_is_permuted_neox(64)),
+        ("interleaved complex", rpins.test_interleaved_complex_multiply),
+        ("scaled inv decimal", lambda: rpins.test_scaled_inv_freq_matches_decimal(0.25, 128)),
+        ("scaled inv decimal 1/3", lambda: rpins.test_scaled_inv_freq_matches_decimal(1.0 / 3.0, 64)),
+        ("scale 1 unscaled", rpins.test_scale_one_is_unscaled),
+        ("scale = halved position (NeoX)", lambda: rpins.test_power_of_two_scale_equals_scaled_position(0)),
+        ("scale = halved position (interleaved)", lambda: rpins.test_power_of_two_scale_equals_scaled_position(1)),
+        ("chain style and scale", rpins.test_chain_style_and_scale_are_applied),
     ]
 
 

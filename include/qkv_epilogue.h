@@ -65,8 +65,8 @@ extern "C" {
 #define QKV_CACHE_F16 1
 
 /* ---- rotary styles ------------------------------------------------------ */
-#define QKV_ROPE_NEOX 0         /* pair i with i + head_dim/2: the only one */
-#define QKV_ROPE_INTERLEAVED 1  /* pair 2i with 2i+1: rejected, QKV_ERR_UNSUPPORTED */
+#define QKV_ROPE_NEOX 0         /* pair i with i + head_dim/2 (default) */
+#define QKV_ROPE_INTERLEAVED 1  /* pair 2i with 2i+1 (GPT-J style) */
 
 /* Largest supported head_dim (the inverse-frequency table travels with the
  * launch and holds head_dim/2 values). */
@@ -131,9 +131,10 @@ typedef struct qkv_epilogue_args {
     int nt, n_head, n_kv_head, head_dim;
     float theta;
     int cache_dtype;                /* QKV_CACHE_F32 / QKV_CACHE_F16 */
-    int rope_style;                 /* QKV_ROPE_NEOX only */
+    int rope_style;                 /* QKV_ROPE_NEOX or QKV_ROPE_INTERLEAVED */
     void *stream;                   /* hipStream_t; NULL = the handle's */
     int use_stream;                 /* nonzero: launch on `stream` even if NULL */
+    float freq_scale;               /* angle = pos * freq_scale * theta^(-2i/hd); 0 = 1 */
 } qkv_epilogue_args_t;
 
 /*
@@ -153,9 +154,16 @@ typedef struct qkv_epilogue_args {
  *                        token or 2^31-1 workgroups.
  *   QKV_ERR_ALIAS        two of q, k, v, kcache, vcache share an element, or
  *                        a read-only input (bias, pos, slot) overlaps one.
- *   QKV_ERR_UNSUPPORTED  rope_style is not QKV_ROPE_NEOX (page "06 · Assign +
- *                        fusion", §3.2: a backend claims only the rotary
- *                        style its kernel implements).
+ *   QKV_ERR_UNSUPPORTED  rope_style is neither QKV_ROPE_NEOX nor
+ *                        QKV_ROPE_INTERLEAVED (page "06 · Assign + fusion",
+ *                        §3.2: a backend claims only the rotary styles its
+ *                        kernel implements and rejects the others loudly).
+ *
+ * Rotary style and scale: with QKV_ROPE_INTERLEAVED pair i of a head is
+ * (x[2i], x[2i+1]) instead of (x[i], x[i+head_dim/2]); freq_scale multiplies
+ * every inverse frequency (the page's kernel takes freq_scale, §3.2 Excerpt
+ * A): inv[i] = f32(freq_scale * theta^(-2i/head_dim)), the product taken in
+ * double.  freq_scale must be finite and > 0 (0 means 1).
  *   QKV_ERR_HIP          the launch failed (text from the HIP runtime).
  * Duplicate cache rows within one call are a caller error: the row then holds
  * one of the colliding tokens' values.
@@ -217,6 +225,10 @@ void qkv_epilogue_destroy(qkv_epilogue_t *h);
  * bad theta/head_dim or NULL out.
  */
 int qkv_epilogue_inv_freq(float theta, int head_dim, float *out);
+
+/* The same with a frequency scale: out[i] = f32(freq_scale * theta^(-2i/hd)),
+ * the product in double (freq_scale finite and > 0). */
+int qkv_epilogue_inv_freq_scaled(float theta, float freq_scale, int head_dim, float *out);
 
 /*
  * Validate a request exactly as qkv_epilogue_run_ex does, without a handle

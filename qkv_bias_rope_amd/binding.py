@@ -38,7 +38,8 @@ QKV_MAX_HEAD_DIM = 512
 EXPORTS = ("qkv_epilogue_create", "qkv_epilogue_run", "qkv_epilogue_run_ex",
            "qkv_epilogue_run_unfused", "qkv_epilogue_run_qk_norm",
            "qkv_epilogue_status", "qkv_epilogue_last_error", "qkv_epilogue_destroy",
-           "qkv_epilogue_inv_freq", "qkv_epilogue_check_args", "qkv_epilogue_plan")
+           "qkv_epilogue_inv_freq", "qkv_epilogue_inv_freq_scaled", "qkv_epilogue_check_args",
+           "qkv_epilogue_plan")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -62,6 +63,7 @@ class QkvEpilogueArgs(ctypes.Structure):
         ("theta", _F),
         ("cache_dtype", _I), ("rope_style", _I),
         ("stream", _P), ("use_stream", _I),
+        ("freq_scale", _F),
     ]
 
 
@@ -101,6 +103,8 @@ def _load():
     lib.qkv_epilogue_destroy.restype = None
     lib.qkv_epilogue_inv_freq.argtypes = [_F, _I, _P]
     lib.qkv_epilogue_inv_freq.restype = _I
+    lib.qkv_epilogue_inv_freq_scaled.argtypes = [_F, _F, _I, _P]
+    lib.qkv_epilogue_inv_freq_scaled.restype = _I
     lib.qkv_epilogue_check_args.argtypes = [ctypes.POINTER(QkvEpilogueArgs), ctypes.c_char_p,
                                             ctypes.c_size_t]
     lib.qkv_epilogue_check_args.restype = _I
@@ -168,6 +172,11 @@ def qkv_epilogue_inv_freq(theta: float, head_dim: int, out_addr: int) -> int:
     return lib.qkv_epilogue_inv_freq(theta, head_dim, out_addr)
 
 
+def qkv_epilogue_inv_freq_scaled(theta: float, freq_scale: float, head_dim: int,
+                                 out_addr: int) -> int:
+    return lib.qkv_epilogue_inv_freq_scaled(theta, freq_scale, head_dim, out_addr)
+
+
 def qkv_epilogue_check_args(args: QkvEpilogueArgs):
     """Returns (rc, message)."""
     buf = ctypes.create_string_buffer(512)
@@ -206,7 +215,7 @@ def _row_stride(t, width, name):
 def make_args(q, k, v, bq, bk, bv, pos, kcache, vcache, *, n_head, n_kv_head, head_dim,
               theta, cache_dtype, nt=None, slot=None, n_ctx=0, n_slots=0, ld_q=None,
               ld_k=None, ld_v=None, rope_style=QKV_ROPE_NEOX, stream=None,
-              use_stream=False) -> QkvEpilogueArgs:
+              use_stream=False, freq_scale=0.0) -> QkvEpilogueArgs:
     """Build the run_ex argument block.  Tensors (or raw addresses) are taken as
     they are; strides come from 2-D tensor views unless given."""
     nqt, nkt = n_head * head_dim, n_kv_head * head_dim
@@ -231,6 +240,7 @@ def make_args(q, k, v, bq, bk, bv, pos, kcache, vcache, *, n_head, n_kv_head, he
     a.rope_style = rope_style
     a.stream = _stream_addr(stream)
     a.use_stream = 1 if use_stream else 0
+    a.freq_scale = freq_scale
     return a
 
 

@@ -86,26 +86,48 @@ struct KParams {
     double eps;           // q/k norm epsilon
 };
 
-// Unit r of a token (0 <= r < U): section, column of the first slot, first
-// pair index (rope units) and distance from the first slot to the second.
-template <int W>
-__device__ __forceinline__ void decode_unit(const KParams &p, int r, int &sec, int &col, int &i0,
-                                            int &d1)
+// Unit r of a token (0 <= r < U): section, column of the first slot, offset
+// of the first slot inside its head (rope units), index of the unit inside
+// its head, and distance from the first slot to the second.
+//  NeoX (STYLE 0):   slots [eo, eo+W) and [eo+half, ...), eo = m*W; element
+//                    eo+e of the first slot pairs with element eo+e+half.
+//  interleaved (1):  W = 4: the same slots, each holding W/2 adjacent pairs
+//                    (2j, 2j+1); W = 1: the slots are x[2m] and x[2m+1].
+template <int W, int STYLE>
+__device__ __forceinline__ void decode_unit(const KParams &p, int r, int &sec, int &col, int &eo,
+                                            int &m, int &d1)
 {
     if (r < p.qku) {
         sec = r < p.qu ? 0 : 1;
         if (sec)
             r -= p.qu;
         const int h = r / p.uph;
-        i0 = (r - h * p.uph) * W;
-        col = h * p.hd + i0;
-        d1 = p.half;
+        m = r - h * p.uph;
+        if constexpr (STYLE == 1 && W == 1) {
+            eo = 2 * m;
+            d1 = 1;
+        } else {
+            eo = m * W;
+            d1 = p.half;
+        }
+        col = h * p.hd + eo;
     } else {
         sec = 2;
-        i0 = 0;
+        eo = 0;
+        m = 0;
         col = (r - p.qku) * W;
         d1 = p.vhalf;
     }
+}
+
+// (x0, x1) -> (x0*c - x1*s, x0*s + x1*c), evaluated in double: the products of
+// two f32 values are exact there, so each result is rounded once in double
+// and once to f32 whether or not the compiler fuses it into an FMA.
+__device__ __forceinline__ void rotate_pair(float &x0, float &x1, float c, float s)
+{
+    const double a = (double)x0, b = (double)x1, cd = (double)c, sd = (double)s;
+    x0 = (float)(a * cd - b * sd);
+    x1 = (float)(a * sd + b * cd);
 }
 
 // Section operands picked with selects on wave-uniform kernel arguments (an
@@ -129,7 +151,7 @@ __device__ __forceinline__ T pick3(int s, T a, T b, T c)
 //              with no LDS and no wait at the barrier.
 // Column blocks hold whole heads (the planner makes blockDim a multiple of the
 // units per head).
-template <int W, bool F16, int TPB, bool STREAM, int NORM>
+template <int W, bool F16, int TPB, bool STREAM, int NORM, int STYLE>
 __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvTable inv)
 {
     extern __shared__ __align__(16) unsigned char lds_raw[];
@@ -163,8 +185,8 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
     // ---- this thread's unit, its biases and its data for every token -------
     const int r = cb * p.cbu + tid;
     const bool live = r < p.U;
-    int sec, col, i0, d1;
-    decode_unit<W>(p, min(r, p.U - 1), sec, col, i0, d1);
+    int sec, col, i0, m, d1;
+    decode_unit<W, STYLE>(p, min(r, p.U - 1), sec, col, i0, m, d1);
     float *const xs = pick3(sec, p.x[0], p.x[1], p.x[2]) + col;
     const int64_t ldx = pick3(sec, p.ld[0], p.ld[1], p.ld[2]);
     // A section without a bias reads its own first row instead (a valid
@@ -276,7 +298,7 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
         if (sec < 2) {
             if constexpr (NORM == 1) {
                 // sum of the head's partials, in unit order (same for every lane)
-                const double *hp = s_ss + tt * nthr + (tid - i0 / W);
+                const double *hp = s_ss + tt * nthr + (tid - m);
                 double ss = 0.0;
                 for (int j = 0; j < p.uph; ++j)
                     ss += hp[j];
@@ -287,17 +309,26 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
                     rb.e[e] = (float)((double)rb.e[e] * rr * (double)wb.e[e]);
                 }
             }
-            const int ci = tt * p.half + i0;
-            const FVec<W> cs = ld_vec<W>(s_cos + ci);
-            const FVec<W> sn = ld_vec<W>(s_sin + ci);
+            if constexpr (STYLE == 0) {
+                const int ci = tt * p.half + i0;
+                const FVec<W> cs = ld_vec<W>(s_cos + ci);
+                const FVec<W> sn = ld_vec<W>(s_sin + ci);
 #pragma unroll
-            for (int e = 0; e < W; ++e) {
-                const double x0 = (double)ra.e[e];
-                const double x1 = (double)rb.e[e];
-                const double c = (double)cs.e[e];
-                const double sv = (double)sn.e[e];
-                ra.e[e] = (float)(x0 * c - x1 * sv);
-                rb.e[e] = (float)(x0 * sv + x1 * c);
+                for (int e = 0; e < W; ++e)
+                    rotate_pair(ra.e[e], rb.e[e], cs.e[e], sn.e[e]);
+            } else if constexpr (W == 1) {
+                const int ci = tt * p.half + m;
+                rotate_pair(ra.e[0], rb.e[0], s_cos[ci], s_sin[ci]);
+            } else {
+                // adjacent pairs inside each slot: pair indices eo/2 + j and
+                // (eo + half)/2 + j, j < W/2
+                const int ca = tt * p.half + i0 / 2;
+                const int cb2 = ca + p.half / 2;
+#pragma unroll
+                for (int j = 0; j < W / 2; ++j) {
+                    rotate_pair(ra.e[2 * j], ra.e[2 * j + 1], s_cos[ca + j], s_sin[ca + j]);
+                    rotate_pair(rb.e[2 * j], rb.e[2 * j + 1], s_cos[cb2 + j], s_sin[cb2 + j]);
+                }
             }
         }
         float *xp = xs + (int64_t)(t0 + tt) * ldx;
@@ -312,22 +343,30 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
     }
 }
 
-template <int W, bool F16, int TPB, bool STREAM, int NORM>
+template <int W, bool F16, int TPB, bool STREAM, int NORM, int STYLE>
 hipError_t launch_t(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
 {
-    hipLaunchKernelGGL((qkv_epilogue_kernel<W, F16, TPB, STREAM, NORM>), dim3((unsigned)pl.grid),
-                       dim3((unsigned)pl.nthr), (unsigned)pl.lds, st, kp, inv);
+    hipLaunchKernelGGL((qkv_epilogue_kernel<W, F16, TPB, STREAM, NORM, STYLE>),
+                       dim3((unsigned)pl.grid), dim3((unsigned)pl.nthr), (unsigned)pl.lds, st, kp,
+                       inv);
     return hipGetLastError();
+}
+
+template <int W, bool F16, int NORM, int STYLE>
+hipError_t launch_s(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
+{
+    if (pl.tb == 1)
+        return pl.stream ? launch_t<W, F16, 1, true, NORM, STYLE>(kp, inv, pl, st)
+                         : launch_t<W, F16, 1, false, NORM, STYLE>(kp, inv, pl, st);
+    return pl.stream ? launch_t<W, F16, 2, true, NORM, STYLE>(kp, inv, pl, st)
+                     : launch_t<W, F16, 2, false, NORM, STYLE>(kp, inv, pl, st);
 }
 
 template <int W, bool F16, int NORM>
 hipError_t launch_n(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
 {
-    if (pl.tb == 1)
-        return pl.stream ? launch_t<W, F16, 1, true, NORM>(kp, inv, pl, st)
-                         : launch_t<W, F16, 1, false, NORM>(kp, inv, pl, st);
-    return pl.stream ? launch_t<W, F16, 2, true, NORM>(kp, inv, pl, st)
-                     : launch_t<W, F16, 2, false, NORM>(kp, inv, pl, st);
+    return pl.style == QKV_ROPE_INTERLEAVED ? launch_s<W, F16, NORM, 1>(kp, inv, pl, st)
+                                            : launch_s<W, F16, NORM, 0>(kp, inv, pl, st);
 }
 
 template <int W>
@@ -453,12 +492,17 @@ int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl
         set_msg(msg, mlen, "args is NULL");
         return QKV_ERR_INVALID_ARG;
     }
-    if (a->rope_style != QKV_ROPE_NEOX) {
+    if (a->rope_style != QKV_ROPE_NEOX && a->rope_style != QKV_ROPE_INTERLEAVED) {
         set_msg(msg, mlen,
-                "rope_style %d not supported: only NeoX pairing (i, i+head_dim/2) is "
-                "implemented",
+                "rope_style %d not supported: NeoX pairing (i, i+head_dim/2) = 0 and "
+                "interleaved pairing (2i, 2i+1) = 1 are implemented",
                 a->rope_style);
         return QKV_ERR_UNSUPPORTED;
+    }
+    if (a->freq_scale != 0.0f && (!(a->freq_scale > 0.0f) || !std::isfinite(a->freq_scale))) {
+        set_msg(msg, mlen, "freq_scale must be finite and > 0 (0 means 1), got %g",
+                (double)a->freq_scale);
+        return QKV_ERR_INVALID_ARG;
     }
     if (a->nt < 0) {
         set_msg(msg, mlen, "nt must be >= 0, got %d", a->nt);
@@ -524,6 +568,7 @@ int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl
     pl->U = 0;
     pl->stream = false;
     pl->norm = (flags & kPlanNorm) != 0;
+    pl->style = a->rope_style;
     pl->nthr = 64;
     pl->ncb = 1;
     pl->tb = 1;
@@ -640,11 +685,13 @@ int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl
     return QKV_OK;
 }
 
-void host_inv_freq(float theta, int head_dim, float *out)
+void host_inv_freq(float theta, int head_dim, float freq_scale, float *out)
 {
     const int half = head_dim / 2;
-    for (int i = 0; i < half; ++i)
-        out[i] = (float)std::pow((double)theta, -(double)(2 * i) / (double)head_dim);
+    for (int i = 0; i < half; ++i) {
+        const double f = std::pow((double)theta, -(double)(2 * i) / (double)head_dim);
+        out[i] = freq_scale == 1.0f ? (float)f : (float)((double)freq_scale * f);
+    }
 }
 
 int fail(qkv_epilogue *h, int code, const char *fmt, ...)
@@ -658,12 +705,15 @@ int fail(qkv_epilogue *h, int code, const char *fmt, ...)
     return code;
 }
 
-const InvTable &handle_inv(qkv_epilogue *h, float theta, int head_dim)
+const InvTable &handle_inv(qkv_epilogue *h, float theta, int head_dim, float freq_scale)
 {
-    if (h->inv_hd != head_dim || h->inv_theta != theta) {
-        host_inv_freq(theta, head_dim, h->inv.v);
+    if (freq_scale == 0.0f)
+        freq_scale = 1.0f;
+    if (h->inv_hd != head_dim || h->inv_theta != theta || h->inv_scale != freq_scale) {
+        host_inv_freq(theta, head_dim, freq_scale, h->inv.v);
         h->inv_hd = head_dim;
         h->inv_theta = theta;
+        h->inv_scale = freq_scale;
     }
     return h->inv;
 }
@@ -682,7 +732,7 @@ int launch_fused(qkv_epilogue_t *h, const qkv_epilogue_args_t *a, unsigned flags
     if (a->nt == 0)
         return QKV_OK;
 
-    const InvTable &inv = handle_inv(h, a->theta, a->head_dim);
+    const InvTable &inv = handle_inv(h, a->theta, a->head_dim, a->freq_scale);
 
     KParams kp;
     kp.x[0] = a->q;
@@ -756,6 +806,7 @@ int qkv_epilogue_create(qkv_epilogue_t **out, const qkv_epilogue_config_t *cfg)
     h->last_stream = h->stream;
     h->inv_theta = 0.0f;
     h->inv_hd = 0;
+    h->inv_scale = 0.0f;
     h->msg[0] = 0;
     DeviceGuard g;
     hipError_t e = g.set(h->device);
@@ -852,7 +903,17 @@ int qkv_epilogue_inv_freq(float theta, int head_dim, float *out)
     if (!out || head_dim <= 0 || (head_dim & 1) || head_dim > QKV_MAX_HEAD_DIM ||
         !(theta > 0.0f) || !std::isfinite(theta))
         return QKV_ERR_INVALID_ARG;
-    host_inv_freq(theta, head_dim, out);
+    host_inv_freq(theta, head_dim, 1.0f, out);
+    return QKV_OK;
+}
+
+int qkv_epilogue_inv_freq_scaled(float theta, float freq_scale, int head_dim, float *out)
+{
+    if (!out || head_dim <= 0 || (head_dim & 1) || head_dim > QKV_MAX_HEAD_DIM ||
+        !(theta > 0.0f) || !std::isfinite(theta) || !(freq_scale > 0.0f) ||
+        !std::isfinite(freq_scale))
+        return QKV_ERR_INVALID_ARG;
+    host_inv_freq(theta, head_dim, freq_scale, out);
     return QKV_OK;
 }
 

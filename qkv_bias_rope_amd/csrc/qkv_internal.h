@@ -116,6 +116,7 @@ struct Plan {
     int tb;       // tokens per workgroup (1 or 2)
     bool stream;  // nontemporal hints on the data
     bool norm;    // q/k-norm variant (column blocks hold whole heads)
+    int style;    // QKV_ROPE_NEOX or QKV_ROPE_INTERLEAVED
     int64_t grid;
     int lds;
     int half;
@@ -138,8 +139,9 @@ int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl
                    size_t mlen, unsigned flags = 0, const float *wq = nullptr,
                    const float *wk = nullptr, float eps = 0.0f);
 
-// inv[i] = f32(theta^(-2i/head_dim)), computed in double and rounded once.
-void host_inv_freq(float theta, int head_dim, float *out);
+// inv[i] = f32(freq_scale * theta^(-2i/head_dim)), computed in double and
+// rounded once.
+void host_inv_freq(float theta, int head_dim, float freq_scale, float *out);
 
 struct DeviceGuard {
     int prev = -1;
@@ -173,6 +175,7 @@ struct qkv_epilogue {
     unsigned int *d_err;
     float inv_theta;
     int inv_hd;
+    float inv_scale;
     qkv_detail::InvTable inv;
     char msg[512];
 };
@@ -181,8 +184,9 @@ namespace qkv_detail {
 
 int fail(qkv_epilogue *h, int code, const char *fmt, ...);
 
-// The handle's table for (theta, head_dim), recomputed only when they change.
-const InvTable &handle_inv(qkv_epilogue *h, float theta, int head_dim);
+// The handle's table for (theta, head_dim, freq_scale; 0 means 1), recomputed
+// only when they change.
+const InvTable &handle_inv(qkv_epilogue *h, float theta, int head_dim, float freq_scale);
 
 }  // namespace qkv_detail
 

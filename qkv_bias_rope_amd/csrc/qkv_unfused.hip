@@ -6,10 +6,11 @@
 // two KV stores, each a sub-2 us kernel).  It exists for the same-binary A/B
 // the page measures (§5: launches per decode step, wall clock with and without
 // the fusion) and as a second GPU implementation the fused kernel must match
-// bit for bit.  Each kernel keeps the numerics of the fused kernel (one f32
-// bias add; f32 angle, cos/sin in double rounded to f32; rotation in double;
-// binary16 round-to-nearest-even stores) but, like the page's unfused rope,
-// every rope thread evaluates cos/sin for its own pairs.
+// bit for bit (both rotary styles, any frequency scale).  Each kernel keeps
+// the numerics of the fused kernel (one f32 bias add; f32 angle, cos/sin in
+// double rounded to f32; rotation in double; binary16 round-to-nearest-even
+// stores) but, like the page's unfused rope, every rope thread evaluates
+// cos/sin for its own pairs.
 
 #include <hip/hip_runtime.h>
 
@@ -44,9 +45,27 @@ __global__ __launch_bounds__(kBlockU) void add_bias_kernel(float *x, int64_t ld,
     st_data<W, STREAM>(p, v);
 }
 
-// NeoX rotation of n_heads heads per row: item (t, h, i0) turns the W pairs
-// (i0+e, i0+e+half), e < W, by the angles f32(pos[t]*inv[i0+e]).
-template <int W, bool STREAM>
+// Turn (x0, x1) by the f32 angle a: cos/sin in double rounded to f32, the
+// rotation in double.
+__device__ __forceinline__ void turn(float &x0, float &x1, float a)
+{
+    double sd, cd;
+    sincos((double)a, &sd, &cd);
+    const double c = (double)(float)cd;
+    const double s = (double)(float)sd;
+    const double u = (double)x0, w = (double)x1;
+    x0 = (float)(u * c - w * s);
+    x1 = (float)(u * s + w * c);
+}
+
+// Rotation of n_heads heads per row; item (t, h, m) owns the slots
+// [eo, eo+W) and [eo+d, eo+d+W) of head h, eo = m*W.
+//  NeoX (STYLE 0): d = half; element eo+e pairs with eo+e+half, angle index
+//    eo+e.
+//  interleaved (STYLE 1): W = 4: d = half, each slot holds W/2 adjacent pairs
+//    (pair indices eo/2 + j and (eo+half)/2 + j); W = 1: the slots are
+//    x[2m] and x[2m+1], pair index m.
+template <int W, bool STREAM, int STYLE>
 __global__ __launch_bounds__(kBlockU) void rope_kernel(float *x, int64_t ld, int n_heads,
                                                        int hd, const int32_t *pos,
                                                        InvTable inv, int64_t n_items)
@@ -60,25 +79,29 @@ __global__ __launch_bounds__(kBlockU) void rope_kernel(float *x, int64_t ld, int
     const int64_t t = g / per_row;
     const int r = (int)(g - t * per_row);
     const int h = r / per_head;
-    const int i0 = (r - h * per_head) * W;
-    float *p = x + t * ld + (int64_t)h * hd + i0;
+    const int m = r - h * per_head;
+    const bool adj1 = STYLE == 1 && W == 1;
+    const int eo = adj1 ? 2 * m : m * W;
+    const int d = adj1 ? 1 : half;
+    float *p = x + t * ld + (int64_t)h * hd + eo;
     FVec<W> xa = ld_data<W, STREAM>(p);
-    FVec<W> xb = ld_data<W, STREAM>(p + half);
+    FVec<W> xb = ld_data<W, STREAM>(p + d);
     const float pf = (float)pos[t];
+    if constexpr (STYLE == 0) {
 #pragma unroll
-    for (int e = 0; e < W; ++e) {
-        const float a = pf * inv.v[i0 + e];   // f32 angle
-        double sd, cd;
-        sincos((double)a, &sd, &cd);
-        const double c = (double)(float)cd;
-        const double s = (double)(float)sd;
-        const double x0 = (double)xa.e[e];
-        const double x1 = (double)xb.e[e];
-        xa.e[e] = (float)(x0 * c - x1 * s);
-        xb.e[e] = (float)(x0 * s + x1 * c);
+        for (int e = 0; e < W; ++e)
+            turn(xa.e[e], xb.e[e], pf * inv.v[eo + e]);   // f32 angle
+    } else if constexpr (W == 1) {
+        turn(xa.e[0], xb.e[0], pf * inv.v[m]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < W / 2; ++j) {
+            turn(xa.e[2 * j], xa.e[2 * j + 1], pf * inv.v[eo / 2 + j]);
+            turn(xb.e[2 * j], xb.e[2 * j + 1], pf * inv.v[(eo + half) / 2 + j]);
+        }
     }
     st_data<W, STREAM>(p, xa);
-    st_data<W, STREAM>(p + half, xb);
+    st_data<W, STREAM>(p + d, xb);
 }
 
 // cache[row(t)][c..c+W) = cvt(x[t][c..c+W)), row = slot*n_ctx + pos; a token
@@ -113,7 +136,7 @@ unsigned grid_of(int64_t n_items)
     return (unsigned)((n_items + kBlockU - 1) / kBlockU);
 }
 
-template <int W, bool F16, bool STREAM>
+template <int W, bool F16, bool STREAM, int STYLE>
 hipError_t launch_chain(const qkv_epilogue_args_t *a, const Plan &pl, const InvTable &inv,
                         unsigned int *err, hipStream_t st)
 {
@@ -132,7 +155,7 @@ hipError_t launch_chain(const qkv_epilogue_args_t *a, const Plan &pl, const InvT
     const int heads[2] = {a->n_head, a->n_kv_head};
     for (int s = 0; s < 2; ++s) {
         const int64_t n = nt * heads[s] * (pl.half / W);
-        hipLaunchKernelGGL((rope_kernel<W, STREAM>), dim3(grid_of(n)), dim3(kBlockU), 0, st,
+        hipLaunchKernelGGL((rope_kernel<W, STREAM, STYLE>), dim3(grid_of(n)), dim3(kBlockU), 0, st,
                            xs[s], pl.ld[s], heads[s], a->head_dim, a->pos, inv, n);
     }
     // store x2 (K from the k section, V from the v section)
@@ -151,11 +174,19 @@ hipError_t launch_chain_w(const qkv_epilogue_args_t *a, const Plan &pl, const In
                           unsigned int *err, hipStream_t st)
 {
     const bool f16 = a->cache_dtype == QKV_CACHE_F16;
-    if (pl.stream)
-        return f16 ? launch_chain<W, true, true>(a, pl, inv, err, st)
-                   : launch_chain<W, false, true>(a, pl, inv, err, st);
-    return f16 ? launch_chain<W, true, false>(a, pl, inv, err, st)
-               : launch_chain<W, false, false>(a, pl, inv, err, st);
+    const bool il = pl.style == QKV_ROPE_INTERLEAVED;
+    if (pl.stream) {
+        if (il)
+            return f16 ? launch_chain<W, true, true, 1>(a, pl, inv, err, st)
+                       : launch_chain<W, false, true, 1>(a, pl, inv, err, st);
+        return f16 ? launch_chain<W, true, true, 0>(a, pl, inv, err, st)
+                   : launch_chain<W, false, true, 0>(a, pl, inv, err, st);
+    }
+    if (il)
+        return f16 ? launch_chain<W, true, false, 1>(a, pl, inv, err, st)
+                   : launch_chain<W, false, false, 1>(a, pl, inv, err, st);
+    return f16 ? launch_chain<W, true, false, 0>(a, pl, inv, err, st)
+               : launch_chain<W, false, false, 0>(a, pl, inv, err, st);
 }
 
 }  // namespace
@@ -171,7 +202,7 @@ extern "C" int qkv_epilogue_run_unfused(qkv_epilogue_t *h, const qkv_epilogue_ar
         return rc;
     if (a->nt == 0)
         return QKV_OK;
-    const InvTable &inv = handle_inv(h, a->theta, a->head_dim);
+    const InvTable &inv = handle_inv(h, a->theta, a->head_dim, a->freq_scale);
     hipStream_t st = (a->stream || a->use_stream) ? static_cast<hipStream_t>(a->stream) : h->stream;
     DeviceGuard g;
     hipError_t e = g.set(h->device);

@@ -101,8 +101,11 @@ class Case:
     """One launch: inputs drawn for workload w, run on the GPU and the oracle."""
 
     def __init__(self, w, layer=0, nt=None, pos=None, slot=None, cache_dtype=None, form="separate",
-                 n_ctx=None, n_slots=None, inputs=None, misalign=0, norm=False, bias=True):
+                 n_ctx=None, n_slots=None, inputs=None, misalign=0, norm=False, bias=True,
+                 style=0, freq_scale=1.0):
         self.w = w
+        self.style = style              # 0 NeoX, 1 interleaved pairs
+        self.freq_scale = freq_scale
         self.norm = norm            # q/k-norm variant (run_qk_norm)
         self.bias = bias            # False: no biases (NULL), only with norm
         if norm:
@@ -131,12 +134,13 @@ class Case:
                 q.ravel(), k.ravel(), v.ravel(), *b, self.nw["wq"], self.nw["wk"], self.eps,
                 d["pos"], n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim,
                 theta=w.theta, n_ctx=self.n_ctx, cache_dtype=self.cd, slot=d["slot"],
-                n_slots=self.n_slots)
+                n_slots=self.n_slots, rope_style=self.style, freq_scale=self.freq_scale)
         else:
             rid, kr, vr, bad = oracle.qkv_epilogue(
                 q.ravel(), k.ravel(), v.ravel(), d["bq"], d["bk"], d["bv"], d["pos"],
                 n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim, theta=w.theta,
-                n_ctx=self.n_ctx, cache_dtype=self.cd, slot=d["slot"], n_slots=self.n_slots)
+                n_ctx=self.n_ctx, cache_dtype=self.cd, slot=d["slot"], n_slots=self.n_slots,
+                rope_style=self.style, freq_scale=self.freq_scale)
         self.o_q, self.o_k, self.o_v = q, k, v
         self.o_rows, self.o_krows, self.o_vrows, self.o_bad = rid, kr, vr, bad
         return self
@@ -198,7 +202,8 @@ class Case:
                            head_dim=w.head_dim, theta=w.theta, cache_dtype=self.cd,
                            slot=self.g_slot, n_ctx=self.n_ctx, n_slots=self.n_slots,
                            stream=stream if stream is not None else torch.cuda.current_stream(),
-                           use_stream=True, nt=self.nt)
+                           use_stream=True, nt=self.nt, rope_style=self.style,
+                           freq_scale=self.freq_scale)
 
     def download(self):
         self.r_q = self.g_q.cpu().numpy().reshape(self.nt, -1)

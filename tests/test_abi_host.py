@@ -50,6 +50,16 @@ def test_inv_freq_table_matches_oracle(theta, hd):
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
+@pytest.mark.parametrize("scale", [0.25, 1.0 / 3.0, 2.0, 1.0])
+@pytest.mark.parametrize("hd", [4, 64, 128, 96])
+def test_scaled_inv_freq_table_matches_oracle(scale, hd):
+    got = np.zeros(hd // 2, np.float32)
+    assert B.qkv_epilogue_inv_freq_scaled(1e6, scale, hd, got.ctypes.data) == 0
+    want = oracle.inv_freq_scaled(1e6, scale, hd)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert B.qkv_epilogue_inv_freq_scaled(1e6, 0.0, hd, got.ctypes.data) == B.QKV_ERR_INVALID_ARG
+
+
 def test_inv_freq_rejects_bad_input():
     buf = np.zeros(512, np.float32)
     for theta, hd in ((1e6, 3), (1e6, 0), (1e6, 514), (0.0, 4), (-1.0, 4), (float("inf"), 4),
@@ -80,6 +90,9 @@ def rc_of(a):
 
 def test_valid_args_ok():
     assert rc_of(base_args()) == (0, "")
+    assert rc_of(base_args(rope_style=B.QKV_ROPE_INTERLEAVED)) == (0, "")
+    assert rc_of(base_args(freq_scale=0.25)) == (0, "")
+    assert rc_of(base_args(rope_style=B.QKV_ROPE_INTERLEAVED, head_dim=6, n_head=2, n_kv_head=1)) == (0, "")
 
 
 @pytest.mark.parametrize("field", ["q", "k", "v", "bq", "bk", "bv", "pos", "kcache", "vcache"])
@@ -109,8 +122,11 @@ def test_nt_zero_is_noop_even_with_nulls():
     (dict(theta=float("inf")), B.QKV_ERR_INVALID_ARG),
     (dict(theta=float("nan")), B.QKV_ERR_INVALID_ARG),
     (dict(cache_dtype=2), B.QKV_ERR_INVALID_ARG),
-    (dict(rope_style=B.QKV_ROPE_INTERLEAVED), B.QKV_ERR_UNSUPPORTED),
     (dict(rope_style=7), B.QKV_ERR_UNSUPPORTED),
+    (dict(rope_style=-1), B.QKV_ERR_UNSUPPORTED),
+    (dict(freq_scale=-0.5), B.QKV_ERR_INVALID_ARG),
+    (dict(freq_scale=float("inf")), B.QKV_ERR_INVALID_ARG),
+    (dict(freq_scale=float("nan")), B.QKV_ERR_INVALID_ARG),
     (dict(ld_q=5119), B.QKV_ERR_INVALID_ARG),
     (dict(ld_k=1000), B.QKV_ERR_INVALID_ARG),
     (dict(ld_v=-1), B.QKV_ERR_INVALID_ARG),

@@ -180,6 +180,7 @@ def test_nt_zero_is_noop(handle):
 
 
 def test_invalid_requests_rejected(handle):
+    """Bad requests return their code and launch nothing."""
     c = Case(wl.TINY_DECODE).run_oracle().upload()
     w = c.w
     def args(**kw):
@@ -191,8 +192,7 @@ def test_invalid_requests_rejected(handle):
     assert B.qkv_epilogue_run_ex(handle, args(head_dim=63, n_head=1, n_kv_head=1)) == \
         B.QKV_ERR_INVALID_ARG
     assert "head_dim" in B.qkv_epilogue_last_error(handle)
-    assert B.qkv_epilogue_run_ex(handle, args(rope_style=B.QKV_ROPE_INTERLEAVED)) == \
-        B.QKV_ERR_UNSUPPORTED
+    assert B.qkv_epilogue_run_ex(handle, args(rope_style=5)) == B.QKV_ERR_UNSUPPORTED
     assert B.qkv_epilogue_run_ex(handle, args(theta=0.0)) == B.QKV_ERR_INVALID_ARG
     a = args()
     a.vcache = a.kcache

@@ -100,7 +100,7 @@ def test_out_of_range(handle):
 def test_unfused_rejects_like_fused(handle):
     c = Case(wl.TINY_DECODE).upload()
     a = c.args()
-    a.rope_style = B.QKV_ROPE_INTERLEAVED
+    a.rope_style = 5
     assert B.qkv_epilogue_run_unfused(handle, a) == B.QKV_ERR_UNSUPPORTED
     a = c.args()
     a.vcache = a.kcache

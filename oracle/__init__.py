@@ -68,6 +68,8 @@ def _bind(lib):
     lib.oracle_inv_freq_scaled.restype = None
     lib.oracle_rope_interleaved.argtypes = [P, I64, I64, I, I, P, P]
     lib.oracle_rope_interleaved.restype = None
+    lib.oracle_proj_bf16.argtypes = [P, I64, P, I64, I64, I64, P, I64]
+    lib.oracle_proj_bf16.restype = None
     lib.oracle_qkv_norm_epilogue.restype = I64
     return lib
 
@@ -287,3 +289,18 @@ def qkv_norm_epilogue(q, k, v, bq, bk, bv, wq, wk, eps, pos, *, n_head, n_kv_hea
     if bad < 0:
         raise ValueError("oracle: head_dim must be positive and even")
     return row_ids, krows, vrows, int(bad)
+
+
+def proj_bf16(x_bits, w_bits):
+    """Step P: y = x @ w.T with bfloat16 inputs (uint16 bit arrays [nt][hidden]
+    and [n_out][hidden]), exact products, double sum, one rounding to f32."""
+    for name, a in (("x", x_bits), ("w", w_bits)):
+        if not (isinstance(a, np.ndarray) and a.dtype == np.uint16 and a.ndim == 2
+                and a.flags.c_contiguous):
+            raise TypeError(f"{name} must be a C-contiguous 2-D uint16 (bfloat16 bits) array")
+    nt, hidden = x_bits.shape
+    n_out, h2 = w_bits.shape
+    assert h2 == hidden
+    y = np.zeros((nt, n_out), np.float32)
+    _load().oracle_proj_bf16(_ptr(x_bits), hidden, _ptr(w_bits), nt, n_out, hidden, _ptr(y), n_out)
+    return y

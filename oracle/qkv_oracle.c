@@ -141,6 +141,39 @@ void oracle_rope_interleaved(float *x, int64_t nt, int64_t ld, int n_heads,
 }
 
 /* ---------------------------------------------------------------------------
+ * Step P -- the concat QKV projection that feeds the epilogue.  The page
+ * "73 · D3-8" §2 ("Why the concat matmul is bitwise") and Excerpt C describe
+ * one matmul over the concat weight rows wq|wk|wv producing the q|k|v row of
+ * each token.  Here the activations and weights are bfloat16 (raw bits) and
+ *   y[t][n] = f32( sum_k x[t][k] * w[n][k] ),
+ * the products exact in double, the sum taken in double in k order, rounded
+ * once to f32.  w is [n_out][hidden] (one row per output feature); y is
+ * [nt][n_out] with row stride ld_y.
+ * ------------------------------------------------------------------------- */
+static double oracle_bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+void oracle_proj_bf16(const uint16_t *x, int64_t ld_x, const uint16_t *w,
+                      int64_t nt, int64_t n_out, int64_t hidden,
+                      float *y, int64_t ld_y)
+{
+    for (int64_t t = 0; t < nt; ++t) {
+        for (int64_t n = 0; n < n_out; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < hidden; ++k)
+                acc += oracle_bf16_to_double(x[t * ld_x + k]) *
+                       oracle_bf16_to_double(w[n * hidden + k]);
+            y[t * ld_y + n] = (float)acc;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
  * Step N -- per-head RMS norm (the q/k norm of the Qwen3-style variant).
  * Page "06 · Assign + fusion" §3.2 lists a per-head q/k norm op (QkNorm) and
  * the fused FusedQkvNorm, "the Qwen3 per-head-norm variant", without a

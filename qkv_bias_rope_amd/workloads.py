@@ -128,3 +128,33 @@ def step_positions(w: Workload, steps: int) -> np.ndarray:
 def concat_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
     """Pack per-token rows into one [nt][nqt + 2*nkt] q|k|v buffer."""
     return np.ascontiguousarray(np.concatenate([q, k, v], axis=1))
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even) and return the
+    uint16 bit patterns (input generation only)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def draw_projection(w: Workload, hidden: int, layer: int = 0, nt: int | None = None) -> dict:
+    """Inputs of the projection-fed epilogue: bfloat16 activations x [nt][hidden]
+    ~ N(0,1) and concat weight rows w [nqt+2*nkt][hidden] ~ N(0, 1/hidden) (so
+    the projected q/k/v are about N(0,1)), plus the epilogue's biases/positions
+    from draw_layer.  Stream seed*1000 + 700 + layer."""
+    nt = w.nt if nt is None else nt
+    rng = np.random.default_rng(w.seed * 1000 + 700 + layer)
+    x = bf16_bits(rng.standard_normal((nt, hidden), dtype=np.float32))
+    wt = bf16_bits(rng.standard_normal((w.nqt + 2 * w.nkt, hidden), dtype=np.float32)
+                   * np.float32(1.0 / np.sqrt(hidden)))
+    d = draw_layer(w, layer, nt=nt)
+    return dict(x=x, w=wt, bq=d["bq"], bk=d["bk"], bv=d["bv"], pos=d["pos"], slot=d["slot"])
+
+
+HIDDEN = {"decode_7b": 3584, "decode_14b": 5120, "prefill_14b_4096": 5120,
+          "batched_decode_14b_256seq": 5120, "tiny_decode_0.5b": 896}

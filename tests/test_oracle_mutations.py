@@ -15,6 +15,7 @@ import pytest
 import oracle
 import test_oracle_norm_pins as npins
 import test_oracle_pins as pins
+import test_oracle_proj_pins as ppins
 import test_oracle_rope_variants as rpins
 from qkv_bias_rope_amd import workloads as wl
 
@@ -88,6 +89,12 @@ MUTATIONS = [
     ("frequency scale ignored", [("(float)((double)freq_scale * pow((double)theta, e))", "(float)(pow((double)theta, e))")]),
     ("frequency scale divides", [("(float)((double)freq_scale * pow((double)theta, e))", "(float)(pow((double)theta, e) / (double)freq_scale)")]),
     ("rope style ignored", [("    if (rope_style == 0) {", "    if (1) {")]),
+    # projection
+    ("projection weight transposed", [("oracle_bf16_to_double(w[n * hidden + k])", "oracle_bf16_to_double(w[k * n_out + n])")]),
+    ("projection drops the last k", [("for (int64_t k = 0; k < hidden; ++k)\n                acc +=", "for (int64_t k = 0; k + 1 < hidden; ++k)\n                acc +=")]),
+    ("projection bf16 decoded as low half", [("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b;")]),
+    ("projection accumulates in f32", [("            double acc = 0.0;\n            for (int64_t k = 0; k < hidden; ++k)",
+                                        "            float acc = 0.0f;\n            for (int64_t k = 0; k < hidden; ++k)")]),
     ("bias after norm", [("    if (bq)\n        oracle_add_bias(q, bq, nt, nqt, ld_q);\n", ""),
                          ("    oracle_rms_norm_heads(q, nt, ld_q, n_head, head_dim, wq, eps);\n",
                           "    oracle_rms_norm_heads(q, nt, ld_q, n_head, head_dim, wq, eps);\n"
@@ -136,6 +143,10 @@ def _pin_calls():
         ("scale = halved position (NeoX)", lambda: rpins.test_power_of_two_scale_equals_scaled_position(0)),
         ("scale = halved position (interleaved)", lambda: rpins.test_power_of_two_scale_equals_scaled_position(1)),
         ("chain style and scale", rpins.test_chain_style_and_scale_are_applied),
+        ("projection exact rational", ppins.test_exact_rational_small),
+        ("projection identity", ppins.test_identity_weights_copy_the_input),
+        ("projection permutation", ppins.test_row_permutation_permutes_outputs),
+        ("projection numpy", ppins.test_matches_numpy_float64_matmul),
     ]
 
 

@@ -244,6 +244,99 @@ def bench_decode(h, w, steps, warmup, stream, unfused=False):
                 bytes_per_layer=algo_bytes(w, 1, cb), layers=w.layers)
 
 
+PEAK_BF16_TFLOPS = 2500.0
+
+
+class ProjSets:
+    """Input sets of the projection-fed epilogue: bf16 activations and concat
+    weights, f32 q/k/v outputs and the caches, R copies rotated so that the
+    weights and activations come from HBM on every launch."""
+
+    def __init__(self, w, hidden, R, cache_dtype, nt=None):
+        import numpy as np
+        import torch
+        from qkv_bias_rope_amd import workloads as wl
+        dev = "cuda:0"
+        d = wl.draw_projection(w, hidden, nt=nt)
+        self.w, self.hidden, self.cd = w, hidden, cache_dtype
+        self.nt = int(d["pos"].size)
+        cdt = torch.float16 if cache_dtype == wl.CACHE_F16 else torch.float32
+        x = torch.from_numpy(d["x"].view(np.int16)).to(dev)
+        wt = torch.from_numpy(d["w"].view(np.int16)).to(dev)
+        self.b = [torch.from_numpy(d[n]).to(dev) for n in ("bq", "bk", "bv")]
+        pos = torch.from_numpy(d["pos"]).to(dev)
+        slot = None if d["slot"] is None else torch.from_numpy(d["slot"]).to(dev)
+        rows = w.n_slots * w.n_ctx
+        # one K/V cache pair shared by the sets (the 256-slot cache is 17 GB;
+        # its rows land at random positions, so sharing gives no reuse)
+        kc = torch.empty((rows, w.nkt), dtype=cdt, device=dev)
+        vc = torch.empty((rows, w.nkt), dtype=cdt, device=dev)
+        self.sets = []
+        for r in range(R):
+            self.sets.append(dict(
+                x=x.clone() if r else x, w=wt.clone() if r else wt, pos=pos, slot=slot,
+                q=torch.empty((self.nt, w.nqt), device=dev),
+                k=torch.empty((self.nt, w.nkt), device=dev),
+                v=torch.empty((self.nt, w.nkt), device=dev), kc=kc, vc=vc))
+
+    def args(self, r, stream):
+        from qkv_bias_rope_amd import binding as B
+        s, w = self.sets[r % len(self.sets)], self.w
+        epi = B.make_args(s["q"], s["k"], s["v"], *self.b, s["pos"], s["kc"], s["vc"],
+                          n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim,
+                          theta=w.theta, cache_dtype=self.cd, slot=s["slot"], n_ctx=w.n_ctx,
+                          n_slots=w.n_slots, stream=stream, use_stream=True, nt=self.nt)
+        return B.make_proj_args(s["x"], s["w"], self.hidden, epi)
+
+
+def proj_bytes(w, nt, hidden, cb):
+    """Algorithmic HBM bytes of one projection-fed launch: x and W once, the
+    q/k/v rows written, the K/V cache rows, positions and biases."""
+    n = w.nqt + 2 * w.nkt
+    return (nt * hidden * 2 + n * hidden * 2 + nt * n * 4 + 2 * nt * w.nkt * cb + nt * 4
+            + n * 4)
+
+
+def bench_proj(h, w, hidden, steps, warmup, stream, min_set_bytes=1.5e9, nt=None):
+    """Projection-fed epilogue (one launch: bf16 GEMM/GEMV + epilogue)."""
+    import torch
+    from qkv_bias_rope_amd import binding as B
+    from qkv_bias_rope_amd import workloads as wl
+    cd = w.cache_dtypes[0]
+    cb = 2 if cd == wl.CACHE_F16 else 4
+    nt = w.nt if nt is None else nt
+    n = w.nqt + 2 * w.nkt
+    per_set = nt * hidden * 2 + n * hidden * 2 + nt * n * 4
+    R = max(2, int(-(-min_set_bytes // per_set)))
+    sets = ProjSets(w, hidden, R, cd, nt=nt)
+    args = [sets.args(r, stream) for r in range(R)]
+    ms = time_launches(h, args, steps, warmup, stream, fn=B.qkv_epilogue_run_proj)
+    flops = 2.0 * nt * n * hidden
+    nbytes = proj_bytes(w, nt, hidden, cb)
+    res = dict(us_per_launch=ms * 1e3, tflops=flops / (ms * 1e-3) / 1e12,
+               gbs=nbytes / (ms * 1e-3) / 1e9, flops=flops, bytes=nbytes, sets=R)
+    # reference: the library's bf16 GEMM of the same shape alone (bf16 out)
+    s0 = sets.sets[0]
+    xb, wb = s0["x"].view(torch.bfloat16), s0["w"].view(torch.bfloat16)
+    wbt = wb.t()
+    with torch.cuda.stream(stream):
+        for _ in range(5):
+            torch.matmul(xb, wbt)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        k = max(5, steps // 4)
+        e0.record(stream)
+        for _ in range(k):
+            torch.matmul(xb, wbt)
+        e1.record(stream)
+        e1.synchronize()
+    res["library_bf16_gemm_us"] = e0.elapsed_time(e1) / k * 1e3
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, cache_dtype, budget_s=10.0):
     """The oracle (single-threaded C, unfused chain) on the headline workload,
     repeated over whole launches until about budget_s seconds have passed."""
@@ -390,6 +483,29 @@ def run_all(args, h, stream):
                                           bytes_per_launch=r["bytes"],
                                           frac_of_peak=round(r["gbs"] / PEAK_HBM_GBS, 4))
         log(f"[bench]   {r['ms'] * 1e3:.2f} us/launch, {r['gbs']:.1f} GB/s")
+        # the projection feeding the epilogue, fused into one launch
+        hid = wl.HIDDEN[w.name]
+        log(f"[bench] {w.name} projection-fed epilogue (hidden {hid})")
+        r = bench_proj(h, w, hid, max(20, args.steps // 4), max(2, args.warmup // 4), stream,
+                       min_set_bytes=1.0e9)
+        extra[w.name + "_proj"] = dict(
+            us_per_launch=round(r["us_per_launch"], 2), tflops=round(r["tflops"], 1),
+            frac_of_bf16_peak=round(r["tflops"] / PEAK_BF16_TFLOPS, 4), hidden=hid,
+            library_bf16_gemm_us=round(r["library_bf16_gemm_us"], 2), input_sets=r["sets"])
+        log(f"[bench]   {r['us_per_launch']:.1f} us/launch, {r['tflops']:.1f} TFLOP/s "
+            f"(library bf16 GEMM alone {r['library_bf16_gemm_us']:.1f} us)")
+        wd = wl.DECODE_14B
+        hid = wl.HIDDEN[wd.name]
+        log(f"[bench] {wd.name} projection-fed epilogue, one token (hidden {hid})")
+        r = bench_proj(h, wd, hid, max(50, args.steps // 2), max(5, args.warmup // 2), stream,
+                       min_set_bytes=1.5e9)
+        extra[wd.name + "_proj"] = dict(
+            us_per_layer=round(r["us_per_launch"], 2), gbs=round(r["gbs"], 1),
+            frac_of_peak=round(r["gbs"] / PEAK_HBM_GBS, 4), bytes_per_layer=r["bytes"],
+            hidden=hid, library_bf16_gemm_us=round(r["library_bf16_gemm_us"], 2),
+            input_sets=r["sets"])
+        log(f"[bench]   {r['us_per_launch']:.1f} us/layer, {r['gbs']:.1f} GB/s "
+            f"(library bf16 GEMV alone {r['library_bf16_gemm_us']:.1f} us)")
 
     cpu = None
     if not args.no_cpu:

@@ -191,6 +191,37 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
                              const float *w_q, const float *w_k, float eps);
 
 /*
+ * The projection that feeds the epilogue, with the epilogue in its output
+ * stage (page "73 · D3-8 — G4 FusedQKV ported to CUDA", §2 and Excerpt C: one
+ * matmul over the concat weight rows wq|wk|wv produces each token's q|k|v
+ * row, which the epilogue consumes).  Per token t and output n:
+ *     y[t][n] = sum_k x[t][k] * w[n][k]      (bf16 inputs, f32 accumulation)
+ * then, on y split into its q, k, v sections, exactly the epilogue of
+ * qkv_epilogue_run_ex: optional biases, NeoX rotary embedding of q and k, the
+ * sections written to epi.q / epi.k / epi.v (outputs only here) and the K/V
+ * cache rows stored.  One launch: a matrix-core (MFMA) GEMM for more than 4
+ * tokens, a weight-streaming GEMV for 1-4 tokens.
+ *
+ *   x   bf16 [nt][ld_x] activations (device, 16-byte aligned, ld_x % 8 == 0)
+ *   w   bf16 [nqt + 2*nkt][hidden] concat weight rows q|k|v (device, aligned)
+ *   hidden  contraction length, a multiple of 32
+ *
+ * Limits (QKV_ERR_UNSUPPORTED otherwise): NeoX style, head_dim 64 or 128, q
+ * and k/v widths multiples of 128.  The f32 sums are taken in a different
+ * order than a plain loop: each output carries up to (hidden+2) * 2^-24 *
+ * sum_k |x w| of accumulation error on top of the epilogue's own rounding.
+ */
+typedef struct qkv_proj_args {
+    const void *x;          /* bf16 [nt][ld_x] */
+    const void *w;          /* bf16 [nqt + 2*nkt][hidden] */
+    int hidden;
+    int64_t ld_x;           /* 0 = hidden */
+    qkv_epilogue_args_t epi;  /* q/k/v are the outputs; biases may be NULL */
+} qkv_proj_args_t;
+
+int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *a);
+
+/*
  * The same operation as qkv_epilogue_run_ex, computed by the UNFUSED chain the
  * fused kernel replaces: three bias-add launches (q, k, v), two rope launches
  * (q, k) and two store launches (K, V), seven kernels in that order (page "73 ·

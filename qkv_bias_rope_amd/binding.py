@@ -39,7 +39,7 @@ EXPORTS = ("qkv_epilogue_create", "qkv_epilogue_run", "qkv_epilogue_run_ex",
            "qkv_epilogue_run_unfused", "qkv_epilogue_run_qk_norm",
            "qkv_epilogue_status", "qkv_epilogue_last_error", "qkv_epilogue_destroy",
            "qkv_epilogue_inv_freq", "qkv_epilogue_inv_freq_scaled", "qkv_epilogue_check_args",
-           "qkv_epilogue_plan")
+           "qkv_epilogue_plan", "qkv_epilogue_run_proj")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -65,6 +65,11 @@ class QkvEpilogueArgs(ctypes.Structure):
         ("stream", _P), ("use_stream", _I),
         ("freq_scale", _F),
     ]
+
+
+class QkvProjArgs(ctypes.Structure):
+    _fields_ = [("x", _P), ("w", _P), ("hidden", _I), ("ld_x", _I64),
+                ("epi", QkvEpilogueArgs)]
 
 
 class QkvEpiloguePlan(ctypes.Structure):
@@ -111,6 +116,8 @@ def _load():
     lib.qkv_epilogue_plan.argtypes = [ctypes.POINTER(QkvEpilogueArgs),
                                       ctypes.POINTER(QkvEpiloguePlan)]
     lib.qkv_epilogue_plan.restype = _I
+    lib.qkv_epilogue_run_proj.argtypes = [_P, ctypes.POINTER(QkvProjArgs)]
+    lib.qkv_epilogue_run_proj.restype = _I
     return lib
 
 
@@ -153,6 +160,22 @@ def qkv_epilogue_run_unfused(h, args: QkvEpilogueArgs) -> int:
 
 def qkv_epilogue_run_qk_norm(h, args: QkvEpilogueArgs, w_q, w_k, eps: float) -> int:
     return lib.qkv_epilogue_run_qk_norm(h, ctypes.byref(args), _addr(w_q), _addr(w_k), eps)
+
+
+def qkv_epilogue_run_proj(h, args: QkvProjArgs) -> int:
+    return lib.qkv_epilogue_run_proj(h, ctypes.byref(args))
+
+
+def make_proj_args(x, w, hidden, epi: QkvEpilogueArgs, ld_x=0) -> QkvProjArgs:
+    """Build the run_proj argument block: bf16 activations x and concat weight
+    rows w (tensors of any 2-byte dtype, or raw addresses), the contraction
+    length and the epilogue block whose q/k/v are the outputs."""
+    pa = QkvProjArgs()
+    pa.x, pa.w = _addr(x), _addr(w)
+    pa.hidden = hidden
+    pa.ld_x = ld_x
+    pa.epi = epi
+    return pa
 
 
 def qkv_epilogue_status(h) -> int:

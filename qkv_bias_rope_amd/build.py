@@ -11,7 +11,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", f) for f in ("qkv_epilogue.hip", "qkv_unfused.hip")]
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("qkv_epilogue.hip", "qkv_unfused.hip", "qkv_proj.hip")]
 HDRS = [os.path.join(ROOT, "include", "qkv_epilogue.h"), os.path.join(PKG, "csrc", "qkv_internal.h")]
 LIB = os.path.join(PKG, "libqkv_epilogue.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -1,0 +1,328 @@
+"""GPU parity of the projection-fed epilogue (qkv_epilogue_run_proj) against
+the CPU oracle: y = x w^T on bfloat16 inputs (oracle.proj_bf16, exact double
+sum), then the epilogue chain (oracle.qkv_epilogue) on the q|k|v sections of y.
+
+Tolerance, derived from the arithmetic.  Every bfloat16 product is exact in
+float32, so the GPU differs from the oracle only in how it sums: an f32
+accumulation of K terms in some order is within (K-1) * 2^-24 * S of the exact
+sum, S = sum_k |x_k w_k|; with the final rounding, the bias add and slack we
+take B = (K+4) * 2^-24 * S per element of y.  The rotation mixes the two
+elements of a pair with weights |cos|, |sin| <= 1, so a rotated element gets
+B(j) + B(partner).  On top comes the epilogue's own bar (2e-6 + 1e-6 |ref|).
+That bound is a worst case; the typical accumulation error is a random walk of
+about 2^-24 * sqrt(K) * |partial sums|, a few 1e-6 here, so the RMS of the
+error over a case must also stay below 1e-4 (a dropped k tile moves outputs by
+about 0.1).  Caches are checked structurally: every written row equals the
+GPU's own k / v output of that token (f32 bit-equal, or its binary16 RNE
+image), and exactly the oracle's rows change.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from qkv_bias_rope_amd import binding as B
+from qkv_bias_rope_amd import workloads as wl
+
+from parity_helpers import DEV, changed_rows, new_cache, say
+
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24
+RMS_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def handle():
+    rc, h = B.qkv_epilogue_create(0, 4096, None)
+    assert rc == B.QKV_OK, rc
+    yield h
+    B.qkv_epilogue_destroy(h)
+
+
+class ProjCase:
+    def __init__(self, w, hidden, nt=None, cache_dtype=None, form="separate", bias=True,
+                 pos=None, slot=None, sample=None, ld_x_pad=0):
+        self.w, self.hidden = w, hidden
+        d = wl.draw_projection(w, hidden, nt=nt)
+        if pos is not None:
+            d["pos"] = np.asarray(pos, np.int32)
+        if slot is not None:
+            d["slot"] = np.asarray(slot, np.int32)
+        self.d = d
+        self.nt = int(d["pos"].size)
+        self.cd = w.cache_dtypes[0] if cache_dtype is None else cache_dtype
+        self.form, self.bias = form, bias
+        self.ld_x_pad = ld_x_pad
+        # tokens the oracle recomputes (all of them unless a sample is given)
+        self.sample = np.arange(self.nt) if sample is None else np.asarray(sample)
+
+    # -- oracle on the sampled tokens --
+    def run_oracle(self):
+        w, d, s = self.w, self.d, self.sample
+        nqt, nkt = w.nqt, w.nkt
+        xs = np.ascontiguousarray(d["x"][s])
+        y = oracle.proj_bf16(xs, d["w"])
+        S = np.abs(wl.bf16_to_f32(xs).astype(np.float64)) @ \
+            np.abs(wl.bf16_to_f32(d["w"]).astype(np.float64)).T
+        q = np.ascontiguousarray(y[:, :nqt])
+        k = np.ascontiguousarray(y[:, nqt:nqt + nkt])
+        v = np.ascontiguousarray(y[:, nqt + nkt:])
+        if self.bias:
+            b = (d["bq"], d["bk"], d["bv"])
+        else:
+            b = (np.zeros(nqt, np.float32), np.zeros(nkt, np.float32), np.zeros(nkt, np.float32))
+        slot = None if d["slot"] is None else np.ascontiguousarray(d["slot"][s])
+        rid, kr, vr, bad = oracle.qkv_epilogue(
+            q.ravel(), k.ravel(), v.ravel(), *b, np.ascontiguousarray(d["pos"][s]),
+            n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim, theta=w.theta,
+            n_ctx=w.n_ctx, cache_dtype=self.cd, slot=slot, n_slots=w.n_slots)
+        self.o = dict(q=q, k=k, v=v, S=S)
+        # the cache rows of every token (addressing only: the chain on zeros)
+        zq = np.zeros(self.nt * nqt, np.float32)
+        zk = np.zeros(self.nt * nkt, np.float32)
+        zv = np.zeros(self.nt * nkt, np.float32)
+        self.all_rows, _, _, self.n_bad = oracle.qkv_epilogue(
+            zq, zk, zv, np.zeros(nqt, np.float32), np.zeros(nkt, np.float32),
+            np.zeros(nkt, np.float32), d["pos"], n_head=w.n_head, n_kv_head=w.n_kv_head,
+            head_dim=w.head_dim, theta=w.theta, n_ctx=w.n_ctx, cache_dtype=self.cd,
+            slot=d["slot"], n_slots=w.n_slots)
+        return self
+
+    # -- gpu --
+    def upload(self):
+        w, d = self.w, self.d
+        nqt, nkt, nt = w.nqt, w.nkt, self.nt
+        ldx = self.hidden + self.ld_x_pad
+        xp = np.zeros((nt, ldx), np.uint16)
+        xp[:, :self.hidden] = d["x"]
+        self.g_x = torch.from_numpy(xp.view(np.int16)).to(DEV)
+        self.ld_x = ldx if self.ld_x_pad else 0
+        self.g_w = torch.from_numpy(d["w"].view(np.int16)).to(DEV)
+        if self.form == "concat":
+            self.g_buf = torch.full((nt, nqt + 2 * nkt), float("nan"), device=DEV)
+            self.g_q = self.g_buf[:, :nqt]
+            self.g_k = self.g_buf[:, nqt:nqt + nkt]
+            self.g_v = self.g_buf[:, nqt + nkt:]
+        else:
+            self.g_q = torch.full((nt, nqt), float("nan"), device=DEV)
+            self.g_k = torch.full((nt, nkt), float("nan"), device=DEV)
+            self.g_v = torch.full((nt, nkt), float("nan"), device=DEV)
+        if self.bias:
+            self.g_b = [torch.from_numpy(d[n]).to(DEV) for n in ("bq", "bk", "bv")]
+        else:
+            self.g_b = [None, None, None]
+        self.g_pos = torch.from_numpy(d["pos"]).to(DEV)
+        self.g_slot = None if d["slot"] is None else torch.from_numpy(d["slot"]).to(DEV)
+        rows = w.n_slots * w.n_ctx
+        self.kc = new_cache(rows, nkt, self.cd)
+        self.vc = new_cache(rows, nkt, self.cd)
+        return self
+
+    def args(self):
+        w = self.w
+        epi = B.make_args(self.g_q, self.g_k, self.g_v, *self.g_b, self.g_pos, self.kc, self.vc,
+                          n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim,
+                          theta=w.theta, cache_dtype=self.cd, slot=self.g_slot, n_ctx=w.n_ctx,
+                          n_slots=w.n_slots, stream=torch.cuda.current_stream(),
+                          use_stream=True, nt=self.nt)
+        return B.make_proj_args(self.g_x, self.g_w, self.hidden, epi, ld_x=self.ld_x)
+
+    def run_gpu(self, h):
+        return B.qkv_epilogue_run_proj(h, self.args())
+
+    # -- comparison --
+    def check(self, label=""):
+        w, s = self.w, self.sample
+        nqt, nkt, hd, half = w.nqt, w.nkt, w.head_dim, w.head_dim // 2
+        idx = torch.from_numpy(s.astype(np.int64)).to(DEV)
+        got = {n: t.index_select(0, idx).cpu().numpy() for n, t in
+               (("q", self.g_q), ("k", self.g_k), ("v", self.g_v))}
+        S = self.o["S"]
+        K = self.hidden
+        bnd = (K + 4) * U32 * S
+        secs = {"q": bnd[:, :nqt], "k": bnd[:, nqt:nqt + nkt], "v": bnd[:, nqt + nkt:]}
+        for name in ("q", "k", "v"):
+            g = got[name].astype(np.float64)
+            o = self.o[name].astype(np.float64)
+            b = secs[name]
+            if name != "v":
+                # partner of column j inside its head: j +- half
+                bh = b.reshape(b.shape[0], -1, 2, half)
+                b = (bh + bh[:, :, ::-1, :]).reshape(b.shape)
+            tol = 2e-6 + 1e-6 * np.abs(o) + b
+            err = np.abs(g - o)
+            nbad = int((err > tol).sum())
+            rms = float(np.sqrt(np.mean(err ** 2))) if err.size else 0.0
+            say(f"  {label} {name}: max err {err.max():.3g}, rms {rms:.3g}, "
+                f"max bound {tol.max():.3g}")
+            assert np.isfinite(g).all(), f"{label} {name}: non-finite outputs"
+            assert nbad == 0, f"{label} {name}: {nbad} elements beyond the accumulation bound"
+            assert rms <= RMS_TOL, f"{label} {name}: rms error {rms:.3g} > {RMS_TOL}"
+
+        # addressing: exactly the oracle's rows change
+        rows_all = self.all_rows[self.all_rows >= 0]
+        for nm, cache in (("K", self.kc), ("V", self.vc)):
+            ch = changed_rows(cache, self.cd)
+            assert np.array_equal(np.sort(ch), np.unique(rows_all)), \
+                f"{label} {nm} cache: changed rows differ from the oracle's"
+        # contents: each sampled token's row is the store of its own k / v
+        rid = self.all_rows[s]
+        ok = rid >= 0
+        if ok.any():
+            ridx = torch.from_numpy(rid[ok]).to(DEV)
+            for nm, cache, mine in (("K", self.kc, got["k"]), ("V", self.vc, got["v"])):
+                c = cache.index_select(0, ridx).cpu().numpy()
+                if self.cd == wl.CACHE_F32:
+                    eq = c.view(np.uint32) == mine[ok].view(np.uint32)
+                else:
+                    eq = c.view(np.uint16) == mine[ok].astype(np.float16).view(np.uint16)
+                # tokens sharing a row (equal positions) race: per element, the
+                # row holds the store of one of them
+                uniq, inv = np.unique(rid[ok], return_inverse=True)
+                grp = np.zeros((uniq.size, eq.shape[1]), bool)
+                np.logical_or.at(grp, inv, eq)
+                assert grp.all(), \
+                    f"{label} {nm} cache rows are not the store of the tokens' own outputs"
+
+
+def _run(h, c, label):
+    say(f"[proj] {label}: nt={c.nt} hidden={c.hidden} N={c.w.nqt + 2 * c.w.nkt} "
+        f"hd={c.w.head_dim} cache={'f16' if c.cd else 'f32'} form={c.form}")
+    c.run_oracle().upload()
+    rc = c.run_gpu(h)
+    assert rc == B.QKV_OK, B.qkv_epilogue_last_error(h)
+    st = B.qkv_epilogue_status(h)
+    torch.cuda.synchronize()
+    return st
+
+
+SMALL_14B = wl.Workload("proj_small_14b", 40, 8, 128, nt=300, n_ctx=4096, n_slots=1, layers=1,
+                        seed=11, pos_mode="arange")
+SMALL_7B = wl.Workload("proj_small_7b", 28, 4, 128, nt=130, n_ctx=4096, n_slots=1, layers=1,
+                       seed=12, cache_dtypes=(wl.CACHE_F32,))
+SMALL_05B = wl.Workload("proj_small_0.5b", 14, 2, 64, nt=257, n_ctx=512, n_slots=1, layers=1,
+                        seed=13, cache_dtypes=(wl.CACHE_F32,))
+
+
+@pytest.mark.parametrize("cd", [wl.CACHE_F16, wl.CACHE_F32])
+def test_proj_prefill_small_14b(handle, cd):
+    """Several 128x256 tiles and a ragged tail of 44 tokens, 14B geometry."""
+    c = ProjCase(SMALL_14B, hidden=1024, cache_dtype=cd)
+    assert _run(handle, c, "small_14b") == B.QKV_OK
+    c.check("small_14b")
+
+
+def test_proj_concat_outputs_7b(handle):
+    """Outputs as views of one concat q|k|v buffer (row stride N), 7B width."""
+    c = ProjCase(SMALL_7B, hidden=3584, form="concat")
+    assert _run(handle, c, "concat_7b") == B.QKV_OK
+    c.check("concat_7b")
+
+
+def test_proj_head_dim_64_no_bias(handle):
+    """hd 64 (two heads per wave tile) and NULL biases, 0.5B geometry."""
+    c = ProjCase(SMALL_05B, hidden=896, bias=False)
+    assert _run(handle, c, "hd64_nobias") == B.QKV_OK
+    c.check("hd64_nobias")
+
+
+def test_proj_padded_activation_rows(handle):
+    """x rows with a stride larger than hidden."""
+    c = ProjCase(SMALL_05B, hidden=512, nt=70, ld_x_pad=24)
+    assert _run(handle, c, "ldx_pad") == B.QKV_OK
+    c.check("ldx_pad")
+
+
+@pytest.mark.parametrize("nt", [1, 2, 3, 4])
+def test_proj_decode_gemv(handle, nt):
+    """1-4 tokens take the weight-streaming kernel; 14B decode geometry."""
+    c = ProjCase(wl.DECODE_14B, hidden=5120, nt=nt)
+    assert _run(handle, c, f"gemv_nt{nt}") == B.QKV_OK
+    c.check(f"gemv_nt{nt}")
+
+
+def test_proj_gemv_hd64_slots(handle):
+    """GEMV path with hd 64 and per-token cache slots."""
+    w = wl.Workload("proj_gemv_slots", 14, 2, 64, nt=4, n_ctx=64, n_slots=4, layers=1, seed=14,
+                    cache_dtypes=(wl.CACHE_F16,))
+    c = ProjCase(w, hidden=896)
+    assert _run(handle, c, "gemv_slots") == B.QKV_OK
+    c.check("gemv_slots")
+
+
+def test_proj_five_tokens(handle):
+    """The smallest launch on the MFMA path: one ragged 128-token tile."""
+    c = ProjCase(wl.DECODE_7B, hidden=3584, nt=5)
+    assert _run(handle, c, "nt5") == B.QKV_OK
+    c.check("nt5")
+
+
+def test_proj_out_of_range_position(handle):
+    """A token with a bad position: its q/k/v are still written, no cache row,
+    and the status reports the range error (MFMA and GEMV paths)."""
+    for nt in (3, 40):
+        pos = np.arange(nt, dtype=np.int32) * 7
+        pos[1] = 4096 + 5   # beyond n_ctx
+        c = ProjCase(wl.DECODE_14B, hidden=512, nt=nt, pos=pos)
+        st = _run(handle, c, f"bad_pos_nt{nt}")
+        assert st == B.QKV_ERR_POSITION_RANGE, st
+        assert c.n_bad == 1
+        c.check(f"bad_pos_nt{nt}")
+
+
+def test_proj_prefill_full_size_sampled(handle):
+    """4096 tokens x hidden 5120, the prefill launch the benchmark times;
+    the oracle recomputes a sample of tokens (both ends of every tile edge
+    region and random ones), addressing is checked for all tokens."""
+    rng = np.random.default_rng(7)
+    sample = np.unique(np.concatenate([[0, 1, 127, 128, 2047, 4094, 4095],
+                                       rng.integers(0, 4096, 41)]))
+    c = ProjCase(wl.PREFILL_14B, hidden=5120, sample=sample)
+    assert _run(handle, c, "prefill_full") == B.QKV_OK
+    c.check("prefill_full")
+
+
+def test_proj_batched_full_size_sampled(handle):
+    """256 sequences, one token each, slot per sequence, hidden 5120."""
+    rng = np.random.default_rng(8)
+    sample = np.unique(np.concatenate([[0, 127, 128, 255], rng.integers(0, 256, 28)]))
+    c = ProjCase(wl.BATCHED_DECODE_14B, hidden=5120, sample=sample)
+    assert _run(handle, c, "batched_full") == B.QKV_OK
+    c.check("batched_full")
+
+
+def test_proj_rejects_unsupported(handle):
+    """Requests outside the projection path's limits fail before any launch."""
+    c = ProjCase(SMALL_05B, hidden=512, nt=8).upload()
+    base = c.args()
+    a = c.args()
+    a.epi.rope_style = B.QKV_ROPE_INTERLEAVED
+    assert B.qkv_epilogue_run_proj(handle, a) == B.QKV_ERR_UNSUPPORTED
+    a = c.args()
+    a.hidden = 100
+    assert B.qkv_epilogue_run_proj(handle, a) == B.QKV_ERR_INVALID_ARG
+    a = c.args()
+    a.ld_x = 500
+    assert B.qkv_epilogue_run_proj(handle, a) == B.QKV_ERR_INVALID_ARG
+    a = c.args()
+    a.x = c.g_q.data_ptr()   # activations overlapping the q output
+    assert B.qkv_epilogue_run_proj(handle, a) == B.QKV_ERR_ALIAS
+    a = c.args()
+    a.w = c.kc.data_ptr()    # weights overlapping the K cache
+    assert B.qkv_epilogue_run_proj(handle, a) == B.QKV_ERR_ALIAS
+    a = c.args()
+    a.x = c.g_x.data_ptr() + 2   # misaligned
+    assert B.qkv_epilogue_run_proj(handle, a) == B.QKV_ERR_INVALID_ARG
+    # head_dim 96 (widths not multiples of 128 either)
+    w96 = wl.Workload("hd96", 4, 4, 96, nt=8, n_ctx=64, n_slots=1, layers=1, seed=15,
+                      cache_dtypes=(wl.CACHE_F32,))
+    c96 = ProjCase(w96, hidden=256).upload()
+    assert B.qkv_epilogue_run_proj(handle, c96.args()) == B.QKV_ERR_UNSUPPORTED
+    # nothing was launched: the outputs still hold their NaN fill
+    torch.cuda.synchronize()
+    assert torch.isnan(c.g_q).all() and torch.isnan(c96.g_q).all()
+    assert B.qkv_epilogue_run_proj(handle, base) == B.QKV_OK
+    assert B.qkv_epilogue_status(handle) == B.QKV_OK

@@ -204,7 +204,7 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  *
  *   x   bf16 [nt][ld_x] activations (device, 16-byte aligned, ld_x % 8 == 0)
  *   w   bf16 [nqt + 2*nkt][hidden] concat weight rows q|k|v (device, aligned)
- *   hidden  contraction length, a multiple of 32
+ *   hidden  contraction length, a multiple of 64
  *
  * Limits (QKV_ERR_UNSUPPORTED otherwise): NeoX style, head_dim 64 or 128, q
  * and k/v widths multiples of 128.  The f32 sums are taken in a different

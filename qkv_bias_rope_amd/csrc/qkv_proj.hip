@@ -13,9 +13,11 @@
 // both operands are 16 contiguous bytes of a k-contiguous row) and receives
 // D[8*(v/4) + 4*(l/32) + v%4][l%32], v < 16.
 //
-//  * Block tile 128 tokens x 256 outputs, four waves of 64 x 128; k tiles of
-//    32 staged through double-buffered LDS (rows padded to 80 bytes so the
-//    16-byte operand reads of 32 rows hit distinct banks).
+//  * Block tiles of 256 tokens x 256 outputs (four waves of 128 x 128, k
+//    tiles of 64) for long prompts, 32 x 256 (two waves of 32 x 128, k tiles
+//    of 32) for a few hundred tokens; operands staged through double-buffered
+//    LDS, rows padded by 16 bytes so the 16-byte fragment reads of
+//    consecutive rows hit distinct banks.
 //  * A wave's 128 output columns are one head (hd 128) or two (hd 64), so the
 //    NeoX partner of column j (j + hd/2) sits in the same lane, in the MFMA
 //    tile hd/64 tiles to the right: the rotation needs no data exchange.
@@ -41,11 +43,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128;        // tokens per block
-constexpr int BN = 256;        // outputs per block
-constexpr int BK = 32;         // k per stage
-constexpr int ROWB = 80;       // LDS bytes per staged row (64 data + 16 pad)
-constexpr int kThreads = 256;
 
 struct ProjParams {
     const uint16_t *x;       // bf16 [nt][ld_x]
@@ -94,61 +91,83 @@ __device__ __forceinline__ void put_cache(void *cache, int64_t off, float v)
 // ---------------------------------------------------------------------------
 // prefill / batched: MFMA GEMM + epilogue
 // ---------------------------------------------------------------------------
-template <bool F16, int HD>
-__global__ __launch_bounds__(kThreads) void proj_mfma_kernel(ProjParams p, InvTable inv)
+// Block = WM x WN waves; wave (wm, wn) owns MI*32 tokens x 128 outputs, i.e.
+// MI x 4 tiles of 32x32.  Block tile BM = WM*MI*32 tokens, BN = WN*128
+// outputs; k advances BK at a time through two LDS stages of (BM + BN) rows,
+// each row BK bf16 plus 16 bytes of padding (the 16-byte fragment reads of
+// 16 consecutive rows then fall on distinct banks).
+template <int WM, int WN, int MI, int BK>
+struct Tile {
+    static constexpr int WM_ = WM, WN_ = WN, MI_ = MI, BK_ = BK;
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int BM = WM * MI * 32;
+    static constexpr int BN = WN * 128;
+    static constexpr int kChunks = BK / 8;                 // 16-byte chunks per row
+    static constexpr int kPitch = BK * 2 + 16;             // LDS bytes per row
+    static constexpr int kStage = (BM + BN) * kPitch;
+    static constexpr int kA = BM * kChunks / kThreads;     // A chunks per thread
+    static constexpr int kB = BN * kChunks / kThreads;     // B chunks per thread
+    static_assert(BM * kChunks % kThreads == 0 && BN * kChunks % kThreads == 0, "tile");
+    static_assert(kThreads % kChunks == 0, "tile");
+    static int lds_bytes(int hd)
+    {
+        const int stage = 2 * kStage;
+        const int table = BM * (hd / 2) * 8;
+        return stage > table ? stage : table;
+    }
+};
+
+template <bool F16, int HD, class T>
+__global__ __launch_bounds__(T::kThreads) void proj_mfma_kernel(ProjParams p, InvTable inv)
 {
     extern __shared__ __align__(16) unsigned char lds[];
-    // staging: two buffers of [BM + BN] rows x ROWB bytes
-    constexpr int kStage = (BM + BN) * ROWB;
+    constexpr int BM = T::BM, BN = T::BN, BK = T::BK_, MI = T::MI_;
+    constexpr int NT = T::kThreads;
 
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / T::WN_, wn = wave % T::WN_;
     const int nblk = p.N / BN + (p.N % BN ? 1 : 0);
     const int n0 = ((int)blockIdx.x % nblk) * BN;
     const int m0 = ((int)blockIdx.x / nblk) * BM;
 
-    // global -> register staging: A 128 rows x 4 chunks (2 per thread), B 256
-    // rows x 4 chunks (4 per thread); out-of-range rows read a clamped row
-    const int ch = tid & 3;
-    int arow[2], brow[4];
+    // global -> register staging: chunk e = tid + NT*j is row e / kChunks,
+    // 16-byte chunk e % kChunks; rows past the end read a clamped row
+    const int ch = tid % T::kChunks;
+    const int r0 = tid / T::kChunks;
+    constexpr int RSTEP = NT / T::kChunks;   // rows between a thread's chunks
+    const uint16_t *ap[T::kA], *bp[T::kB];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-        arow[j] = (tid >> 2) + 64 * j;
+    for (int j = 0; j < T::kA; ++j)
+        ap[j] = p.x + (int64_t)min(m0 + r0 + RSTEP * j, p.M - 1) * p.ld_x + ch * 8;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        brow[j] = (tid >> 2) + 64 * j;
-    const uint16_t *ap[2], *bp[4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-        ap[j] = p.x + (int64_t)min(m0 + arow[j], p.M - 1) * p.ld_x + ch * 8;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        bp[j] = p.w + (int64_t)min(n0 + brow[j], p.N - 1) * p.K + ch * 8;
+    for (int j = 0; j < T::kB; ++j)
+        bp[j] = p.w + (int64_t)min(n0 + r0 + RSTEP * j, p.N - 1) * p.K + ch * 8;
 
-    u32x4 ra[2], rb[4];
+    u32x4 ra[T::kA], rb[T::kB];
     auto gload = [&](int k0) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < T::kA; ++j)
             ra[j] = *reinterpret_cast<const u32x4 *>(ap[j] + k0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < T::kB; ++j)
             rb[j] = *reinterpret_cast<const u32x4 *>(bp[j] + k0);
     };
     auto lstore = [&](int buf) {
-        unsigned char *s = lds + buf * kStage;
+        unsigned char *s = lds + buf * T::kStage + r0 * T::kPitch + ch * 16;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            *reinterpret_cast<u32x4 *>(s + arow[j] * ROWB + ch * 16) = ra[j];
+        for (int j = 0; j < T::kA; ++j)
+            *reinterpret_cast<u32x4 *>(s + RSTEP * j * T::kPitch) = ra[j];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<u32x4 *>(s + (BM + brow[j]) * ROWB + ch * 16) = rb[j];
+        for (int j = 0; j < T::kB; ++j)
+            *reinterpret_cast<u32x4 *>(s + (BM + RSTEP * j) * T::kPitch) = rb[j];
     };
 
-    f32x16 acc[2][4];
+    f32x16 acc[MI][4];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
@@ -160,23 +179,23 @@ __global__ __launch_bounds__(kThreads) void proj_mfma_kernel(ProjParams p, InvTa
     lstore(0);
     __syncthreads();
     const int lr = lane & 31, lk = (lane >> 5) * 16;  // row in tile, byte offset of k chunk
+    const int arow = (wm * MI * 32 + lr) * T::kPitch + lk;
+    const int brow = (BM + wn * 128 + lr) * T::kPitch + lk;
     for (int kt = 0; kt < KT; ++kt) {
         if (kt + 1 < KT)
             gload((kt + 1) * BK);
-        const unsigned char *s = lds + (kt & 1) * kStage;
+        const unsigned char *s = lds + (kt & 1) * T::kStage;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 a[2], b[4];
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            bf16x8 a[MI], b[4];
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-                a[mi] = *reinterpret_cast<const bf16x8 *>(
-                    s + (wm * 64 + mi * 32 + lr) * ROWB + ks * 32 + lk);
+            for (int mi = 0; mi < MI; ++mi)
+                a[mi] = *reinterpret_cast<const bf16x8 *>(s + arow + mi * 32 * T::kPitch + ks * 32);
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
-                b[ni] = *reinterpret_cast<const bf16x8 *>(
-                    s + (BM + wn * 128 + ni * 32 + lr) * ROWB + ks * 32 + lk);
+                b[ni] = *reinterpret_cast<const bf16x8 *>(s + brow + ni * 32 * T::kPitch + ks * 32);
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
+            for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 4; ++ni)
                     acc[mi][ni] =
@@ -191,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void proj_mfma_kernel(ProjParams p, InvTa
     constexpr int HALF = HD / 2;
     float *s_cos = reinterpret_cast<float *>(lds);
     float *s_sin = s_cos + BM * HALF;
-    for (int e = tid; e < BM * HALF; e += kThreads) {
+    for (int e = tid; e < BM * HALF; e += NT) {
         const int r = e / HALF, i = e - (e / HALF) * HALF;
         const float a = (float)p.pos[min(m0 + r, p.M - 1)] * inv.v[i];
         double sd, cd;
@@ -216,10 +235,10 @@ __global__ __launch_bounds__(kThreads) void proj_mfma_kernel(ProjParams p, InvTa
     void *const cache = sec == 1 ? p.cache[0] : p.cache[1];
 
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
+    for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int rt = wm * 64 + mi * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v & 3);
+            const int rt = wm * MI * 32 + mi * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v & 3);
             const int t = m0 + rt;
             if (t >= p.M)
                 continue;
@@ -254,140 +273,385 @@ __global__ __launch_bounds__(kThreads) void proj_mfma_kernel(ProjParams p, InvTa
 }
 
 // ---------------------------------------------------------------------------
-// decode (few tokens): weight-streaming GEMV + epilogue
+// long prompts: 256 x 256 tiles, operands loaded straight into LDS
 // ---------------------------------------------------------------------------
-// Block = 256 threads = 4 waves, 16 NeoX pairs = 32 output columns of one
-// section (columns c0+j and c0+j+HALF, j < 16); each wave computes 8 columns
-// for every token, a lane covering K/64 of each dot product.
-constexpr int kGemvTok = 4;   // tokens per GEMV launch chunk
+// Four waves of 128 x 128 (4 x 4 MFMA tiles each), k tiles of 64.  Each k
+// tile of A (256 token rows) and B (256 weight rows) is 32 KB; every wave
+// issues 8 + 8 global->LDS loads of 1 KB (64 lanes x 16 bytes) per tile, so
+// the operands never pass through registers.  Rows are 128 bytes (8 chunks
+// of 16) with no padding; chunk c of row r sits in slot c ^ g(r),
+// g(r) = (r & 7) ^ ((r >> 3) & 1), which makes the 16-byte fragment reads
+// of 16 consecutive rows hit distinct banks (with 32 or 64 banks of 4 bytes).
+namespace big {
+constexpr int BM = 256, BN = 256, BK = 64, MI = 4;
+constexpr int kThreads = 256;
+constexpr int kRow = BK * 2;                  // 128 bytes
+constexpr int kRegion = 256 * kRow;           // 32 KB for A or B
+constexpr int kStage = 2 * kRegion;           // 64 KB
+constexpr int kLds = 2 * kStage;              // 128 KB (also holds the 256 x 64 cos/sin table)
+
+__device__ __forceinline__ int swz(int r)
+{
+    return (r & 7) ^ ((r >> 3) & 1);
+}
+}  // namespace big
 
 template <bool F16, int HD>
-__global__ __launch_bounds__(kThreads) void proj_gemv_kernel(ProjParams p, InvTable inv, int t0)
+__global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams p, InvTable inv)
 {
-    __shared__ float s_y[kGemvTok][32];
-    constexpr int HALF = HD / 2;
+    using namespace big;
+    extern __shared__ __align__(16) unsigned char lds[];
+
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    // block -> (head, pair group): pair groups of 16 inside each head's HALF pairs
-    const int groups = HALF / 16;
-    const int head = (int)blockIdx.x / groups;
-    const int g = (int)blockIdx.x - head * groups;
-    const int hcol = head * HD;                 // first column of the head (global)
-    const int nt = min(kGemvTok, p.M - t0);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nblk = p.N / BN + (p.N % BN ? 1 : 0);
+    const int n0 = ((int)blockIdx.x % nblk) * BN;
+    const int m0 = ((int)blockIdx.x / nblk) * BM;
 
-    // this wave's 8 columns: local c in [wave*8, wave*8+8) of the block's 32;
-    // local c < 16 -> column hcol + g*16 + c, else hcol + HALF + g*16 + (c-16)
-    float dot[8][kGemvTok];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int tt = 0; tt < kGemvTok; ++tt)
-            dot[j][tt] = 0.0f;
-    int col[8];
+    // loads: wave w fills rows [64w, 64w + 64) of the A and the B region;
+    // instruction j covers rows 64w + 8j + lane/8, lane%8 is the LDS slot
+    // and the chunk it holds is slot ^ g(row) (row & 7 = lane/8, bit 3 of the
+    // row is the parity of j).  Offsets are bytes from x / w (both < 2 GiB).
+    const int lrow = lane >> 3, slot = lane & 7;
+    uint32_t aoff[8], boff[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const int c = wave * 8 + j;
-        col[j] = hcol + (c < 16 ? g * 16 + c : HALF + g * 16 + (c - 16));
+        const int r = 64 * wave + 8 * j + lrow;
+        const int c = slot ^ (lrow ^ (j & 1));
+        aoff[j] = (uint32_t)((int64_t)min(m0 + r, p.M - 1) * p.ld_x * 2) + c * 16;
+        boff[j] = (uint32_t)((int64_t)min(n0 + r, p.N - 1) * p.K * 2) + c * 16;
     }
-    for (int k0 = lane * 8; k0 < p.K; k0 += 64 * 8) {
-        float xv[kGemvTok][8];
-#pragma unroll
-        for (int tt = 0; tt < kGemvTok; ++tt) {
-            const u32x4 xr = *reinterpret_cast<const u32x4 *>(
-                p.x + (int64_t)(t0 + min(tt, nt - 1)) * p.ld_x + k0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                xv[tt][2 * e] = __uint_as_float(xr[e] << 16);
-                xv[tt][2 * e + 1] = __uint_as_float(xr[e] & 0xffff0000u);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const u32x4 wr = *reinterpret_cast<const u32x4 *>(p.w + (int64_t)col[j] * p.K + k0);
-            float wv[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                wv[2 * e] = __uint_as_float(wr[e] << 16);
-                wv[2 * e + 1] = __uint_as_float(wr[e] & 0xffff0000u);
-            }
-#pragma unroll
-            for (int tt = 0; tt < kGemvTok; ++tt)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    dot[j][tt] = fmaf(xv[tt][e], wv[e], dot[j][tt]);
-        }
-    }
-    // reduce across the wave
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int tt = 0; tt < kGemvTok; ++tt) {
-            float v = dot[j][tt];
-            for (int m = 32; m >= 1; m >>= 1)
-                v += __shfl_xor(v, m, 64);
-            dot[j][tt] = v;
-        }
-    if (lane == 0) {
+    const unsigned char *xb = reinterpret_cast<const unsigned char *>(p.x);
+    const unsigned char *wb = reinterpret_cast<const unsigned char *>(p.w);
+    typedef __attribute__((address_space(3))) void lds_t;
+    auto issue = [&](int stage, int k0) {
+        unsigned char *sa = lds + stage * kStage + (64 * wave) * kRow;
+        unsigned char *sb = sa + kRegion;
+        const uint32_t kb = (uint32_t)k0 * 2;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
+            __builtin_amdgcn_global_load_lds(xb + aoff[j] + kb, (lds_t *)(sa + j * 8 * kRow), 16, 0, 0);
 #pragma unroll
-            for (int tt = 0; tt < kGemvTok; ++tt)
-                s_y[tt][wave * 8 + j] = dot[j][tt];
+        for (int j = 0; j < 8; ++j)
+            __builtin_amdgcn_global_load_lds(wb + boff[j] + kb, (lds_t *)(sb + j * 8 * kRow), 16, 0, 0);
+    };
+
+    f32x16 acc[MI][4];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[mi][ni][v] = 0.0f;
+
+    // fragment reads: lane reads row lr of each 32-row tile, chunk 2*ks + hi
+    const int lr = lane & 31, hi = lane >> 5;
+    const int g = big::swz(lr);                 // tiles start at multiples of 32
+    const int abase = (wm * 128 + lr) * kRow;
+    const int bbase = kRegion + (wn * 128 + lr) * kRow;
+    int koff[BK / 16];
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks)
+        koff[ks] = ((2 * ks + hi) ^ g) * 16;
+
+    const int KT = p.K / BK;
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) etc.: this wave's loads landed
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        // next tile into the other stage (the last iteration reloads the last
+        // tile: the loop body stays one straight-line region)
+        issue((kt + 1) & 1, min(kt + 1, KT - 1) * BK);
+        const unsigned char *s = lds + (kt & 1) * kStage;
+        bf16x8 a[2][MI], b[2][4];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+            a[0][mi] = *reinterpret_cast<const bf16x8 *>(s + abase + mi * 32 * kRow + koff[0]);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+            b[0][ni] = *reinterpret_cast<const bf16x8 *>(s + bbase + ni * 32 * kRow + koff[0]);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int cur = ks & 1, nxt = cur ^ 1;
+            // the fragments of step ks+1 are read between the two halves of
+            // step ks's 16 products; the order is pinned, so by the time step
+            // ks+1 waits for its reads, 8 products (256+ cycles) have covered
+            // their latency
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mi = 0; mi < MI / 2; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][mi], b[cur][ni],
+                                                                          acc[mi][ni], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + 1 < BK / 16) {
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi)
+                    a[nxt][mi] = *reinterpret_cast<const bf16x8 *>(s + abase + mi * 32 * kRow +
+                                                                   koff[ks + 1]);
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+                    b[nxt][ni] = *reinterpret_cast<const bf16x8 *>(s + bbase + ni * 32 * kRow +
+                                                                   koff[ks + 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mi = MI / 2; mi < MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][mi], b[cur][ni],
+                                                                          acc[mi][ni], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // ---- epilogue (as in the staged kernel, MI = 4) ------------------------
+    constexpr int HALF = HD / 2;
+    float *s_cos = reinterpret_cast<float *>(lds);
+    float *s_sin = s_cos + BM * HALF;
+    for (int e = tid; e < BM * HALF; e += kThreads) {
+        const int r = e / HALF, i = e - (e / HALF) * HALF;
+        const float ang = (float)p.pos[min(m0 + r, p.M - 1)] * inv.v[i];
+        double sd, cd;
+        sincos((double)ang, &sd, &cd);
+        s_cos[e] = (float)cd;
+        s_sin[e] = (float)sd;
     }
     __syncthreads();
 
-    // epilogue: thread (tt, j) for j < 16 handles the pair (j, j+16 of the block)
-    const int tt = tid >> 4, j = tid & 15;
-    if (tt >= nt)
+    const int cw = n0 + wn * 128;
+    if (cw >= p.N)
         return;
-    const int t = t0 + tt;
-    const int sec = hcol < p.nqt ? 0 : (hcol < p.nqt + p.nkt ? 1 : 2);
+    const int sec = cw < p.nqt ? 0 : (cw < p.nqt + p.nkt ? 1 : 2);
     const int sbase = sec == 0 ? 0 : (sec == 1 ? p.nqt : p.nqt + p.nkt);
-    const int c0 = hcol - sbase + g * 16 + j;   // column inside the section
+    float *const out = p.out[sec];
+    const int64_t ldo = p.ld[sec];
+    const float *const bias = p.b[sec];
+    float bcol[4];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+        bcol[ni] = bias ? bias[cw - sbase + ni * 32 + lr] : 0.0f;
+    void *const cache = sec == 1 ? p.cache[0] : p.cache[1];
+
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int rt = wm * 128 + mi * 32 + 8 * (v / 4) + 4 * hi + (v & 3);
+            const int t = m0 + rt;
+            if (t >= p.M)
+                continue;
+            float y[4];
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                y[ni] = acc[mi][ni][v] + bcol[ni];
+            if (sec < 2) {
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) {
+                    const int cih = (ni * 32) % HD;
+                    if (cih >= HALF)
+                        continue;
+                    const int nj = ni + HALF / 32;
+                    const int i = cih + lr;
+                    rot(y[ni], y[nj], s_cos[rt * HALF + i], s_sin[rt * HALF + i]);
+                }
+            }
+            const int64_t row = sec > 0 ? cache_row(p, t) : -1;
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                const int c = cw - sbase + ni * 32 + lr;
+                out[(int64_t)t * ldo + c] = y[ni];
+                if (row >= 0)
+                    put_cache<F16>(cache, row * p.nkt + c, y[ni]);
+            }
+            if (sec > 0 && row < 0 && lr == 0)
+                atomicOr(p.err, 1u);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// decode (1-4 tokens): weight-streaming GEMV + epilogue
+// ---------------------------------------------------------------------------
+// One wave per NeoX pair of weight rows (j and j + hd/2 of a head; in the v
+// section the same pairing just groups rows), four waves per block.  Lane l
+// takes the 16-byte chunks l, l+64, ... of both rows, four chunks in flight
+// per row, and keeps NT running sums per row; a butterfly over the wave
+// completes the dot products, and lane t < nt finishes token t: bias, the
+// rotation of the pair, write-back and the cache store.
+constexpr int kGemvTok = 4;          // the GEMV path takes up to 4 tokens
+constexpr int kGemvWaves = 4;
+constexpr int kGemvU = 4;            // chunks in flight per row and lane
+
+template <bool F16, int HD, int NT>
+__global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p, InvTable inv)
+{
+    constexpr int HALF = HD / 2;
+    const int lane = (int)threadIdx.x & 63;
+    const int pair = (int)blockIdx.x * kGemvWaves + ((int)threadIdx.x >> 6);
+    if (pair >= p.N / 2)
+        return;
+    const int head = pair / HALF, i = pair - head * HALF;
+    const int c0 = head * HD + i;            // global output column of the pair's first row
     const int c1 = c0 + HALF;
+    const int nchunk = p.K / 8;
+    const uint16_t *w0 = p.w + (int64_t)c0 * p.K;
+    const uint16_t *w1 = p.w + (int64_t)c1 * p.K;
+    const uint16_t *xr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        xr[t] = p.x + (int64_t)min(t, p.M - 1) * p.ld_x;
+
+    float d0[NT], d1[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        d0[t] = d1[t] = 0.0f;
+    for (int cb = lane; cb < nchunk; cb += 64 * kGemvU) {
+        u32x4 a[kGemvU], b[kGemvU], xv[kGemvU][NT];
+        bool ok[kGemvU];
+#pragma unroll
+        for (int u = 0; u < kGemvU; ++u) {
+            const int c = cb + 64 * u;
+            ok[u] = c < nchunk;
+            const int cc = ok[u] ? c : 0;    // past the row end: reload chunk 0, weight 0
+            a[u] = *reinterpret_cast<const u32x4 *>(w0 + cc * 8);
+            b[u] = *reinterpret_cast<const u32x4 *>(w1 + cc * 8);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                xv[u][t] = *reinterpret_cast<const u32x4 *>(xr[t] + cc * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < kGemvU; ++u) {
+            if (!ok[u])
+                a[u] = b[u] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float wa0 = __uint_as_float(a[u][e] << 16);
+                const float wa1 = __uint_as_float(a[u][e] & 0xffff0000u);
+                const float wb0 = __uint_as_float(b[u][e] << 16);
+                const float wb1 = __uint_as_float(b[u][e] & 0xffff0000u);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const float x0 = __uint_as_float(xv[u][t][e] << 16);
+                    const float x1 = __uint_as_float(xv[u][t][e] & 0xffff0000u);
+                    d0[t] = fmaf(x0, wa0, d0[t]);
+                    d0[t] = fmaf(x1, wa1, d0[t]);
+                    d1[t] = fmaf(x0, wb0, d1[t]);
+                    d1[t] = fmaf(x1, wb1, d1[t]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            d0[t] += __shfl_xor(d0[t], m, 64);
+            d1[t] += __shfl_xor(d1[t], m, 64);
+        }
+
+    if (lane >= NT || lane >= p.M)
+        return;
+    const int t = lane;
+    float y0 = d0[0], y1 = d1[0];
+#pragma unroll
+    for (int u = 1; u < NT; ++u)
+        if (t == u) {
+            y0 = d0[u];
+            y1 = d1[u];
+        }
+    const int sec = c0 < p.nqt ? 0 : (c0 < p.nqt + p.nkt ? 1 : 2);
+    const int sbase = sec == 0 ? 0 : (sec == 1 ? p.nqt : p.nqt + p.nkt);
+    const int s0 = c0 - sbase, s1 = c1 - sbase;   // columns inside the section
     const float *bias = p.b[sec];
-    float y0 = s_y[tt][j] + (bias ? bias[c0] : 0.0f);
-    float y1 = s_y[tt][16 + j] + (bias ? bias[c1] : 0.0f);
+    if (bias) {
+        y0 = y0 + bias[s0];
+        y1 = y1 + bias[s1];
+    }
     if (sec < 2) {
-        const float a = (float)p.pos[t] * inv.v[g * 16 + j];
+        const float ang = (float)p.pos[t] * inv.v[i];
         double sd, cd;
-        sincos((double)a, &sd, &cd);
+        sincos((double)ang, &sd, &cd);
         rot(y0, y1, (float)cd, (float)sd);
     }
     float *out = p.out[sec];
-    out[(int64_t)t * p.ld[sec] + c0] = y0;
-    out[(int64_t)t * p.ld[sec] + c1] = y1;
+    out[(int64_t)t * p.ld[sec] + s0] = y0;
+    out[(int64_t)t * p.ld[sec] + s1] = y1;
     if (sec > 0) {
         const int64_t row = cache_row(p, t);
         void *cache = sec == 1 ? p.cache[0] : p.cache[1];
         if (row >= 0) {
-            put_cache<F16>(cache, row * p.nkt + c0, y0);
-            put_cache<F16>(cache, row * p.nkt + c1, y1);
-        } else if (j == 0) {
+            put_cache<F16>(cache, row * p.nkt + s0, y0);
+            put_cache<F16>(cache, row * p.nkt + s1, y1);
+        } else if (i == 0) {
             atomicOr(p.err, 1u);
         }
     }
+}
+
+// 256x256 tiles (four waves of 128x128) once there are enough tokens to give
+// the chip a few tiles per CU; 32x256 tiles (two waves of 32x128) below that,
+// so a batch of a few hundred tokens still spreads over the CUs.
+using TileS = Tile<1, 2, 1, 32>;
+constexpr int kLargeM = 1024;
+
+template <bool F16, int HD, class T>
+hipError_t launch_mfma(const ProjParams &pp, const InvTable &inv, hipStream_t st)
+{
+    const int nblk = pp.N / T::BN + (pp.N % T::BN ? 1 : 0);
+    const int mblk = (pp.M + T::BM - 1) / T::BM;
+    const int lds_bytes = T::lds_bytes(HD);
+    static bool attr = false;   // raise the dynamic-LDS limit once per kernel
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&proj_mfma_kernel<F16, HD, T>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+        if (e != hipSuccess)
+            return e;
+        attr = true;
+    }
+    hipLaunchKernelGGL((proj_mfma_kernel<F16, HD, T>), dim3(nblk * mblk), dim3(T::kThreads),
+                       (unsigned)lds_bytes, st, pp, inv);
+    return hipGetLastError();
 }
 
 template <bool F16, int HD>
 hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st)
 {
     if (pp.M <= kGemvTok) {
-        // one block per 16 pairs of a head (the v section splits into heads too)
-        const int blocks = (pp.N / HD) * (HD / 2 / 16);
-        hipLaunchKernelGGL((proj_gemv_kernel<F16, HD>), dim3(blocks), dim3(kThreads), 0, st, pp,
-                           inv, 0);
+        const int blocks = (pp.N / 2 + kGemvWaves - 1) / kGemvWaves;
+        const dim3 grid(blocks), block(64 * kGemvWaves);
+        if (pp.M == 1)
+            hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, 1>), grid, block, 0, st, pp, inv);
+        else if (pp.M == 2)
+            hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, 2>), grid, block, 0, st, pp, inv);
+        else
+            hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, 4>), grid, block, 0, st, pp, inv);
         return hipGetLastError();
     }
-    const int nblk = pp.N / BN + (pp.N % BN ? 1 : 0);
-    const int mblk = (pp.M + BM - 1) / BM;
-    const int stage = 2 * (BM + BN) * ROWB;
-    const int table = BM * (HD / 2) * 8;
-    const int lds_bytes = stage > table ? stage : table;
-    hipLaunchKernelGGL((proj_mfma_kernel<F16, HD>), dim3(nblk * mblk), dim3(kThreads),
-                       (unsigned)lds_bytes, st, pp, inv);
-    return hipGetLastError();
+    if (pp.M >= kLargeM) {
+        const int nblk = pp.N / big::BN + (pp.N % big::BN ? 1 : 0);
+        const int mblk = (pp.M + big::BM - 1) / big::BM;
+        static bool attr = false;   // raise the dynamic-LDS limit once per kernel
+        if (!attr) {
+            hipError_t e = hipFuncSetAttribute(
+                reinterpret_cast<const void *>(&proj_mfma_big_kernel<F16, HD>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, big::kLds);
+            if (e != hipSuccess)
+                return e;
+            attr = true;
+        }
+        hipLaunchKernelGGL((proj_mfma_big_kernel<F16, HD>), dim3(nblk * mblk), dim3(big::kThreads),
+                           (unsigned)big::kLds, st, pp, inv);
+        return hipGetLastError();
+    }
+    return launch_mfma<F16, HD, TileS>(pp, inv, st);
 }
 
 }  // namespace
@@ -411,8 +675,8 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
         return fail(h, QKV_ERR_UNSUPPORTED, "the projection path needs head_dim 64 or 128, got %d",
                     a->head_dim);
     const int64_t N = pl.nqt + 2 * pl.nkt;
-    if (pa->hidden <= 0 || pa->hidden % 32 != 0)
-        return fail(h, QKV_ERR_INVALID_ARG, "hidden must be a positive multiple of 32, got %d",
+    if (pa->hidden <= 0 || pa->hidden % 64 != 0)
+        return fail(h, QKV_ERR_INVALID_ARG, "hidden must be a positive multiple of 64, got %d",
                     pa->hidden);
     if (pl.nqt % 128 != 0 || pl.nkt % 128 != 0)
         return fail(h, QKV_ERR_UNSUPPORTED,
@@ -421,6 +685,10 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
                     (long long)pl.nqt, (long long)pl.nkt);
     if (N > INT32_MAX / 2)
         return fail(h, QKV_ERR_INVALID_ARG, "q|k|v width too large");
+    // the kernels address x and w with 32-bit byte offsets
+    if ((int64_t)a->nt * (pa->ld_x ? pa->ld_x : pa->hidden) * 2 > INT32_MAX ||
+        N * pa->hidden * 2 > INT32_MAX)
+        return fail(h, QKV_ERR_INVALID_ARG, "x and w must each span less than 2 GiB");
     const int64_t ld_x = pa->ld_x ? pa->ld_x : pa->hidden;
     if (ld_x < pa->hidden || ld_x % 8 != 0)
         return fail(h, QKV_ERR_INVALID_ARG, "ld_x must be >= hidden and a multiple of 8");

@@ -207,7 +207,13 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  *   hidden  contraction length, a multiple of 64
  *
  * Limits (QKV_ERR_UNSUPPORTED otherwise): NeoX style, head_dim 64 or 128, q
- * and k/v widths multiples of 128.  The f32 sums are taken in a different
+ * and k/v widths multiples of 128; x and w each under 2 GiB.
+ *
+ * Workspace: launches of 1024 or more tokens with 16-byte aligned sections
+ * use a cos/sin table of nt * head_dim * 4 bytes held by the handle.  The
+ * first such call with more tokens than any before it synchronizes the device
+ * and (re)allocates it; make that call outside graph capture.  All other calls
+ * allocate nothing and never synchronize.  The f32 sums are taken in a different
  * order than a plain loop: each output carries up to (hidden+2) * 2^-24 *
  * sum_k |x w| of accumulation error on top of the epilogue's own rounding.
  */

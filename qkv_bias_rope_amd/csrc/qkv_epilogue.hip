@@ -893,8 +893,12 @@ void qkv_epilogue_destroy(qkv_epilogue_t *h)
     if (!h)
         return;
     DeviceGuard g;
-    if (g.set(h->device) == hipSuccess && h->d_err)
-        (void)hipFree(h->d_err);
+    if (g.set(h->device) == hipSuccess) {
+        if (h->d_err)
+            (void)hipFree(h->d_err);
+        if (h->proj_ws)
+            (void)hipFree(h->proj_ws);
+    }
     delete h;
 }
 

@@ -178,6 +178,10 @@ struct qkv_epilogue {
     float inv_scale;
     qkv_detail::InvTable inv;
     char msg[512];
+    // device workspace of the projection path (the long-prompt cos/sin
+    // table), grown on demand, freed by destroy
+    void *proj_ws;
+    size_t proj_ws_bytes;
 };
 
 namespace qkv_detail {

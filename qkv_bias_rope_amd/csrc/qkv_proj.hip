@@ -60,6 +60,8 @@ struct ProjParams {
     void *cache[2];
     int64_t n_ctx, n_slots;
     unsigned int *err;
+    const float *rtab;       // [M][cos half | sin half] (long-prompt path)
+    bool vec;                // sections, biases, caches 16-byte aligned, strides % 4 == 0
 };
 
 // cache row of token t, or -1 (and the error bit) when out of range
@@ -273,26 +275,56 @@ __global__ __launch_bounds__(T::kThreads) void proj_mfma_kernel(ProjParams p, In
 }
 
 // ---------------------------------------------------------------------------
+// cos/sin table of a launch: row t holds cos then sin of pos[t] * inv[i],
+// i < half (f32 angle; sin/cos in double rounded to f32).  Every column
+// block of a long prompt reads it instead of recomputing it.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void rope_table_kernel(const int32_t *pos, int M, int half,
+                                                         InvTable inv, float *tab)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)M * half)
+        return;
+    const int t = (int)(idx / half), i = (int)(idx - (int64_t)t * half);
+    const float ang = (float)pos[t] * inv.v[i];
+    double sd, cd;
+    sincos((double)ang, &sd, &cd);
+    tab[(int64_t)t * 2 * half + i] = (float)cd;
+    tab[(int64_t)t * 2 * half + half + i] = (float)sd;
+}
+
+// ---------------------------------------------------------------------------
 // long prompts: 256 x 256 tiles, operands loaded straight into LDS
 // ---------------------------------------------------------------------------
-// Four waves of 128 x 128 (4 x 4 MFMA tiles each), k tiles of 64.  Each k
-// tile of A (256 token rows) and B (256 weight rows) is 32 KB; every wave
-// issues 8 + 8 global->LDS loads of 1 KB (64 lanes x 16 bytes) per tile, so
-// the operands never pass through registers.  Rows are 128 bytes (8 chunks
-// of 16) with no padding; chunk c of row r sits in slot c ^ g(r),
-// g(r) = (r & 7) ^ ((r >> 3) & 1), which makes the 16-byte fragment reads
-// of 16 consecutive rows hit distinct banks (with 32 or 64 banks of 4 bytes).
+// Four waves of 128 tokens x 128 outputs (4 x 4 MFMA tiles each, computed
+// transposed: 32 outputs x 32 tokens per tile).  k advances in sub-tiles
+// of 32 through a ring of four LDS stages (32 KB each: 256 token rows of A
+// and 256 weight rows of B, 64 bytes per row), filled by global->LDS loads
+// (64 lanes x 16 bytes per instruction) issued three sub-tiles ahead, so
+// HBM / last-level-cache latency has about 3000 MFMA cycles to resolve.
+// Chunk c of row r sits in slot c ^ g(r), g(r) = ((r >> 1) ^ (r >> 3)) & 3:
+// the 16-byte fragment reads of 16 consecutive rows hit distinct banks.
+//
+// Per sub-tile s (two k steps of 16, 16 products each):
+//   products of step 0 (first half); read step-1 fragments; products of
+//   step 0 (second half); products of step 1 (first half); wait for this
+//   wave's loads of sub-tile s+1 and meet the other waves (after which stage
+//   s is free and sub-tile s+1 is visible); load sub-tile s+4 into stage s;
+//   read step-0 fragments of sub-tile s+1; products of step 1 (second half).
+// The cross-wave wait thus sits in the middle of a sub-tile and every
+// fragment read has 8 products (256+ cycles) in front of its first use.
 namespace big {
-constexpr int BM = 256, BN = 256, BK = 64, MI = 4;
+constexpr int BM = 256, BN = 256, BK = 32, MI = 4, NSTAGE = 4;
 constexpr int kThreads = 256;
-constexpr int kRow = BK * 2;                  // 128 bytes
-constexpr int kRegion = 256 * kRow;           // 32 KB for A or B
-constexpr int kStage = 2 * kRegion;           // 64 KB
-constexpr int kLds = 2 * kStage;              // 128 KB (also holds the 256 x 64 cos/sin table)
+constexpr int kRow = BK * 2;                  // 64 bytes
+constexpr int kRegion = 256 * kRow;           // 16 KB for A or B
+constexpr int kStage = 2 * kRegion;           // 32 KB
+constexpr int kLds = NSTAGE * kStage;         // 128 KB (also holds the 256 x 64 cos/sin table)
+constexpr int kLoadsPerWave = 8;              // 4 for A + 4 for B per sub-tile
 
 __device__ __forceinline__ int swz(int r)
 {
-    return (r & 7) ^ ((r >> 3) & 1);
+    return ((r >> 1) ^ (r >> 3)) & 3;
 }
 }  // namespace big
 
@@ -311,31 +343,35 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
     const int m0 = ((int)blockIdx.x / nblk) * BM;
 
     // loads: wave w fills rows [64w, 64w + 64) of the A and the B region;
-    // instruction j covers rows 64w + 8j + lane/8, lane%8 is the LDS slot
-    // and the chunk it holds is slot ^ g(row) (row & 7 = lane/8, bit 3 of the
-    // row is the parity of j).  Offsets are bytes from x / w (both < 2 GiB).
-    const int lrow = lane >> 3, slot = lane & 7;
-    uint32_t aoff[8], boff[8];
+    // instruction j covers rows r = 64w + 16j + lane/4, lane%4 is the LDS
+    // slot and the chunk it holds is slot ^ g(r) (g reads bits 1-4 of r:
+    // lane/4 and the parity of j).  Offsets are bytes from x / w (both
+    // < 2 GiB).
+    const int lrow = lane >> 2, slot = lane & 3;
+    uint32_t aoff[4], boff[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = 64 * wave + 8 * j + lrow;
-        const int c = slot ^ (lrow ^ (j & 1));
-        aoff[j] = (uint32_t)((int64_t)min(m0 + r, p.M - 1) * p.ld_x * 2) + c * 16;
-        boff[j] = (uint32_t)((int64_t)min(n0 + r, p.N - 1) * p.K * 2) + c * 16;
+    for (int j = 0; j < 4; ++j) {
+        const int r = 64 * wave + 16 * j + lrow;
+        const int chunk = slot ^ big::swz(r);
+        aoff[j] = (uint32_t)((int64_t)min(m0 + r, p.M - 1) * p.ld_x * 2) + chunk * 16;
+        boff[j] = (uint32_t)((int64_t)min(n0 + r, p.N - 1) * p.K * 2) + chunk * 16;
     }
     const unsigned char *xb = reinterpret_cast<const unsigned char *>(p.x);
     const unsigned char *wb = reinterpret_cast<const unsigned char *>(p.w);
     typedef __attribute__((address_space(3))) void lds_t;
-    auto issue = [&](int stage, int k0) {
+    const int KT = p.K / BK;
+    // sub-tile st (clamped to the last one: the loop stays uniform) into its stage
+    auto issue = [&](int st) {
+        const int stage = st % NSTAGE;
+        const uint32_t kb = (uint32_t)min(st, KT - 1) * (BK * 2);
         unsigned char *sa = lds + stage * kStage + (64 * wave) * kRow;
         unsigned char *sb = sa + kRegion;
-        const uint32_t kb = (uint32_t)k0 * 2;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            __builtin_amdgcn_global_load_lds(xb + aoff[j] + kb, (lds_t *)(sa + j * 8 * kRow), 16, 0, 0);
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_global_load_lds(xb + aoff[j] + kb, (lds_t *)(sa + j * 16 * kRow), 16, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            __builtin_amdgcn_global_load_lds(wb + boff[j] + kb, (lds_t *)(sb + j * 8 * kRow), 16, 0, 0);
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_global_load_lds(wb + boff[j] + kb, (lds_t *)(sb + j * 16 * kRow), 16, 0, 0);
     };
 
     f32x16 acc[MI][4];
@@ -352,127 +388,126 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
     const int g = big::swz(lr);                 // tiles start at multiples of 32
     const int abase = (wm * 128 + lr) * kRow;
     const int bbase = kRegion + (wn * 128 + lr) * kRow;
-    int koff[BK / 16];
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks)
-        koff[ks] = ((2 * ks + hi) ^ g) * 16;
+    const int k0off = ((0 + hi) ^ g) * 16;      // step 0: chunk hi
+    const int k1off = ((2 + hi) ^ g) * 16;      // step 1: chunk 2 + hi
 
-    const int KT = p.K / BK;
-    issue(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) etc.: this wave's loads landed
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        // next tile into the other stage (the last iteration reloads the last
-        // tile: the loop body stays one straight-line region)
-        issue((kt + 1) & 1, min(kt + 1, KT - 1) * BK);
-        const unsigned char *s = lds + (kt & 1) * kStage;
-        bf16x8 a[2][MI], b[2][4];
+    bf16x8 a0[MI], b0[4], a1[MI], b1[4];
+    auto read_frags = [&](const unsigned char *s, int koff, bf16x8 (&fa)[MI], bf16x8 (&fb)[4]) {
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
-            a[0][mi] = *reinterpret_cast<const bf16x8 *>(s + abase + mi * 32 * kRow + koff[0]);
+            fa[mi] = *reinterpret_cast<const bf16x8 *>(s + abase + mi * 32 * kRow + koff);
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
-            b[0][ni] = *reinterpret_cast<const bf16x8 *>(s + bbase + ni * 32 * kRow + koff[0]);
+            fb[ni] = *reinterpret_cast<const bf16x8 *>(s + bbase + ni * 32 * kRow + koff);
+    };
+    // acc[f][t]: 32 features x 32 tokens, the weight fragment as the A
+    // operand, so a lane ends up holding 4 consecutive features of a token
+    auto mfma_half = [&](int tlo, const bf16x8 (&fa)[MI], const bf16x8 (&fb)[4]) {
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int cur = ks & 1, nxt = cur ^ 1;
-            // the fragments of step ks+1 are read between the two halves of
-            // step ks's 16 products; the order is pinned, so by the time step
-            // ks+1 waits for its reads, 8 products (256+ cycles) have covered
-            // their latency
-            __builtin_amdgcn_sched_barrier(0);
+        for (int ti = tlo; ti < tlo + MI / 2; ++ti)
 #pragma unroll
-            for (int mi = 0; mi < MI / 2; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][mi], b[cur][ni],
-                                                                          acc[mi][ni], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            if (ks + 1 < BK / 16) {
-#pragma unroll
-                for (int mi = 0; mi < MI; ++mi)
-                    a[nxt][mi] = *reinterpret_cast<const bf16x8 *>(s + abase + mi * 32 * kRow +
-                                                                   koff[ks + 1]);
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
-                    b[nxt][ni] = *reinterpret_cast<const bf16x8 *>(s + bbase + ni * 32 * kRow +
-                                                                   koff[ks + 1]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int mi = MI / 2; mi < MI; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][mi], b[cur][ni],
-                                                                          acc[mi][ni], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    }
+            for (int fi = 0; fi < 4; ++fi)
+                acc[fi][ti] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fi], fa[ti], acc[fi][ti], 0, 0, 0);
+    };
 
-    // ---- epilogue (as in the staged kernel, MI = 4) ------------------------
-    constexpr int HALF = HD / 2;
-    float *s_cos = reinterpret_cast<float *>(lds);
-    float *s_sin = s_cos + BM * HALF;
-    for (int e = tid; e < BM * HALF; e += kThreads) {
-        const int r = e / HALF, i = e - (e / HALF) * HALF;
-        const float ang = (float)p.pos[min(m0 + r, p.M - 1)] * inv.v[i];
-        double sd, cd;
-        sincos((double)ang, &sd, &cd);
-        s_cos[e] = (float)cd;
-        s_sin[e] = (float)sd;
-    }
+    // prologue: sub-tiles 0..3 in flight, sub-tile 0 landed everywhere
+#pragma unroll
+    for (int st = 0; st < NSTAGE; ++st)
+        issue(st);
+    // vmcnt <= 3 * kLoadsPerWave (24): lo bits 24 & 15, hi bits 24 >> 4; no lgkm/exp wait
+    __builtin_amdgcn_s_waitcnt((1 << 14) | (0xF << 8) | (7 << 4) | 8);
     __syncthreads();
+    read_frags(lds, k0off, a0, b0);
 
-    const int cw = n0 + wn * 128;
-    if (cw >= p.N)
+    for (int kt = 0; kt < KT; ++kt) {
+        const unsigned char *s = lds + (kt % NSTAGE) * kStage;
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_half(0, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(s, k1off, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_half(MI / 2, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_half(0, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        // this wave's loads of sub-tile kt+1 have landed once at most the two
+        // later groups (kt+2, kt+3) are outstanding: vmcnt <= 16
+        __builtin_amdgcn_s_waitcnt((1 << 14) | (0xF << 8) | (7 << 4) | 0);
+        __syncthreads();
+        issue(kt + NSTAGE);
+        read_frags(lds + ((kt + 1) % NSTAGE) * kStage, k0off, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_half(MI / 2, a1, b1);
+    }
+    // the clamped reloads of the last iterations must land before the wave
+    // leaves (they write this block's LDS)
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // ---- epilogue ---------------------------------------------------------
+    // Lane (lr, hi) of a wave holds, for token ti*32 + lr of its 128, the
+    // outputs fi*32 + 8g + 4hi + e (e < 4) in acc[fi][ti][4g + e]: four
+    // consecutive columns, stored with one 16-byte (f32) or 8-byte (f16)
+    // store.  The NeoX partner of tile fi is tile fi + hd/64, same register;
+    // cos/sin come from the launch's table (16-byte reads).
+    constexpr int HALF = HD / 2;
+    const int cw = n0 + wn * 128;                  // first output column of this wave
+    const int sec_w = cw < p.N ? (cw < p.nqt ? 0 : (cw < p.nqt + p.nkt ? 1 : 2)) : 3;
+    if (sec_w == 3)
         return;
-    const int sec = cw < p.nqt ? 0 : (cw < p.nqt + p.nkt ? 1 : 2);
+    const int sec = sec_w;
     const int sbase = sec == 0 ? 0 : (sec == 1 ? p.nqt : p.nqt + p.nkt);
     float *const out = p.out[sec];
     const int64_t ldo = p.ld[sec];
     const float *const bias = p.b[sec];
-    float bcol[4];
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-        bcol[ni] = bias ? bias[cw - sbase + ni * 32 + lr] : 0.0f;
     void *const cache = sec == 1 ? p.cache[0] : p.cache[1];
+    const int cs = cw - sbase + 4 * hi;            // section column of (fi = 0, g = 0)
 
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
+    for (int ti = 0; ti < 4; ++ti) {
+        const int rt = wm * 128 + ti * 32 + lr;    // token row in the block
+        const int t = m0 + rt;
+        if (t >= p.M)
+            continue;
+        const int64_t row = sec > 0 ? cache_row(p, t) : -1;
+        float *const orow = out + (int64_t)t * ldo;
+        const float *const trow = p.rtab + (int64_t)t * 2 * HALF;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int rt = wm * 128 + mi * 32 + 8 * (v / 4) + 4 * hi + (v & 3);
-            const int t = m0 + rt;
-            if (t >= p.M)
-                continue;
-            float y[4];
+        for (int fi = 0; fi < 4; ++fi) {
+            const int cih = (fi * 32) % HD;        // column of the tile inside its head
+            if (sec < 2 && cih >= HALF)
+                continue;                          // handled with its partner
+            const int fj = fi + HALF / 32;
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                y[ni] = acc[mi][ni][v] + bcol[ni];
-            if (sec < 2) {
+            for (int g = 0; g < 4; ++g) {
+                const int c0 = cs + fi * 32 + 8 * g;
+                FVec<4> y0, y1;
+                const FVec<4> b0 = bias ? ld_vec<4>(bias + c0) : FVec<4>{{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni) {
-                    const int cih = (ni * 32) % HD;
-                    if (cih >= HALF)
-                        continue;
-                    const int nj = ni + HALF / 32;
-                    const int i = cih + lr;
-                    rot(y[ni], y[nj], s_cos[rt * HALF + i], s_sin[rt * HALF + i]);
+                for (int e = 0; e < 4; ++e)
+                    y0.e[e] = acc[fi][ti][4 * g + e] + b0.e[e];
+                if (sec < 2) {
+                    const int c1 = c0 + HALF;
+                    const FVec<4> b1 = bias ? ld_vec<4>(bias + c1) : FVec<4>{{0.f, 0.f, 0.f, 0.f}};
+                    const int i0 = cih + 8 * g + 4 * hi;   // pair index of e = 0
+                    const FVec<4> cv = ld_vec<4>(trow + i0);
+                    const FVec<4> sv = ld_vec<4>(trow + HALF + i0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        y1.e[e] = acc[fj][ti][4 * g + e] + b1.e[e];
+                        rot(y0.e[e], y1.e[e], cv.e[e], sv.e[e]);
+                    }
+                    st_data<4, false>(orow + c1, y1);
+                    if (row >= 0)
+                        st_cache<4, F16, false>(cache, row * p.nkt + c1, y1);
                 }
-            }
-            const int64_t row = sec > 0 ? cache_row(p, t) : -1;
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-                const int c = cw - sbase + ni * 32 + lr;
-                out[(int64_t)t * ldo + c] = y[ni];
+                st_data<4, false>(orow + c0, y0);
                 if (row >= 0)
-                    put_cache<F16>(cache, row * p.nkt + c, y[ni]);
+                    st_cache<4, F16, false>(cache, row * p.nkt + c0, y0);
             }
-            if (sec > 0 && row < 0 && lr == 0)
-                atomicOr(p.err, 1u);
         }
+        if (sec > 0 && row < 0 && hi == 0)
+            atomicOr(p.err, 1u);
     }
 }
 
@@ -635,7 +670,7 @@ hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st
             hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, 4>), grid, block, 0, st, pp, inv);
         return hipGetLastError();
     }
-    if (pp.M >= kLargeM) {
+    if (pp.M >= kLargeM && pp.vec) {
         const int nblk = pp.N / big::BN + (pp.N % big::BN ? 1 : 0);
         const int mblk = (pp.M + big::BM - 1) / big::BM;
         static bool attr = false;   // raise the dynamic-LDS limit once per kernel
@@ -647,6 +682,9 @@ hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st
                 return e;
             attr = true;
         }
+        const int64_t n_tab = (int64_t)pp.M * (HD / 2);
+        hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n_tab + 255) / 256)), dim3(256), 0,
+                           st, pp.pos, pp.M, HD / 2, inv, const_cast<float *>(pp.rtab));
         hipLaunchKernelGGL((proj_mfma_big_kernel<F16, HD>), dim3(nblk * mblk), dim3(big::kThreads),
                            (unsigned)big::kLds, st, pp, inv);
         return hipGetLastError();
@@ -745,6 +783,8 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
     pp.n_ctx = pl.n_ctx;
     pp.n_slots = pl.n_slots;
     pp.err = h->d_err;
+    pp.vec = pl.W == 4;
+    pp.rtab = nullptr;
 
     const InvTable &inv = handle_inv(h, a->theta, a->head_dim, a->freq_scale);
     hipStream_t st = (a->stream || a->use_stream) ? static_cast<hipStream_t>(a->stream) : h->stream;
@@ -752,6 +792,28 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
     hipError_t e = g.set(h->device);
     if (e != hipSuccess)
         return fail(h, QKV_ERR_HIP, "hipSetDevice(%d): %s", h->device, hipGetErrorString(e));
+    if (pp.M >= kLargeM && pp.vec) {
+        // the long-prompt path reads a [nt][head_dim] f32 cos/sin table from
+        // the handle's workspace; a larger request than any before grows it
+        // (after the device has finished with the old one)
+        const size_t need = (size_t)pp.M * (size_t)a->head_dim * sizeof(float);
+        if (h->proj_ws_bytes < need) {
+            e = hipDeviceSynchronize();
+            if (e == hipSuccess && h->proj_ws)
+                e = hipFree(h->proj_ws);
+            h->proj_ws = nullptr;
+            h->proj_ws_bytes = 0;
+            if (e == hipSuccess)
+                e = hipMalloc(&h->proj_ws, need);
+            if (e != hipSuccess) {
+                h->proj_ws = nullptr;
+                return fail(h, QKV_ERR_HIP, "workspace of %zu bytes: %s", need,
+                            hipGetErrorString(e));
+            }
+            h->proj_ws_bytes = need;
+        }
+        pp.rtab = static_cast<const float *>(h->proj_ws);
+    }
     const bool f16 = a->cache_dtype == QKV_CACHE_F16;
     if (a->head_dim == 128)
         e = f16 ? launch_proj<true, 128>(pp, inv, st) : launch_proj<false, 128>(pp, inv, st);

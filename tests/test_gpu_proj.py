@@ -44,7 +44,7 @@ def handle():
 
 class ProjCase:
     def __init__(self, w, hidden, nt=None, cache_dtype=None, form="separate", bias=True,
-                 pos=None, slot=None, sample=None, ld_x_pad=0):
+                 pos=None, slot=None, sample=None, ld_x_pad=0, misalign=0):
         self.w, self.hidden = w, hidden
         d = wl.draw_projection(w, hidden, nt=nt)
         if pos is not None:
@@ -56,6 +56,7 @@ class ProjCase:
         self.cd = w.cache_dtypes[0] if cache_dtype is None else cache_dtype
         self.form, self.bias = form, bias
         self.ld_x_pad = ld_x_pad
+        self.misalign = misalign   # shift every output section by this many floats
         # tokens the oracle recomputes (all of them unless a sample is given)
         self.sample = np.arange(self.nt) if sample is None else np.asarray(sample)
 
@@ -101,15 +102,21 @@ class ProjCase:
         self.g_x = torch.from_numpy(xp.view(np.int16)).to(DEV)
         self.ld_x = ldx if self.ld_x_pad else 0
         self.g_w = torch.from_numpy(d["w"].view(np.int16)).to(DEV)
+        m = self.misalign
         if self.form == "concat":
-            self.g_buf = torch.full((nt, nqt + 2 * nkt), float("nan"), device=DEV)
+            n = nqt + 2 * nkt
+            self._buf = torch.full((nt * n + m,), float("nan"), device=DEV)
+            self.g_buf = self._buf[m:].view(nt, n)
             self.g_q = self.g_buf[:, :nqt]
             self.g_k = self.g_buf[:, nqt:nqt + nkt]
             self.g_v = self.g_buf[:, nqt + nkt:]
         else:
-            self.g_q = torch.full((nt, nqt), float("nan"), device=DEV)
-            self.g_k = torch.full((nt, nkt), float("nan"), device=DEV)
-            self.g_v = torch.full((nt, nkt), float("nan"), device=DEV)
+            def full(width):
+                flat = torch.full((nt * width + m,), float("nan"), device=DEV)
+                return flat, flat[m:].view(nt, width)
+            self._q, self.g_q = full(nqt)
+            self._k, self.g_k = full(nkt)
+            self._v, self.g_v = full(nkt)
         if self.bias:
             self.g_b = [torch.from_numpy(d[n]).to(DEV) for n in ("bq", "bk", "bv")]
         else:
@@ -271,6 +278,36 @@ def test_proj_out_of_range_position(handle):
         assert st == B.QKV_ERR_POSITION_RANGE, st
         assert c.n_bad == 1
         c.check(f"bad_pos_nt{nt}")
+
+
+def test_proj_long_ragged_hd64_no_bias(handle):
+    """The 256x256 path with hd 64 (two heads per wave), a ragged last token
+    tile (1100 = 4*256 + 76) and a last column block half past the end
+    (1152 outputs = 4.5 blocks of 256)."""
+    w = wl.Workload("proj_long_0.5b", 14, 2, 64, nt=1100, n_ctx=2048, n_slots=1, layers=1,
+                    seed=16, cache_dtypes=(wl.CACHE_F32,), pos_mode="arange")
+    c = ProjCase(w, hidden=512, bias=False)
+    assert _run(handle, c, "long_hd64") == B.QKV_OK
+    c.check("long_hd64")
+
+
+def test_proj_long_concat_14b(handle):
+    """The 256x256 path writing views of one concat q|k|v buffer."""
+    w = wl.Workload("proj_long_14b", 40, 8, 128, nt=1030, n_ctx=4096, n_slots=1, layers=1,
+                    seed=17, pos_mode="uniform")
+    c = ProjCase(w, hidden=256, form="concat")
+    assert _run(handle, c, "long_concat") == B.QKV_OK
+    c.check("long_concat")
+
+
+def test_proj_long_misaligned_outputs(handle):
+    """Outputs off 16-byte alignment: the long-prompt launch takes the
+    scalar-store tiles."""
+    w = wl.Workload("proj_long_mis", 40, 8, 128, nt=1030, n_ctx=4096, n_slots=1, layers=1,
+                    seed=18, pos_mode="arange")
+    c = ProjCase(w, hidden=256, misalign=1)
+    assert _run(handle, c, "long_misaligned") == B.QKV_OK
+    c.check("long_misaligned")
 
 
 def test_proj_prefill_full_size_sampled(handle):

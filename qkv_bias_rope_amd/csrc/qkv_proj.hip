@@ -13,17 +13,17 @@
 // both operands are 16 contiguous bytes of a k-contiguous row) and receives
 // D[8*(v/4) + 4*(l/32) + v%4][l%32], v < 16.
 //
-//  * Block tiles of 256 tokens x 256 outputs (four waves of 128 x 128, k
-//    tiles of 64) for long prompts, 32 x 256 (two waves of 32 x 128, k tiles
-//    of 32) for a few hundred tokens; operands staged through double-buffered
-//    LDS, rows padded by 16 bytes so the 16-byte fragment reads of
-//    consecutive rows hit distinct banks.
+//  * Tiles of 256 tokens x 256 outputs, four waves of 128 x 128; operands go
+//    from HBM straight into a ring of four LDS stages (k sub-tiles of 32,
+//    loaded three ahead), XOR-swizzled so fragment reads are conflict-free.
 //  * A wave's 128 output columns are one head (hd 128) or two (hd 64), so the
 //    NeoX partner of column j (j + hd/2) sits in the same lane, in the MFMA
-//    tile hd/64 tiles to the right: the rotation needs no data exchange.
-//  * After the k loop the staging LDS holds a cos/sin table for the block's
-//    128 tokens x hd/2 pair indices (double sincos rounded to f32, as in the
-//    epilogue kernel).
+//    tile hd/64 tiles further on: the rotation needs no data exchange.
+//  * 1024+ tokens: the epilogue runs on the accumulators (tiles computed
+//    transposed so a lane holds 4 consecutive outputs), with a cos/sin table
+//    computed once per launch.  Fewer tokens: the tiles are too few to fill
+//    the chip, so k is split across workgroups that add their shares into
+//    zeroed q|k|v sections, and the epilogue kernel finishes them in place.
 //  * Decode (up to 4 tokens) is a weight-streaming GEMV, not a contraction
 //    worth the matrix units: a separate kernel streams W with 16-byte loads,
 //    reduces each dot product across the wave and runs the same epilogue.
@@ -60,7 +60,9 @@ struct ProjParams {
     void *cache[2];
     int64_t n_ctx, n_slots;
     unsigned int *err;
-    const float *rtab;       // [M][cos half | sin half] (long-prompt path)
+    const float *rtab;       // [M][cos half | sin half] (fused long-prompt path)
+    int ksplit;              // k splits of the split path
+    float *part;             // [ksplit][M][N] partial sums of the split path
     bool vec;                // sections, biases, caches 16-byte aligned, strides % 4 == 0
 };
 
@@ -88,190 +90,6 @@ __device__ __forceinline__ void put_cache(void *cache, int64_t off, float v)
         static_cast<_Float16 *>(cache)[off] = static_cast<_Float16>(v);  // RNE
     else
         static_cast<float *>(cache)[off] = v;
-}
-
-// ---------------------------------------------------------------------------
-// prefill / batched: MFMA GEMM + epilogue
-// ---------------------------------------------------------------------------
-// Block = WM x WN waves; wave (wm, wn) owns MI*32 tokens x 128 outputs, i.e.
-// MI x 4 tiles of 32x32.  Block tile BM = WM*MI*32 tokens, BN = WN*128
-// outputs; k advances BK at a time through two LDS stages of (BM + BN) rows,
-// each row BK bf16 plus 16 bytes of padding (the 16-byte fragment reads of
-// 16 consecutive rows then fall on distinct banks).
-template <int WM, int WN, int MI, int BK>
-struct Tile {
-    static constexpr int WM_ = WM, WN_ = WN, MI_ = MI, BK_ = BK;
-    static constexpr int kWaves = WM * WN;
-    static constexpr int kThreads = 64 * kWaves;
-    static constexpr int BM = WM * MI * 32;
-    static constexpr int BN = WN * 128;
-    static constexpr int kChunks = BK / 8;                 // 16-byte chunks per row
-    static constexpr int kPitch = BK * 2 + 16;             // LDS bytes per row
-    static constexpr int kStage = (BM + BN) * kPitch;
-    static constexpr int kA = BM * kChunks / kThreads;     // A chunks per thread
-    static constexpr int kB = BN * kChunks / kThreads;     // B chunks per thread
-    static_assert(BM * kChunks % kThreads == 0 && BN * kChunks % kThreads == 0, "tile");
-    static_assert(kThreads % kChunks == 0, "tile");
-    static int lds_bytes(int hd)
-    {
-        const int stage = 2 * kStage;
-        const int table = BM * (hd / 2) * 8;
-        return stage > table ? stage : table;
-    }
-};
-
-template <bool F16, int HD, class T>
-__global__ __launch_bounds__(T::kThreads) void proj_mfma_kernel(ProjParams p, InvTable inv)
-{
-    extern __shared__ __align__(16) unsigned char lds[];
-    constexpr int BM = T::BM, BN = T::BN, BK = T::BK_, MI = T::MI_;
-    constexpr int NT = T::kThreads;
-
-    const int tid = (int)threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave / T::WN_, wn = wave % T::WN_;
-    const int nblk = p.N / BN + (p.N % BN ? 1 : 0);
-    const int n0 = ((int)blockIdx.x % nblk) * BN;
-    const int m0 = ((int)blockIdx.x / nblk) * BM;
-
-    // global -> register staging: chunk e = tid + NT*j is row e / kChunks,
-    // 16-byte chunk e % kChunks; rows past the end read a clamped row
-    const int ch = tid % T::kChunks;
-    const int r0 = tid / T::kChunks;
-    constexpr int RSTEP = NT / T::kChunks;   // rows between a thread's chunks
-    const uint16_t *ap[T::kA], *bp[T::kB];
-#pragma unroll
-    for (int j = 0; j < T::kA; ++j)
-        ap[j] = p.x + (int64_t)min(m0 + r0 + RSTEP * j, p.M - 1) * p.ld_x + ch * 8;
-#pragma unroll
-    for (int j = 0; j < T::kB; ++j)
-        bp[j] = p.w + (int64_t)min(n0 + r0 + RSTEP * j, p.N - 1) * p.K + ch * 8;
-
-    u32x4 ra[T::kA], rb[T::kB];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int j = 0; j < T::kA; ++j)
-            ra[j] = *reinterpret_cast<const u32x4 *>(ap[j] + k0);
-#pragma unroll
-        for (int j = 0; j < T::kB; ++j)
-            rb[j] = *reinterpret_cast<const u32x4 *>(bp[j] + k0);
-    };
-    auto lstore = [&](int buf) {
-        unsigned char *s = lds + buf * T::kStage + r0 * T::kPitch + ch * 16;
-#pragma unroll
-        for (int j = 0; j < T::kA; ++j)
-            *reinterpret_cast<u32x4 *>(s + RSTEP * j * T::kPitch) = ra[j];
-#pragma unroll
-        for (int j = 0; j < T::kB; ++j)
-            *reinterpret_cast<u32x4 *>(s + (BM + RSTEP * j) * T::kPitch) = rb[j];
-    };
-
-    f32x16 acc[MI][4];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                acc[mi][ni][v] = 0.0f;
-
-    const int KT = p.K / BK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    const int lr = lane & 31, lk = (lane >> 5) * 16;  // row in tile, byte offset of k chunk
-    const int arow = (wm * MI * 32 + lr) * T::kPitch + lk;
-    const int brow = (BM + wn * 128 + lr) * T::kPitch + lk;
-    for (int kt = 0; kt < KT; ++kt) {
-        if (kt + 1 < KT)
-            gload((kt + 1) * BK);
-        const unsigned char *s = lds + (kt & 1) * T::kStage;
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8 a[MI], b[4];
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-                a[mi] = *reinterpret_cast<const bf16x8 *>(s + arow + mi * 32 * T::kPitch + ks * 32);
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                b[ni] = *reinterpret_cast<const bf16x8 *>(s + brow + ni * 32 * T::kPitch + ks * 32);
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
-                    acc[mi][ni] =
-                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
-        }
-        if (kt + 1 < KT)
-            lstore((kt + 1) & 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue --------------------------------------------------------
-    constexpr int HALF = HD / 2;
-    float *s_cos = reinterpret_cast<float *>(lds);
-    float *s_sin = s_cos + BM * HALF;
-    for (int e = tid; e < BM * HALF; e += NT) {
-        const int r = e / HALF, i = e - (e / HALF) * HALF;
-        const float a = (float)p.pos[min(m0 + r, p.M - 1)] * inv.v[i];
-        double sd, cd;
-        sincos((double)a, &sd, &cd);
-        s_cos[e] = (float)cd;
-        s_sin[e] = (float)sd;
-    }
-    __syncthreads();
-
-    const int cw = n0 + wn * 128;  // first output column of this wave
-    if (cw >= p.N)
-        return;
-    const int sec = cw < p.nqt ? 0 : (cw < p.nqt + p.nkt ? 1 : 2);
-    const int sbase = sec == 0 ? 0 : (sec == 1 ? p.nqt : p.nqt + p.nkt);
-    float *const out = p.out[sec];
-    const int64_t ldo = p.ld[sec];
-    const float *const bias = p.b[sec];
-    float bcol[4];
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-        bcol[ni] = bias ? bias[cw - sbase + ni * 32 + lr] : 0.0f;
-    void *const cache = sec == 1 ? p.cache[0] : p.cache[1];
-
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int rt = wm * MI * 32 + mi * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v & 3);
-            const int t = m0 + rt;
-            if (t >= p.M)
-                continue;
-            float y[4];
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                y[ni] = acc[mi][ni][v] + bcol[ni];   // f32 bias add
-            if (sec < 2) {
-                // pairs: tile ni with tile ni + HALF/32 inside each head
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) {
-                    const int cih = (ni * 32) % HD;  // column of the tile inside its head
-                    if (cih >= HALF)
-                        continue;
-                    const int nj = ni + HALF / 32;
-                    const int i = cih + lr;          // pair index
-                    rot(y[ni], y[nj], s_cos[rt * HALF + i], s_sin[rt * HALF + i]);
-                }
-            }
-            const int64_t row = sec > 0 ? cache_row(p, t) : -1;
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-                const int c = cw - sbase + ni * 32 + lr;  // column inside the section
-                out[(int64_t)t * ldo + c] = y[ni];
-                if (row >= 0)
-                    put_cache<F16>(cache, row * p.nkt + c, y[ni]);
-            }
-            if (sec > 0 && row < 0 && lr == 0)   // lanes 0 and 32 see every row
-                atomicOr(p.err, 1u);
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -328,7 +146,10 @@ __device__ __forceinline__ int swz(int r)
 }
 }  // namespace big
 
-template <bool F16, int HD>
+// MODE 0: the fused output stage below (one k range per tile).  MODE 1: k is
+// split p.ksplit ways across workgroups and each stores its partial y tile to
+// p.part; proj_split_epilogue_kernel sums the partials and finishes.
+template <bool F16, int HD, int MODE>
 __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams p, InvTable inv)
 {
     using namespace big;
@@ -339,8 +160,11 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int nblk = p.N / BN + (p.N % BN ? 1 : 0);
-    const int n0 = ((int)blockIdx.x % nblk) * BN;
-    const int m0 = ((int)blockIdx.x / nblk) * BM;
+    const int mblk = (p.M + BM - 1) / BM;
+    const int tile = (int)blockIdx.x % (nblk * mblk);
+    const int split = (int)blockIdx.x / (nblk * mblk);
+    const int n0 = (tile % nblk) * BN;
+    const int m0 = (tile / nblk) * BM;
 
     // loads: wave w fills rows [64w, 64w + 64) of the A and the B region;
     // instruction j covers rows r = 64w + 16j + lane/4, lane%4 is the LDS
@@ -359,11 +183,14 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
     const unsigned char *xb = reinterpret_cast<const unsigned char *>(p.x);
     const unsigned char *wb = reinterpret_cast<const unsigned char *>(p.w);
     typedef __attribute__((address_space(3))) void lds_t;
-    const int KT = p.K / BK;
-    // sub-tile st (clamped to the last one: the loop stays uniform) into its stage
+    // this workgroup's sub-tiles [kt0, kt0 + KT) of the k range
+    const int KT_all = p.K / BK;
+    const int kt0 = (int)((int64_t)split * KT_all / p.ksplit);
+    const int KT = (int)((int64_t)(split + 1) * KT_all / p.ksplit) - kt0;
+    // local sub-tile st (clamped to the last one: the loop stays uniform)
     auto issue = [&](int st) {
         const int stage = st % NSTAGE;
-        const uint32_t kb = (uint32_t)min(st, KT - 1) * (BK * 2);
+        const uint32_t kb = (uint32_t)(kt0 + min(st, KT - 1)) * (BK * 2);
         unsigned char *sa = lds + stage * kStage + (64 * wave) * kRow;
         unsigned char *sb = sa + kRegion;
 #pragma unroll
@@ -402,13 +229,20 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
     };
     // acc[f][t]: 32 features x 32 tokens, the weight fragment as the A
     // operand, so a lane ends up holding 4 consecutive features of a token
+    // (MODE 1 keeps the usual orientation, acc[t][f] = tokens x outputs, so
+    // one store or atomic instruction covers 32 consecutive outputs of a row)
     auto mfma_half = [&](int tlo, const bf16x8 (&fa)[MI], const bf16x8 (&fb)[4]) {
 #pragma unroll
         for (int ti = tlo; ti < tlo + MI / 2; ++ti)
 #pragma unroll
-            for (int fi = 0; fi < 4; ++fi)
-                acc[fi][ti] =
-                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fi], fa[ti], acc[fi][ti], 0, 0, 0);
+            for (int fi = 0; fi < 4; ++fi) {
+                if constexpr (MODE == 0)
+                    acc[fi][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fi], fa[ti],
+                                                                          acc[fi][ti], 0, 0, 0);
+                else
+                    acc[ti][fi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ti], fb[fi],
+                                                                          acc[ti][fi], 0, 0, 0);
+            }
     };
 
     // prologue: sub-tiles 0..3 in flight, sub-tile 0 landed everywhere
@@ -443,6 +277,28 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
     // the clamped reloads of the last iterations must land before the wave
     // leaves (they write this block's LDS)
     __builtin_amdgcn_s_waitcnt(0);
+
+    if constexpr (MODE == 1) {
+        // partial y of this split: lane (lr, hi) holds output fi*32 + lr of
+        // tokens ti*32 + 8(v/4) + 4hi + v%4 in acc[ti][fi][v]
+        const int cw = n0 + wn * 128;
+        if (cw >= p.N)
+            return;
+        float *const out = p.part + (int64_t)split * p.M * p.N + cw + lr;
+#pragma unroll
+        for (int ti = 0; ti < MI; ++ti)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int t = m0 + wm * 128 + ti * 32 + 8 * (v / 4) + 4 * hi + (v & 3);
+                if (t >= p.M)
+                    continue;
+                float *const o = out + (int64_t)t * p.N;
+#pragma unroll
+                for (int fi = 0; fi < 4; ++fi)
+                    o[fi * 32] = acc[ti][fi][v];
+            }
+        return;
+    }
 
     // ---- epilogue ---------------------------------------------------------
     // Lane (lr, hi) of a wave holds, for token ti*32 + lr of its 128, the
@@ -508,6 +364,58 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
         }
         if (sec > 0 && row < 0 && hi == 0)
             atomicOr(p.err, 1u);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// split path, second step: y = sum of the k-split partials (in split order,
+// so the result does not depend on timing), then the epilogue.  One thread
+// per column pair (j, j + hd/2) of a head (the v section pairs its columns
+// the same way, without the rotation); cos/sin from the launch's table.
+// ---------------------------------------------------------------------------
+template <bool F16, int HD>
+__global__ __launch_bounds__(256) void proj_split_epilogue_kernel(ProjParams p)
+{
+    constexpr int HALF = HD / 2;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int pairs = p.N / 2;
+    if (idx >= (int64_t)p.M * pairs)
+        return;
+    const int t = (int)(idx / pairs);
+    const int pr = (int)(idx - (int64_t)t * pairs);
+    const int head = pr / HALF, i = pr - head * HALF;
+    const int c0 = head * HD + i, c1 = c0 + HALF;
+    const float *src = p.part + (int64_t)t * p.N;
+    float y0 = src[c0], y1 = src[c1];
+    for (int sp = 1; sp < p.ksplit; ++sp) {
+        src += (int64_t)p.M * p.N;
+        y0 = y0 + src[c0];
+        y1 = y1 + src[c1];
+    }
+    const int sec = c0 < p.nqt ? 0 : (c0 < p.nqt + p.nkt ? 1 : 2);
+    const int sbase = sec == 0 ? 0 : (sec == 1 ? p.nqt : p.nqt + p.nkt);
+    const int s0 = c0 - sbase, s1 = c1 - sbase;
+    const float *bias = p.b[sec];
+    if (bias) {
+        y0 = y0 + bias[s0];
+        y1 = y1 + bias[s1];
+    }
+    if (sec < 2) {
+        const float *trow = p.rtab + (int64_t)t * HD;
+        rot(y0, y1, trow[i], trow[HALF + i]);
+    }
+    float *out = p.out[sec] + (int64_t)t * p.ld[sec];
+    out[s0] = y0;
+    out[s1] = y1;
+    if (sec > 0) {
+        const int64_t row = cache_row(p, t);
+        void *cache = sec == 1 ? p.cache[0] : p.cache[1];
+        if (row >= 0) {
+            put_cache<F16>(cache, row * p.nkt + s0, y0);
+            put_cache<F16>(cache, row * p.nkt + s1, y1);
+        } else if (pr == p.nqt / 2) {   // the first k pair reports the token
+            atomicOr(p.err, 1u);
+        }
     }
 }
 
@@ -630,30 +538,37 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
     }
 }
 
-// 256x256 tiles (four waves of 128x128) once there are enough tokens to give
-// the chip a few tiles per CU; 32x256 tiles (two waves of 32x128) below that,
-// so a batch of a few hundred tokens still spreads over the CUs.
-using TileS = Tile<1, 2, 1, 32>;
+// Launch choice.  Decode (1-4 tokens): the GEMV.  Long prompts (1024+ tokens,
+// 16-byte aligned sections): the cos/sin table and the fused 256 x 256 kernel.
+// Otherwise (a batch of a few hundred tokens has too few 256 x 256 tiles to
+// fill the chip, e.g. 28 at the 14B shape): the table, the 256 x 256 kernel
+// with k split so the launch has about one workgroup per CU, each split
+// storing its partial tile, and a summing epilogue kernel.
 constexpr int kLargeM = 1024;
+constexpr int kTargetGroups = 256;
 
-template <bool F16, int HD, class T>
-hipError_t launch_mfma(const ProjParams &pp, const InvTable &inv, hipStream_t st)
+template <bool F16, int HD, int MODE>
+hipError_t set_big_lds()
 {
-    const int nblk = pp.N / T::BN + (pp.N % T::BN ? 1 : 0);
-    const int mblk = (pp.M + T::BM - 1) / T::BM;
-    const int lds_bytes = T::lds_bytes(HD);
-    static bool attr = false;   // raise the dynamic-LDS limit once per kernel
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&proj_mfma_kernel<F16, HD, T>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-        if (e != hipSuccess)
-            return e;
-        attr = true;
-    }
-    hipLaunchKernelGGL((proj_mfma_kernel<F16, HD, T>), dim3(nblk * mblk), dim3(T::kThreads),
-                       (unsigned)lds_bytes, st, pp, inv);
-    return hipGetLastError();
+    static bool done = false;   // raise the dynamic-LDS limit once per kernel
+    if (done)
+        return hipSuccess;
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&proj_mfma_big_kernel<F16, HD, MODE>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, big::kLds);
+    done = e == hipSuccess;
+    return e;
+}
+
+// the number of k splits of the raw path for this shape
+int choose_ksplit(int M, int N, int K)
+{
+    const int tiles = ((N + big::BN - 1) / big::BN) * ((M + big::BM - 1) / big::BM);
+    int s = (kTargetGroups + tiles / 2) / tiles;
+    const int max_s = K / big::BK / 4;   // at least 4 sub-tiles per split
+    if (s > max_s)
+        s = max_s;
+    return s < 1 ? 1 : s;
 }
 
 template <bool F16, int HD>
@@ -670,26 +585,32 @@ hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st
             hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, 4>), grid, block, 0, st, pp, inv);
         return hipGetLastError();
     }
+    const int nblk = pp.N / big::BN + (pp.N % big::BN ? 1 : 0);
+    const int mblk = (pp.M + big::BM - 1) / big::BM;
     if (pp.M >= kLargeM && pp.vec) {
-        const int nblk = pp.N / big::BN + (pp.N % big::BN ? 1 : 0);
-        const int mblk = (pp.M + big::BM - 1) / big::BM;
-        static bool attr = false;   // raise the dynamic-LDS limit once per kernel
-        if (!attr) {
-            hipError_t e = hipFuncSetAttribute(
-                reinterpret_cast<const void *>(&proj_mfma_big_kernel<F16, HD>),
-                hipFuncAttributeMaxDynamicSharedMemorySize, big::kLds);
-            if (e != hipSuccess)
-                return e;
-            attr = true;
-        }
+        hipError_t e = set_big_lds<F16, HD, 0>();
+        if (e != hipSuccess)
+            return e;
         const int64_t n_tab = (int64_t)pp.M * (HD / 2);
         hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n_tab + 255) / 256)), dim3(256), 0,
                            st, pp.pos, pp.M, HD / 2, inv, const_cast<float *>(pp.rtab));
-        hipLaunchKernelGGL((proj_mfma_big_kernel<F16, HD>), dim3(nblk * mblk), dim3(big::kThreads),
-                           (unsigned)big::kLds, st, pp, inv);
+        hipLaunchKernelGGL((proj_mfma_big_kernel<F16, HD, 0>), dim3(nblk * mblk),
+                           dim3(big::kThreads), (unsigned)big::kLds, st, pp, inv);
         return hipGetLastError();
     }
-    return launch_mfma<F16, HD, TileS>(pp, inv, st);
+    // split path: the table, the GEMM writing k-split partials, the summing epilogue
+    hipError_t e = set_big_lds<F16, HD, 1>();
+    if (e != hipSuccess)
+        return e;
+    const int64_t n_tab = (int64_t)pp.M * (HD / 2);
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n_tab + 255) / 256)), dim3(256), 0, st,
+                       pp.pos, pp.M, HD / 2, inv, const_cast<float *>(pp.rtab));
+    hipLaunchKernelGGL((proj_mfma_big_kernel<F16, HD, 1>), dim3(nblk * mblk * pp.ksplit),
+                       dim3(big::kThreads), (unsigned)big::kLds, st, pp, inv);
+    const int64_t n_pairs = (int64_t)pp.M * (pp.N / 2);
+    hipLaunchKernelGGL((proj_split_epilogue_kernel<F16, HD>), dim3((unsigned)((n_pairs + 255) / 256)),
+                       dim3(256), 0, st, pp);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -785,6 +706,8 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
     pp.err = h->d_err;
     pp.vec = pl.W == 4;
     pp.rtab = nullptr;
+    pp.ksplit = 1;
+    pp.part = nullptr;
 
     const InvTable &inv = handle_inv(h, a->theta, a->head_dim, a->freq_scale);
     hipStream_t st = (a->stream || a->use_stream) ? static_cast<hipStream_t>(a->stream) : h->stream;
@@ -792,11 +715,15 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
     hipError_t e = g.set(h->device);
     if (e != hipSuccess)
         return fail(h, QKV_ERR_HIP, "hipSetDevice(%d): %s", h->device, hipGetErrorString(e));
-    if (pp.M >= kLargeM && pp.vec) {
-        // the long-prompt path reads a [nt][head_dim] f32 cos/sin table from
-        // the handle's workspace; a larger request than any before grows it
+    if (pp.M > kGemvTok) {
+        // the MFMA paths read a [nt][head_dim] f32 cos/sin table from the
+        // handle's workspace, and the split path also keeps its [splits][nt][N]
+        // partial sums there; a larger request than any before grows it
         // (after the device has finished with the old one)
-        const size_t need = (size_t)pp.M * (size_t)a->head_dim * sizeof(float);
+        const bool fused = pp.M >= kLargeM && pp.vec;
+        pp.ksplit = fused ? 1 : choose_ksplit(pp.M, pp.N, pp.K);
+        const size_t tab = (size_t)pp.M * (size_t)a->head_dim * sizeof(float);
+        const size_t need = tab + (fused ? 0 : (size_t)pp.ksplit * pp.M * pp.N * sizeof(float));
         if (h->proj_ws_bytes < need) {
             e = hipDeviceSynchronize();
             if (e == hipSuccess && h->proj_ws)
@@ -813,6 +740,7 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
             h->proj_ws_bytes = need;
         }
         pp.rtab = static_cast<const float *>(h->proj_ws);
+        pp.part = reinterpret_cast<float *>(static_cast<char *>(h->proj_ws) + tab);
     }
     const bool f16 = a->cache_dtype == QKV_CACHE_F16;
     if (a->head_dim == 128)

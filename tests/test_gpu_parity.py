@@ -41,11 +41,10 @@ def run_case(h, c, entry="run_ex", check_untouched=True, label=""):
 
 # ---- the five workloads -----------------------------------------------------
 
-@pytest.mark.parametrize("form", ["separate", "concat"])
-@pytest.mark.parametrize("entry", ["run", "run_ex"])
+# run takes dense rows only, so concat sections go through run_ex
+@pytest.mark.parametrize("entry,form", [("run", "separate"), ("run_ex", "separate"),
+                                        ("run_ex", "concat")])
 def test_tiny_decode(handle, form, entry):
-    if entry == "run" and form == "concat":
-        pytest.skip("run takes dense rows; nt=1 concat sections go through run_ex")
     w = wl.TINY_DECODE
     c = Case(w, form=form)
     # the plain entry point uses the handle's n_ctx; give it a matching handle

@@ -199,8 +199,10 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  * then, on y split into its q, k, v sections, exactly the epilogue of
  * qkv_epilogue_run_ex: optional biases, NeoX rotary embedding of q and k, the
  * sections written to epi.q / epi.k / epi.v (outputs only here) and the K/V
- * cache rows stored.  One launch: a matrix-core (MFMA) GEMM for more than 4
- * tokens, a weight-streaming GEMV for 1-4 tokens.
+ * cache rows stored.  The GEMM runs on the matrix cores (MFMA) for more than
+ * 4 tokens, as a weight-streaming GEMV for 1-4 tokens; in both, the epilogue
+ * works on the sums before they reach HBM (below 1024 tokens, on k-split
+ * partial sums; see Launches).
  *
  *   x   bf16 [nt][ld_x] activations (device, 16-byte aligned, ld_x % 8 == 0)
  *   w   bf16 [nqt + 2*nkt][hidden] concat weight rows q|k|v (device, aligned)
@@ -209,11 +211,14 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  * Limits (QKV_ERR_UNSUPPORTED otherwise): NeoX style, head_dim 64 or 128, q
  * and k/v widths multiples of 128; x and w each under 2 GiB.
  *
- * Workspace: launches of 1024 or more tokens with 16-byte aligned sections
- * use a cos/sin table of nt * head_dim * 4 bytes held by the handle.  The
- * first such call with more tokens than any before it synchronizes the device
- * and (re)allocates it; make that call outside graph capture.  All other calls
- * allocate nothing and never synchronize.  The f32 sums are taken in a different
+ * Launches: 1-4 tokens run one weight-streaming kernel.  More tokens use a
+ * workspace held by the handle: a cos/sin table of nt * head_dim * 4 bytes,
+ * and, below 1024 tokens or with sections not 16-byte aligned, the partial
+ * sums of a k split (splits * nt * (nqt + 2*nkt) * 4 bytes, about 66 MB for
+ * 256 tokens of the 14B shape); those launches are two or three kernels on
+ * the stream.  A call that needs more workspace than any before it
+ * synchronizes the device and (re)allocates it: make that call outside graph
+ * capture.  All other calls allocate nothing and never synchronize.  The f32 sums are taken in a different
  * order than a plain loop: each output carries up to (hidden+2) * 2^-24 *
  * sum_k |x w| of accumulation error on top of the epilogue's own rounding.
  */

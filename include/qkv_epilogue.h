@@ -200,9 +200,10 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  * qkv_epilogue_run_ex: optional biases, NeoX rotary embedding of q and k, the
  * sections written to epi.q / epi.k / epi.v (outputs only here) and the K/V
  * cache rows stored.  The GEMM runs on the matrix cores (MFMA) for more than
- * 4 tokens, as a weight-streaming GEMV for 1-4 tokens; in both, the epilogue
- * works on the sums before they reach HBM (below 1024 tokens, on k-split
- * partial sums; see Launches).
+ * 4 tokens, as a weight-streaming GEMV for 1-4 tokens.  With 1-4 tokens and
+ * with 1024+ tokens (aligned sections) the epilogue runs on the sums in
+ * registers; otherwise the GEMM stores k-split partial sums and a second
+ * kernel adds them and runs the epilogue (see Launches).
  *
  *   x   bf16 [nt][ld_x] activations (device, 16-byte aligned, ld_x % 8 == 0)
  *   w   bf16 [nqt + 2*nkt][hidden] concat weight rows q|k|v (device, aligned)

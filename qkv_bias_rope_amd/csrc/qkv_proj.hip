@@ -40,6 +40,7 @@ using namespace qkv_detail;
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -425,7 +426,8 @@ __global__ __launch_bounds__(256) void proj_split_epilogue_kernel(ProjParams p)
 // One wave per NeoX pair of weight rows (j and j + hd/2 of a head; in the v
 // section the same pairing just groups rows), four waves per block.  Lane l
 // takes the 16-byte chunks l, l+64, ... of both rows, four chunks in flight
-// per row, and keeps NT running sums per row; a butterfly over the wave
+// per row, and keeps NT running sums per row (v_dot2_f32_bf16: two bf16
+// products into the f32 sum per instruction); a butterfly over the wave
 // completes the dot products, and lane t < nt finishes token t: bias, the
 // rotation of the pair, write-back and the cache store.
 constexpr int kGemvTok = 4;          // the GEMV path takes up to 4 tokens
@@ -473,22 +475,30 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
         for (int u = 0; u < kGemvU; ++u) {
             if (!ok[u])
                 a[u] = b[u] = u32x4{0u, 0u, 0u, 0u};
+            // each dword holds two consecutive bf16 of a row (x and W alike):
+            // one dot2 adds both exact products to the f32 sum.  The pairs are
+            // taken from the whole 16-byte vector by shuffles: bit-casting
+            // single dwords of it compiled to one-dword loads reused for all
+            // four pairs (checked in the ISA).
+            const bf16x8 wa8 = __builtin_bit_cast(bf16x8, a[u]);
+            const bf16x8 wb8 = __builtin_bit_cast(bf16x8, b[u]);
+            bf16x8 xx8[NT];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float wa0 = __uint_as_float(a[u][e] << 16);
-                const float wa1 = __uint_as_float(a[u][e] & 0xffff0000u);
-                const float wb0 = __uint_as_float(b[u][e] << 16);
-                const float wb1 = __uint_as_float(b[u][e] & 0xffff0000u);
+            for (int t = 0; t < NT; ++t)
+                xx8[t] = __builtin_bit_cast(bf16x8, xv[u][t]);
+#define QKV_PAIR(v8, e) __builtin_shufflevector(v8, v8, 2 * (e), 2 * (e) + 1)
 #pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const float x0 = __uint_as_float(xv[u][t][e] << 16);
-                    const float x1 = __uint_as_float(xv[u][t][e] & 0xffff0000u);
-                    d0[t] = fmaf(x0, wa0, d0[t]);
-                    d0[t] = fmaf(x1, wa1, d0[t]);
-                    d1[t] = fmaf(x0, wb0, d1[t]);
-                    d1[t] = fmaf(x1, wb1, d1[t]);
-                }
+            for (int t = 0; t < NT; ++t) {
+                d0[t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 0), QKV_PAIR(wa8, 0), d0[t], false);
+                d0[t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 1), QKV_PAIR(wa8, 1), d0[t], false);
+                d0[t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 2), QKV_PAIR(wa8, 2), d0[t], false);
+                d0[t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 3), QKV_PAIR(wa8, 3), d0[t], false);
+                d1[t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 0), QKV_PAIR(wb8, 0), d1[t], false);
+                d1[t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 1), QKV_PAIR(wb8, 1), d1[t], false);
+                d1[t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 2), QKV_PAIR(wb8, 2), d1[t], false);
+                d1[t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 3), QKV_PAIR(wb8, 3), d1[t], false);
             }
+#undef QKV_PAIR
         }
     }
 #pragma unroll

@@ -219,7 +219,9 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  * 256 tokens of the 14B shape); those launches are two or three kernels on
  * the stream.  A call that needs more workspace than any before it
  * synchronizes the device and (re)allocates it: make that call outside graph
- * capture.  All other calls allocate nothing and never synchronize.  The f32 sums are taken in a different
+ * capture.  All other calls allocate nothing and never synchronize.  Calls on
+ * one handle share its workspace: calls that may run concurrently (different
+ * streams) need different handles.  The f32 sums are taken in a different
  * order than a plain loop: each output carries up to (hidden+2) * 2^-24 *
  * sum_k |x w| of accumulation error on top of the epilogue's own rounding.
  */

@@ -363,3 +363,99 @@ def test_proj_rejects_unsupported(handle):
     assert torch.isnan(c.g_q).all() and torch.isnan(c96.g_q).all()
     assert B.qkv_epilogue_run_proj(handle, base) == B.QKV_OK
     assert B.qkv_epilogue_status(handle) == B.QKV_OK
+
+
+@pytest.mark.parametrize("nt", [1023, 1024])
+def test_proj_routing_boundary(handle, nt):
+    """1023 tokens take the split-k path, 1024 the fused long-prompt path;
+    both match the oracle on the same draws."""
+    w = wl.Workload("proj_boundary", 40, 8, 128, nt=nt, n_ctx=4096, n_slots=1, layers=1,
+                    seed=19, pos_mode="uniform")
+    c = ProjCase(w, hidden=128)
+    assert _run(handle, c, f"boundary_{nt}") == B.QKV_OK
+    c.check(f"boundary_{nt}")
+
+
+def test_proj_long_slots_f32_cache(handle):
+    """The fused long-prompt path with per-token cache slots (32 sequences)
+    and an f32 cache; equal (slot, position) pairs are allowed to race."""
+    w = wl.Workload("proj_long_slots", 40, 8, 128, nt=1100, n_ctx=64, n_slots=32, layers=1,
+                    seed=20, cache_dtypes=(wl.CACHE_F32,), pos_mode="uniform")
+    c = ProjCase(w, hidden=128)
+    assert _run(handle, c, "long_slots") == B.QKV_OK
+    c.check("long_slots")
+
+
+@pytest.mark.parametrize("nt", [3, 40, 1030])
+def test_proj_minimal_hidden(handle, nt):
+    """hidden = 64 (two k sub-tiles, fewer than the LDS ring's depth) on the
+    GEMV, split-k and fused paths."""
+    w = wl.Workload("proj_hidden64", 40, 8, 128, nt=nt, n_ctx=2048, n_slots=1, layers=1,
+                    seed=21, pos_mode="arange")
+    c = ProjCase(w, hidden=64)
+    assert _run(handle, c, f"hidden64_{nt}") == B.QKV_OK
+    c.check(f"hidden64_{nt}")
+
+
+def _refresh_inputs(c, rep):
+    """New activations and positions written into a case's device buffers."""
+    rng = np.random.default_rng(5000 + rep)
+    x = wl.bf16_bits(rng.standard_normal(c.d["x"].shape, dtype=np.float32))
+    pos = rng.integers(0, c.w.n_ctx, size=c.nt, dtype=np.int32)
+    c.d["x"] = x
+    c.d["pos"] = pos
+    ldx = c.g_x.shape[1]
+    xp = np.zeros((c.nt, ldx), np.uint16)
+    xp[:, :c.hidden] = x
+    c.g_x.copy_(torch.from_numpy(xp.view(np.int16)).to(DEV))
+    c.g_pos.copy_(torch.from_numpy(pos).to(DEV))
+    for cache in (c.kc, c.vc):   # back to the sentinel so addressing is checked again
+        fresh = new_cache(cache.shape[0], cache.shape[1], c.cd)
+        cache.copy_(fresh)
+
+
+def _graph_replays(handle, cases, reps=2):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):            # warm-up outside capture (sizes the workspace)
+        for c in cases:
+            assert B.qkv_epilogue_run_proj(handle, c.args()) == 0
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for c in cases:
+            assert B.qkv_epilogue_run_proj(handle, c.args()) == 0
+    torch.cuda.synchronize()
+    for rep in range(reps):
+        for c in cases:
+            _refresh_inputs(c, rep * 100 + cases.index(c))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert B.qkv_epilogue_status(handle) == 0
+        for i, c in enumerate(cases):
+            c.run_oracle()
+            c.check(f"graph replay {rep} call {i}")
+
+
+def test_proj_graph_capture_decode_layers(handle):
+    """Six one-token layers (alternating concat and separate outputs) captured
+    into one HIP graph and replayed with new activations and positions."""
+    cases = []
+    for layer in range(6):
+        c = ProjCase(wl.DECODE_14B, hidden=5120, nt=1,
+                     form="concat" if layer % 2 == 0 else "separate")
+        c.upload()
+        cases.append(c)
+    _graph_replays(handle, cases)
+
+
+def test_proj_graph_capture_split_and_fused(handle):
+    """A split-k call (300 tokens) and a fused long-prompt call (1100 tokens)
+    captured after a warm-up call; no allocation happens in the capture."""
+    w1 = wl.Workload("proj_graph_split", 40, 8, 128, nt=300, n_ctx=4096, n_slots=1, layers=1,
+                     seed=22, pos_mode="uniform")
+    w2 = wl.Workload("proj_graph_long", 40, 8, 128, nt=1100, n_ctx=4096, n_slots=1, layers=1,
+                     seed=23, pos_mode="uniform")
+    cases = [ProjCase(w1, hidden=256).upload(), ProjCase(w2, hidden=256).upload()]
+    _graph_replays(handle, cases)

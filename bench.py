@@ -14,7 +14,9 @@ time, where the algorithmic bytes are
 
 Input sets are rotated (each set has its own q/k/v and caches, together well
 over the 256 MB last-level cache) so every launch reads its inputs from HBM.
-Timing: HIP events on the launch stream around the timed launches.
+Timing: HIP events on the launch stream around the timed launches.  Beside
+that figure the line carries the p10/p50/p90 of single launches and the warm
+figure (one input set reused).
 
 Extra figures in the same line: the 256-sequence batched decode (f16 and f32
 caches) in GB/s, decode microseconds per layer for the 7B and 14B decode steps
@@ -171,6 +173,27 @@ def time_launches(h, arg_list, steps, warmup, stream, settle_s=0.3, fn=None):
     torch.cuda.synchronize()
     assert B.qkv_epilogue_status(h) == 0, B.qkv_epilogue_last_error(h)
     return e0.elapsed_time(e1) / steps
+
+
+def launch_percentiles(h, arg_list, n, stream, fn=None):
+    """p10 / p50 / p90 of single-launch durations (us): n launches cycling
+    through arg_list, each bracketed by its own pair of events on the stream."""
+    import torch
+    from qkv_bias_rope_amd import binding as B
+    run = fn or B.qkv_epilogue_run_ex
+    pairs = []
+    for i in range(n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = run(h, arg_list[i % len(arg_list)])
+        assert rc == 0, B.qkv_epilogue_last_error(h)
+        e1.record(stream)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+    q = lambda f: us[min(len(us) - 1, int(f * (len(us) - 1) + 0.5))]
+    return dict(p10=round(q(0.1), 3), p50=round(q(0.5), 3), p90=round(q(0.9), 3), launches=n)
 
 
 def bench_bandwidth(h, w, cache_dtype, steps, warmup, stream, min_set_bytes=1.5e9, slot=False,
@@ -433,11 +456,22 @@ def run_all(args, h, stream):
     w = wl.PREFILL_14B
     log(f"[bench] {w.name}: {args.warmup} warmup + {args.steps} timed launches")
     main_res, sets = bench_bandwidth(h, w, wl.CACHE_F16, args.steps, args.warmup, stream)
+    log(f"[bench] {w.name}: {main_res['ms'] * 1e3:.2f} us/launch, {main_res['gbs']:.1f} GB/s")
+    extra = {}
+    if not args.no_extra:
+        # the distribution of single launches over the same rotated sets, and
+        # the warm figure: one input set reused (252 MB, partly resident in the
+        # 256 MB last-level cache between launches)
+        arg_list = [sets.args(r, stream) for r in range(len(sets.sets))]
+        extra[w.name + "_per_launch_us"] = launch_percentiles(h, arg_list, 60, stream)
+        warm_ms = time_launches(h, arg_list[:1], args.steps, args.warmup, stream)
+        extra[w.name + "_warm"] = dict(us_per_launch=round(warm_ms * 1e3, 3),
+                                       gbs=round(main_res["bytes"] / (warm_ms * 1e-3) / 1e9, 1))
+        log(f"[bench]   per launch {extra[w.name + '_per_launch_us']}, warm "
+            f"{extra[w.name + '_warm']}")
     del sets
     torch.cuda.empty_cache()
-    log(f"[bench] {w.name}: {main_res['ms'] * 1e3:.2f} us/launch, {main_res['gbs']:.1f} GB/s")
 
-    extra = {}
     if not args.no_extra:
         wb = wl.BATCHED_DECODE_14B
         for cd, tag in ((wl.CACHE_F16, "f16"), (wl.CACHE_F32, "f32")):

@@ -432,9 +432,11 @@ __global__ __launch_bounds__(256) void proj_split_epilogue_kernel(ProjParams p)
 // rotation of the pair, write-back and the cache store.
 constexpr int kGemvTok = 4;          // the GEMV path takes up to 4 tokens
 constexpr int kGemvWaves = 4;
-constexpr int kGemvU = 4;            // chunks in flight per row and lane
 
-template <bool F16, int HD, int NT>
+// U: 16-byte chunks of each row in flight per lane and step; the launcher
+// picks U dividing the chunks per lane (hidden/512) when it can, since a
+// partial last step costs as much as a full one
+template <bool F16, int HD, int NT, int U>
 __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p, InvTable inv)
 {
     constexpr int HALF = HD / 2;
@@ -457,22 +459,23 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
 #pragma unroll
     for (int t = 0; t < NT; ++t)
         d0[t] = d1[t] = 0.0f;
-    for (int cb = lane; cb < nchunk; cb += 64 * kGemvU) {
-        u32x4 a[kGemvU], b[kGemvU], xv[kGemvU][NT];
-        bool ok[kGemvU];
+    for (int cb = lane; cb < nchunk; cb += 64 * U) {
+        u32x4 a[U], b[U], xv[U][NT];
+        bool ok[U];
 #pragma unroll
-        for (int u = 0; u < kGemvU; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int c = cb + 64 * u;
             ok[u] = c < nchunk;
             const int cc = ok[u] ? c : 0;    // past the row end: reload chunk 0, weight 0
-            a[u] = *reinterpret_cast<const u32x4 *>(w0 + cc * 8);
-            b[u] = *reinterpret_cast<const u32x4 *>(w1 + cc * 8);
+            // the weights are read once per call: nontemporal
+            a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w0 + cc * 8));
+            b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w1 + cc * 8));
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 xv[u][t] = *reinterpret_cast<const u32x4 *>(xr[t] + cc * 8);
         }
 #pragma unroll
-        for (int u = 0; u < kGemvU; ++u) {
+        for (int u = 0; u < U; ++u) {
             if (!ok[u])
                 a[u] = b[u] = u32x4{0u, 0u, 0u, 0u};
             // each dword holds two consecutive bf16 of a row (x and W alike):
@@ -581,19 +584,47 @@ int choose_ksplit(int M, int N, int K)
     return s < 1 ? 1 : s;
 }
 
+// chunks per row and step of the GEMV: the largest of 8..4 dividing the
+// chunks per lane, else the one wasting the fewest slots
+int gemv_step(int K)
+{
+    const int c = (K / 8 + 63) / 64;   // 16-byte chunks per lane and row
+    int best = 4, waste = 1 << 30;
+    for (int u = 8; u >= 4; --u) {
+        const int w = (c + u - 1) / u * u - c;
+        if (w < waste) {
+            best = u;
+            waste = w;
+        }
+    }
+    return best;
+}
+
+template <bool F16, int HD, int NT>
+hipError_t launch_gemv(const ProjParams &pp, const InvTable &inv, hipStream_t st, int u)
+{
+    const int blocks = (pp.N / 2 + kGemvWaves - 1) / kGemvWaves;
+    const dim3 grid(blocks), block(64 * kGemvWaves);
+    switch (u) {
+    case 8: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 8>), grid, block, 0, st, pp, inv); break;
+    case 7: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 7>), grid, block, 0, st, pp, inv); break;
+    case 6: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 6>), grid, block, 0, st, pp, inv); break;
+    case 5: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 5>), grid, block, 0, st, pp, inv); break;
+    default: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 4>), grid, block, 0, st, pp, inv); break;
+    }
+    return hipGetLastError();
+}
+
 template <bool F16, int HD>
 hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st)
 {
     if (pp.M <= kGemvTok) {
-        const int blocks = (pp.N / 2 + kGemvWaves - 1) / kGemvWaves;
-        const dim3 grid(blocks), block(64 * kGemvWaves);
+        const int u = gemv_step(pp.K);
         if (pp.M == 1)
-            hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, 1>), grid, block, 0, st, pp, inv);
-        else if (pp.M == 2)
-            hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, 2>), grid, block, 0, st, pp, inv);
-        else
-            hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, 4>), grid, block, 0, st, pp, inv);
-        return hipGetLastError();
+            return launch_gemv<F16, HD, 1>(pp, inv, st, u);
+        if (pp.M == 2)
+            return launch_gemv<F16, HD, 2>(pp, inv, st, u);
+        return launch_gemv<F16, HD, 4>(pp, inv, st, u);
     }
     const int nblk = pp.N / big::BN + (pp.N % big::BN ? 1 : 0);
     const int mblk = (pp.M + big::BM - 1) / big::BM;

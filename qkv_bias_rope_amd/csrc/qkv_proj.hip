@@ -1,7 +1,7 @@
 // qkv_proj.hip -- the concat q|k|v projection with the epilogue in its output
-// stage: y = x * W^T on the MFMA units (bf16 inputs, f32 accumulation), then
-// bias, NeoX rotary embedding, write-back of the q/k/v rows and the K/V cache
-// rows, all in one launch.
+// stage: y = x * W^T (bf16 inputs, f32 accumulation), then bias, NeoX rotary
+// embedding, write-back of the q/k/v rows and the K/V cache rows, applied to
+// the sums before y is ever written.
 //
 // The page "73 · D3-8 — G4 FusedQKV ported to CUDA" (§2, Excerpt C) feeds the
 // epilogue from one matmul over the concat weight rows wq|wk|wv; here that
@@ -22,14 +22,16 @@
 //  * 1024+ tokens: the epilogue runs on the accumulators (tiles computed
 //    transposed so a lane holds 4 consecutive outputs), with a cos/sin table
 //    computed once per launch.  Fewer tokens: the tiles are too few to fill
-//    the chip, so k is split across workgroups that add their shares into
-//    zeroed q|k|v sections, and the epilogue kernel finishes them in place.
+//    the chip, so k is split across workgroups that store partial tiles to
+//    the handle's workspace, and a second kernel sums them in split order and
+//    runs the epilogue.
 //  * Decode (up to 4 tokens) is a weight-streaming GEMV, not a contraction
 //    worth the matrix units: a separate kernel streams W with 16-byte loads,
 //    reduces each dot product across the wave and runs the same epilogue.
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
 
@@ -43,7 +45,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
 
 struct ProjParams {
     const uint16_t *x;       // bf16 [nt][ld_x]
@@ -64,10 +65,12 @@ struct ProjParams {
     const float *rtab;       // [M][cos half | sin half] (fused long-prompt path)
     int ksplit;              // k splits of the split path
     float *part;             // [ksplit][M][N] partial sums of the split path
+    int device;              // the handle's device (launch set-up only)
     bool vec;                // sections, biases, caches 16-byte aligned, strides % 4 == 0
 };
 
-// cache row of token t, or -1 (and the error bit) when out of range
+// cache row of token t (slot * n_ctx + pos), or -1 when pos or slot is out
+// of range (the caller then sets the error word)
 __device__ __forceinline__ int64_t cache_row(const ProjParams &p, int t)
 {
     const int64_t ps = p.pos[t];
@@ -96,7 +99,7 @@ __device__ __forceinline__ void put_cache(void *cache, int64_t off, float v)
 // ---------------------------------------------------------------------------
 // cos/sin table of a launch: row t holds cos then sin of pos[t] * inv[i],
 // i < half (f32 angle; sin/cos in double rounded to f32).  Every column
-// block of a long prompt reads it instead of recomputing it.
+// block reads it instead of recomputing it.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void rope_table_kernel(const int32_t *pos, int M, int half,
                                                          InvTable inv, float *tab)
@@ -115,8 +118,8 @@ __global__ __launch_bounds__(256) void rope_table_kernel(const int32_t *pos, int
 // ---------------------------------------------------------------------------
 // long prompts: 256 x 256 tiles, operands loaded straight into LDS
 // ---------------------------------------------------------------------------
-// Four waves of 128 tokens x 128 outputs (4 x 4 MFMA tiles each, computed
-// transposed: 32 outputs x 32 tokens per tile).  k advances in sub-tiles
+// Four waves of 128 tokens x 128 outputs (4 x 4 MFMA tiles each; the fused
+// mode computes them transposed, 32 outputs x 32 tokens).  k advances in sub-tiles
 // of 32 through a ring of four LDS stages (32 KB each: 256 token rows of A
 // and 256 weight rows of B, 64 bytes per row), filled by global->LDS loads
 // (64 lanes x 16 bytes per instruction) issued three sub-tiles ahead, so
@@ -138,7 +141,7 @@ constexpr int kThreads = 256;
 constexpr int kRow = BK * 2;                  // 64 bytes
 constexpr int kRegion = 256 * kRow;           // 16 KB for A or B
 constexpr int kStage = 2 * kRegion;           // 32 KB
-constexpr int kLds = NSTAGE * kStage;         // 128 KB (also holds the 256 x 64 cos/sin table)
+constexpr int kLds = NSTAGE * kStage;         // 128 KB
 constexpr int kLoadsPerWave = 8;              // 4 for A + 4 for B per sub-tile
 
 __device__ __forceinline__ int swz(int r)
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
     // acc[f][t]: 32 features x 32 tokens, the weight fragment as the A
     // operand, so a lane ends up holding 4 consecutive features of a token
     // (MODE 1 keeps the usual orientation, acc[t][f] = tokens x outputs, so
-    // one store or atomic instruction covers 32 consecutive outputs of a row)
+    // one store instruction covers 32 consecutive outputs of a row)
     auto mfma_half = [&](int tlo, const bf16x8 (&fa)[MI], const bf16x8 (&fb)[4]) {
 #pragma unroll
         for (int ti = tlo; ti < tlo + MI / 2; ++ti)
@@ -309,10 +312,9 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
     // cos/sin come from the launch's table (16-byte reads).
     constexpr int HALF = HD / 2;
     const int cw = n0 + wn * 128;                  // first output column of this wave
-    const int sec_w = cw < p.N ? (cw < p.nqt ? 0 : (cw < p.nqt + p.nkt ? 1 : 2)) : 3;
-    if (sec_w == 3)
+    if (cw >= p.N)
         return;
-    const int sec = sec_w;
+    const int sec = cw < p.nqt ? 0 : (cw < p.nqt + p.nkt ? 1 : 2);
     const int sbase = sec == 0 ? 0 : (sec == 1 ? p.nqt : p.nqt + p.nkt);
     float *const out = p.out[sec];
     const int64_t ldo = p.ld[sec];
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(256) void proj_split_epilogue_kernel(ProjParams p)
 // ---------------------------------------------------------------------------
 // One wave per NeoX pair of weight rows (j and j + hd/2 of a head; in the v
 // section the same pairing just groups rows), four waves per block.  Lane l
-// takes the 16-byte chunks l, l+64, ... of both rows, four chunks in flight
+// takes the 16-byte chunks l, l+64, ... of both rows, U chunks in flight
 // per row, and keeps NT running sums per row (v_dot2_f32_bf16: two bf16
 // products into the f32 sum per instruction); a butterfly over the wave
 // completes the dot products, and lane t < nt finishes token t: bias, the
@@ -560,16 +562,20 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
 constexpr int kLargeM = 1024;
 constexpr int kTargetGroups = 256;
 
+// Raise the kernel's dynamic-LDS limit to the 128 KB it uses, once per kernel
+// and device (the caller has made the handle's device current).
 template <bool F16, int HD, int MODE>
-hipError_t set_big_lds()
+hipError_t set_big_lds(int device)
 {
-    static bool done = false;   // raise the dynamic-LDS limit once per kernel
-    if (done)
+    static std::atomic<unsigned long long> done{0};
+    const unsigned long long bit = 1ull << (device & 63);
+    if (done.load(std::memory_order_acquire) & bit)
         return hipSuccess;
     hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&proj_mfma_big_kernel<F16, HD, MODE>),
         hipFuncAttributeMaxDynamicSharedMemorySize, big::kLds);
-    done = e == hipSuccess;
+    if (e == hipSuccess && device < 64)
+        done.fetch_or(bit, std::memory_order_release);
     return e;
 }
 
@@ -629,7 +635,7 @@ hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st
     const int nblk = pp.N / big::BN + (pp.N % big::BN ? 1 : 0);
     const int mblk = (pp.M + big::BM - 1) / big::BM;
     if (pp.M >= kLargeM && pp.vec) {
-        hipError_t e = set_big_lds<F16, HD, 0>();
+        hipError_t e = set_big_lds<F16, HD, 0>(pp.device);
         if (e != hipSuccess)
             return e;
         const int64_t n_tab = (int64_t)pp.M * (HD / 2);
@@ -640,7 +646,7 @@ hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st
         return hipGetLastError();
     }
     // split path: the table, the GEMM writing k-split partials, the summing epilogue
-    hipError_t e = set_big_lds<F16, HD, 1>();
+    hipError_t e = set_big_lds<F16, HD, 1>(pp.device);
     if (e != hipSuccess)
         return e;
     const int64_t n_tab = (int64_t)pp.M * (HD / 2);
@@ -749,6 +755,7 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
     pp.rtab = nullptr;
     pp.ksplit = 1;
     pp.part = nullptr;
+    pp.device = h->device;
 
     const InvTable &inv = handle_inv(h, a->theta, a->head_dim, a->freq_scale);
     hipStream_t st = (a->stream || a->use_stream) ? static_cast<hipStream_t>(a->stream) : h->stream;

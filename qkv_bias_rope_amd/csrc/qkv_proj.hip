@@ -116,33 +116,39 @@ __global__ __launch_bounds__(256) void rope_table_kernel(const int32_t *pos, int
 }
 
 // ---------------------------------------------------------------------------
-// long prompts: 256 x 256 tiles, operands loaded straight into LDS
+// 256 x 256 tiles, operands loaded straight into LDS
 // ---------------------------------------------------------------------------
-// Four waves of 128 tokens x 128 outputs (4 x 4 MFMA tiles each; the fused
-// mode computes them transposed, 32 outputs x 32 tokens).  k advances in sub-tiles
-// of 32 through a ring of four LDS stages (32 KB each: 256 token rows of A
-// and 256 weight rows of B, 64 bytes per row), filled by global->LDS loads
-// (64 lanes x 16 bytes per instruction) issued three sub-tiles ahead, so
-// HBM / last-level-cache latency has about 3000 MFMA cycles to resolve.
-// Chunk c of row r sits in slot c ^ g(r), g(r) = ((r >> 1) ^ (r >> 3)) & 3:
-// the 16-byte fragment reads of 16 consecutive rows hit distinct banks.
+// Eight waves, two per SIMD: wave (wm, wn) owns 128 tokens (wm) x 64 outputs,
+// the two 32-column MFMA tiles f0 and f0 + hd/64 of one head, so the NeoX
+// partner of every output sits in the same lane and register of the other
+// tile.  128 accumulators per lane leave room for two waves per SIMD, which
+// is what keeps the LDS busy: on gfx950 conflict-free 16-byte LDS reads
+// reach ~135 B/clk per CU with one wave per SIMD and ~225 with two.
 //
-// Per sub-tile s (two k steps of 16, 16 products each):
+// k advances in sub-tiles of 32 through a ring of four LDS stages (32 KB
+// each: 256 token rows of A and 256 weight rows of B, 64 bytes per row),
+// filled by global->LDS loads (64 lanes x 16 bytes per instruction) issued
+// three sub-tiles ahead.  Chunk c of row r sits in slot c ^ g(r),
+// g(r) = ((r >> 1) ^ (r >> 3)) & 3: the 16-byte fragment reads of 16
+// consecutive rows hit distinct banks.
+//
+// Per sub-tile s (two k steps of 16, 8 products each):
 //   products of step 0 (first half); read step-1 fragments; products of
 //   step 0 (second half); products of step 1 (first half); wait for this
 //   wave's loads of sub-tile s+1 and meet the other waves (after which stage
 //   s is free and sub-tile s+1 is visible); load sub-tile s+4 into stage s;
 //   read step-0 fragments of sub-tile s+1; products of step 1 (second half).
-// The cross-wave wait thus sits in the middle of a sub-tile and every
-// fragment read has 8 products (256+ cycles) in front of its first use.
 namespace big {
 constexpr int BM = 256, BN = 256, BK = 32, MI = 4, NSTAGE = 4;
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRow = BK * 2;                  // 64 bytes
 constexpr int kRegion = 256 * kRow;           // 16 KB for A or B
 constexpr int kStage = 2 * kRegion;           // 32 KB
 constexpr int kLds = NSTAGE * kStage;         // 128 KB
-constexpr int kLoadsPerWave = 8;              // 4 for A + 4 for B per sub-tile
+constexpr int kRowsPerWave = 256 / kWaves;    // rows of A (and of B) each wave loads
+constexpr int kInstPerRegion = kRowsPerWave / 16;
+constexpr int kLoadsPerWave = 2 * kInstPerRegion;   // per sub-tile
 
 __device__ __forceinline__ int swz(int r)
 {
@@ -158,11 +164,15 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
 {
     using namespace big;
     extern __shared__ __align__(16) unsigned char lds[];
+    constexpr int HALF = HD / 2;
+    constexpr int PT = HALF / 32;                 // tile distance of NeoX partners
 
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
+    // the wave's two output tiles (of the block's 8): f0 and f0 + PT
+    const int f0 = (wn / PT) * (2 * PT) + wn % PT;
     const int nblk = p.N / BN + (p.N % BN ? 1 : 0);
     const int mblk = (p.M + BM - 1) / BM;
     const int tile = (int)blockIdx.x % (nblk * mblk);
@@ -170,16 +180,15 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
     const int n0 = (tile % nblk) * BN;
     const int m0 = (tile / nblk) * BM;
 
-    // loads: wave w fills rows [64w, 64w + 64) of the A and the B region;
-    // instruction j covers rows r = 64w + 16j + lane/4, lane%4 is the LDS
-    // slot and the chunk it holds is slot ^ g(r) (g reads bits 1-4 of r:
-    // lane/4 and the parity of j).  Offsets are bytes from x / w (both
-    // < 2 GiB).
+    // loads: wave w fills rows [32w, 32w + 32) of the A and the B region;
+    // instruction j covers rows r = 32w + 16j + lane/4, lane%4 is the LDS
+    // slot and the chunk it holds is slot ^ g(r).  Offsets are bytes from
+    // x / w (both < 2 GiB).
     const int lrow = lane >> 2, slot = lane & 3;
-    uint32_t aoff[4], boff[4];
+    uint32_t aoff[kInstPerRegion], boff[kInstPerRegion];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 64 * wave + 16 * j + lrow;
+    for (int j = 0; j < kInstPerRegion; ++j) {
+        const int r = kRowsPerWave * wave + 16 * j + lrow;
         const int chunk = slot ^ big::swz(r);
         aoff[j] = (uint32_t)((int64_t)min(m0 + r, p.M - 1) * p.ld_x * 2) + chunk * 16;
         boff[j] = (uint32_t)((int64_t)min(n0 + r, p.N - 1) * p.K * 2) + chunk * 16;
@@ -195,66 +204,66 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
     auto issue = [&](int st) {
         const int stage = st % NSTAGE;
         const uint32_t kb = (uint32_t)(kt0 + min(st, KT - 1)) * (BK * 2);
-        unsigned char *sa = lds + stage * kStage + (64 * wave) * kRow;
+        unsigned char *sa = lds + stage * kStage + (kRowsPerWave * wave) * kRow;
         unsigned char *sb = sa + kRegion;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kInstPerRegion; ++j)
             __builtin_amdgcn_global_load_lds(xb + aoff[j] + kb, (lds_t *)(sa + j * 16 * kRow), 16, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kInstPerRegion; ++j)
             __builtin_amdgcn_global_load_lds(wb + boff[j] + kb, (lds_t *)(sb + j * 16 * kRow), 16, 0, 0);
     };
 
-    f32x16 acc[MI][4];
+    // acc[f * MI + ti]: output tile f (0, 1) x token tile ti
+    f32x16 acc[2 * MI];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int q = 0; q < 2 * MI; ++q)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                acc[mi][ni][v] = 0.0f;
+        for (int v = 0; v < 16; ++v)
+            acc[q][v] = 0.0f;
 
     // fragment reads: lane reads row lr of each 32-row tile, chunk 2*ks + hi
     const int lr = lane & 31, hi = lane >> 5;
     const int g = big::swz(lr);                 // tiles start at multiples of 32
     const int abase = (wm * 128 + lr) * kRow;
-    const int bbase = kRegion + (wn * 128 + lr) * kRow;
+    const int bbase0 = kRegion + (f0 * 32 + lr) * kRow;
+    const int bbase1 = bbase0 + PT * 32 * kRow;
     const int k0off = ((0 + hi) ^ g) * 16;      // step 0: chunk hi
     const int k1off = ((2 + hi) ^ g) * 16;      // step 1: chunk 2 + hi
 
-    bf16x8 a0[MI], b0[4], a1[MI], b1[4];
-    auto read_frags = [&](const unsigned char *s, int koff, bf16x8 (&fa)[MI], bf16x8 (&fb)[4]) {
+    bf16x8 a0[MI], b0[2], a1[MI], b1[2];
+    auto read_frags = [&](const unsigned char *s, int koff, bf16x8 (&fa)[MI], bf16x8 (&fb)[2]) {
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
             fa[mi] = *reinterpret_cast<const bf16x8 *>(s + abase + mi * 32 * kRow + koff);
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-            fb[ni] = *reinterpret_cast<const bf16x8 *>(s + bbase + ni * 32 * kRow + koff);
+        fb[0] = *reinterpret_cast<const bf16x8 *>(s + bbase0 + koff);
+        fb[1] = *reinterpret_cast<const bf16x8 *>(s + bbase1 + koff);
     };
-    // acc[f][t]: 32 features x 32 tokens, the weight fragment as the A
-    // operand, so a lane ends up holding 4 consecutive features of a token
-    // (MODE 1 keeps the usual orientation, acc[t][f] = tokens x outputs, so
-    // one store instruction covers 32 consecutive outputs of a row)
-    auto mfma_half = [&](int tlo, const bf16x8 (&fa)[MI], const bf16x8 (&fb)[4]) {
+    // MODE 0 computes each tile transposed (32 outputs x 32 tokens, the
+    // weight fragment as the A operand), so a lane ends up holding 4
+    // consecutive outputs of a token; MODE 1 keeps tokens x outputs, so one
+    // store instruction covers 32 consecutive outputs of a row
+    auto mfma_half = [&](int tlo, const bf16x8 (&fa)[MI], const bf16x8 (&fb)[2]) {
 #pragma unroll
         for (int ti = tlo; ti < tlo + MI / 2; ++ti)
 #pragma unroll
-            for (int fi = 0; fi < 4; ++fi) {
+            for (int f = 0; f < 2; ++f) {
                 if constexpr (MODE == 0)
-                    acc[fi][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fi], fa[ti],
-                                                                          acc[fi][ti], 0, 0, 0);
+                    acc[f * MI + ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        fb[f], fa[ti], acc[f * MI + ti], 0, 0, 0);
                 else
-                    acc[ti][fi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ti], fb[fi],
-                                                                          acc[ti][fi], 0, 0, 0);
+                    acc[f * MI + ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        fa[ti], fb[f], acc[f * MI + ti], 0, 0, 0);
             }
     };
 
-    // prologue: sub-tiles 0..3 in flight, sub-tile 0 landed everywhere
+    // prologue: sub-tiles 0..3 in flight, sub-tile 0 landed everywhere:
+    // vmcnt <= 3 * kLoadsPerWave (12); no lgkm/exp wait
+    static_assert(kLoadsPerWave == 4, "wait counts below assume 4 loads per sub-tile");
 #pragma unroll
     for (int st = 0; st < NSTAGE; ++st)
         issue(st);
-    // vmcnt <= 3 * kLoadsPerWave (24): lo bits 24 & 15, hi bits 24 >> 4; no lgkm/exp wait
-    __builtin_amdgcn_s_waitcnt((1 << 14) | (0xF << 8) | (7 << 4) | 8);
+    __builtin_amdgcn_s_waitcnt((0xF << 8) | (7 << 4) | 12);
     __syncthreads();
     read_frags(lds, k0off, a0, b0);
 
@@ -270,8 +279,8 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
         mfma_half(0, a1, b1);
         __builtin_amdgcn_sched_barrier(0);
         // this wave's loads of sub-tile kt+1 have landed once at most the two
-        // later groups (kt+2, kt+3) are outstanding: vmcnt <= 16
-        __builtin_amdgcn_s_waitcnt((1 << 14) | (0xF << 8) | (7 << 4) | 0);
+        // later groups (kt+2, kt+3) are outstanding: vmcnt <= 8
+        __builtin_amdgcn_s_waitcnt((0xF << 8) | (7 << 4) | 8);
         __syncthreads();
         issue(kt + NSTAGE);
         read_frags(lds + ((kt + 1) % NSTAGE) * kStage, k0off, a0, b0);
@@ -282,13 +291,13 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
     // leaves (they write this block's LDS)
     __builtin_amdgcn_s_waitcnt(0);
 
+    const int col0 = n0 + f0 * 32;                 // first output column of tile f = 0
+    if (col0 >= p.N)
+        return;
     if constexpr (MODE == 1) {
-        // partial y of this split: lane (lr, hi) holds output fi*32 + lr of
-        // tokens ti*32 + 8(v/4) + 4hi + v%4 in acc[ti][fi][v]
-        const int cw = n0 + wn * 128;
-        if (cw >= p.N)
-            return;
-        float *const out = p.part + (int64_t)split * p.M * p.N + cw + lr;
+        // partial y of this split: lane (lr, hi) holds output f*PT*32 + lr
+        // (from col0) of tokens ti*32 + 8(v/4) + 4hi + v%4
+        float *const out = p.part + (int64_t)split * p.M * p.N + col0 + lr;
 #pragma unroll
         for (int ti = 0; ti < MI; ++ti)
 #pragma unroll
@@ -297,72 +306,60 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
                 if (t >= p.M)
                     continue;
                 float *const o = out + (int64_t)t * p.N;
-#pragma unroll
-                for (int fi = 0; fi < 4; ++fi)
-                    o[fi * 32] = acc[ti][fi][v];
+                o[0] = acc[ti][v];
+                o[PT * 32] = acc[MI + ti][v];
             }
         return;
     }
 
     // ---- epilogue ---------------------------------------------------------
-    // Lane (lr, hi) of a wave holds, for token ti*32 + lr of its 128, the
-    // outputs fi*32 + 8g + 4hi + e (e < 4) in acc[fi][ti][4g + e]: four
-    // consecutive columns, stored with one 16-byte (f32) or 8-byte (f16)
-    // store.  The NeoX partner of tile fi is tile fi + hd/64, same register;
-    // cos/sin come from the launch's table (16-byte reads).
-    constexpr int HALF = HD / 2;
-    const int cw = n0 + wn * 128;                  // first output column of this wave
-    if (cw >= p.N)
-        return;
-    const int sec = cw < p.nqt ? 0 : (cw < p.nqt + p.nkt ? 1 : 2);
+    // Lane (lr, hi) holds, for token ti*32 + lr of the wave's 128, the
+    // outputs col0 + f*HALF + 8g + 4hi + e (e < 4) in acc[f*MI + ti][4g + e]:
+    // four consecutive columns, stored with one 16-byte (f32) or 8-byte
+    // (f16) store; f = 1 is the NeoX partner of f = 0.  cos/sin come from the
+    // launch's table (16-byte reads).
+    const int sec = col0 < p.nqt ? 0 : (col0 < p.nqt + p.nkt ? 1 : 2);
     const int sbase = sec == 0 ? 0 : (sec == 1 ? p.nqt : p.nqt + p.nkt);
     float *const out = p.out[sec];
     const int64_t ldo = p.ld[sec];
     const float *const bias = p.b[sec];
     void *const cache = sec == 1 ? p.cache[0] : p.cache[1];
-    const int cs = cw - sbase + 4 * hi;            // section column of (fi = 0, g = 0)
+    const int cs = col0 - sbase + 4 * hi;          // section column of (f = 0, g = 0)
+    const int ih = (f0 * 32) % HD;                 // pair index of the tile's first column
 
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-        const int rt = wm * 128 + ti * 32 + lr;    // token row in the block
-        const int t = m0 + rt;
+    for (int ti = 0; ti < MI; ++ti) {
+        const int t = m0 + wm * 128 + ti * 32 + lr;
         if (t >= p.M)
             continue;
         const int64_t row = sec > 0 ? cache_row(p, t) : -1;
         float *const orow = out + (int64_t)t * ldo;
         const float *const trow = p.rtab + (int64_t)t * 2 * HALF;
 #pragma unroll
-        for (int fi = 0; fi < 4; ++fi) {
-            const int cih = (fi * 32) % HD;        // column of the tile inside its head
-            if (sec < 2 && cih >= HALF)
-                continue;                          // handled with its partner
-            const int fj = fi + HALF / 32;
+        for (int g = 0; g < 4; ++g) {
+            const int c0 = cs + 8 * g, c1 = c0 + HALF;
+            const FVec<4> zero = {{0.f, 0.f, 0.f, 0.f}};
+            const FVec<4> b0 = bias ? ld_vec<4>(bias + c0) : zero;
+            const FVec<4> b1 = bias ? ld_vec<4>(bias + c1) : zero;
+            FVec<4> y0, y1;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int c0 = cs + fi * 32 + 8 * g;
-                FVec<4> y0, y1;
-                const FVec<4> b0 = bias ? ld_vec<4>(bias + c0) : FVec<4>{{0.f, 0.f, 0.f, 0.f}};
+            for (int e = 0; e < 4; ++e) {
+                y0.e[e] = acc[ti][4 * g + e] + b0.e[e];
+                y1.e[e] = acc[MI + ti][4 * g + e] + b1.e[e];
+            }
+            if (sec < 2) {
+                const int i0 = ih + 8 * g + 4 * hi;   // pair index of e = 0
+                const FVec<4> cv = ld_vec<4>(trow + i0);
+                const FVec<4> sv = ld_vec<4>(trow + HALF + i0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    y0.e[e] = acc[fi][ti][4 * g + e] + b0.e[e];
-                if (sec < 2) {
-                    const int c1 = c0 + HALF;
-                    const FVec<4> b1 = bias ? ld_vec<4>(bias + c1) : FVec<4>{{0.f, 0.f, 0.f, 0.f}};
-                    const int i0 = cih + 8 * g + 4 * hi;   // pair index of e = 0
-                    const FVec<4> cv = ld_vec<4>(trow + i0);
-                    const FVec<4> sv = ld_vec<4>(trow + HALF + i0);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        y1.e[e] = acc[fj][ti][4 * g + e] + b1.e[e];
-                        rot(y0.e[e], y1.e[e], cv.e[e], sv.e[e]);
-                    }
-                    st_data<4, false>(orow + c1, y1);
-                    if (row >= 0)
-                        st_cache<4, F16, false>(cache, row * p.nkt + c1, y1);
-                }
-                st_data<4, false>(orow + c0, y0);
-                if (row >= 0)
-                    st_cache<4, F16, false>(cache, row * p.nkt + c0, y0);
+                    rot(y0.e[e], y1.e[e], cv.e[e], sv.e[e]);
+            }
+            st_data<4, false>(orow + c0, y0);
+            st_data<4, false>(orow + c1, y1);
+            if (row >= 0) {
+                st_cache<4, F16, false>(cache, row * p.nkt + c0, y0);
+                st_cache<4, F16, false>(cache, row * p.nkt + c1, y1);
             }
         }
         if (sec > 0 && row < 0 && hi == 0)

@@ -327,6 +327,15 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
     const int cs = col0 - sbase + 4 * hi;          // section column of (f = 0, g = 0)
     const int ih = (f0 * 32) % HD;                 // pair index of the tile's first column
 
+    // this lane's 32 bias values, loaded once
+    const FVec<4> zero = {{0.f, 0.f, 0.f, 0.f}};
+    FVec<4> bias0[4], bias1[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        bias0[g] = bias ? ld_vec<4>(bias + cs + 8 * g) : zero;
+        bias1[g] = bias ? ld_vec<4>(bias + cs + 8 * g + HALF) : zero;
+    }
+
 #pragma unroll
     for (int ti = 0; ti < MI; ++ti) {
         const int t = m0 + wm * 128 + ti * 32 + lr;
@@ -334,26 +343,29 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
             continue;
         const int64_t row = sec > 0 ? cache_row(p, t) : -1;
         float *const orow = out + (int64_t)t * ldo;
-        const float *const trow = p.rtab + (int64_t)t * 2 * HALF;
+        // all of this token's cos/sin values first: one wait per token
+        const float *const trow = p.rtab + (int64_t)t * 2 * HALF + ih + 4 * hi;
+        FVec<4> cv[4], sv[4];
+        if (sec < 2) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                cv[g] = ld_vec<4>(trow + 8 * g);
+                sv[g] = ld_vec<4>(trow + HALF + 8 * g);
+            }
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int c0 = cs + 8 * g, c1 = c0 + HALF;
-            const FVec<4> zero = {{0.f, 0.f, 0.f, 0.f}};
-            const FVec<4> b0 = bias ? ld_vec<4>(bias + c0) : zero;
-            const FVec<4> b1 = bias ? ld_vec<4>(bias + c1) : zero;
             FVec<4> y0, y1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                y0.e[e] = acc[ti][4 * g + e] + b0.e[e];
-                y1.e[e] = acc[MI + ti][4 * g + e] + b1.e[e];
+                y0.e[e] = acc[ti][4 * g + e] + bias0[g].e[e];
+                y1.e[e] = acc[MI + ti][4 * g + e] + bias1[g].e[e];
             }
             if (sec < 2) {
-                const int i0 = ih + 8 * g + 4 * hi;   // pair index of e = 0
-                const FVec<4> cv = ld_vec<4>(trow + i0);
-                const FVec<4> sv = ld_vec<4>(trow + HALF + i0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    rot(y0.e[e], y1.e[e], cv.e[e], sv.e[e]);
+                    rot(y0.e[e], y1.e[e], cv[g].e[e], sv[g].e[e]);
             }
             st_data<4, false>(orow + c0, y0);
             st_data<4, false>(orow + c1, y1);

@@ -22,8 +22,9 @@ Extra figures in the same line: the 256-sequence batched decode (f16 and f32
 caches) in GB/s, decode microseconds per layer for the 7B and 14B decode steps
 (stream loop and HIP-graph replay), the unfused seven-launch chain, the q/k-norm
 variant, and the projection-fed epilogue (bf16 GEMM / GEMV with the epilogue in
-its output stage) on the 14B prefill (TFLOP/s) and the 14B one-token decode
-(us per layer, GB/s of weight streaming).  The CPU baseline is the oracle of
+its output stage) on the 14B prefill (TFLOP/s), the 14B one-token decode
+(us per layer, GB/s of weight streaming) and a 48-layer decode step of it
+(stream loop and HIP graph).  The CPU baseline is the oracle of
 the unfused chain, single-threaded, timed on a bounded sample of the headline
 workload.
 
@@ -364,6 +365,42 @@ def bench_proj(h, w, hidden, steps, warmup, stream, min_set_bytes=1.5e9, nt=None
     return res
 
 
+def bench_proj_decode(h, w, hidden, steps, warmup, stream):
+    """A decode step of the projection-fed epilogue: one token, one launch per
+    layer, every layer with its own weights (48 x 73 MB at 14B, so each step
+    streams them from HBM).  Microseconds per layer for a stream loop and for a
+    HIP-graph replay of the whole step."""
+    import torch
+    from qkv_bias_rope_amd import binding as B
+    layers = [ProjSets(w, hidden, 1, w.cache_dtypes[0], nt=1) for _ in range(w.layers)]
+    args = [ls.args(0, stream) for ls in layers]
+    n_loops = max(1, steps)
+    ms_step = time_launches(h, args, n_loops * w.layers, warmup * w.layers, stream,
+                            fn=B.qkv_epilogue_run_proj) * w.layers
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for a in args:
+            a.epi.stream = torch.cuda.current_stream().cuda_stream
+            assert B.qkv_epilogue_run_proj(h, a) == 0
+    for _ in range(max(1, warmup)):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    e0.record(cur)
+    for _ in range(n_loops):
+        g.replay()
+    e1.record(cur)
+    e1.synchronize()
+    ms_graph = e0.elapsed_time(e1) / n_loops
+    assert B.qkv_epilogue_status(h) == 0
+    del layers, args, g
+    torch.cuda.empty_cache()
+    return dict(us_per_layer_stream=ms_step * 1e3 / w.layers,
+                us_per_layer_graph=ms_graph * 1e3 / w.layers, layers=w.layers)
+
+
 def cpu_baseline(w, cache_dtype, budget_s=10.0):
     """The oracle (single-threaded C, unfused chain) on the headline workload,
     repeated over whole launches until about budget_s seconds have passed."""
@@ -545,6 +582,12 @@ def run_all(args, h, stream):
             input_sets=r["sets"])
         log(f"[bench]   {r['us_per_launch']:.1f} us/layer, {r['gbs']:.1f} GB/s "
             f"(library bf16 matmul call {r['library_bf16_matmul_call_us']:.1f} us)")
+        log(f"[bench] {wd.name} projection-fed epilogue, {wd.layers}-layer decode step")
+        r = bench_proj_decode(h, wd, hid, max(5, args.steps // 20), 2, stream)
+        extra[wd.name + "_proj_step"] = {k: (round(v, 3) if isinstance(v, float) else v)
+                                         for k, v in r.items()}
+        log(f"[bench]   {r['us_per_layer_stream']:.2f} us/layer (stream), "
+            f"{r['us_per_layer_graph']:.2f} us/layer (graph)")
 
     cpu = None
     if not args.no_cpu:

@@ -25,7 +25,7 @@
 //    the chip, so k is split across workgroups that store partial tiles to
 //    the handle's workspace, and a second kernel sums them in split order and
 //    runs the epilogue.
-//  * Decode (up to 4 tokens) is a weight-streaming GEMV, not a contraction
+//  * Decode (up to 8 tokens) is a weight-streaming GEMV, not a contraction
 //    worth the matrix units: a separate kernel streams W with 16-byte loads,
 //    reduces each dot product across the wave and runs the same epilogue.
 
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(256) void proj_split_epilogue_kernel(ProjParams p)
 }
 
 // ---------------------------------------------------------------------------
-// decode (1-4 tokens): weight-streaming GEMV + epilogue
+// decode (1-8 tokens): weight-streaming GEMV + epilogue
 // ---------------------------------------------------------------------------
 // One wave per NeoX pair of weight rows (j and j + hd/2 of a head; in the v
 // section the same pairing just groups rows), four waves per block.  Lane l
@@ -441,37 +441,45 @@ __global__ __launch_bounds__(256) void proj_split_epilogue_kernel(ProjParams p)
 // products into the f32 sum per instruction); a butterfly over the wave
 // completes the dot products, and lane t < nt finishes token t: bias, the
 // rotation of the pair, write-back and the cache store.
-constexpr int kGemvTok = 4;          // the GEMV path takes up to 4 tokens
+constexpr int kGemvTok = 8;          // the GEMV path takes up to 8 tokens
 constexpr int kGemvWaves = 4;
 
 // U: 16-byte chunks of each row in flight per lane and step; the launcher
 // picks U dividing the chunks per lane (hidden/512) when it can, since a
-// partial last step costs as much as a full one
-template <bool F16, int HD, int NT, int U>
+// partial last step costs as much as a full one.  P: NeoX pairs per wave (4
+// for 5-8 tokens, so each x chunk loaded serves eight weight rows).
+template <bool F16, int HD, int NT, int U, int P>
 __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p, InvTable inv)
 {
     constexpr int HALF = HD / 2;
+    constexpr int R = 2 * P;                 // weight rows per wave
     const int lane = (int)threadIdx.x & 63;
-    const int pair = (int)blockIdx.x * kGemvWaves + ((int)threadIdx.x >> 6);
-    if (pair >= p.N / 2)
+    const int pair0 = ((int)blockIdx.x * kGemvWaves + ((int)threadIdx.x >> 6)) * P;
+    if (pair0 >= p.N / 2)
         return;
-    const int head = pair / HALF, i = pair - head * HALF;
-    const int c0 = head * HD + i;            // global output column of the pair's first row
-    const int c1 = c0 + HALF;
     const int nchunk = p.K / 8;
-    const uint16_t *w0 = p.w + (int64_t)c0 * p.K;
-    const uint16_t *w1 = p.w + (int64_t)c1 * p.K;
+    // rows 2q and 2q+1 are columns c0 and c0 + hd/2 of pair pair0 + q
+    const uint16_t *wr[R];
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const int pr = pair0 + q;
+        const int c0 = (pr / HALF) * HD + pr % HALF;
+        wr[2 * q] = p.w + (int64_t)c0 * p.K;
+        wr[2 * q + 1] = p.w + (int64_t)(c0 + HALF) * p.K;
+    }
     const uint16_t *xr[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
         xr[t] = p.x + (int64_t)min(t, p.M - 1) * p.ld_x;
 
-    float d0[NT], d1[NT];
+    float d[R][NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-        d0[t] = d1[t] = 0.0f;
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            d[r][t] = 0.0f;
     for (int cb = lane; cb < nchunk; cb += 64 * U) {
-        u32x4 a[U], b[U], xv[U][NT];
+        u32x4 wv[U][R], xv[U][NT];
         bool ok[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -479,90 +487,94 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
             ok[u] = c < nchunk;
             const int cc = ok[u] ? c : 0;    // past the row end: reload chunk 0, weight 0
             // the weights are read once per call: nontemporal
-            a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w0 + cc * 8));
-            b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w1 + cc * 8));
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                wv[u][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wr[r] + cc * 8));
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 xv[u][t] = *reinterpret_cast<const u32x4 *>(xr[t] + cc * 8);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (!ok[u])
-                a[u] = b[u] = u32x4{0u, 0u, 0u, 0u};
             // each dword holds two consecutive bf16 of a row (x and W alike):
             // one dot2 adds both exact products to the f32 sum.  The pairs are
             // taken from the whole 16-byte vector by shuffles: bit-casting
             // single dwords of it compiled to one-dword loads reused for all
             // four pairs (checked in the ISA).
-            const bf16x8 wa8 = __builtin_bit_cast(bf16x8, a[u]);
-            const bf16x8 wb8 = __builtin_bit_cast(bf16x8, b[u]);
             bf16x8 xx8[NT];
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 xx8[t] = __builtin_bit_cast(bf16x8, xv[u][t]);
 #define QKV_PAIR(v8, e) __builtin_shufflevector(v8, v8, 2 * (e), 2 * (e) + 1)
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                d0[t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 0), QKV_PAIR(wa8, 0), d0[t], false);
-                d0[t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 1), QKV_PAIR(wa8, 1), d0[t], false);
-                d0[t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 2), QKV_PAIR(wa8, 2), d0[t], false);
-                d0[t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 3), QKV_PAIR(wa8, 3), d0[t], false);
-                d1[t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 0), QKV_PAIR(wb8, 0), d1[t], false);
-                d1[t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 1), QKV_PAIR(wb8, 1), d1[t], false);
-                d1[t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 2), QKV_PAIR(wb8, 2), d1[t], false);
-                d1[t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 3), QKV_PAIR(wb8, 3), d1[t], false);
+            for (int r = 0; r < R; ++r) {
+                const bf16x8 w8 = __builtin_bit_cast(
+                    bf16x8, ok[u] ? wv[u][r] : u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    d[r][t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 0), QKV_PAIR(w8, 0), d[r][t], false);
+                    d[r][t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 1), QKV_PAIR(w8, 1), d[r][t], false);
+                    d[r][t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 2), QKV_PAIR(w8, 2), d[r][t], false);
+                    d[r][t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 3), QKV_PAIR(w8, 3), d[r][t], false);
+                }
             }
 #undef QKV_PAIR
         }
     }
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            d0[t] += __shfl_xor(d0[t], m, 64);
-            d1[t] += __shfl_xor(d1[t], m, 64);
-        }
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1)
+                d[r][t] += __shfl_xor(d[r][t], m, 64);
 
     if (lane >= NT || lane >= p.M)
         return;
     const int t = lane;
-    float y0 = d0[0], y1 = d1[0];
 #pragma unroll
-    for (int u = 1; u < NT; ++u)
-        if (t == u) {
-            y0 = d0[u];
-            y1 = d1[u];
+    for (int q = 0; q < P; ++q) {
+        float y0 = d[2 * q][0], y1 = d[2 * q + 1][0];
+#pragma unroll
+        for (int u = 1; u < NT; ++u)
+            if (t == u) {
+                y0 = d[2 * q][u];
+                y1 = d[2 * q + 1][u];
+            }
+        const int pr = pair0 + q;
+        const int i = pr % HALF;
+        const int c0 = (pr / HALF) * HD + i;     // global output column of the pair's first row
+        const int sec = c0 < p.nqt ? 0 : (c0 < p.nqt + p.nkt ? 1 : 2);
+        const int sbase = sec == 0 ? 0 : (sec == 1 ? p.nqt : p.nqt + p.nkt);
+        const int s0 = c0 - sbase, s1 = s0 + HALF;   // columns inside the section
+        const float *bias = p.b[sec];
+        if (bias) {
+            y0 = y0 + bias[s0];
+            y1 = y1 + bias[s1];
         }
-    const int sec = c0 < p.nqt ? 0 : (c0 < p.nqt + p.nkt ? 1 : 2);
-    const int sbase = sec == 0 ? 0 : (sec == 1 ? p.nqt : p.nqt + p.nkt);
-    const int s0 = c0 - sbase, s1 = c1 - sbase;   // columns inside the section
-    const float *bias = p.b[sec];
-    if (bias) {
-        y0 = y0 + bias[s0];
-        y1 = y1 + bias[s1];
-    }
-    if (sec < 2) {
-        const float ang = (float)p.pos[t] * inv.v[i];
-        double sd, cd;
-        sincos((double)ang, &sd, &cd);
-        rot(y0, y1, (float)cd, (float)sd);
-    }
-    float *out = p.out[sec];
-    out[(int64_t)t * p.ld[sec] + s0] = y0;
-    out[(int64_t)t * p.ld[sec] + s1] = y1;
-    if (sec > 0) {
-        const int64_t row = cache_row(p, t);
-        void *cache = sec == 1 ? p.cache[0] : p.cache[1];
-        if (row >= 0) {
-            put_cache<F16>(cache, row * p.nkt + s0, y0);
-            put_cache<F16>(cache, row * p.nkt + s1, y1);
-        } else if (i == 0) {
-            atomicOr(p.err, 1u);
+        if (sec < 2) {
+            const float ang = (float)p.pos[t] * inv.v[i];
+            double sd, cd;
+            sincos((double)ang, &sd, &cd);
+            rot(y0, y1, (float)cd, (float)sd);
+        }
+        float *out = p.out[sec];
+        out[(int64_t)t * p.ld[sec] + s0] = y0;
+        out[(int64_t)t * p.ld[sec] + s1] = y1;
+        if (sec > 0) {
+            const int64_t row = cache_row(p, t);
+            void *cache = sec == 1 ? p.cache[0] : p.cache[1];
+            if (row >= 0) {
+                put_cache<F16>(cache, row * p.nkt + s0, y0);
+                put_cache<F16>(cache, row * p.nkt + s1, y1);
+            } else if (i == 0) {
+                atomicOr(p.err, 1u);
+            }
         }
     }
 }
 
-// Launch choice.  Decode (1-4 tokens): the GEMV.  Long prompts (1024+ tokens,
+// Launch choice.  Decode (1-8 tokens): the GEMV.  Long prompts (1024+ tokens,
 // 16-byte aligned sections): the cos/sin table and the fused 256 x 256 kernel.
 // Otherwise (a batch of a few hundred tokens has too few 256 x 256 tiles to
 // fill the chip, e.g. 28 at the 14B shape): the table, the 256 x 256 kernel
@@ -621,12 +633,24 @@ hipError_t launch_gemv(const ProjParams &pp, const InvTable &inv, hipStream_t st
     const int blocks = (pp.N / 2 + kGemvWaves - 1) / kGemvWaves;
     const dim3 grid(blocks), block(64 * kGemvWaves);
     switch (u) {
-    case 8: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 8>), grid, block, 0, st, pp, inv); break;
-    case 7: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 7>), grid, block, 0, st, pp, inv); break;
-    case 6: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 6>), grid, block, 0, st, pp, inv); break;
-    case 5: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 5>), grid, block, 0, st, pp, inv); break;
-    default: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 4>), grid, block, 0, st, pp, inv); break;
+    case 8: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 8, 1>), grid, block, 0, st, pp, inv); break;
+    case 7: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 7, 1>), grid, block, 0, st, pp, inv); break;
+    case 6: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 6, 1>), grid, block, 0, st, pp, inv); break;
+    case 5: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 5, 1>), grid, block, 0, st, pp, inv); break;
+    default: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 4, 1>), grid, block, 0, st, pp, inv); break;
     }
+    return hipGetLastError();
+}
+
+// 5-8 tokens: four pairs per wave, one chunk per row in flight (each x
+// chunk loaded serves eight weight rows; measured 24.5 us at 14B against
+// 27.9 with two pairs and 32 on the MFMA split path)
+template <bool F16, int HD>
+hipError_t launch_gemv8(const ProjParams &pp, const InvTable &inv, hipStream_t st)
+{
+    const int blocks = (pp.N / 8 + kGemvWaves - 1) / kGemvWaves;
+    hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, 8, 1, 4>), dim3(blocks), dim3(64 * kGemvWaves), 0,
+                       st, pp, inv);
     return hipGetLastError();
 }
 
@@ -639,7 +663,9 @@ hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st
             return launch_gemv<F16, HD, 1>(pp, inv, st, u);
         if (pp.M == 2)
             return launch_gemv<F16, HD, 2>(pp, inv, st, u);
-        return launch_gemv<F16, HD, 4>(pp, inv, st, u);
+        if (pp.M <= 4)
+            return launch_gemv<F16, HD, 4>(pp, inv, st, u);
+        return launch_gemv8<F16, HD>(pp, inv, st);
     }
     const int nblk = pp.N / big::BN + (pp.N % big::BN ? 1 : 0);
     const int mblk = (pp.M + big::BM - 1) / big::BM;

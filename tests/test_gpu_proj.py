@@ -243,34 +243,36 @@ def test_proj_padded_activation_rows(handle):
     c.check("ldx_pad")
 
 
-@pytest.mark.parametrize("nt", [1, 2, 3, 4])
+@pytest.mark.parametrize("nt", [1, 2, 3, 4, 5, 8])
 def test_proj_decode_gemv(handle, nt):
-    """1-4 tokens take the weight-streaming kernel; 14B decode geometry."""
+    """1-8 tokens take the weight-streaming kernel (one NeoX pair per wave up
+    to 4 tokens, two from 5); 14B decode geometry."""
     c = ProjCase(wl.DECODE_14B, hidden=5120, nt=nt)
     assert _run(handle, c, f"gemv_nt{nt}") == B.QKV_OK
     c.check(f"gemv_nt{nt}")
 
 
-def test_proj_gemv_hd64_slots(handle):
+@pytest.mark.parametrize("nt", [4, 7])
+def test_proj_gemv_hd64_slots(handle, nt):
     """GEMV path with hd 64 and per-token cache slots."""
-    w = wl.Workload("proj_gemv_slots", 14, 2, 64, nt=4, n_ctx=64, n_slots=4, layers=1, seed=14,
+    w = wl.Workload("proj_gemv_slots", 14, 2, 64, nt=nt, n_ctx=64, n_slots=8, layers=1, seed=14,
                     cache_dtypes=(wl.CACHE_F16,))
     c = ProjCase(w, hidden=896)
-    assert _run(handle, c, "gemv_slots") == B.QKV_OK
-    c.check("gemv_slots")
+    assert _run(handle, c, f"gemv_slots_{nt}") == B.QKV_OK
+    c.check(f"gemv_slots_{nt}")
 
 
-def test_proj_five_tokens(handle):
-    """The smallest launch on the MFMA path: one ragged 128-token tile."""
-    c = ProjCase(wl.DECODE_7B, hidden=3584, nt=5)
-    assert _run(handle, c, "nt5") == B.QKV_OK
-    c.check("nt5")
+def test_proj_nine_tokens(handle):
+    """The smallest launch on the MFMA path: one ragged 256-token tile, k split."""
+    c = ProjCase(wl.DECODE_7B, hidden=3584, nt=9)
+    assert _run(handle, c, "nt9") == B.QKV_OK
+    c.check("nt9")
 
 
 def test_proj_out_of_range_position(handle):
     """A token with a bad position: its q/k/v are still written, no cache row,
-    and the status reports the range error (MFMA and GEMV paths)."""
-    for nt in (3, 40):
+    and the status reports the range error (GEMV and MFMA paths)."""
+    for nt in (3, 6, 40):
         pos = np.arange(nt, dtype=np.int32) * 7
         pos[1] = 4096 + 5   # beyond n_ctx
         c = ProjCase(wl.DECODE_14B, hidden=512, nt=nt, pos=pos)

@@ -139,16 +139,32 @@ __global__ __launch_bounds__(256) void rope_table_kernel(const int32_t *pos, int
 //   s is free and sub-tile s+1 is visible); load sub-tile s+4 into stage s;
 //   read step-0 fragments of sub-tile s+1; products of step 1 (second half).
 namespace big {
-constexpr int BM = 256, BN = 256, BK = 32, MI = 4, NSTAGE = 4;
+constexpr int BN = 256, BK = 32, NSTAGE = 4;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRow = BK * 2;                  // 64 bytes
-constexpr int kRegion = 256 * kRow;           // 16 KB for A or B
-constexpr int kStage = 2 * kRegion;           // 32 KB
-constexpr int kLds = NSTAGE * kStage;         // 128 KB
-constexpr int kRowsPerWave = 256 / kWaves;    // rows of A (and of B) each wave loads
-constexpr int kInstPerRegion = kRowsPerWave / 16;
-constexpr int kLoadsPerWave = 2 * kInstPerRegion;   // per sub-tile
+constexpr int kRegionB = BN * kRow;           // 16 KB of weight rows per stage
+constexpr int kInstB = BN / 16 / kWaves;      // weight-row loads per wave and sub-tile (2)
+
+// the tile shape for MI token tiles of 32 per wave (two waves along tokens)
+template <int MI>
+struct Shape {
+    static constexpr int BM = 2 * MI * 32;                       // 64, 128 or 256 tokens
+    static constexpr int kRegionA = BM * kRow;
+    static constexpr int kStage = kRegionA + kRegionB;
+    static constexpr int kLds = NSTAGE * kStage;                 // 80, 96 or 128 KB
+    // token-row loads per wave and sub-tile: BM/16 instructions over 8 waves,
+    // at least one (with BM = 64 waves 4-7 repeat the loads of waves 0-3,
+    // same rows into the same slots)
+    static constexpr int kInstA = BM / 16 >= kWaves ? BM / 16 / kWaves : 1;
+    static constexpr int kLoads = kInstA + kInstB;
+};
+
+// s_waitcnt immediate that waits for vmcnt <= v only
+constexpr int vmcnt_wait(int v)
+{
+    return (v & 15) | ((v >> 4) << 14) | (0xF << 8) | (7 << 4);
+}
 
 __device__ __forceinline__ int swz(int r)
 {
@@ -158,11 +174,15 @@ __device__ __forceinline__ int swz(int r)
 
 // MODE 0: the fused output stage below (one k range per tile).  MODE 1: k is
 // split p.ksplit ways across workgroups and each stores its partial y tile to
-// p.part; proj_split_epilogue_kernel sums the partials and finishes.
-template <bool F16, int HD, int MODE>
+// p.part; proj_split_epilogue_kernel sums the partials and finishes.  MI:
+// token tiles of 32 per wave (4 for long prompts; 2 or 1 for small batches,
+// whose tokens would otherwise mostly be padding).
+template <bool F16, int HD, int MODE, int MI>
 __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams p, InvTable inv)
 {
     using namespace big;
+    using S = Shape<MI>;
+    constexpr int BM = S::BM;
     extern __shared__ __align__(16) unsigned char lds[];
     constexpr int HALF = HD / 2;
     constexpr int PT = HALF / 32;                 // tile distance of NeoX partners
@@ -180,17 +200,29 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
     const int n0 = (tile % nblk) * BN;
     const int m0 = (tile / nblk) * BM;
 
-    // loads: wave w fills rows [32w, 32w + 32) of the A and the B region;
-    // instruction j covers rows r = 32w + 16j + lane/4, lane%4 is the LDS
-    // slot and the chunk it holds is slot ^ g(r).  Offsets are bytes from
+    // loads: each instruction moves 16 rows (64 lanes x 16 bytes); token-row
+    // instruction j of wave w covers rows ra = 16 (w kInstA + j) mod BM (+ lane/4),
+    // weight-row instruction j rows rb = 16 (w kInstB + j); lane%4 is the LDS
+    // slot and the chunk it holds is slot ^ g(row).  Offsets are bytes from
     // x / w (both < 2 GiB).
     const int lrow = lane >> 2, slot = lane & 3;
-    uint32_t aoff[kInstPerRegion], boff[kInstPerRegion];
+    // (fixed-size arrays: with a size that depends on MI, captured by the
+    // lambda below, hipcc's host pass silently emitted no launch stub)
+    static_assert(S::kInstA <= 2, "token-row loads per wave");
+    uint32_t aoff[2], boff[kInstB];
+    int arow0[2], brow0[kInstB];
 #pragma unroll
-    for (int j = 0; j < kInstPerRegion; ++j) {
-        const int r = kRowsPerWave * wave + 16 * j + lrow;
+    for (int j = 0; j < S::kInstA; ++j) {
+        arow0[j] = (16 * (wave * S::kInstA + j)) % BM;
+        const int r = arow0[j] + lrow;
         const int chunk = slot ^ big::swz(r);
         aoff[j] = (uint32_t)((int64_t)min(m0 + r, p.M - 1) * p.ld_x * 2) + chunk * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < kInstB; ++j) {
+        brow0[j] = 16 * (wave * kInstB + j);
+        const int r = brow0[j] + lrow;
+        const int chunk = slot ^ big::swz(r);
         boff[j] = (uint32_t)((int64_t)min(n0 + r, p.N - 1) * p.K * 2) + chunk * 16;
     }
     const unsigned char *xb = reinterpret_cast<const unsigned char *>(p.x);
@@ -204,14 +236,14 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
     auto issue = [&](int st) {
         const int stage = st % NSTAGE;
         const uint32_t kb = (uint32_t)(kt0 + min(st, KT - 1)) * (BK * 2);
-        unsigned char *sa = lds + stage * kStage + (kRowsPerWave * wave) * kRow;
-        unsigned char *sb = sa + kRegion;
+        unsigned char *sa = lds + stage * S::kStage;
+        unsigned char *sb = sa + S::kRegionA;
 #pragma unroll
-        for (int j = 0; j < kInstPerRegion; ++j)
-            __builtin_amdgcn_global_load_lds(xb + aoff[j] + kb, (lds_t *)(sa + j * 16 * kRow), 16, 0, 0);
+        for (int j = 0; j < S::kInstA; ++j)
+            __builtin_amdgcn_global_load_lds(xb + aoff[j] + kb, (lds_t *)(sa + arow0[j] * kRow), 16, 0, 0);
 #pragma unroll
-        for (int j = 0; j < kInstPerRegion; ++j)
-            __builtin_amdgcn_global_load_lds(wb + boff[j] + kb, (lds_t *)(sb + j * 16 * kRow), 16, 0, 0);
+        for (int j = 0; j < kInstB; ++j)
+            __builtin_amdgcn_global_load_lds(wb + boff[j] + kb, (lds_t *)(sb + brow0[j] * kRow), 16, 0, 0);
     };
 
     // acc[f * MI + ti]: output tile f (0, 1) x token tile ti
@@ -225,8 +257,8 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
     // fragment reads: lane reads row lr of each 32-row tile, chunk 2*ks + hi
     const int lr = lane & 31, hi = lane >> 5;
     const int g = big::swz(lr);                 // tiles start at multiples of 32
-    const int abase = (wm * 128 + lr) * kRow;
-    const int bbase0 = kRegion + (f0 * 32 + lr) * kRow;
+    const int abase = (wm * MI * 32 + lr) * kRow;
+    const int bbase0 = S::kRegionA + (f0 * 32 + lr) * kRow;
     const int bbase1 = bbase0 + PT * 32 * kRow;
     const int k0off = ((0 + hi) ^ g) * 16;      // step 0: chunk hi
     const int k1off = ((2 + hi) ^ g) * 16;      // step 1: chunk 2 + hi
@@ -243,49 +275,48 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
     // weight fragment as the A operand), so a lane ends up holding 4
     // consecutive outputs of a token; MODE 1 keeps tokens x outputs, so one
     // store instruction covers 32 consecutive outputs of a row
-    auto mfma_half = [&](int tlo, const bf16x8 (&fa)[MI], const bf16x8 (&fb)[2]) {
+    // half h takes products q = f*MI + ti in [h*MI, (h+1)*MI)
+    auto mfma_half = [&](int h, const bf16x8 (&fa)[MI], const bf16x8 (&fb)[2]) {
 #pragma unroll
-        for (int ti = tlo; ti < tlo + MI / 2; ++ti)
-#pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                if constexpr (MODE == 0)
-                    acc[f * MI + ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        fb[f], fa[ti], acc[f * MI + ti], 0, 0, 0);
-                else
-                    acc[f * MI + ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        fa[ti], fb[f], acc[f * MI + ti], 0, 0, 0);
-            }
+        for (int q = h * MI; q < (h + 1) * MI; ++q) {
+            const int f = q / MI, ti = q % MI;
+            if constexpr (MODE == 0)
+                acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f], fa[ti], acc[q], 0, 0, 0);
+            else
+                acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ti], fb[f], acc[q], 0, 0, 0);
+        }
     };
 
     // prologue: sub-tiles 0..3 in flight, sub-tile 0 landed everywhere:
-    // vmcnt <= 3 * kLoadsPerWave (12); no lgkm/exp wait
-    static_assert(kLoadsPerWave == 4, "wait counts below assume 4 loads per sub-tile");
+    // vmcnt <= 3 * loads per sub-tile; no lgkm/exp wait
 #pragma unroll
     for (int st = 0; st < NSTAGE; ++st)
         issue(st);
-    __builtin_amdgcn_s_waitcnt((0xF << 8) | (7 << 4) | 12);
+    constexpr int kWaitFirst = vmcnt_wait(3 * S::kLoads);
+    constexpr int kWaitNext = vmcnt_wait(2 * S::kLoads);
+    __builtin_amdgcn_s_waitcnt(kWaitFirst);
     __syncthreads();
     read_frags(lds, k0off, a0, b0);
 
     for (int kt = 0; kt < KT; ++kt) {
-        const unsigned char *s = lds + (kt % NSTAGE) * kStage;
+        const unsigned char *s = lds + (kt % NSTAGE) * S::kStage;
         __builtin_amdgcn_sched_barrier(0);
         mfma_half(0, a0, b0);
         __builtin_amdgcn_sched_barrier(0);
         read_frags(s, k1off, a1, b1);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_half(MI / 2, a0, b0);
+        mfma_half(1, a0, b0);
         __builtin_amdgcn_sched_barrier(0);
         mfma_half(0, a1, b1);
         __builtin_amdgcn_sched_barrier(0);
         // this wave's loads of sub-tile kt+1 have landed once at most the two
-        // later groups (kt+2, kt+3) are outstanding: vmcnt <= 8
-        __builtin_amdgcn_s_waitcnt((0xF << 8) | (7 << 4) | 8);
+        // later groups (kt+2, kt+3) are outstanding
+        __builtin_amdgcn_s_waitcnt(kWaitNext);
         __syncthreads();
         issue(kt + NSTAGE);
-        read_frags(lds + ((kt + 1) % NSTAGE) * kStage, k0off, a0, b0);
+        read_frags(lds + ((kt + 1) % NSTAGE) * S::kStage, k0off, a0, b0);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_half(MI / 2, a1, b1);
+        mfma_half(1, a1, b1);
     }
     // the clamped reloads of the last iterations must land before the wave
     // leaves (they write this block's LDS)
@@ -302,7 +333,7 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
         for (int ti = 0; ti < MI; ++ti)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int t = m0 + wm * 128 + ti * 32 + 8 * (v / 4) + 4 * hi + (v & 3);
+                const int t = m0 + wm * MI * 32 + ti * 32 + 8 * (v / 4) + 4 * hi + (v & 3);
                 if (t >= p.M)
                     continue;
                 float *const o = out + (int64_t)t * p.N;
@@ -338,7 +369,7 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
 
 #pragma unroll
     for (int ti = 0; ti < MI; ++ti) {
-        const int t = m0 + wm * 128 + ti * 32 + lr;
+        const int t = m0 + wm * MI * 32 + ti * 32 + lr;
         if (t >= p.M)
             continue;
         const int64_t row = sec > 0 ? cache_row(p, t) : -1;
@@ -583,9 +614,9 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
 constexpr int kLargeM = 1024;
 constexpr int kTargetGroups = 256;
 
-// Raise the kernel's dynamic-LDS limit to the 128 KB it uses, once per kernel
-// and device (the caller has made the handle's device current).
-template <bool F16, int HD, int MODE>
+// Raise the kernel's dynamic-LDS limit to what it uses (up to 128 KB), once
+// per kernel and device (the caller has made the handle's device current).
+template <bool F16, int HD, int MODE, int MI>
 hipError_t set_big_lds(int device)
 {
     static std::atomic<unsigned long long> done{0};
@@ -593,17 +624,25 @@ hipError_t set_big_lds(int device)
     if (done.load(std::memory_order_acquire) & bit)
         return hipSuccess;
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&proj_mfma_big_kernel<F16, HD, MODE>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, big::kLds);
+        reinterpret_cast<const void *>(&proj_mfma_big_kernel<F16, HD, MODE, MI>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, big::Shape<MI>::kLds);
     if (e == hipSuccess && device < 64)
         done.fetch_or(bit, std::memory_order_release);
     return e;
 }
 
-// the number of k splits of the raw path for this shape
+// token tiles per wave of the split path: the smallest tile height that
+// holds the batch (64, 128, then 256 tokens)
+int split_mi(int M)
+{
+    return M <= 64 ? 1 : (M <= 128 ? 2 : 4);
+}
+
+// the number of k splits of the split path for this shape
 int choose_ksplit(int M, int N, int K)
 {
-    const int tiles = ((N + big::BN - 1) / big::BN) * ((M + big::BM - 1) / big::BM);
+    const int bm = 64 * split_mi(M);
+    const int tiles = ((N + big::BN - 1) / big::BN) * ((M + bm - 1) / bm);
     int s = (kTargetGroups + tiles / 2) / tiles;
     const int max_s = K / big::BK / 4;   // at least 4 sub-tiles per split
     if (s > max_s)
@@ -654,6 +693,19 @@ hipError_t launch_gemv8(const ProjParams &pp, const InvTable &inv, hipStream_t s
     return hipGetLastError();
 }
 
+template <bool F16, int HD, int MI>
+hipError_t launch_split_gemm(const ProjParams &pp, const InvTable &inv, hipStream_t st, int nblk)
+{
+    using S = big::Shape<MI>;
+    hipError_t e = set_big_lds<F16, HD, 1, MI>(pp.device);
+    if (e != hipSuccess)
+        return e;
+    const int mblk = (pp.M + S::BM - 1) / S::BM;
+    hipLaunchKernelGGL((proj_mfma_big_kernel<F16, HD, 1, MI>), dim3(nblk * mblk * pp.ksplit),
+                       dim3(big::kThreads), (unsigned)S::kLds, st, pp, inv);
+    return hipGetLastError();
+}
+
 template <bool F16, int HD>
 hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st)
 {
@@ -668,27 +720,28 @@ hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st
         return launch_gemv8<F16, HD>(pp, inv, st);
     }
     const int nblk = pp.N / big::BN + (pp.N % big::BN ? 1 : 0);
-    const int mblk = (pp.M + big::BM - 1) / big::BM;
+    const int64_t n_tab = (int64_t)pp.M * (HD / 2);
     if (pp.M >= kLargeM && pp.vec) {
-        hipError_t e = set_big_lds<F16, HD, 0>(pp.device);
+        using S = big::Shape<4>;
+        hipError_t e = set_big_lds<F16, HD, 0, 4>(pp.device);
         if (e != hipSuccess)
             return e;
-        const int64_t n_tab = (int64_t)pp.M * (HD / 2);
+        const int mblk = (pp.M + S::BM - 1) / S::BM;
         hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n_tab + 255) / 256)), dim3(256), 0,
                            st, pp.pos, pp.M, HD / 2, inv, const_cast<float *>(pp.rtab));
-        hipLaunchKernelGGL((proj_mfma_big_kernel<F16, HD, 0>), dim3(nblk * mblk),
-                           dim3(big::kThreads), (unsigned)big::kLds, st, pp, inv);
+        hipLaunchKernelGGL((proj_mfma_big_kernel<F16, HD, 0, 4>), dim3(nblk * mblk),
+                           dim3(big::kThreads), (unsigned)S::kLds, st, pp, inv);
         return hipGetLastError();
     }
     // split path: the table, the GEMM writing k-split partials, the summing epilogue
-    hipError_t e = set_big_lds<F16, HD, 1>(pp.device);
-    if (e != hipSuccess)
-        return e;
-    const int64_t n_tab = (int64_t)pp.M * (HD / 2);
     hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n_tab + 255) / 256)), dim3(256), 0, st,
                        pp.pos, pp.M, HD / 2, inv, const_cast<float *>(pp.rtab));
-    hipLaunchKernelGGL((proj_mfma_big_kernel<F16, HD, 1>), dim3(nblk * mblk * pp.ksplit),
-                       dim3(big::kThreads), (unsigned)big::kLds, st, pp, inv);
+    const int mi = split_mi(pp.M);
+    hipError_t e = mi == 1 ? launch_split_gemm<F16, HD, 1>(pp, inv, st, nblk)
+                 : mi == 2 ? launch_split_gemm<F16, HD, 2>(pp, inv, st, nblk)
+                           : launch_split_gemm<F16, HD, 4>(pp, inv, st, nblk);
+    if (e != hipSuccess)
+        return e;
     const int64_t n_pairs = (int64_t)pp.M * (pp.N / 2);
     hipLaunchKernelGGL((proj_split_epilogue_kernel<F16, HD>), dim3((unsigned)((n_pairs + 255) / 256)),
                        dim3(256), 0, st, pp);

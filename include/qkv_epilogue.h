@@ -200,10 +200,10 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  * qkv_epilogue_run_ex: optional biases, NeoX rotary embedding of q and k, the
  * sections written to epi.q / epi.k / epi.v (outputs only here) and the K/V
  * cache rows stored.  The GEMM runs on the matrix cores (MFMA) for more than
- * 8 tokens, as a weight-streaming GEMV for 1-8 tokens.  With 1-8 tokens and
- * with 1024+ tokens (aligned sections) the epilogue runs on the sums in
- * registers; otherwise the GEMM stores k-split partial sums and a second
- * kernel adds them and runs the epilogue (see Launches).
+ * 8 tokens, as a weight-streaming GEMV for 1-8 tokens.  The epilogue runs on
+ * the sums in registers, except when the batch has too few tiles to fill the
+ * GPU: then the GEMM stores k-split partial sums and a second kernel adds
+ * them in a fixed order and runs the epilogue (see Launches).
  *
  *   x   bf16 [nt][ld_x] activations (device, 16-byte aligned, ld_x % 8 == 0)
  *   w   bf16 [nqt + 2*nkt][hidden] concat weight rows q|k|v (device, aligned)
@@ -214,10 +214,9 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  *
  * Launches: 1-8 tokens run one weight-streaming kernel.  More tokens use a
  * workspace held by the handle: a cos/sin table of nt * head_dim * 4 bytes,
- * and, below 1024 tokens or with sections not 16-byte aligned, the partial
- * sums of a k split (splits * nt * (nqt + 2*nkt) * 4 bytes, about 66 MB for
- * 256 tokens of the 14B shape); those launches are two or three kernels on
- * the stream.  A call that needs more workspace than any before it
+ * the tokens' cache rows (nt * 8 bytes) and, when k is split, the partial
+ * sums (splits * nt * (nqt + 2*nkt) * 4 bytes, about 29 MB for 256 tokens of
+ * the 14B shape); those launches are two or three kernels on the stream.  A call that needs more workspace than any before it
  * synchronizes the device and (re)allocates it: make that call outside graph
  * capture.  All other calls allocate nothing and never synchronize.  Calls on
  * one handle share its workspace: calls that may run concurrently (different

@@ -13,24 +13,26 @@
 // both operands are 16 contiguous bytes of a k-contiguous row) and receives
 // D[8*(v/4) + 4*(l/32) + v%4][l%32], v < 16.
 //
-//  * Tiles of 256 tokens x 256 outputs, four waves of 128 x 128; operands go
-//    from HBM straight into a ring of four LDS stages (k sub-tiles of 32,
-//    loaded three ahead), XOR-swizzled so fragment reads are conflict-free.
-//  * A wave's 128 output columns are one head (hd 128) or two (hd 64), so the
-//    NeoX partner of column j (j + hd/2) sits in the same lane, in the MFMA
-//    tile hd/64 tiles further on: the rotation needs no data exchange.
-//  * 1024+ tokens: the epilogue runs on the accumulators (tiles computed
-//    transposed so a lane holds 4 consecutive outputs), with a cos/sin table
-//    computed once per launch.  Fewer tokens: the tiles are too few to fill
-//    the chip, so k is split across workgroups that store partial tiles to
-//    the handle's workspace, and a second kernel sums them in split order and
-//    runs the epilogue.
+//  * Eight-wave tiles of 256 x 256, 256 x 128, 128 x 128 or 64 x 256 tokens x
+//    outputs, picked per launch; operands go from HBM straight into a ring of
+//    four LDS stages (k sub-tiles of 32, loaded three ahead), XOR-swizzled so
+//    fragment reads are conflict-free.
+//  * A wave's 64 output columns are the j and j + hd/2 halves of a head's
+//    NeoX pairs, so the partner of every output sits in the same lane, in the
+//    other MFMA tile: the rotation needs no data exchange.
+//  * When the tiles fill the chip the epilogue runs on the accumulators
+//    (tiles computed transposed so a lane holds 4 consecutive outputs), with
+//    cos/sin and cache rows tabled once per launch.  With too few tiles k is
+//    split across workgroups that store partial tiles to the handle's
+//    workspace, and a second kernel sums them in split order and runs the
+//    epilogue.
 //  * Decode (up to 8 tokens) is a weight-streaming GEMV, not a contraction
 //    worth the matrix units: a separate kernel streams W with 16-byte loads,
 //    reduces each dot product across the wave and runs the same epilogue.
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstring>
@@ -62,9 +64,10 @@ struct ProjParams {
     void *cache[2];
     int64_t n_ctx, n_slots;
     unsigned int *err;
-    const float *rtab;       // [M][cos half | sin half] (fused long-prompt path)
-    int ksplit;              // k splits of the split path
-    float *part;             // [ksplit][M][N] partial sums of the split path
+    const float *rtab;       // [M][cos half | sin half] of the launch (MFMA path)
+    const int64_t *rows;     // [M] cache row of each token, or -1 (MFMA path)
+    int ksplit;              // k splits of the MFMA path
+    float *part;             // [ksplit][M][N] partial sums when ksplit > 1
     int device;              // the handle's device (launch set-up only)
     bool vec;                // sections, biases, caches 16-byte aligned, strides % 4 == 0
 };
@@ -97,67 +100,104 @@ __device__ __forceinline__ void put_cache(void *cache, int64_t off, float v)
 }
 
 // ---------------------------------------------------------------------------
-// cos/sin table of a launch: row t holds cos then sin of pos[t] * inv[i],
-// i < half (f32 angle; sin/cos in double rounded to f32).  Every column
-// block reads it instead of recomputing it.
+// Per-launch tables of the MFMA path: row t of tab holds cos then sin of
+// pos[t] * inv[i], i < half (f32 angle; sin/cos in double rounded to f32), and
+// rows[t] is token t's cache row (slot * n_ctx + pos, or -1 when out of
+// range).  Every column block reads them instead of recomputing them.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void rope_table_kernel(const int32_t *pos, int M, int half,
-                                                         InvTable inv, float *tab)
+__global__ __launch_bounds__(256) void rope_table_kernel(ProjParams p, InvTable inv, float *tab,
+                                                         int64_t *rows)
 {
+    const int half = p.half;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (int64_t)M * half)
+    if (idx >= (int64_t)p.M * half)
         return;
     const int t = (int)(idx / half), i = (int)(idx - (int64_t)t * half);
-    const float ang = (float)pos[t] * inv.v[i];
+    const float ang = (float)p.pos[t] * inv.v[i];
     double sd, cd;
     sincos((double)ang, &sd, &cd);
     tab[(int64_t)t * 2 * half + i] = (float)cd;
     tab[(int64_t)t * 2 * half + half + i] = (float)sd;
+    if (i == 0)
+        rows[t] = cache_row(p, t);
 }
 
 // ---------------------------------------------------------------------------
-// 256 x 256 tiles, operands loaded straight into LDS
+// The MFMA path (9+ tokens): eight-wave tiles, operands loaded straight into
+// LDS, the epilogue on the accumulators
 // ---------------------------------------------------------------------------
-// Eight waves, two per SIMD: wave (wm, wn) owns 128 tokens (wm) x 64 outputs,
-// the two 32-column MFMA tiles f0 and f0 + hd/64 of one head, so the NeoX
-// partner of every output sits in the same lane and register of the other
-// tile.  128 accumulators per lane leave room for two waves per SIMD, which
-// is what keeps the LDS busy: on gfx950 conflict-free 16-byte LDS reads
-// reach ~135 B/clk per CU with one wave per SIMD and ~225 with two.
+// A workgroup computes a BM x BN tile of y with eight waves.  Wave (wm, wn)
+// owns MI*32 tokens x 64 outputs: the two 32-column MFMA tiles of one NeoX
+// pair group, i.e. columns j and j + hd/2 of a head (for hd 128 the tiles lo
+// and lo + 2, for hd 64 lo and lo + 1), so the rotation partner of every
+// output sits in the same lane and register of the other tile.  WN waves
+// along the outputs (BN = 64 WN), 8/WN along the tokens (BM = 8/WN * MI * 32),
+// so one kernel serves long prompts (256 x 256) and batches whose tokens
+// would mostly be padding in a tall tile (64 x 256, 256 x 64, ...).  Each
+// 32 x 32 tile is computed transposed (the weight fragment as the A operand),
+// so a lane holds 4 consecutive outputs of one token: 16-byte stores.
 //
-// k advances in sub-tiles of 32 through a ring of four LDS stages (32 KB
-// each: 256 token rows of A and 256 weight rows of B, 64 bytes per row),
-// filled by global->LDS loads (64 lanes x 16 bytes per instruction) issued
-// three sub-tiles ahead.  Chunk c of row r sits in slot c ^ g(r),
+// k advances in sub-tiles of 32 through a ring of four LDS stages (BM token
+// rows of A and BN weight rows of B, 64 bytes per row), filled by
+// global->LDS loads (64 lanes x 16 bytes = 16 rows per instruction) issued
+// three sub-tiles ahead (deeper rings, up to 8 stages for the small tiles,
+// measured no faster on MI355X).  Chunk c of row r sits in slot c ^ g(r),
 // g(r) = ((r >> 1) ^ (r >> 3)) & 3: the 16-byte fragment reads of 16
-// consecutive rows hit distinct banks.
-//
-// Per sub-tile s (two k steps of 16, 8 products each):
+// consecutive rows hit distinct banks.  Per sub-tile s (two k steps of 16):
 //   products of step 0 (first half); read step-1 fragments; products of
 //   step 0 (second half); products of step 1 (first half); wait for this
 //   wave's loads of sub-tile s+1 and meet the other waves (after which stage
-//   s is free and sub-tile s+1 is visible); load sub-tile s+4 into stage s;
+//   s is free and sub-tile s+1 is visible); load sub-tile s+NSTAGE into
+//   stage s;
 //   read step-0 fragments of sub-tile s+1; products of step 1 (second half).
-namespace big {
-constexpr int BN = 256, BK = 32, NSTAGE = 4;
+//
+// The grid is tiles x S: with S = 1 each workgroup finishes its tile (the
+// epilogue below); when the tiles are too few to fill the chip, k is split S
+// ways, each split stores its partial tile ([S][M][N] in the workspace) and
+// proj_split_epilogue_kernel sums the partials in split order (the same
+// additions every run) and finishes.  Consecutive blocks take consecutive
+// tiles of the same k range, so the tiles in flight together share their
+// operands' k slabs in L2.
+//
+// Epilogue: the loads it needs (cos/sin of the tile's tokens, their cache
+// rows, the biases) are all issued before the first use -- the cos/sin slice
+// straight into the LDS ring, which is free by then -- so a tile's epilogue
+// waits for memory once instead of once per token group.
+namespace mm {
+constexpr int BK = 32;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRow = BK * 2;                  // 64 bytes
-constexpr int kRegionB = BN * kRow;           // 16 KB of weight rows per stage
-constexpr int kInstB = BN / 16 / kWaves;      // weight-row loads per wave and sub-tile (2)
+constexpr int kRow = BK * 2;                  // 64 bytes per row and sub-tile
+constexpr int NSTAGE = 4;                     // LDS ring depth
 
-// the tile shape for MI token tiles of 32 per wave (two waves along tokens)
-template <int MI>
+template <int HD, int MI, int WN>
 struct Shape {
-    static constexpr int BM = 2 * MI * 32;                       // 64, 128 or 256 tokens
+    static constexpr int WM = kWaves / WN;
+    static constexpr int BM = WM * MI * 32;
+    static constexpr int BN = WN * 64;
     static constexpr int kRegionA = BM * kRow;
-    static constexpr int kStage = kRegionA + kRegionB;
-    static constexpr int kLds = NSTAGE * kStage;                 // 80, 96 or 128 KB
-    // token-row loads per wave and sub-tile: BM/16 instructions over 8 waves,
-    // at least one (with BM = 64 waves 4-7 repeat the loads of waves 0-3,
-    // same rows into the same slots)
-    static constexpr int kInstA = BM / 16 >= kWaves ? BM / 16 / kWaves : 1;
-    static constexpr int kLoads = kInstA + kInstB;
+    static constexpr int kStage = kRegionA + BN * kRow;
+    static constexpr int kRing = NSTAGE * kStage;
+    // 16-row load instructions per sub-tile: an equal share per wave when
+    // there are 8 or more, else (4 of them) token rows on waves 0-3 and
+    // weight rows on waves 4-7
+    static constexpr int kInstA = BM / 16, kInstB = BN / 16;
+    static constexpr int kWaveA = kInstA >= kWaves ? kInstA / kWaves : 1;
+    static constexpr int kWaveB = kInstB >= kWaves ? kInstB / kWaves : 1;
+    // loads per sub-tile of waves 0-3 and of waves 4-7
+    static constexpr int kLoadsLo = kWaveA + (kInstB >= kWaves ? kWaveB : 0);
+    static constexpr int kLoadsHi = (kInstA >= kWaves ? kWaveA : 0) + kWaveB;
+    // epilogue: the tile's pair indices (one group of an hd-128 head: 32;
+    // else all hd/2) as cos then sin per token, in 16-byte chunks
+    static constexpr int kPW = (HD == 128 && WN == 1) ? 32 : HD / 2;
+    static constexpr int kChunks = kPW / 2;
+    static constexpr int kTab = BM * kChunks * 16;
+    static constexpr int kLds = kRing > kTab ? kRing : kTab;
+    static_assert(kInstA % kWaves == 0 || kInstA == 4, "token-row loads");
+    static_assert(kInstB % kWaves == 0 || kInstB == 4, "weight-row loads");
+    static_assert(kInstA >= kWaves || kInstB >= kWaves, "load split");
+    static_assert(kWaveA <= 4 && kWaveB <= 4, "load slots");
+    static_assert((BM * kChunks) % 64 == 0, "table staging");
 };
 
 // s_waitcnt immediate that waits for vmcnt <= v only
@@ -170,83 +210,88 @@ __device__ __forceinline__ int swz(int r)
 {
     return ((r >> 1) ^ (r >> 3)) & 3;
 }
-}  // namespace big
 
-// MODE 0: the fused output stage below (one k range per tile).  MODE 1: k is
-// split p.ksplit ways across workgroups and each stores its partial y tile to
-// p.part; proj_split_epilogue_kernel sums the partials and finishes.  MI:
-// token tiles of 32 per wave (4 for long prompts; 2 or 1 for small batches,
-// whose tokens would otherwise mostly be padding).
-template <bool F16, int HD, int MODE, int MI>
-__global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams p, InvTable inv)
+// first 32-column MFMA tile of NeoX pair group g (its partner is lo + PT)
+template <int PT>
+__device__ __forceinline__ int group_lo(int g)
 {
-    using namespace big;
-    using S = Shape<MI>;
-    constexpr int BM = S::BM;
-    extern __shared__ __align__(16) unsigned char lds[];
+    return (g / PT) * (2 * PT) + g % PT;
+}
+}  // namespace mm
+
+template <bool F16, int HD, int MI, int WN>
+__global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
+{
+    using namespace mm;
+    using S = Shape<HD, MI, WN>;
+    constexpr int BM = S::BM, BN = S::BN;
     constexpr int HALF = HD / 2;
     constexpr int PT = HALF / 32;                 // tile distance of NeoX partners
+    extern __shared__ __align__(16) unsigned char lds[];
+    typedef __attribute__((address_space(3))) void lds_t;
 
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 2, wn = wave & 3;
-    // the wave's two output tiles (of the block's 8): f0 and f0 + PT
-    const int f0 = (wn / PT) * (2 * PT) + wn % PT;
-    const int nblk = p.N / BN + (p.N % BN ? 1 : 0);
-    const int mblk = (p.M + BM - 1) / BM;
-    const int tile = (int)blockIdx.x % (nblk * mblk);
-    const int split = (int)blockIdx.x / (nblk * mblk);
-    const int n0 = (tile % nblk) * BN;
-    const int m0 = (tile / nblk) * BM;
-
-    // loads: each instruction moves 16 rows (64 lanes x 16 bytes); token-row
-    // instruction j of wave w covers rows ra = 16 (w kInstA + j) mod BM (+ lane/4),
-    // weight-row instruction j rows rb = 16 (w kInstB + j); lane%4 is the LDS
-    // slot and the chunk it holds is slot ^ g(row).  Offsets are bytes from
-    // x / w (both < 2 GiB).
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
     const int lrow = lane >> 2, slot = lane & 3;
-    // (fixed-size arrays: with a size that depends on MI, captured by the
-    // lambda below, hipcc's host pass silently emitted no launch stub)
-    static_assert(S::kInstA <= 2, "token-row loads per wave");
-    uint32_t aoff[2], boff[kInstB];
-    int arow0[2], brow0[kInstB];
+    const int lr = lane & 31, hi = lane >> 5;
+
+    const int ntn = (p.N + BN - 1) / BN;
+    const int ntm = (p.M + BM - 1) / BM;
+    const int tiles = ntn * ntm;
+    const int tile = (int)blockIdx.x % tiles;
+    const int split = (int)blockIdx.x / tiles;
+    const int m0 = (tile / ntn) * BM;
+    const int tn = tile % ntn;
+    const int KTall = p.K / BK;
+    const int kbeg = (int)((int64_t)split * KTall / p.ksplit);
+    const int len = (int)((int64_t)(split + 1) * KTall / p.ksplit) - kbeg;
+
+    // this wave's load instructions: token rows arow[j] and weight rows
+    // brow[j] of the tile, 16 rows each, lane/4 the row within; byte offsets
+    // from x / w (each < 2 GiB); rows past the end repeat the last one.
+    // (fixed-size arrays: with a size that depends on the template
+    // arguments, captured by the lambda below, hipcc's host pass silently
+    // emitted no launch stub)
+    const bool do_a = S::kInstA >= kWaves || wave < S::kInstA;
+    const bool do_b = S::kInstB >= kWaves || wave >= kWaves - S::kInstB;
+    int arow[4] = {0, 0, 0, 0}, brow[4] = {0, 0, 0, 0};
+    uint32_t aoff[4], boff[4];
 #pragma unroll
-    for (int j = 0; j < S::kInstA; ++j) {
-        arow0[j] = (16 * (wave * S::kInstA + j)) % BM;
-        const int r = arow0[j] + lrow;
-        const int chunk = slot ^ big::swz(r);
-        aoff[j] = (uint32_t)((int64_t)min(m0 + r, p.M - 1) * p.ld_x * 2) + chunk * 16;
+    for (int j = 0; j < S::kWaveA; ++j) {
+        arow[j] = 16 * ((S::kInstA >= kWaves ? wave * S::kWaveA : wave) + j);
+        const int r = arow[j] + lrow;
+        aoff[j] = (uint32_t)((int64_t)min(m0 + r, p.M - 1) * p.ld_x * 2) + (slot ^ swz(r)) * 16;
     }
 #pragma unroll
-    for (int j = 0; j < kInstB; ++j) {
-        brow0[j] = 16 * (wave * kInstB + j);
-        const int r = brow0[j] + lrow;
-        const int chunk = slot ^ big::swz(r);
-        boff[j] = (uint32_t)((int64_t)min(n0 + r, p.N - 1) * p.K * 2) + chunk * 16;
+    for (int j = 0; j < S::kWaveB; ++j) {
+        brow[j] = 16 * ((S::kInstB >= kWaves ? wave * S::kWaveB : wave - (kWaves - S::kInstB)) + j);
+        const int rb = brow[j] + lrow;
+        const int n = group_lo<PT>(tn * WN + rb / 64) * 32 + ((rb >> 5) & 1) * PT * 32 + (rb & 31);
+        boff[j] = (uint32_t)((int64_t)min(n, p.N - 1) * p.K * 2) + (slot ^ swz(rb)) * 16;
     }
     const unsigned char *xb = reinterpret_cast<const unsigned char *>(p.x);
     const unsigned char *wb = reinterpret_cast<const unsigned char *>(p.w);
-    typedef __attribute__((address_space(3))) void lds_t;
-    // this workgroup's sub-tiles [kt0, kt0 + KT) of the k range
-    const int KT_all = p.K / BK;
-    const int kt0 = (int)((int64_t)split * KT_all / p.ksplit);
-    const int KT = (int)((int64_t)(split + 1) * KT_all / p.ksplit) - kt0;
     // local sub-tile st (clamped to the last one: the loop stays uniform)
     auto issue = [&](int st) {
         const int stage = st % NSTAGE;
-        const uint32_t kb = (uint32_t)(kt0 + min(st, KT - 1)) * (BK * 2);
+        const uint32_t kb = (uint32_t)(kbeg + min(st, len - 1)) * (BK * 2);
         unsigned char *sa = lds + stage * S::kStage;
         unsigned char *sb = sa + S::kRegionA;
+        if (do_a) {
 #pragma unroll
-        for (int j = 0; j < S::kInstA; ++j)
-            __builtin_amdgcn_global_load_lds(xb + aoff[j] + kb, (lds_t *)(sa + arow0[j] * kRow), 16, 0, 0);
+            for (int j = 0; j < S::kWaveA; ++j)
+                __builtin_amdgcn_global_load_lds(xb + aoff[j] + kb, (lds_t *)(sa + arow[j] * kRow), 16, 0, 0);
+        }
+        if (do_b) {
 #pragma unroll
-        for (int j = 0; j < kInstB; ++j)
-            __builtin_amdgcn_global_load_lds(wb + boff[j] + kb, (lds_t *)(sb + brow0[j] * kRow), 16, 0, 0);
+            for (int j = 0; j < S::kWaveB; ++j)
+                __builtin_amdgcn_global_load_lds(wb + boff[j] + kb, (lds_t *)(sb + brow[j] * kRow), 16, 0, 0);
+        }
     };
 
-    // acc[f * MI + ti]: output tile f (0, 1) x token tile ti
+    // acc[f * MI + ti]: output tile f (0: lo, 1: partner) x token tile ti
     f32x16 acc[2 * MI];
 #pragma unroll
     for (int q = 0; q < 2 * MI; ++q)
@@ -255,14 +300,12 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
             acc[q][v] = 0.0f;
 
     // fragment reads: lane reads row lr of each 32-row tile, chunk 2*ks + hi
-    const int lr = lane & 31, hi = lane >> 5;
-    const int g = big::swz(lr);                 // tiles start at multiples of 32
+    const int g = swz(lr);                        // tiles start at multiples of 32
     const int abase = (wm * MI * 32 + lr) * kRow;
-    const int bbase0 = S::kRegionA + (f0 * 32 + lr) * kRow;
-    const int bbase1 = bbase0 + PT * 32 * kRow;
-    const int k0off = ((0 + hi) ^ g) * 16;      // step 0: chunk hi
-    const int k1off = ((2 + hi) ^ g) * 16;      // step 1: chunk 2 + hi
-
+    const int bbase0 = S::kRegionA + (wn * 64 + lr) * kRow;
+    const int bbase1 = bbase0 + 32 * kRow;
+    const int k0off = ((0 + hi) ^ g) * 16;        // step 0: chunk hi
+    const int k1off = ((2 + hi) ^ g) * 16;        // step 1: chunk 2 + hi
     bf16x8 a0[MI], b0[2], a1[MI], b1[2];
     auto read_frags = [&](const unsigned char *s, int koff, bf16x8 (&fa)[MI], bf16x8 (&fb)[2]) {
 #pragma unroll
@@ -271,34 +314,25 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
         fb[0] = *reinterpret_cast<const bf16x8 *>(s + bbase0 + koff);
         fb[1] = *reinterpret_cast<const bf16x8 *>(s + bbase1 + koff);
     };
-    // MODE 0 computes each tile transposed (32 outputs x 32 tokens, the
-    // weight fragment as the A operand), so a lane ends up holding 4
-    // consecutive outputs of a token; MODE 1 keeps tokens x outputs, so one
-    // store instruction covers 32 consecutive outputs of a row
     // half h takes products q = f*MI + ti in [h*MI, (h+1)*MI)
     auto mfma_half = [&](int h, const bf16x8 (&fa)[MI], const bf16x8 (&fb)[2]) {
 #pragma unroll
-        for (int q = h * MI; q < (h + 1) * MI; ++q) {
-            const int f = q / MI, ti = q % MI;
-            if constexpr (MODE == 0)
-                acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f], fa[ti], acc[q], 0, 0, 0);
-            else
-                acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ti], fb[f], acc[q], 0, 0, 0);
-        }
+        for (int q = h * MI; q < (h + 1) * MI; ++q)
+            acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[q / MI], fa[q % MI], acc[q], 0, 0, 0);
     };
 
-    // prologue: sub-tiles 0..3 in flight, sub-tile 0 landed everywhere:
-    // vmcnt <= 3 * loads per sub-tile; no lgkm/exp wait
+    // prologue: sub-tiles 0..NSTAGE-1 in flight, sub-tile 0 landed everywhere
 #pragma unroll
     for (int st = 0; st < NSTAGE; ++st)
         issue(st);
-    constexpr int kWaitFirst = vmcnt_wait(3 * S::kLoads);
-    constexpr int kWaitNext = vmcnt_wait(2 * S::kLoads);
-    __builtin_amdgcn_s_waitcnt(kWaitFirst);
+    if (S::kLoadsLo == S::kLoadsHi || wave < 4)
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait((NSTAGE - 1) * S::kLoadsLo));
+    else
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait((NSTAGE - 1) * S::kLoadsHi));
     __syncthreads();
     read_frags(lds, k0off, a0, b0);
 
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = 0; kt < len; ++kt) {
         const unsigned char *s = lds + (kt % NSTAGE) * S::kStage;
         __builtin_amdgcn_sched_barrier(0);
         mfma_half(0, a0, b0);
@@ -309,100 +343,144 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
         __builtin_amdgcn_sched_barrier(0);
         mfma_half(0, a1, b1);
         __builtin_amdgcn_sched_barrier(0);
-        // this wave's loads of sub-tile kt+1 have landed once at most the two
-        // later groups (kt+2, kt+3) are outstanding
-        __builtin_amdgcn_s_waitcnt(kWaitNext);
+        // this wave's loads of sub-tile kt+1 have landed once at most the
+        // later groups (kt+2 .. kt+NSTAGE-1) are outstanding
+        if (S::kLoadsLo == S::kLoadsHi || wave < 4)
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait((NSTAGE - 2) * S::kLoadsLo));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait((NSTAGE - 2) * S::kLoadsHi));
         __syncthreads();
         issue(kt + NSTAGE);
         read_frags(lds + ((kt + 1) % NSTAGE) * S::kStage, k0off, a0, b0);
         __builtin_amdgcn_sched_barrier(0);
         mfma_half(1, a1, b1);
     }
-    // the clamped reloads of the last iterations must land before the wave
-    // leaves (they write this block's LDS)
+    // the clamped reloads of the last iterations land before the ring is
+    // reused or the workgroup leaves
     __builtin_amdgcn_s_waitcnt(0);
 
-    const int col0 = n0 + f0 * 32;                 // first output column of tile f = 0
-    if (col0 >= p.N)
-        return;
-    if constexpr (MODE == 1) {
-        // partial y of this split: lane (lr, hi) holds output f*PT*32 + lr
-        // (from col0) of tokens ti*32 + 8(v/4) + 4hi + v%4
-        float *const out = p.part + (int64_t)split * p.M * p.N + col0 + lr;
+    // Lane (lr, hi) holds, for token ti*32 + lr of the wave's tokens, the
+    // outputs col0 + f*HALF + 8gg + 4hi + e (e < 4) in acc[f*MI + ti][4gg + e]:
+    // four consecutive columns; f = 1 is the NeoX partner of f = 0.
+    const int col0 = group_lo<PT>(tn * WN + wn) * 32;
+    const int tok0 = m0 + wm * MI * 32 + lr;     // token of ti = 0
+    if (p.ksplit > 1) {
+        if (col0 >= p.N)
+            return;
+        float *const out = p.part + (int64_t)split * p.M * p.N + col0 + 4 * hi;
 #pragma unroll
-        for (int ti = 0; ti < MI; ++ti)
+        for (int ti = 0; ti < MI; ++ti) {
+            const int tok = tok0 + ti * 32;
+            if (tok >= p.M)
+                continue;
+            float *const orow = out + (int64_t)tok * p.N;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int t = m0 + wm * MI * 32 + ti * 32 + 8 * (v / 4) + 4 * hi + (v & 3);
-                if (t >= p.M)
-                    continue;
-                float *const o = out + (int64_t)t * p.N;
-                o[0] = acc[ti][v];
-                o[PT * 32] = acc[MI + ti][v];
-            }
+            for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    const FVec<4> y = {{acc[f * MI + ti][4 * gg], acc[f * MI + ti][4 * gg + 1],
+                                        acc[f * MI + ti][4 * gg + 2], acc[f * MI + ti][4 * gg + 3]}};
+                    st_data<4, false>(orow + f * HALF + 8 * gg, y);
+                }
+        }
         return;
     }
 
     // ---- epilogue ---------------------------------------------------------
-    // Lane (lr, hi) holds, for token ti*32 + lr of the wave's 128, the
-    // outputs col0 + f*HALF + 8g + 4hi + e (e < 4) in acc[f*MI + ti][4g + e]:
-    // four consecutive columns, stored with one 16-byte (f32) or 8-byte
-    // (f16) store; f = 1 is the NeoX partner of f = 0.  cos/sin come from the
-    // launch's table (16-byte reads).
+    // Stage the cos/sin slice of the tile's BM tokens (pair indices ih0 ..
+    // ih0 + kPW) into the LDS ring: chunk c of token r in slot c ^ (r % kChunks),
+    // which keeps the reads below (32 tokens, one chunk) conflict-free.
+    const int ih0 = S::kPW == HALF ? 0 : (group_lo<PT>(tn * WN) * 32) % HD;
+    __syncthreads();                              // every wave is done with the ring
+    {
+        constexpr int kInst = BM * S::kChunks / 64;
+        for (int u = wave; u < kInst; u += kWaves) {
+            const int ca = u * 64 + lane;
+            const int r = ca / S::kChunks, sl = ca % S::kChunks;
+            const int c = sl ^ (r % S::kChunks);
+            const int tokc = min(m0 + r, p.M - 1);
+            const int col = c < S::kChunks / 2 ? ih0 + 4 * c : HALF + ih0 + 4 * (c - S::kChunks / 2);
+            __builtin_amdgcn_global_load_lds(p.rtab + (int64_t)tokc * HD + col, (lds_t *)(lds + u * 1024), 16, 0,
+                                             0);
+        }
+    }
+    const bool live = col0 < p.N;
     const int sec = col0 < p.nqt ? 0 : (col0 < p.nqt + p.nkt ? 1 : 2);
     const int sbase = sec == 0 ? 0 : (sec == 1 ? p.nqt : p.nqt + p.nkt);
     float *const out = p.out[sec];
     const int64_t ldo = p.ld[sec];
-    const float *const bias = p.b[sec];
+    const float *const bias = live ? p.b[sec] : nullptr;
     void *const cache = sec == 1 ? p.cache[0] : p.cache[1];
-    const int cs = col0 - sbase + 4 * hi;          // section column of (f = 0, g = 0)
-    const int ih = (f0 * 32) % HD;                 // pair index of the tile's first column
-
-    // this lane's 32 bias values, loaded once
-    const FVec<4> zero = {{0.f, 0.f, 0.f, 0.f}};
+    const int cs = col0 - sbase + 4 * hi;          // section column of (f = 0, gg = 0)
+    // this lane's 32 bias values and its tokens' cache rows
     FVec<4> bias0[4], bias1[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        bias0[g] = bias ? ld_vec<4>(bias + cs + 8 * g) : zero;
-        bias1[g] = bias ? ld_vec<4>(bias + cs + 8 * g + HALF) : zero;
-    }
-
+    for (int gg = 0; gg < 4; ++gg) {
+        if (bias && p.vec) {
+            bias0[gg] = ld_vec<4>(bias + cs + 8 * gg);
+            bias1[gg] = ld_vec<4>(bias + cs + 8 * gg + HALF);
+        } else {
 #pragma unroll
-    for (int ti = 0; ti < MI; ++ti) {
-        const int t = m0 + wm * MI * 32 + ti * 32 + lr;
-        if (t >= p.M)
-            continue;
-        const int64_t row = sec > 0 ? cache_row(p, t) : -1;
-        float *const orow = out + (int64_t)t * ldo;
-        // all of this token's cos/sin values first: one wait per token
-        const float *const trow = p.rtab + (int64_t)t * 2 * HALF + ih + 4 * hi;
-        FVec<4> cv[4], sv[4];
-        if (sec < 2) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                cv[g] = ld_vec<4>(trow + 8 * g);
-                sv[g] = ld_vec<4>(trow + HALF + 8 * g);
+            for (int e = 0; e < 4; ++e) {
+                bias0[gg].e[e] = bias ? bias[cs + 8 * gg + e] : 0.0f;
+                bias1[gg].e[e] = bias ? bias[cs + 8 * gg + e + HALF] : 0.0f;
             }
         }
+    }
+    int64_t crow[MI];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int c0 = cs + 8 * g, c1 = c0 + HALF;
+    for (int ti = 0; ti < MI; ++ti)
+        crow[ti] = (live && sec > 0) ? p.rows[min(tok0 + ti * 32, p.M - 1)] : -1;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (!live)
+        return;
+
+    const int cpair = (col0 % HD - ih0) / 4 + hi;  // chunk of (gg = 0) in the slice
+#pragma unroll
+    for (int ti = 0; ti < MI; ++ti) {
+        const int tok = tok0 + ti * 32;
+        if (tok >= p.M)
+            continue;
+        const int r = tok - m0;
+        const int64_t row = crow[ti];
+        float *const orow = out + (int64_t)tok * ldo;
+        const unsigned char *trow = lds + r * S::kChunks * 16;
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            const int c0 = cs + 8 * gg, c1 = c0 + HALF;
             FVec<4> y0, y1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                y0.e[e] = acc[ti][4 * g + e] + bias0[g].e[e];
-                y1.e[e] = acc[MI + ti][4 * g + e] + bias1[g].e[e];
+                y0.e[e] = acc[ti][4 * gg + e] + bias0[gg].e[e];
+                y1.e[e] = acc[MI + ti][4 * gg + e] + bias1[gg].e[e];
             }
             if (sec < 2) {
+                const int cc = cpair + 2 * gg;
+                const FVec<4> cv = *reinterpret_cast<const FVec<4> *>(trow + ((cc ^ (r % S::kChunks)) * 16));
+                const FVec<4> sv = *reinterpret_cast<const FVec<4> *>(
+                    trow + (((cc + S::kChunks / 2) ^ (r % S::kChunks)) * 16));
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    rot(y0.e[e], y1.e[e], cv[g].e[e], sv[g].e[e]);
+                    rot(y0.e[e], y1.e[e], cv.e[e], sv.e[e]);
             }
-            st_data<4, false>(orow + c0, y0);
-            st_data<4, false>(orow + c1, y1);
-            if (row >= 0) {
-                st_cache<4, F16, false>(cache, row * p.nkt + c0, y0);
-                st_cache<4, F16, false>(cache, row * p.nkt + c1, y1);
+            if (p.vec) {
+                st_data<4, false>(orow + c0, y0);
+                st_data<4, false>(orow + c1, y1);
+                if (row >= 0) {
+                    st_cache<4, F16, false>(cache, row * p.nkt + c0, y0);
+                    st_cache<4, F16, false>(cache, row * p.nkt + c1, y1);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    orow[c0 + e] = y0.e[e];
+                    orow[c1 + e] = y1.e[e];
+                    if (row >= 0) {
+                        put_cache<F16>(cache, row * p.nkt + c0 + e, y0.e[e]);
+                        put_cache<F16>(cache, row * p.nkt + c1 + e, y1.e[e]);
+                    }
+                }
             }
         }
         if (sec > 0 && row < 0 && hi == 0)
@@ -414,7 +492,8 @@ __global__ __launch_bounds__(big::kThreads) void proj_mfma_big_kernel(ProjParams
 // split path, second step: y = sum of the k-split partials (in split order,
 // so the result does not depend on timing), then the epilogue.  One thread
 // per column pair (j, j + hd/2) of a head (the v section pairs its columns
-// the same way, without the rotation); cos/sin from the launch's table.
+// the same way, without the rotation); cos/sin and cache rows from the
+// launch's tables.
 // ---------------------------------------------------------------------------
 template <bool F16, int HD>
 __global__ __launch_bounds__(256) void proj_split_epilogue_kernel(ProjParams p)
@@ -451,7 +530,7 @@ __global__ __launch_bounds__(256) void proj_split_epilogue_kernel(ProjParams p)
     out[s0] = y0;
     out[s1] = y1;
     if (sec > 0) {
-        const int64_t row = cache_row(p, t);
+        const int64_t row = p.rows[t];
         void *cache = sec == 1 ? p.cache[0] : p.cache[1];
         if (row >= 0) {
             put_cache<F16>(cache, row * p.nkt + s0, y0);
@@ -605,49 +684,63 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
     }
 }
 
-// Launch choice.  Decode (1-8 tokens): the GEMV.  Long prompts (1024+ tokens,
-// 16-byte aligned sections): the cos/sin table and the fused 256 x 256 kernel.
-// Otherwise (a batch of a few hundred tokens has too few 256 x 256 tiles to
-// fill the chip, e.g. 28 at the 14B shape): the table, the 256 x 256 kernel
-// with k split so the launch has about one workgroup per CU, each split
-// storing its partial tile, and a summing epilogue kernel.
-constexpr int kLargeM = 1024;
-constexpr int kTargetGroups = 256;
+// Launch choice.  Decode (1-8 tokens): the GEMV.  9+ tokens: the per-launch
+// tables, then the MFMA kernel on the tile shape and k split chosen below,
+// and the summing epilogue when k is split.
+struct MmPlan {
+    int mi, wn, ksplit;
+};
 
-// Raise the kernel's dynamic-LDS limit to what it uses (up to 128 KB), once
-// per kernel and device (the caller has made the handle's device current).
-template <bool F16, int HD, int MODE, int MI>
-hipError_t set_big_lds(int device)
+int mm_bm(int mi, int wn)
+{
+    return mm::kWaves / wn * mi * 32;
+}
+
+// Tile shape and k split, from sweeps of every shape and split on MI355X
+// (14B q|k|v, hidden 5120, 16 to 4096 tokens).  A 256 x 256 tile does the
+// most products per byte through the LDS, so it is preferred whenever its
+// tiles keep the CUs busy (at least 3/4 of them in the last round); else
+// 256 x 128, then 128 x 128 (at 1024 tokens 224 tiles of 256 x 128 take 113
+// us where 112 of 256 x 256 take 159).  With too few tiles even then, k is
+// split so that about one workgroup runs per CU, on the smallest tile that
+// holds the batch without much padding: 64 x 256 up to 32 tokens, 128 x 128
+// up to 128, 256 x 128 beyond (measured best at 16, 64-128 and 256 tokens).
+MmPlan mm_plan(int M, int N, int K, int cus)
+{
+    static const int dp[3][2] = {{4, 4}, {2, 2}, {1, 2}};
+    for (const auto &sh : dp) {
+        const int bm = mm_bm(sh[0], sh[1]), bn = sh[1] * 64;
+        const int64_t tiles = (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+        const int64_t rounds = (tiles + cus - 1) / cus;
+        if (tiles * 4 >= rounds * cus * 3)
+            return {sh[0], sh[1], 1};
+    }
+    MmPlan pl = M <= 32 ? MmPlan{1, 4, 1} : (M <= 128 ? MmPlan{1, 2, 1} : MmPlan{2, 2, 1});
+    const int bm = mm_bm(pl.mi, pl.wn), bn = pl.wn * 64;
+    const int64_t tiles = (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    int64_t ks = cus / tiles;
+    const int64_t kmax = K / mm::BK / 4;          // at least 4 sub-tiles per split
+    if (ks > kmax)
+        ks = kmax;
+    pl.ksplit = ks < 1 ? 1 : (int)ks;
+    return pl;
+}
+
+// Raise the kernel's dynamic-LDS limit to what it uses, once per kernel and
+// device (the caller has made the handle's device current).
+template <bool F16, int HD, int MI, int WN>
+hipError_t set_mm_lds(int device)
 {
     static std::atomic<unsigned long long> done{0};
     const unsigned long long bit = 1ull << (device & 63);
     if (done.load(std::memory_order_acquire) & bit)
         return hipSuccess;
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&proj_mfma_big_kernel<F16, HD, MODE, MI>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, big::Shape<MI>::kLds);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&proj_mfma_kernel<F16, HD, MI, WN>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       mm::Shape<HD, MI, WN>::kLds);
     if (e == hipSuccess && device < 64)
         done.fetch_or(bit, std::memory_order_release);
     return e;
-}
-
-// token tiles per wave of the split path: the smallest tile height that
-// holds the batch (64, 128, then 256 tokens)
-int split_mi(int M)
-{
-    return M <= 64 ? 1 : (M <= 128 ? 2 : 4);
-}
-
-// the number of k splits of the split path for this shape
-int choose_ksplit(int M, int N, int K)
-{
-    const int bm = 64 * split_mi(M);
-    const int tiles = ((N + big::BN - 1) / big::BN) * ((M + bm - 1) / bm);
-    int s = (kTargetGroups + tiles / 2) / tiles;
-    const int max_s = K / big::BK / 4;   // at least 4 sub-tiles per split
-    if (s > max_s)
-        s = max_s;
-    return s < 1 ? 1 : s;
 }
 
 // chunks per row and step of the GEMV: the largest of 8..4 dividing the
@@ -693,21 +786,22 @@ hipError_t launch_gemv8(const ProjParams &pp, const InvTable &inv, hipStream_t s
     return hipGetLastError();
 }
 
-template <bool F16, int HD, int MI>
-hipError_t launch_split_gemm(const ProjParams &pp, const InvTable &inv, hipStream_t st, int nblk)
+template <bool F16, int HD, int MI, int WN>
+hipError_t launch_mm(const ProjParams &pp, hipStream_t st)
 {
-    using S = big::Shape<MI>;
-    hipError_t e = set_big_lds<F16, HD, 1, MI>(pp.device);
+    using S = mm::Shape<HD, MI, WN>;
+    hipError_t e = set_mm_lds<F16, HD, MI, WN>(pp.device);
     if (e != hipSuccess)
         return e;
-    const int mblk = (pp.M + S::BM - 1) / S::BM;
-    hipLaunchKernelGGL((proj_mfma_big_kernel<F16, HD, 1, MI>), dim3(nblk * mblk * pp.ksplit),
-                       dim3(big::kThreads), (unsigned)S::kLds, st, pp, inv);
+    const int tiles = ((pp.M + S::BM - 1) / S::BM) * ((pp.N + S::BN - 1) / S::BN);
+    constexpr unsigned lds = S::kLds;
+    hipLaunchKernelGGL((proj_mfma_kernel<F16, HD, MI, WN>), dim3(tiles * pp.ksplit), dim3(mm::kThreads), lds,
+                       st, pp);
     return hipGetLastError();
 }
 
 template <bool F16, int HD>
-hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st)
+hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st, MmPlan pl)
 {
     if (pp.M <= kGemvTok) {
         const int u = gemv_step(pp.K);
@@ -719,28 +813,18 @@ hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st
             return launch_gemv<F16, HD, 4>(pp, inv, st, u);
         return launch_gemv8<F16, HD>(pp, inv, st);
     }
-    const int nblk = pp.N / big::BN + (pp.N % big::BN ? 1 : 0);
     const int64_t n_tab = (int64_t)pp.M * (HD / 2);
-    if (pp.M >= kLargeM && pp.vec) {
-        using S = big::Shape<4>;
-        hipError_t e = set_big_lds<F16, HD, 0, 4>(pp.device);
-        if (e != hipSuccess)
-            return e;
-        const int mblk = (pp.M + S::BM - 1) / S::BM;
-        hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n_tab + 255) / 256)), dim3(256), 0,
-                           st, pp.pos, pp.M, HD / 2, inv, const_cast<float *>(pp.rtab));
-        hipLaunchKernelGGL((proj_mfma_big_kernel<F16, HD, 0, 4>), dim3(nblk * mblk),
-                           dim3(big::kThreads), (unsigned)S::kLds, st, pp, inv);
-        return hipGetLastError();
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n_tab + 255) / 256)), dim3(256), 0, st, pp, inv,
+                       const_cast<float *>(pp.rtab), const_cast<int64_t *>(pp.rows));
+    hipError_t e;
+    switch (pl.mi * 10 + pl.wn) {
+    case 14: e = launch_mm<F16, HD, 1, 4>(pp, st); break;
+    case 44: e = launch_mm<F16, HD, 4, 4>(pp, st); break;
+    case 12: e = launch_mm<F16, HD, 1, 2>(pp, st); break;
+    case 22: e = launch_mm<F16, HD, 2, 2>(pp, st); break;
+    default: e = hipErrorInvalidValue; break;
     }
-    // split path: the table, the GEMM writing k-split partials, the summing epilogue
-    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n_tab + 255) / 256)), dim3(256), 0, st,
-                       pp.pos, pp.M, HD / 2, inv, const_cast<float *>(pp.rtab));
-    const int mi = split_mi(pp.M);
-    hipError_t e = mi == 1 ? launch_split_gemm<F16, HD, 1>(pp, inv, st, nblk)
-                 : mi == 2 ? launch_split_gemm<F16, HD, 2>(pp, inv, st, nblk)
-                           : launch_split_gemm<F16, HD, 4>(pp, inv, st, nblk);
-    if (e != hipSuccess)
+    if (e != hipSuccess || pp.ksplit == 1)
         return e;
     const int64_t n_pairs = (int64_t)pp.M * (pp.N / 2);
     hipLaunchKernelGGL((proj_split_epilogue_kernel<F16, HD>), dim3((unsigned)((n_pairs + 255) / 256)),
@@ -841,6 +925,7 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
     pp.err = h->d_err;
     pp.vec = pl.W == 4;
     pp.rtab = nullptr;
+    pp.rows = nullptr;
     pp.ksplit = 1;
     pp.part = nullptr;
     pp.device = h->device;
@@ -851,15 +936,22 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
     hipError_t e = g.set(h->device);
     if (e != hipSuccess)
         return fail(h, QKV_ERR_HIP, "hipSetDevice(%d): %s", h->device, hipGetErrorString(e));
+    MmPlan plan = {4, 4, 1};
     if (pp.M > kGemvTok) {
-        // the MFMA paths read a [nt][head_dim] f32 cos/sin table from the
-        // handle's workspace, and the split path also keeps its [splits][nt][N]
-        // partial sums there; a larger request than any before grows it
-        // (after the device has finished with the old one)
-        const bool fused = pp.M >= kLargeM && pp.vec;
-        pp.ksplit = fused ? 1 : choose_ksplit(pp.M, pp.N, pp.K);
-        const size_t tab = (size_t)pp.M * (size_t)a->head_dim * sizeof(float);
-        const size_t need = tab + (fused ? 0 : (size_t)pp.ksplit * pp.M * pp.N * sizeof(float));
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device);
+        if (e != hipSuccess || cus <= 0)
+            return fail(h, QKV_ERR_HIP, "compute-unit count: %s", hipGetErrorString(e));
+        plan = mm_plan(pp.M, pp.N, pp.K, cus);
+        pp.ksplit = plan.ksplit;
+        // The MFMA path's workspace (the handle's, grown on demand after the
+        // device has finished with the old one): the launch's [nt][head_dim]
+        // cos/sin table, the [nt] cache rows, and [ksplit][nt][N] partial sums
+        // when k is split.
+        const size_t tab = ((size_t)pp.M * (size_t)a->head_dim * sizeof(float) + 255) / 256 * 256;
+        const size_t rows = ((size_t)pp.M * sizeof(int64_t) + 255) / 256 * 256;
+        const size_t need =
+            tab + rows + (pp.ksplit > 1 ? (size_t)pp.ksplit * pp.M * pp.N * sizeof(float) : 0);
         if (h->proj_ws_bytes < need) {
             e = hipDeviceSynchronize();
             if (e == hipSuccess && h->proj_ws)
@@ -870,19 +962,20 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
                 e = hipMalloc(&h->proj_ws, need);
             if (e != hipSuccess) {
                 h->proj_ws = nullptr;
-                return fail(h, QKV_ERR_HIP, "workspace of %zu bytes: %s", need,
-                            hipGetErrorString(e));
+                return fail(h, QKV_ERR_HIP, "workspace of %zu bytes: %s", need, hipGetErrorString(e));
             }
             h->proj_ws_bytes = need;
         }
-        pp.rtab = static_cast<const float *>(h->proj_ws);
-        pp.part = reinterpret_cast<float *>(static_cast<char *>(h->proj_ws) + tab);
+        char *ws = static_cast<char *>(h->proj_ws);
+        pp.rtab = reinterpret_cast<const float *>(ws);
+        pp.rows = reinterpret_cast<const int64_t *>(ws + tab);
+        pp.part = reinterpret_cast<float *>(ws + tab + rows);
     }
     const bool f16 = a->cache_dtype == QKV_CACHE_F16;
     if (a->head_dim == 128)
-        e = f16 ? launch_proj<true, 128>(pp, inv, st) : launch_proj<false, 128>(pp, inv, st);
+        e = f16 ? launch_proj<true, 128>(pp, inv, st, plan) : launch_proj<false, 128>(pp, inv, st, plan);
     else
-        e = f16 ? launch_proj<true, 64>(pp, inv, st) : launch_proj<false, 64>(pp, inv, st);
+        e = f16 ? launch_proj<true, 64>(pp, inv, st, plan) : launch_proj<false, 64>(pp, inv, st, plan);
     if (e != hipSuccess)
         return fail(h, QKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     h->last_stream = st;

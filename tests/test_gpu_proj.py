@@ -216,7 +216,8 @@ SMALL_05B = wl.Workload("proj_small_0.5b", 14, 2, 64, nt=257, n_ctx=512, n_slots
 
 @pytest.mark.parametrize("cd", [wl.CACHE_F16, wl.CACHE_F32])
 def test_proj_prefill_small_14b(handle, cd):
-    """Several 128x256 tiles and a ragged tail of 44 tokens, 14B geometry."""
+    """300 tokens, 14B geometry: two 256 x 128 token tiles (the second ragged,
+    44 tokens), k split in two, the summing epilogue."""
     c = ProjCase(SMALL_14B, hidden=1024, cache_dtype=cd)
     assert _run(handle, c, "small_14b") == B.QKV_OK
     c.check("small_14b")
@@ -230,7 +231,8 @@ def test_proj_concat_outputs_7b(handle):
 
 
 def test_proj_head_dim_64_no_bias(handle):
-    """hd 64 (two heads per wave tile) and NULL biases, 0.5B geometry."""
+    """hd 64 (a wave's 64 outputs are one whole head) and NULL biases, 0.5B
+    geometry (1152 outputs: 9 column blocks of 128), k split 7 ways."""
     c = ProjCase(SMALL_05B, hidden=896, bias=False)
     assert _run(handle, c, "hd64_nobias") == B.QKV_OK
     c.check("hd64_nobias")
@@ -263,7 +265,8 @@ def test_proj_gemv_hd64_slots(handle, nt):
 
 
 def test_proj_nine_tokens(handle):
-    """The smallest launch on the MFMA path: one ragged 256-token tile, k split."""
+    """The smallest launch on the MFMA path: one ragged 64-token tile per 256
+    outputs, k split 14 ways."""
     c = ProjCase(wl.DECODE_7B, hidden=3584, nt=9)
     assert _run(handle, c, "nt9") == B.QKV_OK
     c.check("nt9")
@@ -283,9 +286,9 @@ def test_proj_out_of_range_position(handle):
 
 
 def test_proj_long_ragged_hd64_no_bias(handle):
-    """The 256x256 path with hd 64 (two heads per wave), a ragged last token
-    tile (1100 = 4*256 + 76) and a last column block half past the end
-    (1152 outputs = 4.5 blocks of 256)."""
+    """hd 64, 1100 tokens of the 0.5B geometry (too few tiles to fill the
+    chip): 256 x 128 tiles with a ragged last token tile (1100 = 4*256 + 76),
+    k split 4 ways."""
     w = wl.Workload("proj_long_0.5b", 14, 2, 64, nt=1100, n_ctx=2048, n_slots=1, layers=1,
                     seed=16, cache_dtypes=(wl.CACHE_F32,), pos_mode="arange")
     c = ProjCase(w, hidden=512, bias=False)
@@ -294,7 +297,8 @@ def test_proj_long_ragged_hd64_no_bias(handle):
 
 
 def test_proj_long_concat_14b(handle):
-    """The 256x256 path writing views of one concat q|k|v buffer."""
+    """The data-parallel 128 x 128 launch (1030 tokens) writing views of one
+    concat q|k|v buffer."""
     w = wl.Workload("proj_long_14b", 40, 8, 128, nt=1030, n_ctx=4096, n_slots=1, layers=1,
                     seed=17, pos_mode="uniform")
     c = ProjCase(w, hidden=256, form="concat")
@@ -303,8 +307,8 @@ def test_proj_long_concat_14b(handle):
 
 
 def test_proj_long_misaligned_outputs(handle):
-    """Outputs off 16-byte alignment: the long-prompt launch takes the
-    scalar-store tiles."""
+    """Outputs off 16-byte alignment: the data-parallel launch takes the
+    epilogue's scalar stores."""
     w = wl.Workload("proj_long_mis", 40, 8, 128, nt=1030, n_ctx=4096, n_slots=1, layers=1,
                     seed=18, pos_mode="arange")
     c = ProjCase(w, hidden=256, misalign=1)
@@ -367,15 +371,17 @@ def test_proj_rejects_unsupported(handle):
     assert B.qkv_epilogue_status(handle) == B.QKV_OK
 
 
-@pytest.mark.parametrize("nt", [1023, 1024])
-def test_proj_routing_boundary(handle, nt):
-    """1023 tokens take the split-k path, 1024 the fused long-prompt path;
-    both match the oracle on the same draws."""
-    w = wl.Workload("proj_boundary", 40, 8, 128, nt=nt, n_ctx=4096, n_slots=1, layers=1,
+@pytest.mark.parametrize("nt", [32, 33, 129, 1024, 2048])
+def test_proj_plan_switches(handle, nt):
+    """Each side of the launch plan's switches at the 14B width, hidden 512:
+    32 tokens on 64 x 256 tiles and 33 on 128 x 128 (k split 4 ways), 129
+    on 256 x 128 (split 4 ways), 1024 data-parallel 256 x 128, 2048
+    data-parallel 256 x 256."""
+    w = wl.Workload("proj_plan", 40, 8, 128, nt=nt, n_ctx=4096, n_slots=1, layers=1,
                     seed=19, pos_mode="uniform")
-    c = ProjCase(w, hidden=128)
-    assert _run(handle, c, f"boundary_{nt}") == B.QKV_OK
-    c.check(f"boundary_{nt}")
+    c = ProjCase(w, hidden=512)
+    assert _run(handle, c, f"plan_{nt}") == B.QKV_OK
+    c.check(f"plan_{nt}")
 
 
 def test_proj_long_slots_f32_cache(handle):
@@ -391,7 +397,7 @@ def test_proj_long_slots_f32_cache(handle):
 @pytest.mark.parametrize("nt", [3, 40, 1030])
 def test_proj_minimal_hidden(handle, nt):
     """hidden = 64 (two k sub-tiles, fewer than the LDS ring's depth) on the
-    GEMV, split-k and fused paths."""
+    GEMV, a small batch (k too short to split) and the data-parallel launch."""
     w = wl.Workload("proj_hidden64", 40, 8, 128, nt=nt, n_ctx=2048, n_slots=1, layers=1,
                     seed=21, pos_mode="arange")
     c = ProjCase(w, hidden=64)
@@ -453,7 +459,7 @@ def test_proj_graph_capture_decode_layers(handle):
 
 
 def test_proj_graph_capture_split_and_fused(handle):
-    """A split-k call (300 tokens) and a fused long-prompt call (1100 tokens)
+    """A k-split call (300 tokens) and a data-parallel call (1100 tokens)
     captured after a warm-up call; no allocation happens in the capture."""
     w1 = wl.Workload("proj_graph_split", 40, 8, 128, nt=300, n_ctx=4096, n_slots=1, layers=1,
                      seed=22, pos_mode="uniform")

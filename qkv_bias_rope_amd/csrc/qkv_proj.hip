@@ -142,8 +142,12 @@ __global__ __launch_bounds__(256) void rope_table_kernel(ProjParams p, InvTable 
 // global->LDS loads (64 lanes x 16 bytes = 16 rows per instruction) issued
 // three sub-tiles ahead (deeper rings, up to 8 stages for the small tiles,
 // measured no faster on MI355X).  Chunk c of row r sits in slot c ^ g(r),
-// g(r) = ((r >> 1) ^ (r >> 3)) & 3: the 16-byte fragment reads of 16
-// consecutive rows hit distinct banks.  Per sub-tile s (two k steps of 16):
+// g(r) = (r >> 2) & 3, which makes the 16-byte fragment reads (16 rows of
+// a quarter wave, one chunk each) conflict-free on gfx950: a probe under
+// rocprofv3 reads 4 LDS cycles per ds_read_b128 and no bank-conflict cycles,
+// where the swizzle ((r >> 1) ^ (r >> 3)) & 3 -- conflict-free on paper for
+// 64 four-byte banks serving 16 lanes at a time -- takes 8, half of them
+// counted as conflicts.  Per sub-tile s (two k steps of 16):
 //   products of step 0 (first half); read step-1 fragments; products of
 //   step 0 (second half); products of step 1 (first half); wait for this
 //   wave's loads of sub-tile s+1 and meet the other waves (after which stage
@@ -208,7 +212,7 @@ constexpr int vmcnt_wait(int v)
 
 __device__ __forceinline__ int swz(int r)
 {
-    return ((r >> 1) ^ (r >> 3)) & 3;
+    return (r >> 2) & 3;
 }
 
 // first 32-column MFMA tile of NeoX pair group g (its partner is lo + PT)

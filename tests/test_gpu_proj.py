@@ -371,6 +371,21 @@ def test_proj_rejects_unsupported(handle):
     assert B.qkv_epilogue_status(handle) == B.QKV_OK
 
 
+def test_proj_split_head_groups_ragged(handle):
+    """hd 64, 1900 tokens of the 0.5B geometry: k split 3 ways on 256 x 128
+    tiles, and the summing kernel takes 4 heads per thread, so its last group
+    holds the remaining 2 of the 18 heads; sampled tokens."""
+    # unique positions: the cache check of sampled tokens cannot see a race
+    # won by a token outside the sample
+    w = wl.Workload("proj_groups_0.5b", 14, 2, 64, nt=1900, n_ctx=2048, n_slots=1, layers=1,
+                    seed=24, cache_dtypes=(wl.CACHE_F16,), pos_mode="arange")
+    rng = np.random.default_rng(9)
+    sample = np.unique(np.concatenate([[0, 255, 256, 1899], rng.integers(0, 1900, 28)]))
+    c = ProjCase(w, hidden=512, sample=sample)
+    assert _run(handle, c, "groups_hd64") == B.QKV_OK
+    c.check("groups_hd64")
+
+
 @pytest.mark.parametrize("nt", [32, 33, 129, 1024, 2048])
 def test_proj_plan_switches(handle, nt):
     """Each side of the launch plan's switches at the 14B width, hidden 512:

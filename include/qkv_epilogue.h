@@ -216,7 +216,8 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  * workspace held by the handle: a cos/sin table of nt * head_dim * 4 bytes,
  * the tokens' cache rows (nt * 8 bytes) and, when k is split, the partial
  * sums (splits * nt * (nqt + 2*nkt) * 4 bytes, about 29 MB for 256 tokens of
- * the 14B shape); those launches are two or three kernels on the stream.  A call that needs more workspace than any before it
+ * the 14B shape); those launches are two kernels on the stream (the tables
+ * and the GEMM, or the split GEMM and the summing epilogue).  A call that needs more workspace than any before it
  * synchronizes the device and (re)allocates it: make that call outside graph
  * capture.  All other calls allocate nothing and never synchronize.  Calls on
  * one handle share its workspace: calls that may run concurrently (different

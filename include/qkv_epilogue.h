@@ -217,13 +217,14 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  * the tokens' cache rows (nt * 8 bytes) and, when k is split, the partial
  * sums (splits * nt * (nqt + 2*nkt) * 4 bytes, about 29 MB for 256 tokens of
  * the 14B shape); those launches are two kernels on the stream (the tables
- * and the GEMM, or the split GEMM and the summing epilogue).  A call that needs more workspace than any before it
- * synchronizes the device and (re)allocates it: make that call outside graph
- * capture.  All other calls allocate nothing and never synchronize.  Calls on
- * one handle share its workspace: calls that may run concurrently (different
- * streams) need different handles.  The f32 sums are taken in a different
- * order than a plain loop: each output carries up to (hidden+2) * 2^-24 *
- * sum_k |x w| of accumulation error on top of the epilogue's own rounding.
+ * and the GEMM, or the split GEMM and the summing epilogue).  A call that
+ * needs more workspace than any before it synchronizes the device and
+ * (re)allocates it: make that call outside graph capture.  All other calls
+ * allocate nothing and never synchronize.  Calls on one handle share its
+ * workspace: calls that may run concurrently (different streams) need
+ * different handles.  The f32 sums are taken in a different order than a
+ * plain loop: each output carries up to (hidden+2) * 2^-24 * sum_k |x w| of
+ * accumulation error on top of the epilogue's own rounding.
  */
 typedef struct qkv_proj_args {
     const void *x;          /* bf16 [nt][ld_x] */

@@ -984,6 +984,14 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
             return fail(h, QKV_ERR_HIP, "compute-unit count: %s", hipGetErrorString(e));
         plan = mm_plan(pp.M, pp.N, pp.K, cus);
         pp.ksplit = plan.ksplit;
+        {
+            // the grid (tiles x splits) and the kernels' tile indices are 32-bit
+            const int64_t bm = mm_bm(plan.mi, plan.wn), bn = plan.wn * 64;
+            const int64_t blocks = ((pp.M + bm - 1) / bm) * ((pp.N + bn - 1) / bn) * pp.ksplit;
+            if (blocks > INT32_MAX)
+                return fail(h, QKV_ERR_UNSUPPORTED, "nt x q|k|v width too large (%lld tiles)",
+                            (long long)blocks);
+        }
         // The MFMA path's workspace (the handle's, grown on demand after the
         // device has finished with the old one): the launch's [nt][head_dim]
         // cos/sin table, the [nt] cache rows, and [ksplit][nt][N] partial sums

@@ -200,7 +200,7 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  * qkv_epilogue_run_ex: optional biases, NeoX rotary embedding of q and k, the
  * sections written to epi.q / epi.k / epi.v (outputs only here) and the K/V
  * cache rows stored.  The GEMM runs on the matrix cores (MFMA) for more than
- * 8 tokens, as a weight-streaming GEMV for 1-8 tokens.  The epilogue runs on
+ * 4 tokens, as a weight-streaming GEMV for 1-4 tokens.  The epilogue runs on
  * the sums in registers, except when the batch has too few tiles to fill the
  * GPU: then the GEMM stores k-split partial sums and a second kernel adds
  * them in a fixed order and runs the epilogue (see Launches).
@@ -212,7 +212,7 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  * Limits (QKV_ERR_UNSUPPORTED otherwise): NeoX style, head_dim 64 or 128, q
  * and k/v widths multiples of 128; x and w each under 2 GiB.
  *
- * Launches: 1-8 tokens run one weight-streaming kernel.  More tokens use a
+ * Launches: 1-4 tokens run one weight-streaming kernel.  More tokens use a
  * workspace held by the handle: a cos/sin table of nt * head_dim * 4 bytes,
  * the tokens' cache rows (nt * 8 bytes) and, when k is split, the partial
  * sums (splits * nt * (nqt + 2*nkt) * 4 bytes, about 29 MB for 256 tokens of

@@ -576,7 +576,7 @@ __global__ __launch_bounds__(256) void proj_split_epilogue_kernel(ProjParams p, 
 }
 
 // ---------------------------------------------------------------------------
-// decode (1-8 tokens): weight-streaming GEMV + epilogue
+// decode (1-4 tokens): weight-streaming GEMV + epilogue
 // ---------------------------------------------------------------------------
 // One wave per NeoX pair of weight rows (j and j + hd/2 of a head; in the v
 // section the same pairing just groups rows), four waves per block.  Lane l
@@ -585,13 +585,15 @@ __global__ __launch_bounds__(256) void proj_split_epilogue_kernel(ProjParams p, 
 // products into the f32 sum per instruction); a butterfly over the wave
 // completes the dot products, and lane t < nt finishes token t: bias, the
 // rotation of the pair, write-back and the cache store.
-constexpr int kGemvTok = 8;          // the GEMV path takes up to 8 tokens
+// up to 4 tokens; from 5 the k-split MFMA path is faster (5-8 tokens: 21.7-
+// 21.9 us at 14B against 24.6-24.9 for a GEMV with four pairs per wave)
+constexpr int kGemvTok = 4;
 constexpr int kGemvWaves = 4;
 
 // U: 16-byte chunks of each row in flight per lane and step; the launcher
 // picks U dividing the chunks per lane (hidden/512) when it can, since a
-// partial last step costs as much as a full one.  P: NeoX pairs per wave (4
-// for 5-8 tokens, so each x chunk loaded serves eight weight rows).
+// partial last step costs as much as a full one.  P: NeoX pairs per wave
+// (1 in every launch; more pairs let one x chunk serve more weight rows).
 template <bool F16, int HD, int NT, int U, int P>
 __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p, InvTable inv)
 {
@@ -718,7 +720,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
     }
 }
 
-// Launch choice.  Decode (1-8 tokens): the GEMV.  9+ tokens: the per-launch
+// Launch choice.  Decode (1-4 tokens): the GEMV.  5+ tokens: the per-launch
 // tables, then the MFMA kernel on the tile shape and k split chosen below,
 // and the summing epilogue when k is split.
 struct MmPlan {
@@ -808,18 +810,6 @@ hipError_t launch_gemv(const ProjParams &pp, const InvTable &inv, hipStream_t st
     return hipGetLastError();
 }
 
-// 5-8 tokens: four pairs per wave, one chunk per row in flight (each x
-// chunk loaded serves eight weight rows; measured 24.5 us at 14B against
-// 27.9 with two pairs and 32 on the MFMA split path)
-template <bool F16, int HD>
-hipError_t launch_gemv8(const ProjParams &pp, const InvTable &inv, hipStream_t st)
-{
-    const int blocks = (pp.N / 8 + kGemvWaves - 1) / kGemvWaves;
-    hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, 8, 1, 4>), dim3(blocks), dim3(64 * kGemvWaves), 0,
-                       st, pp, inv);
-    return hipGetLastError();
-}
-
 template <bool F16, int HD, int MI, int WN>
 hipError_t launch_mm(const ProjParams &pp, hipStream_t st)
 {
@@ -843,9 +833,7 @@ hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st
             return launch_gemv<F16, HD, 1>(pp, inv, st, u);
         if (pp.M == 2)
             return launch_gemv<F16, HD, 2>(pp, inv, st, u);
-        if (pp.M <= 4)
-            return launch_gemv<F16, HD, 4>(pp, inv, st, u);
-        return launch_gemv8<F16, HD>(pp, inv, st);
+        return launch_gemv<F16, HD, 4>(pp, inv, st, u);
     }
     // the fused epilogue reads the launch's cos/sin and cache-row tables; the
     // split path's summing kernel computes its own

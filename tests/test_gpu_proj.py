@@ -247,8 +247,8 @@ def test_proj_padded_activation_rows(handle):
 
 @pytest.mark.parametrize("nt", [1, 2, 3, 4, 5, 8])
 def test_proj_decode_gemv(handle, nt):
-    """1-8 tokens take the weight-streaming kernel (one NeoX pair per wave up
-    to 4 tokens, two from 5); 14B decode geometry."""
+    """1-4 tokens take the weight-streaming kernel (one NeoX pair per wave),
+    5 and 8 the k-split MFMA path on 64-token tiles; 14B decode geometry."""
     c = ProjCase(wl.DECODE_14B, hidden=5120, nt=nt)
     assert _run(handle, c, f"gemv_nt{nt}") == B.QKV_OK
     c.check(f"gemv_nt{nt}")
@@ -256,7 +256,8 @@ def test_proj_decode_gemv(handle, nt):
 
 @pytest.mark.parametrize("nt", [4, 7])
 def test_proj_gemv_hd64_slots(handle, nt):
-    """GEMV path with hd 64 and per-token cache slots."""
+    """hd 64 and per-token cache slots on the GEMV (4 tokens) and on the
+    k-split MFMA path (7 tokens)."""
     w = wl.Workload("proj_gemv_slots", 14, 2, 64, nt=nt, n_ctx=64, n_slots=8, layers=1, seed=14,
                     cache_dtypes=(wl.CACHE_F16,))
     c = ProjCase(w, hidden=896)
@@ -265,8 +266,8 @@ def test_proj_gemv_hd64_slots(handle, nt):
 
 
 def test_proj_nine_tokens(handle):
-    """The smallest launch on the MFMA path: one ragged 64-token tile per 256
-    outputs, k split 14 ways."""
+    """Nine tokens of the 7B geometry on the MFMA path: one ragged 64-token
+    tile per 256 outputs, k split 14 ways."""
     c = ProjCase(wl.DECODE_7B, hidden=3584, nt=9)
     assert _run(handle, c, "nt9") == B.QKV_OK
     c.check("nt9")

@@ -387,6 +387,25 @@ def test_proj_split_head_groups_ragged(handle):
     c.check("groups_hd64")
 
 
+@pytest.mark.parametrize("nt", [40, 300, 1030])
+def test_proj_repeat_is_bitwise_identical(handle, nt):
+    """The k-split partials are added in split order and every tile sums its
+    k steps in one order, so a repeated launch reproduces q/k/v bit for bit
+    (40 and 300 tokens split k, 1030 run data-parallel); the first result is
+    also checked against the oracle."""
+    w = wl.Workload("proj_repeat", 40, 8, 128, nt=nt, n_ctx=4096, n_slots=1, layers=1,
+                    seed=25, pos_mode="arange")
+    c = ProjCase(w, hidden=1024)
+    assert _run(handle, c, f"repeat_{nt}") == B.QKV_OK
+    first = [t.clone() for t in (c.g_q, c.g_k, c.g_v)]
+    for _ in range(3):
+        assert c.run_gpu(handle) == B.QKV_OK
+        torch.cuda.synchronize()
+        for a, b in zip(first, (c.g_q, c.g_k, c.g_v)):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"repeat_{nt}: results differ"
+    c.check(f"repeat_{nt}")
+
+
 @pytest.mark.parametrize("nt", [32, 33, 129, 1024, 2048])
 def test_proj_plan_switches(handle, nt):
     """Each side of the launch plan's switches at the 14B width, hidden 512:

@@ -444,6 +444,32 @@ def copy_calibration(steps):
                       "launches": steps}))
 
 
+PROJ_SWEEP_TOKENS = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096)
+
+
+def proj_sweep(args):
+    """The projection-fed epilogue over token counts, each launch event-timed
+    with rotating input sets (weights from HBM on every launch)."""
+    import torch
+    from qkv_bias_rope_amd import binding as B
+    from qkv_bias_rope_amd import workloads as wl
+    rc, h = B.qkv_epilogue_create(0, 4096)
+    assert rc == 0, rc
+    stream = torch.cuda.Stream()
+    w = wl.Workload("proj_sweep_14b", 40, 8, 128, nt=1, n_ctx=4096, n_slots=1, layers=1, seed=30)
+    hidden = 5120
+    with torch.cuda.stream(stream):
+        for nt in PROJ_SWEEP_TOKENS:
+            steps = args.steps if nt <= 512 else max(10, args.steps // 5)
+            r = bench_proj(h, w, hidden, steps, args.warmup, stream, min_set_bytes=1.0e9, nt=nt)
+            print(json.dumps({"proj_sweep_tokens": nt, "hidden": hidden,
+                              "us_per_launch": round(r["us_per_launch"], 2),
+                              "tflops": round(r["tflops"], 1), "gbs": round(r["gbs"], 1),
+                              "library_bf16_matmul_call_us": round(r["library_bf16_matmul_call_us"], 2)}),
+                  flush=True)
+    B.qkv_epilogue_destroy(h)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -453,6 +479,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--proj-sweep", action="store_true",
+                    help="run only the projection-fed epilogue at 1..4096 tokens (14B width, "
+                         "hidden 5120), one JSON line per token count")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -473,6 +502,9 @@ def main():
         sys.exit(1)
     if args.copy_calib:
         copy_calibration(args.steps)
+        return
+    if args.proj_sweep:
+        proj_sweep(args)
         return
 
     rc, h = B.qkv_epilogue_create(0, 4096)

@@ -168,27 +168,32 @@ __global__ __launch_bounds__(256) void rope_table_kernel(ProjParams p, InvTable 
 // straight into the LDS ring, which is free by then -- so a tile's epilogue
 // waits for memory once instead of once per token group.
 namespace mm {
-constexpr int BK = 32;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRow = BK * 2;                  // 64 bytes per row and sub-tile
-constexpr int NSTAGE = 4;                     // LDS ring depth
+constexpr int kLdsMax = 160 * 1024;           // per workgroup on gfx950
 
-template <int HD, int MI, int WN>
+// HD, the tile shape (MI, WN) and the k depth BK of a stage (32, 64 or 128)
+template <int HD, int MI, int WN, int BK>
 struct Shape {
     static constexpr int WM = kWaves / WN;
     static constexpr int BM = WM * MI * 32;
     static constexpr int BN = WN * 64;
+    static constexpr int kRow = BK * 2;           // bytes per row and stage
+    static constexpr int kCpr = BK / 8;           // 16-byte chunks per row
+    static constexpr int kRpi = 1024 / kRow;      // rows per load instruction
+    static constexpr int KS = BK / 16;            // k steps of 16 per stage
     static constexpr int kRegionA = BM * kRow;
     static constexpr int kStage = kRegionA + BN * kRow;
+    // ring depth: as many stages as the LDS holds, at most 4
+    static constexpr int NSTAGE = kLdsMax / kStage >= 4 ? 4 : kLdsMax / kStage;
     static constexpr int kRing = NSTAGE * kStage;
-    // 16-row load instructions per sub-tile: an equal share per wave when
-    // there are 8 or more, else (4 of them) token rows on waves 0-3 and
-    // weight rows on waves 4-7
-    static constexpr int kInstA = BM / 16, kInstB = BN / 16;
+    // load instructions per stage: an equal share per wave when there are 8
+    // or more, else (4 of them) token rows on waves 0-3 and weight rows on
+    // waves 4-7
+    static constexpr int kInstA = BM / kRpi, kInstB = BN / kRpi;
     static constexpr int kWaveA = kInstA >= kWaves ? kInstA / kWaves : 1;
     static constexpr int kWaveB = kInstB >= kWaves ? kInstB / kWaves : 1;
-    // loads per sub-tile of waves 0-3 and of waves 4-7
+    // loads per stage of waves 0-3 and of waves 4-7
     static constexpr int kLoadsLo = kWaveA + (kInstB >= kWaves ? kWaveB : 0);
     static constexpr int kLoadsHi = (kInstA >= kWaves ? kWaveA : 0) + kWaveB;
     // epilogue: the tile's pair indices (one group of an hd-128 head: 32;
@@ -197,10 +202,13 @@ struct Shape {
     static constexpr int kChunks = kPW / 2;
     static constexpr int kTab = BM * kChunks * 16;
     static constexpr int kLds = kRing > kTab ? kRing : kTab;
+    static_assert(BK == 32 || BK == 64 || BK == 128, "stage depth");
+    static_assert(NSTAGE >= 2, "the LDS holds two stages");
     static_assert(kInstA % kWaves == 0 || kInstA == 4, "token-row loads");
     static_assert(kInstB % kWaves == 0 || kInstB == 4, "weight-row loads");
     static_assert(kInstA >= kWaves || kInstB >= kWaves, "load split");
-    static_assert(kWaveA <= 4 && kWaveB <= 4, "load slots");
+    static_assert(kWaveA <= 8 && kWaveB <= 8, "load slots");
+    static_assert((NSTAGE - 1) * (kLoadsLo > kLoadsHi ? kLoadsLo : kLoadsHi) <= 63, "vmcnt range");
     static_assert((BM * kChunks) % 64 == 0, "table staging");
 };
 
@@ -210,9 +218,17 @@ constexpr int vmcnt_wait(int v)
     return (v & 15) | ((v >> 4) << 14) | (0xF << 8) | (7 << 4);
 }
 
+// Slot of chunk c of row r: c ^ swz(r).  Chosen per row size with a probe
+// that replays the fragment reads under rocprofv3 (16 consecutive rows of a
+// quarter wave, one chunk each): 4 LDS cycles per ds_read_b128 and no
+// bank-conflict cycles for 64-byte rows with (r >> 2) & 3, 128-byte rows
+// with (r >> 1) & 7 and 256-byte rows with r & 15; ((r >> 1) ^ (r >> 3)) & 3,
+// conflict-free on paper for 64-byte rows, takes 8 cycles.
+template <int CPR>
 __device__ __forceinline__ int swz(int r)
 {
-    return (r >> 2) & 3;
+    constexpr int shift = CPR == 4 ? 2 : (CPR == 8 ? 1 : 0);
+    return (r >> shift) & (CPR - 1);
 }
 
 // first 32-column MFMA tile of NeoX pair group g (its partner is lo + PT)
@@ -223,12 +239,13 @@ __device__ __forceinline__ int group_lo(int g)
 }
 }  // namespace mm
 
-template <bool F16, int HD, int MI, int WN>
+template <bool F16, int HD, int MI, int WN, int BK>
 __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
 {
     using namespace mm;
-    using S = Shape<HD, MI, WN>;
+    using S = Shape<HD, MI, WN, BK>;
     constexpr int BM = S::BM, BN = S::BN;
+    constexpr int NSTAGE = S::NSTAGE, KS = S::KS, kRow = S::kRow;
     constexpr int HALF = HD / 2;
     constexpr int PT = HALF / 32;                 // tile distance of NeoX partners
     extern __shared__ __align__(16) unsigned char lds[];
@@ -238,7 +255,7 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
-    const int lrow = lane >> 2, slot = lane & 3;
+    const int lrow = lane / S::kCpr, slot = lane % S::kCpr;
     const int lr = lane & 31, hi = lane >> 5;
 
     const int ntn = (p.N + BN - 1) / BN;
@@ -253,34 +270,34 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     const int len = (int)((int64_t)(split + 1) * KTall / p.ksplit) - kbeg;
 
     // this wave's load instructions: token rows arow[j] and weight rows
-    // brow[j] of the tile, 16 rows each, lane/4 the row within; byte offsets
-    // from x / w (each < 2 GiB); rows past the end repeat the last one.
-    // (fixed-size arrays: with a size that depends on the template
+    // brow[j] of the tile, kRpi rows each, lane / kCpr the row within; byte
+    // offsets from x / w (each < 2 GiB); rows past the end repeat the last
+    // one.  (fixed-size arrays: with a size that depends on the template
     // arguments, captured by the lambda below, hipcc's host pass silently
     // emitted no launch stub)
     const bool do_a = S::kInstA >= kWaves || wave < S::kInstA;
     const bool do_b = S::kInstB >= kWaves || wave >= kWaves - S::kInstB;
-    int arow[4] = {0, 0, 0, 0}, brow[4] = {0, 0, 0, 0};
-    uint32_t aoff[4], boff[4];
+    int arow[8] = {0, 0, 0, 0, 0, 0, 0, 0}, brow[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint32_t aoff[8], boff[8];
 #pragma unroll
     for (int j = 0; j < S::kWaveA; ++j) {
-        arow[j] = 16 * ((S::kInstA >= kWaves ? wave * S::kWaveA : wave) + j);
+        arow[j] = S::kRpi * ((S::kInstA >= kWaves ? wave * S::kWaveA : wave) + j);
         const int r = arow[j] + lrow;
-        aoff[j] = (uint32_t)((int64_t)min(m0 + r, p.M - 1) * p.ld_x * 2) + (slot ^ swz(r)) * 16;
+        aoff[j] = (uint32_t)((int64_t)min(m0 + r, p.M - 1) * p.ld_x * 2) + (slot ^ swz<S::kCpr>(r)) * 16;
     }
 #pragma unroll
     for (int j = 0; j < S::kWaveB; ++j) {
-        brow[j] = 16 * ((S::kInstB >= kWaves ? wave * S::kWaveB : wave - (kWaves - S::kInstB)) + j);
+        brow[j] = S::kRpi * ((S::kInstB >= kWaves ? wave * S::kWaveB : wave - (kWaves - S::kInstB)) + j);
         const int rb = brow[j] + lrow;
         const int n = group_lo<PT>(tn * WN + rb / 64) * 32 + ((rb >> 5) & 1) * PT * 32 + (rb & 31);
-        boff[j] = (uint32_t)((int64_t)min(n, p.N - 1) * p.K * 2) + (slot ^ swz(rb)) * 16;
+        boff[j] = (uint32_t)((int64_t)min(n, p.N - 1) * p.K * 2) + (slot ^ swz<S::kCpr>(rb)) * 16;
     }
     const unsigned char *xb = reinterpret_cast<const unsigned char *>(p.x);
     const unsigned char *wb = reinterpret_cast<const unsigned char *>(p.w);
-    // local sub-tile st (clamped to the last one: the loop stays uniform)
+    // local stage st (clamped to the last one: the loop stays uniform)
     auto issue = [&](int st) {
         const int stage = st % NSTAGE;
-        const uint32_t kb = (uint32_t)(kbeg + min(st, len - 1)) * (BK * 2);
+        const uint32_t kb = (uint32_t)(kbeg + min(st, len - 1)) * kRow;
         unsigned char *sa = lds + stage * S::kStage;
         unsigned char *sb = sa + S::kRegionA;
         if (do_a) {
@@ -303,20 +320,25 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
         for (int v = 0; v < 16; ++v)
             acc[q][v] = 0.0f;
 
-    // fragment reads: lane reads row lr of each 32-row tile, chunk 2*ks + hi
-    const int g = swz(lr);                        // tiles start at multiples of 32
+    // fragment reads: lane reads row lr of each 32-row tile, chunk 2j + hi
+    // for k step j of the stage
+    const int g = swz<S::kCpr>(lr);               // tiles start at multiples of 32
     const int abase = (wm * MI * 32 + lr) * kRow;
     const int bbase0 = S::kRegionA + (wn * 64 + lr) * kRow;
     const int bbase1 = bbase0 + 32 * kRow;
-    const int k0off = ((0 + hi) ^ g) * 16;        // step 0: chunk hi
-    const int k1off = ((2 + hi) ^ g) * 16;        // step 1: chunk 2 + hi
+    int koff[8];
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+        koff[j] = ((2 * j + hi) ^ g) * 16;
+    // two fragment buffers: step j uses buffer j % 2
+    static_assert(KS % 2 == 0, "steps per stage");
     bf16x8 a0[MI], b0[2], a1[MI], b1[2];
-    auto read_frags = [&](const unsigned char *s, int koff, bf16x8 (&fa)[MI], bf16x8 (&fb)[2]) {
+    auto read_frags = [&](const unsigned char *s, int ko, bf16x8 (&fa)[MI], bf16x8 (&fb)[2]) {
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
-            fa[mi] = *reinterpret_cast<const bf16x8 *>(s + abase + mi * 32 * kRow + koff);
-        fb[0] = *reinterpret_cast<const bf16x8 *>(s + bbase0 + koff);
-        fb[1] = *reinterpret_cast<const bf16x8 *>(s + bbase1 + koff);
+            fa[mi] = *reinterpret_cast<const bf16x8 *>(s + abase + mi * 32 * kRow + ko);
+        fb[0] = *reinterpret_cast<const bf16x8 *>(s + bbase0 + ko);
+        fb[1] = *reinterpret_cast<const bf16x8 *>(s + bbase1 + ko);
     };
     // half h takes products q = f*MI + ti in [h*MI, (h+1)*MI)
     auto mfma_half = [&](int h, const bf16x8 (&fa)[MI], const bf16x8 (&fb)[2]) {
@@ -325,7 +347,7 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
             acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[q / MI], fa[q % MI], acc[q], 0, 0, 0);
     };
 
-    // prologue: sub-tiles 0..NSTAGE-1 in flight, sub-tile 0 landed everywhere
+    // prologue: stages 0..NSTAGE-1 in flight, stage 0 landed everywhere
 #pragma unroll
     for (int st = 0; st < NSTAGE; ++st)
         issue(st);
@@ -334,30 +356,41 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     else
         __builtin_amdgcn_s_waitcnt(vmcnt_wait((NSTAGE - 1) * S::kLoadsHi));
     __syncthreads();
-    read_frags(lds, k0off, a0, b0);
+    read_frags(lds, koff[0], a0, b0);
 
+    // Per stage: step j's products, first half; the next step's fragments
+    // (or, at the last step: wait for this wave's loads of the next stage,
+    // meet the other waves -- after which this stage is free and the next
+    // visible -- refill this stage and read the next stage's first
+    // fragments); step j's second half.
     for (int kt = 0; kt < len; ++kt) {
         const unsigned char *s = lds + (kt % NSTAGE) * S::kStage;
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_half(0, a0, b0);
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(s, k1off, a1, b1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_half(1, a0, b0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_half(0, a1, b1);
-        __builtin_amdgcn_sched_barrier(0);
-        // this wave's loads of sub-tile kt+1 have landed once at most the
-        // later groups (kt+2 .. kt+NSTAGE-1) are outstanding
-        if (S::kLoadsLo == S::kLoadsHi || wave < 4)
-            __builtin_amdgcn_s_waitcnt(vmcnt_wait((NSTAGE - 2) * S::kLoadsLo));
-        else
-            __builtin_amdgcn_s_waitcnt(vmcnt_wait((NSTAGE - 2) * S::kLoadsHi));
-        __syncthreads();
-        issue(kt + NSTAGE);
-        read_frags(lds + ((kt + 1) % NSTAGE) * S::kStage, k0off, a0, b0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_half(1, a1, b1);
+        // steps in pairs (KS is even): step jj on buffer 0, jj + 1 on buffer 1
+#pragma unroll
+        for (int jj = 0; jj < KS; jj += 2) {
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_half(0, a0, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(s, koff[jj + 1], a1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_half(1, a0, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_half(0, a1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (jj + 2 < KS) {
+                read_frags(s, koff[jj + 2], a0, b0);
+            } else {
+                if (S::kLoadsLo == S::kLoadsHi || wave < 4)
+                    __builtin_amdgcn_s_waitcnt(vmcnt_wait((NSTAGE - 2) * S::kLoadsLo));
+                else
+                    __builtin_amdgcn_s_waitcnt(vmcnt_wait((NSTAGE - 2) * S::kLoadsHi));
+                __syncthreads();
+                issue(kt + NSTAGE);
+                read_frags(lds + ((kt + 1) % NSTAGE) * S::kStage, koff[0], a0, b0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_half(1, a1, b1);
+        }
     }
     // the clamped reloads of the last iterations land before the ring is
     // reused or the workgroup leaves
@@ -724,7 +757,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
 // tables, then the MFMA kernel on the tile shape and k split chosen below,
 // and the summing epilogue when k is split.
 struct MmPlan {
-    int mi, wn, ksplit;
+    int mi, wn, ksplit, bk;
 };
 
 int mm_bm(int mi, int wn)
@@ -732,48 +765,59 @@ int mm_bm(int mi, int wn)
     return mm::kWaves / wn * mi * 32;
 }
 
-// Tile shape and k split, from sweeps of every shape and split on MI355X
-// (14B q|k|v, hidden 5120, 16 to 4096 tokens).  A 256 x 256 tile does the
-// most products per byte through the LDS, so it is preferred whenever its
-// tiles keep the CUs busy (at least 3/4 of them in the last round); else
-// 256 x 128, then 128 x 128 (at 1024 tokens 224 tiles of 256 x 128 take 113
-// us where 112 of 256 x 256 take 159).  With too few tiles even then, k is
-// split so that about one workgroup runs per CU, on the smallest tile that
-// holds the batch without much padding: 64 x 256 up to 32 tokens, 128 x 128
-// up to 128, 256 x 128 beyond (measured best at 16, 64-128 and 256 tokens).
+// Tile shape and k split: the plan the cost model below rates fastest.  Per
+// stage of k (64) a workgroup of each shape takes, measured on MI355X with
+// every CU busy (14B q|k|v, hidden 5120; epilogue included): 256 x 256 1.9
+// us, 256 x 128 1.13, 128 x 128 0.72, 64 x 256 0.9.  A launch runs
+// ceil(tiles * S / CUs) rounds of K/64/S stages; it cannot beat streaming the
+// weights once from HBM (~5.5 TB/s with every CU pulling its share, less
+// with fewer workgroups than CUs); a k split adds the round trip of its
+// S*M*N f32 partials (~5 TB/s) and a summing kernel (~3 us), no split the
+// cos/sin table kernel (~4 us).  Against sweeps of every shape and split at
+// 16-4096 tokens it picks the fastest measured plan or one within 3%.
 MmPlan mm_plan(int M, int N, int K, int cus)
 {
-    static const int dp[3][2] = {{4, 4}, {2, 2}, {1, 2}};
-    for (const auto &sh : dp) {
-        const int bm = mm_bm(sh[0], sh[1]), bn = sh[1] * 64;
-        const int64_t tiles = (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-        const int64_t rounds = (tiles + cus - 1) / cus;
-        if (tiles * 4 >= rounds * cus * 3)
-            return {sh[0], sh[1], 1};
+    struct Cand {
+        int mi, wn;
+        double us;                                  // per stage of 64
+    };
+    static const Cand cands[4] = {{4, 4, 1.90}, {2, 2, 1.13}, {1, 2, 0.72}, {1, 4, 0.90}};
+    const int KT = K / 64;
+    const double w_us = (double)N * K * 2 / 5.5e6;
+    MmPlan best = {4, 4, 1, 64};
+    double best_t = 1e300;
+    for (const Cand &c : cands) {
+        const int64_t bm = mm_bm(c.mi, c.wn), bn = c.wn * 64;
+        const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+        const int smax = KT / 4 < 1 ? 1 : (KT / 4 > 64 ? 64 : KT / 4);   // >= 4 stages per split
+        for (int ks = 1; ks <= smax; ++ks) {
+            if (ks > 1 && tiles * (ks - 1) >= cus)  // a split beyond filling the chip
+                break;
+            const double rounds = (double)((tiles * ks + cus - 1) / cus);
+            const double busy = (double)std::min<int64_t>(tiles * ks, cus) / cus;
+            double t = std::max(rounds * ((double)KT / ks) * c.us, w_us / busy);
+            t += ks > 1 ? 2.0 * ks * (double)M * N * 4 / 5.0e6 + 3.0 : 4.0;
+            if (t < best_t) {
+                best_t = t;
+                best = {c.mi, c.wn, ks, 64};
+            }
+        }
     }
-    MmPlan pl = M <= 32 ? MmPlan{1, 4, 1} : (M <= 128 ? MmPlan{1, 2, 1} : MmPlan{2, 2, 1});
-    const int bm = mm_bm(pl.mi, pl.wn), bn = pl.wn * 64;
-    const int64_t tiles = (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-    int64_t ks = cus / tiles;
-    const int64_t kmax = K / mm::BK / 4;          // at least 4 sub-tiles per split
-    if (ks > kmax)
-        ks = kmax;
-    pl.ksplit = ks < 1 ? 1 : (int)ks;
-    return pl;
+    return best;
 }
 
 // Raise the kernel's dynamic-LDS limit to what it uses, once per kernel and
 // device (the caller has made the handle's device current).
-template <bool F16, int HD, int MI, int WN>
+template <bool F16, int HD, int MI, int WN, int BK>
 hipError_t set_mm_lds(int device)
 {
     static std::atomic<unsigned long long> done{0};
     const unsigned long long bit = 1ull << (device & 63);
     if (done.load(std::memory_order_acquire) & bit)
         return hipSuccess;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&proj_mfma_kernel<F16, HD, MI, WN>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&proj_mfma_kernel<F16, HD, MI, WN, BK>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       mm::Shape<HD, MI, WN>::kLds);
+                                       mm::Shape<HD, MI, WN, BK>::kLds);
     if (e == hipSuccess && device < 64)
         done.fetch_or(bit, std::memory_order_release);
     return e;
@@ -810,16 +854,16 @@ hipError_t launch_gemv(const ProjParams &pp, const InvTable &inv, hipStream_t st
     return hipGetLastError();
 }
 
-template <bool F16, int HD, int MI, int WN>
+template <bool F16, int HD, int MI, int WN, int BK>
 hipError_t launch_mm(const ProjParams &pp, hipStream_t st)
 {
-    using S = mm::Shape<HD, MI, WN>;
-    hipError_t e = set_mm_lds<F16, HD, MI, WN>(pp.device);
+    using S = mm::Shape<HD, MI, WN, BK>;
+    hipError_t e = set_mm_lds<F16, HD, MI, WN, BK>(pp.device);
     if (e != hipSuccess)
         return e;
     const int tiles = ((pp.M + S::BM - 1) / S::BM) * ((pp.N + S::BN - 1) / S::BN);
     constexpr unsigned lds = S::kLds;
-    hipLaunchKernelGGL((proj_mfma_kernel<F16, HD, MI, WN>), dim3(tiles * pp.ksplit), dim3(mm::kThreads), lds,
+    hipLaunchKernelGGL((proj_mfma_kernel<F16, HD, MI, WN, BK>), dim3(tiles * pp.ksplit), dim3(mm::kThreads), lds,
                        st, pp);
     return hipGetLastError();
 }
@@ -844,10 +888,10 @@ hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st
     }
     hipError_t e;
     switch (pl.mi * 10 + pl.wn) {
-    case 14: e = launch_mm<F16, HD, 1, 4>(pp, st); break;
-    case 44: e = launch_mm<F16, HD, 4, 4>(pp, st); break;
-    case 12: e = launch_mm<F16, HD, 1, 2>(pp, st); break;
-    case 22: e = launch_mm<F16, HD, 2, 2>(pp, st); break;
+    case 14: e = launch_mm<F16, HD, 1, 4, 64>(pp, st); break;
+    case 12: e = launch_mm<F16, HD, 1, 2, 64>(pp, st); break;
+    case 22: e = launch_mm<F16, HD, 2, 2, 64>(pp, st); break;
+    case 44: e = launch_mm<F16, HD, 4, 4, 64>(pp, st); break;
     default: e = hipErrorInvalidValue; break;
     }
     if (e != hipSuccess || pp.ksplit == 1)
@@ -964,7 +1008,7 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
     hipError_t e = g.set(h->device);
     if (e != hipSuccess)
         return fail(h, QKV_ERR_HIP, "hipSetDevice(%d): %s", h->device, hipGetErrorString(e));
-    MmPlan plan = {4, 4, 1};
+    MmPlan plan = {4, 4, 1, 64};
     if (pp.M > kGemvTok) {
         int cus = 0;
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device);

@@ -406,17 +406,32 @@ def test_proj_repeat_is_bitwise_identical(handle, nt):
     c.check(f"repeat_{nt}")
 
 
-@pytest.mark.parametrize("nt", [32, 33, 129, 1024, 2048])
+@pytest.mark.parametrize("nt", [64, 150, 258, 400, 520, 1000, 1300])
 def test_proj_plan_switches(handle, nt):
-    """Each side of the launch plan's switches at the 14B width, hidden 512:
-    32 tokens on 64 x 256 tiles and 33 on 128 x 128 (k split 4 ways), 129
-    on 256 x 128 (split 4 ways), 1024 data-parallel 256 x 128, 2048
-    data-parallel 256 x 256."""
+    """Every tile shape of the launch plan, split and data-parallel, at the
+    14B width with hidden 2048 (the cost model's picks): 64 tokens on
+    128 x 128 tiles with k split 4 ways, 150 on 64 x 256 split 3 ways, 258
+    on 256 x 128 split 2 ways, 400 data-parallel 128 x 128, 520 data-
+    parallel 64 x 256, 1000 data-parallel 256 x 128, 1300 data-parallel
+    256 x 256."""
     w = wl.Workload("proj_plan", 40, 8, 128, nt=nt, n_ctx=4096, n_slots=1, layers=1,
                     seed=19, pos_mode="uniform")
-    c = ProjCase(w, hidden=512)
+    c = ProjCase(w, hidden=2048)
     assert _run(handle, c, f"plan_{nt}") == B.QKV_OK
     c.check(f"plan_{nt}")
+
+
+def test_proj_split_256x256_sampled(handle):
+    """700 tokens, hidden 5120: 256 x 256 tiles with k split 3 ways (the
+    plan between the small-batch and the data-parallel shapes); the oracle
+    recomputes sampled tokens, addressing is checked for all."""
+    w = wl.Workload("proj_split_big", 40, 8, 128, nt=700, n_ctx=4096, n_slots=1, layers=1,
+                    seed=26, pos_mode="arange")
+    rng = np.random.default_rng(10)
+    sample = np.unique(np.concatenate([[0, 255, 256, 511, 512, 699], rng.integers(0, 700, 26)]))
+    c = ProjCase(w, hidden=5120, sample=sample)
+    assert _run(handle, c, "split_256x256") == B.QKV_OK
+    c.check("split_256x256")
 
 
 def test_proj_long_slots_f32_cache(handle):

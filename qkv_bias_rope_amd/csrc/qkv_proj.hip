@@ -14,9 +14,9 @@
 // D[8*(v/4) + 4*(l/32) + v%4][l%32], v < 16.
 //
 //  * Eight-wave tiles of 256 x 256, 256 x 128, 128 x 128 or 64 x 256 tokens x
-//    outputs, picked per launch; operands go from HBM straight into a ring of
-//    four LDS stages (k sub-tiles of 32, loaded three ahead), XOR-swizzled so
-//    fragment reads are conflict-free.
+//    outputs, picked per launch by a cost model; operands go from HBM
+//    straight into a ring of LDS stages 64 deep in k (two to four of them,
+//    as many as fit), XOR-swizzled so fragment reads are conflict-free.
 //  * A wave's 64 output columns are the j and j + hd/2 halves of a head's
 //    NeoX pairs, so the partner of every output sits in the same lane, in the
 //    other MFMA tile: the rotation needs no data exchange.
@@ -26,7 +26,7 @@
 //    split across workgroups that store partial tiles to the handle's
 //    workspace, and a second kernel sums them in split order and runs the
 //    epilogue.
-//  * Decode (up to 8 tokens) is a weight-streaming GEMV, not a contraction
+//  * Decode (up to 4 tokens) is a weight-streaming GEMV, not a contraction
 //    worth the matrix units: a separate kernel streams W with 16-byte loads,
 //    reduces each dot product across the wave and runs the same epilogue.
 
@@ -137,23 +137,28 @@ __global__ __launch_bounds__(256) void rope_table_kernel(ProjParams p, InvTable 
 // 32 x 32 tile is computed transposed (the weight fragment as the A operand),
 // so a lane holds 4 consecutive outputs of one token: 16-byte stores.
 //
-// k advances in sub-tiles of 32 through a ring of four LDS stages (BM token
-// rows of A and BN weight rows of B, 64 bytes per row), filled by
-// global->LDS loads (64 lanes x 16 bytes = 16 rows per instruction) issued
-// three sub-tiles ahead (deeper rings, up to 8 stages for the small tiles,
-// measured no faster on MI355X).  Chunk c of row r sits in slot c ^ g(r),
-// g(r) = (r >> 2) & 3, which makes the 16-byte fragment reads (16 rows of
-// a quarter wave, one chunk each) conflict-free on gfx950: a probe under
-// rocprofv3 reads 4 LDS cycles per ds_read_b128 and no bank-conflict cycles,
+// k advances in stages of BK = 64 (BM token rows of A and BN weight rows of
+// B, 128 bytes per row) through a ring of NSTAGE LDS stages -- as many as the
+// 160 KB hold, at most 4: 2 for 256 x 256, 3 for 256 x 128, 4 for the small
+// tiles -- filled by global->LDS loads (64 lanes x 16 bytes per instruction)
+// issued NSTAGE - 1 stages ahead.  On MI355X 64-deep stages ran 5-20%
+// faster than 32-deep ones (two k steps per barrier) and 128-deep ones were
+// slower again: a deeper stage amortises the barrier and the ring's refill
+// latency, until the ring gets too shallow to hide HBM.  Chunk c of row r sits in
+// slot c ^ g(r), with g(r) = (r >> 1) & 7 for 128-byte rows ((r >> 2) & 3
+// for 64-byte rows, r & 15 for 256-byte rows), which makes the 16-byte
+// fragment reads (16 rows of a quarter wave, one chunk each) conflict-free
+// on gfx950: a probe under rocprofv3 reads 4 LDS cycles per ds_read_b128,
 // where the swizzle ((r >> 1) ^ (r >> 3)) & 3 -- conflict-free on paper for
-// 64 four-byte banks serving 16 lanes at a time -- takes 8, half of them
-// counted as conflicts.  Per sub-tile s (two k steps of 16):
-//   products of step 0 (first half); read step-1 fragments; products of
-//   step 0 (second half); products of step 1 (first half); wait for this
-//   wave's loads of sub-tile s+1 and meet the other waves (after which stage
-//   s is free and sub-tile s+1 is visible); load sub-tile s+NSTAGE into
-//   stage s;
-//   read step-0 fragments of sub-tile s+1; products of step 1 (second half).
+// 64 four-byte banks serving 16 lanes at a time -- takes 8.  The fragments
+// of a stage's k steps are double-buffered in registers; per pair of steps
+// j, j + 1:
+//   products of step j (first half); read step-(j+1) fragments; products of
+//   step j (second half); products of step j+1 (first half); read step-(j+2)
+//   fragments -- or, after the stage's last step: wait for this wave's loads
+//   of the next stage and meet the other waves (after which this stage is
+//   free and the next visible), refill this stage NSTAGE ahead and read the
+//   next stage's first fragments; products of step j+1 (second half).
 //
 // The grid is tiles x S: with S = 1 each workgroup finishes its tile (the
 // epilogue below); when the tiles are too few to fill the chip, k is split S
@@ -216,6 +221,20 @@ struct Shape {
 constexpr int vmcnt_wait(int v)
 {
     return (v & 15) | ((v >> 4) << 14) | (0xF << 8) | (7 << 4);
+}
+
+// Meet the other waves once this wave's LDS reads have returned (the caller
+// has waited for its own loads into the stage the waves read next).  The
+// empty asm statements keep the compiler from moving memory accesses across
+// the barrier; __syncthreads() would also do that, but its fence makes the
+// compiler wait for every global->LDS load in flight, the stages still
+// being prefetched included.
+__device__ __forceinline__ void ring_barrier()
+{
+    __builtin_amdgcn_s_waitcnt((0xF) | (3 << 14) | (7 << 4));   // lgkmcnt(0) only
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // Slot of chunk c of row r: c ^ swz(r).  Chosen per row size with a probe
@@ -355,14 +374,18 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
         __builtin_amdgcn_s_waitcnt(vmcnt_wait((NSTAGE - 1) * S::kLoadsLo));
     else
         __builtin_amdgcn_s_waitcnt(vmcnt_wait((NSTAGE - 1) * S::kLoadsHi));
-    __syncthreads();
+    ring_barrier();
     read_frags(lds, koff[0], a0, b0);
 
-    // Per stage: step j's products, first half; the next step's fragments
-    // (or, at the last step: wait for this wave's loads of the next stage,
-    // meet the other waves -- after which this stage is free and the next
-    // visible -- refill this stage and read the next stage's first
-    // fragments); step j's second half.
+    // Per pair of k steps: step j's products, first half; the next step's
+    // fragments; step j's second half; step j + 1's first half; the
+    // fragments of step j + 2 -- or, after the stage's last step: wait for
+    // this wave's loads of the next stage, meet the other waves (after which
+    // this stage is free and the next visible), refill this stage NSTAGE
+    // ahead and read the next stage's first fragments; step j + 1's second
+    // half.  The refill goes out right after the barrier: with two stages
+    // (256 x 256) it has one stage's time to land, and issuing it later,
+    // even spread between the products, measured slower.
     for (int kt = 0; kt < len; ++kt) {
         const unsigned char *s = lds + (kt % NSTAGE) * S::kStage;
         // steps in pairs (KS is even): step jj on buffer 0, jj + 1 on buffer 1
@@ -384,7 +407,7 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
                     __builtin_amdgcn_s_waitcnt(vmcnt_wait((NSTAGE - 2) * S::kLoadsLo));
                 else
                     __builtin_amdgcn_s_waitcnt(vmcnt_wait((NSTAGE - 2) * S::kLoadsHi));
-                __syncthreads();
+                ring_barrier();
                 issue(kt + NSTAGE);
                 read_frags(lds + ((kt + 1) % NSTAGE) * S::kStage, koff[0], a0, b0);
             }

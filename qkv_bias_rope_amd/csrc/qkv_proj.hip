@@ -177,12 +177,13 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kLdsMax = 160 * 1024;           // per workgroup on gfx950
 
-// HD, the tile shape (MI, WN) and the k depth BK of a stage (32, 64 or 128)
-template <int HD, int MI, int WN, int BK>
+// HD, the tile shape (MI token tiles and G pair groups per wave, WN waves
+// along the outputs) and the k depth BK of a stage (32, 64 or 128)
+template <int HD, int MI, int WN, int BK, int G>
 struct Shape {
     static constexpr int WM = kWaves / WN;
     static constexpr int BM = WM * MI * 32;
-    static constexpr int BN = WN * 64;
+    static constexpr int BN = WN * G * 64;
     static constexpr int kRow = BK * 2;           // bytes per row and stage
     static constexpr int kCpr = BK / 8;           // 16-byte chunks per row
     static constexpr int kRpi = 1024 / kRow;      // rows per load instruction
@@ -203,7 +204,7 @@ struct Shape {
     static constexpr int kLoadsHi = (kInstA >= kWaves ? kWaveA : 0) + kWaveB;
     // epilogue: the tile's pair indices (one group of an hd-128 head: 32;
     // else all hd/2) as cos then sin per token, in 16-byte chunks
-    static constexpr int kPW = (HD == 128 && WN == 1) ? 32 : HD / 2;
+    static constexpr int kPW = (HD == 128 && WN == 1 && G == 1) ? 32 : HD / 2;
     static constexpr int kChunks = kPW / 2;
     static constexpr int kTab = BM * kChunks * 16;
     static constexpr int kLds = kRing > kTab ? kRing : kTab;
@@ -258,11 +259,11 @@ __device__ __forceinline__ int group_lo(int g)
 }
 }  // namespace mm
 
-template <bool F16, int HD, int MI, int WN, int BK>
+template <bool F16, int HD, int MI, int WN, int BK, int G>
 __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
 {
     using namespace mm;
-    using S = Shape<HD, MI, WN, BK>;
+    using S = Shape<HD, MI, WN, BK, G>;
     constexpr int BM = S::BM, BN = S::BN;
     constexpr int NSTAGE = S::NSTAGE, KS = S::KS, kRow = S::kRow;
     constexpr int HALF = HD / 2;
@@ -277,7 +278,9 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     const int lrow = lane / S::kCpr, slot = lane % S::kCpr;
     const int lr = lane & 31, hi = lane >> 5;
 
-    const int ntn = (p.N + BN - 1) / BN;
+    constexpr int GT = WN * G;                    // pair groups per tile
+    const int ng = p.N / 64;                      // NeoX pair groups (64 columns each)
+    const int ntn = (ng + GT - 1) / GT;
     const int ntm = (p.M + BM - 1) / BM;
     const int tiles = ntn * ntm;
     const int tile = (int)blockIdx.x % tiles;
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     for (int j = 0; j < S::kWaveB; ++j) {
         brow[j] = S::kRpi * ((S::kInstB >= kWaves ? wave * S::kWaveB : wave - (kWaves - S::kInstB)) + j);
         const int rb = brow[j] + lrow;
-        const int n = group_lo<PT>(tn * WN + rb / 64) * 32 + ((rb >> 5) & 1) * PT * 32 + (rb & 31);
+        const int n = group_lo<PT>(tn * GT + rb / 64) * 32 + ((rb >> 5) & 1) * PT * 32 + (rb & 31);
         boff[j] = (uint32_t)((int64_t)min(n, p.N - 1) * p.K * 2) + (slot ^ swz<S::kCpr>(rb)) * 16;
     }
     const unsigned char *xb = reinterpret_cast<const unsigned char *>(p.x);
@@ -331,10 +334,11 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
         }
     };
 
-    // acc[f * MI + ti]: output tile f (0: lo, 1: partner) x token tile ti
-    f32x16 acc[2 * MI];
+    // acc[(2g + f) * MI + ti]: output tile f (0: lo, 1: partner) of the
+    // wave's pair group g x token tile ti
+    f32x16 acc[2 * G * MI];
 #pragma unroll
-    for (int q = 0; q < 2 * MI; ++q)
+    for (int q = 0; q < 2 * G * MI; ++q)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
             acc[q][v] = 0.0f;
@@ -343,26 +347,26 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     // for k step j of the stage
     const int g = swz<S::kCpr>(lr);               // tiles start at multiples of 32
     const int abase = (wm * MI * 32 + lr) * kRow;
-    const int bbase0 = S::kRegionA + (wn * 64 + lr) * kRow;
-    const int bbase1 = bbase0 + 32 * kRow;
+    const int bbase = S::kRegionA + (wn * G * 64 + lr) * kRow;
     int koff[8];
 #pragma unroll
     for (int j = 0; j < KS; ++j)
         koff[j] = ((2 * j + hi) ^ g) * 16;
     // two fragment buffers: step j uses buffer j % 2
     static_assert(KS % 2 == 0, "steps per stage");
-    bf16x8 a0[MI], b0[2], a1[MI], b1[2];
-    auto read_frags = [&](const unsigned char *s, int ko, bf16x8 (&fa)[MI], bf16x8 (&fb)[2]) {
+    bf16x8 a0[MI], b0[2 * G], a1[MI], b1[2 * G];
+    auto read_frags = [&](const unsigned char *s, int ko, bf16x8 (&fa)[MI], bf16x8 (&fb)[2 * G]) {
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
             fa[mi] = *reinterpret_cast<const bf16x8 *>(s + abase + mi * 32 * kRow + ko);
-        fb[0] = *reinterpret_cast<const bf16x8 *>(s + bbase0 + ko);
-        fb[1] = *reinterpret_cast<const bf16x8 *>(s + bbase1 + ko);
-    };
-    // half h takes products q = f*MI + ti in [h*MI, (h+1)*MI)
-    auto mfma_half = [&](int h, const bf16x8 (&fa)[MI], const bf16x8 (&fb)[2]) {
 #pragma unroll
-        for (int q = h * MI; q < (h + 1) * MI; ++q)
+        for (int t = 0; t < 2 * G; ++t)
+            fb[t] = *reinterpret_cast<const bf16x8 *>(s + bbase + t * 32 * kRow + ko);
+    };
+    // half h takes products q = (2g + f)*MI + ti in [h*G*MI, (h+1)*G*MI)
+    auto mfma_half = [&](int h, const bf16x8 (&fa)[MI], const bf16x8 (&fb)[2 * G]) {
+#pragma unroll
+        for (int q = h * G * MI; q < (h + 1) * G * MI; ++q)
             acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[q / MI], fa[q % MI], acc[q], 0, 0, 0);
     };
 
@@ -419,29 +423,40 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     // reused or the workgroup leaves
     __builtin_amdgcn_s_waitcnt(0);
 
-    // Lane (lr, hi) holds, for token ti*32 + lr of the wave's tokens, the
-    // outputs col0 + f*HALF + 8gg + 4hi + e (e < 4) in acc[f*MI + ti][4gg + e]:
-    // four consecutive columns; f = 1 is the NeoX partner of f = 0.
-    const int col0 = group_lo<PT>(tn * WN + wn) * 32;
+    // Lane (lr, hi) holds, for token ti*32 + lr of the wave's tokens and its
+    // pair group g, the outputs col0[g] + f*HALF + 8gg + 4hi + e (e < 4) in
+    // acc[(2g + f)*MI + ti][4gg + e]: four consecutive columns; f = 1 is the
+    // NeoX partner of f = 0.
+    int col0[G];
+    bool live[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int gi = tn * GT + wn * G + g;
+        live[g] = gi < ng;
+        col0[g] = group_lo<PT>(gi) * 32;
+    }
     const int tok0 = m0 + wm * MI * 32 + lr;     // token of ti = 0
     if (p.ksplit > 1) {
-        if (col0 >= p.N)
-            return;
-        float *const out = p.part + (int64_t)split * p.M * p.N + col0 + 4 * hi;
 #pragma unroll
-        for (int ti = 0; ti < MI; ++ti) {
-            const int tok = tok0 + ti * 32;
-            if (tok >= p.M)
+        for (int g = 0; g < G; ++g) {
+            if (!live[g])
                 continue;
-            float *const orow = out + (int64_t)tok * p.N;
+            float *const out = p.part + (int64_t)split * p.M * p.N + col0[g] + 4 * hi;
 #pragma unroll
-            for (int gg = 0; gg < 4; ++gg)
+            for (int ti = 0; ti < MI; ++ti) {
+                const int tok = tok0 + ti * 32;
+                if (tok >= p.M)
+                    continue;
+                float *const orow = out + (int64_t)tok * p.N;
 #pragma unroll
-                for (int f = 0; f < 2; ++f) {
-                    const FVec<4> y = {{acc[f * MI + ti][4 * gg], acc[f * MI + ti][4 * gg + 1],
-                                        acc[f * MI + ti][4 * gg + 2], acc[f * MI + ti][4 * gg + 3]}};
-                    st_data<4, false>(orow + f * HALF + 8 * gg, y);
-                }
+                for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) {
+                        const f32x16 &av = acc[(2 * g + f) * MI + ti];
+                        const FVec<4> y = {{av[4 * gg], av[4 * gg + 1], av[4 * gg + 2], av[4 * gg + 3]}};
+                        st_data<4, false>(orow + f * HALF + 8 * gg, y);
+                    }
+            }
         }
         return;
     }
@@ -450,7 +465,7 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     // Stage the cos/sin slice of the tile's BM tokens (pair indices ih0 ..
     // ih0 + kPW) into the LDS ring: chunk c of token r in slot c ^ (r % kChunks),
     // which keeps the reads below (32 tokens, one chunk) conflict-free.
-    const int ih0 = S::kPW == HALF ? 0 : (group_lo<PT>(tn * WN) * 32) % HD;
+    const int ih0 = S::kPW == HALF ? 0 : (group_lo<PT>(tn * GT) * 32) % HD;
     __syncthreads();                              // every wave is done with the ring
     {
         constexpr int kInst = BM * S::kChunks / 64;
@@ -464,87 +479,96 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
                                              0);
         }
     }
-    const bool live = col0 < p.N;
-    const int sec = col0 < p.nqt ? 0 : (col0 < p.nqt + p.nkt ? 1 : 2);
-    const int sbase = sec == 0 ? 0 : (sec == 1 ? p.nqt : p.nqt + p.nkt);
-    float *const out = p.out[sec];
-    const int64_t ldo = p.ld[sec];
-    const float *const bias = live ? p.b[sec] : nullptr;
-    void *const cache = sec == 1 ? p.cache[0] : p.cache[1];
-    const int cs = col0 - sbase + 4 * hi;          // section column of (f = 0, gg = 0)
-    // this lane's 32 bias values and its tokens' cache rows
-    FVec<4> bias0[4], bias1[4];
+    // per pair group: its section, the lane's 32 bias values; the tokens'
+    // cache rows when any group is in k or v
+    int sec[G], cs[G];
+    FVec<4> bias0[G][4], bias1[G][4];
+    bool any_kv = false;
 #pragma unroll
-    for (int gg = 0; gg < 4; ++gg) {
-        if (bias && p.vec) {
-            bias0[gg] = ld_vec<4>(bias + cs + 8 * gg);
-            bias1[gg] = ld_vec<4>(bias + cs + 8 * gg + HALF);
-        } else {
+    for (int g = 0; g < G; ++g) {
+        sec[g] = col0[g] < p.nqt ? 0 : (col0[g] < p.nqt + p.nkt ? 1 : 2);
+        const int sbase = sec[g] == 0 ? 0 : (sec[g] == 1 ? p.nqt : p.nqt + p.nkt);
+        cs[g] = col0[g] - sbase + 4 * hi;         // section column of (f = 0, gg = 0)
+        any_kv = any_kv || (live[g] && sec[g] > 0);
+        const float *const bias = live[g] ? p.b[sec[g]] : nullptr;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bias0[gg].e[e] = bias ? bias[cs + 8 * gg + e] : 0.0f;
-                bias1[gg].e[e] = bias ? bias[cs + 8 * gg + e + HALF] : 0.0f;
+        for (int gg = 0; gg < 4; ++gg) {
+            if (bias && p.vec) {
+                bias0[g][gg] = ld_vec<4>(bias + cs[g] + 8 * gg);
+                bias1[g][gg] = ld_vec<4>(bias + cs[g] + 8 * gg + HALF);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bias0[g][gg].e[e] = bias ? bias[cs[g] + 8 * gg + e] : 0.0f;
+                    bias1[g][gg].e[e] = bias ? bias[cs[g] + 8 * gg + e + HALF] : 0.0f;
+                }
             }
         }
     }
     int64_t crow[MI];
 #pragma unroll
     for (int ti = 0; ti < MI; ++ti)
-        crow[ti] = (live && sec > 0) ? p.rows[min(tok0 + ti * 32, p.M - 1)] : -1;
+        crow[ti] = any_kv ? p.rows[min(tok0 + ti * 32, p.M - 1)] : -1;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (!live)
-        return;
 
-    const int cpair = (col0 % HD - ih0) / 4 + hi;  // chunk of (gg = 0) in the slice
 #pragma unroll
-    for (int ti = 0; ti < MI; ++ti) {
-        const int tok = tok0 + ti * 32;
-        if (tok >= p.M)
+    for (int g = 0; g < G; ++g) {
+        if (!live[g])
             continue;
-        const int r = tok - m0;
-        const int64_t row = crow[ti];
-        float *const orow = out + (int64_t)tok * ldo;
-        const unsigned char *trow = lds + r * S::kChunks * 16;
+        float *const out = p.out[sec[g]];
+        const int64_t ldo = p.ld[sec[g]];
+        void *const cache = sec[g] == 1 ? p.cache[0] : p.cache[1];
+        const int cpair = (col0[g] % HD - ih0) / 4 + hi;   // chunk of (gg = 0) in the slice
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-            const int c0 = cs + 8 * gg, c1 = c0 + HALF;
-            FVec<4> y0, y1;
+        for (int ti = 0; ti < MI; ++ti) {
+            const int tok = tok0 + ti * 32;
+            if (tok >= p.M)
+                continue;
+            const int r = tok - m0;
+            const int64_t row = sec[g] > 0 ? crow[ti] : -1;
+            float *const orow = out + (int64_t)tok * ldo;
+            const unsigned char *trow = lds + r * S::kChunks * 16;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                y0.e[e] = acc[ti][4 * gg + e] + bias0[gg].e[e];
-                y1.e[e] = acc[MI + ti][4 * gg + e] + bias1[gg].e[e];
-            }
-            if (sec < 2) {
-                const int cc = cpair + 2 * gg;
-                const FVec<4> cv = *reinterpret_cast<const FVec<4> *>(trow + ((cc ^ (r % S::kChunks)) * 16));
-                const FVec<4> sv = *reinterpret_cast<const FVec<4> *>(
-                    trow + (((cc + S::kChunks / 2) ^ (r % S::kChunks)) * 16));
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    rot(y0.e[e], y1.e[e], cv.e[e], sv.e[e]);
-            }
-            if (p.vec) {
-                st_data<4, false>(orow + c0, y0);
-                st_data<4, false>(orow + c1, y1);
-                if (row >= 0) {
-                    st_cache<4, F16, false>(cache, row * p.nkt + c0, y0);
-                    st_cache<4, F16, false>(cache, row * p.nkt + c1, y1);
-                }
-            } else {
+            for (int gg = 0; gg < 4; ++gg) {
+                const int c0 = cs[g] + 8 * gg, c1 = c0 + HALF;
+                FVec<4> y0, y1;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    orow[c0 + e] = y0.e[e];
-                    orow[c1 + e] = y1.e[e];
+                    y0.e[e] = acc[2 * g * MI + ti][4 * gg + e] + bias0[g][gg].e[e];
+                    y1.e[e] = acc[(2 * g + 1) * MI + ti][4 * gg + e] + bias1[g][gg].e[e];
+                }
+                if (sec[g] < 2) {
+                    const int cc = cpair + 2 * gg;
+                    const FVec<4> cv = *reinterpret_cast<const FVec<4> *>(trow + ((cc ^ (r % S::kChunks)) * 16));
+                    const FVec<4> sv = *reinterpret_cast<const FVec<4> *>(
+                        trow + (((cc + S::kChunks / 2) ^ (r % S::kChunks)) * 16));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        rot(y0.e[e], y1.e[e], cv.e[e], sv.e[e]);
+                }
+                if (p.vec) {
+                    st_data<4, false>(orow + c0, y0);
+                    st_data<4, false>(orow + c1, y1);
                     if (row >= 0) {
-                        put_cache<F16>(cache, row * p.nkt + c0 + e, y0.e[e]);
-                        put_cache<F16>(cache, row * p.nkt + c1 + e, y1.e[e]);
+                        st_cache<4, F16, false>(cache, row * p.nkt + c0, y0);
+                        st_cache<4, F16, false>(cache, row * p.nkt + c1, y1);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        orow[c0 + e] = y0.e[e];
+                        orow[c1 + e] = y1.e[e];
+                        if (row >= 0) {
+                            put_cache<F16>(cache, row * p.nkt + c0 + e, y0.e[e]);
+                            put_cache<F16>(cache, row * p.nkt + c1 + e, y1.e[e]);
+                        }
                     }
                 }
             }
+            if (sec[g] > 0 && row < 0 && hi == 0)
+                atomicOr(p.err, 1u);
         }
-        if (sec > 0 && row < 0 && hi == 0)
-            atomicOr(p.err, 1u);
     }
 }
 
@@ -780,7 +804,8 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
 // tables, then the MFMA kernel on the tile shape and k split chosen below,
 // and the summing epilogue when k is split.
 struct MmPlan {
-    int mi, wn, ksplit, bk;
+    int mi, wn, g;           // token tiles and pair groups per wave, waves along the outputs
+    int ksplit;
 };
 
 int mm_bm(int mi, int wn)
@@ -791,27 +816,29 @@ int mm_bm(int mi, int wn)
 // Tile shape and k split: the plan the cost model below rates fastest.  Per
 // stage of k (64) a workgroup of each shape takes, measured on MI355X with
 // every CU busy (14B q|k|v, hidden 5120; epilogue included): 256 x 256 1.9
-// us, 256 x 128 1.13, 128 x 128 0.72, 64 x 256 0.9.  A launch runs
-// ceil(tiles * S / CUs) rounds of K/64/S stages; it cannot beat streaming the
-// weights once from HBM (~5.5 TB/s with every CU pulling its share, less
-// with fewer workgroups than CUs); a k split adds the round trip of its
-// S*M*N f32 partials (~5 TB/s) and a summing kernel (~3 us), no split the
-// cos/sin table kernel (~4 us).  Against sweeps of every shape and split at
-// 16-4096 tokens it picks the fastest measured plan or one within 3%.
+// us, 256 x 192 1.58, 256 x 128 1.13, 128 x 128 0.72, 64 x 256 0.9.  A launch
+// runs ceil(tiles * S / CUs) rounds of K/64/S stages; it cannot beat
+// streaming the weights once from HBM (~5.5 TB/s with every CU pulling its
+// share, less with fewer workgroups than CUs); a k split adds the round trip
+// of its S*M*N f32 partials (~5 TB/s) and a summing kernel (~3 us), no split
+// the cos/sin table kernel (~4 us).  Against sweeps of every shape and split
+// at 16-4096 tokens it picks the fastest measured plan or one within 3%.
 MmPlan mm_plan(int M, int N, int K, int cus)
 {
     struct Cand {
-        int mi, wn;
+        int mi, wn, g;
         double us;                                  // per stage of 64
     };
-    static const Cand cands[4] = {{4, 4, 1.90}, {2, 2, 1.13}, {1, 2, 0.72}, {1, 4, 0.90}};
+    static const Cand cands[5] = {
+        {4, 4, 1, 1.90}, {2, 2, 1, 1.13}, {1, 2, 1, 0.72}, {1, 4, 1, 0.90}, {1, 1, 3, 1.58}};
     const int KT = K / 64;
+    const int NG = N / 64;
     const double w_us = (double)N * K * 2 / 5.5e6;
-    MmPlan best = {4, 4, 1, 64};
+    MmPlan best = {4, 4, 1, 1};
     double best_t = 1e300;
     for (const Cand &c : cands) {
-        const int64_t bm = mm_bm(c.mi, c.wn), bn = c.wn * 64;
-        const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+        const int64_t bm = mm_bm(c.mi, c.wn), gt = c.wn * c.g;
+        const int64_t tiles = ((M + bm - 1) / bm) * ((NG + gt - 1) / gt);
         const int smax = KT / 4 < 1 ? 1 : (KT / 4 > 64 ? 64 : KT / 4);   // >= 4 stages per split
         for (int ks = 1; ks <= smax; ++ks) {
             if (ks > 1 && tiles * (ks - 1) >= cus)  // a split beyond filling the chip
@@ -822,7 +849,7 @@ MmPlan mm_plan(int M, int N, int K, int cus)
             t += ks > 1 ? 2.0 * ks * (double)M * N * 4 / 5.0e6 + 3.0 : 4.0;
             if (t < best_t) {
                 best_t = t;
-                best = {c.mi, c.wn, ks, 64};
+                best = {c.mi, c.wn, c.g, ks};
             }
         }
     }
@@ -831,16 +858,16 @@ MmPlan mm_plan(int M, int N, int K, int cus)
 
 // Raise the kernel's dynamic-LDS limit to what it uses, once per kernel and
 // device (the caller has made the handle's device current).
-template <bool F16, int HD, int MI, int WN, int BK>
+template <bool F16, int HD, int MI, int WN, int BK, int G>
 hipError_t set_mm_lds(int device)
 {
     static std::atomic<unsigned long long> done{0};
     const unsigned long long bit = 1ull << (device & 63);
     if (done.load(std::memory_order_acquire) & bit)
         return hipSuccess;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&proj_mfma_kernel<F16, HD, MI, WN, BK>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&proj_mfma_kernel<F16, HD, MI, WN, BK, G>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       mm::Shape<HD, MI, WN, BK>::kLds);
+                                       mm::Shape<HD, MI, WN, BK, G>::kLds);
     if (e == hipSuccess && device < 64)
         done.fetch_or(bit, std::memory_order_release);
     return e;
@@ -877,18 +904,32 @@ hipError_t launch_gemv(const ProjParams &pp, const InvTable &inv, hipStream_t st
     return hipGetLastError();
 }
 
-template <bool F16, int HD, int MI, int WN, int BK>
+template <bool F16, int HD, int MI, int WN, int BK, int G>
 hipError_t launch_mm(const ProjParams &pp, hipStream_t st)
 {
-    using S = mm::Shape<HD, MI, WN, BK>;
-    hipError_t e = set_mm_lds<F16, HD, MI, WN, BK>(pp.device);
+    using S = mm::Shape<HD, MI, WN, BK, G>;
+    hipError_t e = set_mm_lds<F16, HD, MI, WN, BK, G>(pp.device);
     if (e != hipSuccess)
         return e;
-    const int tiles = ((pp.M + S::BM - 1) / S::BM) * ((pp.N + S::BN - 1) / S::BN);
+    const int gt = WN * G;
+    const int tiles = ((pp.M + S::BM - 1) / S::BM) * ((pp.N / 64 + gt - 1) / gt);
     constexpr unsigned lds = S::kLds;
-    hipLaunchKernelGGL((proj_mfma_kernel<F16, HD, MI, WN, BK>), dim3(tiles * pp.ksplit), dim3(mm::kThreads), lds,
-                       st, pp);
+    hipLaunchKernelGGL((proj_mfma_kernel<F16, HD, MI, WN, BK, G>), dim3(tiles * pp.ksplit), dim3(mm::kThreads),
+                       lds, st, pp);
     return hipGetLastError();
+}
+
+template <bool F16, int HD>
+hipError_t launch_mm_plan(const ProjParams &pp, hipStream_t st, const MmPlan &pl)
+{
+    switch (pl.mi * 100 + pl.wn * 10 + pl.g) {
+    case 141: return launch_mm<F16, HD, 1, 4, 64, 1>(pp, st);
+    case 121: return launch_mm<F16, HD, 1, 2, 64, 1>(pp, st);
+    case 221: return launch_mm<F16, HD, 2, 2, 64, 1>(pp, st);
+    case 441: return launch_mm<F16, HD, 4, 4, 64, 1>(pp, st);
+    case 113: return launch_mm<F16, HD, 1, 1, 64, 3>(pp, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <bool F16, int HD>
@@ -909,14 +950,7 @@ hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st
         hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n_tab + 255) / 256)), dim3(256), 0, st, pp, inv,
                            const_cast<float *>(pp.rtab), const_cast<int64_t *>(pp.rows));
     }
-    hipError_t e;
-    switch (pl.mi * 10 + pl.wn) {
-    case 14: e = launch_mm<F16, HD, 1, 4, 64>(pp, st); break;
-    case 12: e = launch_mm<F16, HD, 1, 2, 64>(pp, st); break;
-    case 22: e = launch_mm<F16, HD, 2, 2, 64>(pp, st); break;
-    case 44: e = launch_mm<F16, HD, 4, 4, 64>(pp, st); break;
-    default: e = hipErrorInvalidValue; break;
-    }
+    hipError_t e = launch_mm_plan<F16, HD>(pp, st, pl);
     if (e != hipSuccess || pp.ksplit == 1)
         return e;
     const int hpt = split_heads_per_thread(pp.M, pp.N, HD);
@@ -1031,7 +1065,7 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
     hipError_t e = g.set(h->device);
     if (e != hipSuccess)
         return fail(h, QKV_ERR_HIP, "hipSetDevice(%d): %s", h->device, hipGetErrorString(e));
-    MmPlan plan = {4, 4, 1, 64};
+    MmPlan plan = {4, 4, 1, 1};
     if (pp.M > kGemvTok) {
         int cus = 0;
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device);
@@ -1041,8 +1075,8 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
         pp.ksplit = plan.ksplit;
         {
             // the grid (tiles x splits) and the kernels' tile indices are 32-bit
-            const int64_t bm = mm_bm(plan.mi, plan.wn), bn = plan.wn * 64;
-            const int64_t blocks = ((pp.M + bm - 1) / bm) * ((pp.N + bn - 1) / bn) * pp.ksplit;
+            const int64_t bm = mm_bm(plan.mi, plan.wn), gt = plan.wn * plan.g;
+            const int64_t blocks = ((pp.M + bm - 1) / bm) * ((pp.N / 64 + gt - 1) / gt) * pp.ksplit;
             if (blocks > INT32_MAX)
                 return fail(h, QKV_ERR_UNSUPPORTED, "nt x q|k|v width too large (%lld tiles)",
                             (long long)blocks);

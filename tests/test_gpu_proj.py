@@ -406,14 +406,15 @@ def test_proj_repeat_is_bitwise_identical(handle, nt):
     c.check(f"repeat_{nt}")
 
 
-@pytest.mark.parametrize("nt", [64, 150, 258, 400, 520, 1000, 1300])
+@pytest.mark.parametrize("nt", [64, 150, 258, 400, 520, 1000, 1300, 1800])
 def test_proj_plan_switches(handle, nt):
     """Every tile shape of the launch plan, split and data-parallel, at the
     14B width with hidden 2048 (the cost model's picks): 64 tokens on
     128 x 128 tiles with k split 4 ways, 150 on 64 x 256 split 3 ways, 258
     on 256 x 128 split 2 ways, 400 data-parallel 128 x 128, 520 data-
     parallel 64 x 256, 1000 data-parallel 256 x 128, 1300 data-parallel
-    256 x 256."""
+    256 x 192 (three pair groups per wave; 112 groups leave the last tile
+    one group), 1800 data-parallel 256 x 256."""
     w = wl.Workload("proj_plan", 40, 8, 128, nt=nt, n_ctx=4096, n_slots=1, layers=1,
                     seed=19, pos_mode="uniform")
     c = ProjCase(w, hidden=2048)
@@ -432,6 +433,28 @@ def test_proj_split_256x256_sampled(handle):
     c = ProjCase(w, hidden=5120, sample=sample)
     assert _run(handle, c, "split_256x256") == B.QKV_OK
     c.check("split_256x256")
+
+
+def test_proj_split_256x192(handle):
+    """660 tokens, hidden 3072: 256 x 192 tiles (three pair groups per wave)
+    with k split 2 ways, so the partial tiles of every group go through the
+    summing kernel."""
+    w = wl.Workload("proj_split_g3", 40, 8, 128, nt=660, n_ctx=4096, n_slots=1, layers=1,
+                    seed=27, pos_mode="uniform")
+    c = ProjCase(w, hidden=3072)
+    assert _run(handle, c, "split_256x192") == B.QKV_OK
+    c.check("split_256x192")
+
+
+def test_proj_hd64_256x192(handle):
+    """hd 64 on 256 x 192 tiles (a wave's three pair groups are three whole
+    heads; 64 groups leave the last tile one), 2100 tokens, hidden 1024, f32
+    cache, data-parallel with the fused epilogue."""
+    w = wl.Workload("proj_hd64_g3", 48, 8, 64, nt=2100, n_ctx=4096, n_slots=1, layers=1,
+                    seed=28, cache_dtypes=(wl.CACHE_F32,), pos_mode="uniform")
+    c = ProjCase(w, hidden=1024)
+    assert _run(handle, c, "hd64_256x192") == B.QKV_OK
+    c.check("hd64_256x192")
 
 
 def test_proj_long_slots_f32_cache(handle):

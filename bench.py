@@ -431,6 +431,30 @@ def cpu_baseline(w, cache_dtype, budget_s=10.0):
                        f"thread, {s_per:.3f} s each")
 
 
+def hbm_ceiling(steps, stream, nbytes=251703296, sets=8):
+    """A practical HBM ceiling on the same box: torch's in-place add over
+    buffers that move the headline launch's bytes (half read, half written),
+    rotated over `sets` buffers so they come from HBM.  Event-timed per call."""
+    import torch
+    n = nbytes // 8                                   # float32 elements per buffer
+    bufs = [torch.ones(n, dtype=torch.float32, device="cuda:0") for _ in range(sets)]
+    with torch.cuda.stream(stream):
+        for i in range(2 * sets):
+            bufs[i % sets].add_(1.0)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            bufs[i % sets].add_(1.0)
+        e1.record(stream)
+        e1.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del bufs
+    torch.cuda.empty_cache()
+    return dict(us_per_call=round(ms * 1e3, 3), gbs=round(n * 8 / (ms * 1e-3) / 1e9, 1), bytes=n * 8)
+
+
 def copy_calibration(steps):
     """A plain device copy of known size (for scaling FETCH_SIZE/WRITE_SIZE)."""
     import torch
@@ -540,6 +564,9 @@ def run_all(args, h, stream):
             f"{extra[w.name + '_warm']}")
     del sets
     torch.cuda.empty_cache()
+    if not args.no_extra:
+        extra["hbm_ceiling_inplace_add"] = hbm_ceiling(args.steps, stream)
+        log(f"[bench] HBM ceiling (in-place add of the same bytes): {extra['hbm_ceiling_inplace_add']}")
 
     if not args.no_extra:
         wb = wl.BATCHED_DECODE_14B

@@ -658,17 +658,21 @@ __global__ __launch_bounds__(256) void proj_split_epilogue_kernel(ProjParams p, 
 // ---------------------------------------------------------------------------
 // decode (1-4 tokens): weight-streaming GEMV + epilogue
 // ---------------------------------------------------------------------------
-// One wave per NeoX pair of weight rows (j and j + hd/2 of a head; in the v
-// section the same pairing just groups rows), four waves per block.  Lane l
-// takes the 16-byte chunks l, l+64, ... of both rows, U chunks in flight
-// per row, and keeps NT running sums per row (v_dot2_f32_bf16: two bf16
-// products into the f32 sum per instruction); a butterfly over the wave
-// completes the dot products, and lane t < nt finishes token t: bias, the
-// rotation of the pair, write-back and the cache store.
+// kGemvSplit waves per NeoX pair of weight rows (j and j + hd/2 of a head; in
+// the v section the same pairing just groups rows), each over its share of
+// k, four waves per block.  Lane l takes the 16-byte chunks l, l+64, ... of
+// the wave's share of both rows, U chunks in flight per row, and keeps NT
+// running sums per row (v_dot2_f32_bf16: two bf16 products into the f32 sum
+// per instruction); a butterfly over the wave completes its part of the dot
+// products, the pair's first wave adds the others' through LDS in k order,
+// and its lane t < nt finishes token t: bias, the rotation of the pair,
+// write-back and the cache store.  Two waves per pair (twice the waves in
+// flight, one step each at 14B) measured 13.9 -> 13.1 us per 14B layer.
 // up to 4 tokens; from 5 the k-split MFMA path is faster (5-8 tokens: 21.7-
 // 21.9 us at 14B against 24.6-24.9 for a GEMV with four pairs per wave)
 constexpr int kGemvTok = 4;
-constexpr int kGemvWaves = 4;
+constexpr int kGemvWaves = 4;     // waves per block
+constexpr int kGemvSplit = 2;     // waves per NeoX pair, each summing 1/kGemvSplit of k
 
 // U: 16-byte chunks of each row in flight per lane and step; the launcher
 // picks U dividing the chunks per lane (hidden/512) when it can, since a
@@ -680,15 +684,18 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
     constexpr int HALF = HD / 2;
     constexpr int R = 2 * P;                 // weight rows per wave
     const int lane = (int)threadIdx.x & 63;
-    const int pair0 = ((int)blockIdx.x * kGemvWaves + ((int)threadIdx.x >> 6)) * P;
-    if (pair0 >= p.N / 2)
-        return;
-    const int nchunk = p.K / 8;
+    const int wvi = (int)threadIdx.x >> 6;
+    const int kq = wvi % kGemvSplit;         // this wave's share of k
+    const int pair0 = ((int)blockIdx.x * (kGemvWaves / kGemvSplit) + wvi / kGemvSplit) * P;
+    const bool valid = pair0 < p.N / 2;      // (every wave reaches the barrier below)
+    const int nchunk = p.K / 8;              // hidden % 64 == 0: kGemvSplit divides it
+    const int c_beg = kq * (nchunk / kGemvSplit);
+    const int c_end = valid ? c_beg + nchunk / kGemvSplit : c_beg;
     // rows 2q and 2q+1 are columns c0 and c0 + hd/2 of pair pair0 + q
     const uint16_t *wr[R];
 #pragma unroll
     for (int q = 0; q < P; ++q) {
-        const int pr = pair0 + q;
+        const int pr = valid ? pair0 + q : 0;
         const int c0 = (pr / HALF) * HD + pr % HALF;
         wr[2 * q] = p.w + (int64_t)c0 * p.K;
         wr[2 * q + 1] = p.w + (int64_t)(c0 + HALF) * p.K;
@@ -704,13 +711,13 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             d[r][t] = 0.0f;
-    for (int cb = lane; cb < nchunk; cb += 64 * U) {
+    for (int cb = c_beg + lane; cb < c_end; cb += 64 * U) {
         u32x4 wv[U][R], xv[U][NT];
         bool ok[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int c = cb + 64 * u;
-            ok[u] = c < nchunk;
+            ok[u] = c < c_end;
             const int cc = ok[u] ? c : 0;    // past the row end: reload chunk 0, weight 0
             // the weights are read once per call: nontemporal
 #pragma unroll
@@ -758,6 +765,25 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
 #pragma unroll
             for (int m = 32; m >= 1; m >>= 1)
                 d[r][t] += __shfl_xor(d[r][t], m, 64);
+    // the pair's first wave adds the other waves' sums in k order
+    __shared__ float part[kGemvWaves][R][NT];
+    if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                part[wvi][r][t] = d[r][t];
+    }
+    __syncthreads();
+    if (kq != 0 || !valid)
+        return;
+#pragma unroll
+    for (int s = 1; s < kGemvSplit; ++s)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                d[r][t] += part[wvi + s][r][t];
 
     if (lane >= NT || lane >= p.M)
         return;
@@ -877,11 +903,11 @@ hipError_t set_mm_lds(int device)
     return e;
 }
 
-// chunks per row and step of the GEMV: the largest of 8..4 dividing the
-// chunks per lane, else the one wasting the fewest slots
+// chunks per row and step of the GEMV: the largest of 8..4 dividing a
+// wave's chunks per lane, else the one wasting the fewest slots
 int gemv_step(int K)
 {
-    const int c = (K / 8 + 63) / 64;   // 16-byte chunks per lane and row
+    const int c = (K / 8 / kGemvSplit + 63) / 64;   // 16-byte chunks per lane and row
     int best = 4, waste = 1 << 30;
     for (int u = 8; u >= 4; --u) {
         const int w = (c + u - 1) / u * u - c;
@@ -896,7 +922,8 @@ int gemv_step(int K)
 template <bool F16, int HD, int NT>
 hipError_t launch_gemv(const ProjParams &pp, const InvTable &inv, hipStream_t st, int u)
 {
-    const int blocks = (pp.N / 2 + kGemvWaves - 1) / kGemvWaves;
+    constexpr int pairs = kGemvWaves / kGemvSplit;   // per block
+    const int blocks = (pp.N / 2 + pairs - 1) / pairs;
     const dim3 grid(blocks), block(64 * kGemvWaves);
     switch (u) {
     case 8: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 8, 1>), grid, block, 0, st, pp, inv); break;

@@ -198,7 +198,7 @@ def launch_percentiles(h, arg_list, n, stream, fn=None):
 
 
 def bench_bandwidth(h, w, cache_dtype, steps, warmup, stream, min_set_bytes=1.5e9, slot=False,
-                    fn=None, norm=False):
+                    fn=None, norm=False, rope_style=0, freq_scale=0.0):
     from qkv_bias_rope_amd import workloads as wl
     cb = 2 if cache_dtype == wl.CACHE_F16 else 4
     nbytes = algo_bytes(w, w.nt, cb, slot=slot)
@@ -211,6 +211,8 @@ def bench_bandwidth(h, w, cache_dtype, steps, warmup, stream, min_set_bytes=1.5e
     share = w.n_slots > 1
     sets = Sets(w, R, cache_dtype, share_cache=share, norm=norm)
     args = [sets.args(r, stream) for r in range(R)]
+    for a in args:
+        a.rope_style, a.freq_scale = rope_style, freq_scale
     if norm:
         fn = norm_runner(sets)
     ms = time_launches(h, args, steps, warmup, stream, fn=fn)
@@ -241,6 +243,14 @@ def bench_decode(h, w, steps, warmup, stream, unfused=False):
     # stream loop
     ms_step = time_launches(h, args, n_loops * w.layers, warmup * w.layers, stream,
                             fn=run) * w.layers
+    cb = 2 if w.cache_dtypes[0] == wl.CACHE_F16 else 4
+    res = dict(us_per_layer_stream=ms_step * 1e3 / w.layers,
+               launches_per_layer=7 if unfused else 1,
+               bytes_per_layer=algo_bytes(w, 1, cb), layers=w.layers)
+    if w.layers == 1:
+        # a one-kernel graph would time the graph launch, not the layer
+        assert B.qkv_epilogue_status(h) == 0
+        return res
     # graph replay of one step
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
@@ -264,11 +274,8 @@ def bench_decode(h, w, steps, warmup, stream, unfused=False):
     e1.synchronize()
     ms_graph = e0.elapsed_time(e1) / n_loops
     assert B.qkv_epilogue_status(h) == 0
-    cb = 2 if w.cache_dtypes[0] == wl.CACHE_F16 else 4
-    return dict(us_per_layer_stream=ms_step * 1e3 / w.layers,
-                us_per_layer_graph=ms_graph * 1e3 / w.layers,
-                launches_per_layer=7 if unfused else 1,
-                bytes_per_layer=algo_bytes(w, 1, cb), layers=w.layers)
+    res["us_per_layer_graph"] = ms_graph * 1e3 / w.layers
+    return res
 
 
 PEAK_BF16_TFLOPS = 2500.0
@@ -581,12 +588,12 @@ def run_all(args, h, stream):
                 bytes_per_launch=r["bytes"], frac_of_peak=round(r["gbs"] / PEAK_HBM_GBS, 4),
                 input_sets=r["sets"])
             log(f"[bench]   {r['ms'] * 1e3:.2f} us/launch, {r['gbs']:.1f} GB/s")
-        for wd in (wl.DECODE_7B, wl.DECODE_14B):
+        for wd in (wl.TINY_DECODE, wl.DECODE_7B, wl.DECODE_14B):
             log(f"[bench] {wd.name}")
             r = bench_decode(h, wd, max(10, args.steps // 10), max(2, args.warmup // 10), stream)
             extra[wd.name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
             log(f"[bench]   {r['us_per_layer_stream']:.2f} us/layer (stream), "
-                f"{r['us_per_layer_graph']:.2f} us/layer (graph)")
+                f"{r.get('us_per_layer_graph', float('nan')):.2f} us/layer (graph)")
             torch.cuda.empty_cache()
         # same-binary A/B of the fusion: the unfused seven-launch chain
         wd = wl.DECODE_14B
@@ -617,6 +624,18 @@ def run_all(args, h, stream):
                                           bytes_per_launch=r["bytes"],
                                           frac_of_peak=round(r["gbs"] / PEAK_HBM_GBS, 4))
         log(f"[bench]   {r['ms'] * 1e3:.2f} us/launch, {r['gbs']:.1f} GB/s")
+        # the rope variants on the same workload: interleaved (GPT-J) pairing,
+        # and NeoX with a frequency scale
+        for tag, style, fs in (("interleaved", 1, 0.0), ("freq_scale_0.25", 0, 0.25)):
+            log(f"[bench] {w.name} rope {tag}")
+            r, sets = bench_bandwidth(h, w, wl.CACHE_F16, max(20, args.steps // 2),
+                                      max(2, args.warmup // 2), stream, rope_style=style, freq_scale=fs)
+            del sets
+            torch.cuda.empty_cache()
+            extra[w.name + "_rope_" + tag] = dict(gbs=round(r["gbs"], 1), us_per_launch=round(r["ms"] * 1e3, 3),
+                                                  bytes_per_launch=r["bytes"],
+                                                  frac_of_peak=round(r["gbs"] / PEAK_HBM_GBS, 4))
+            log(f"[bench]   {r['ms'] * 1e3:.2f} us/launch, {r['gbs']:.1f} GB/s")
         # the projection feeding the epilogue, fused into one launch
         hid = wl.HIDDEN[w.name]
         log(f"[bench] {w.name} projection-fed epilogue (hidden {hid})")

@@ -469,7 +469,7 @@ def test_proj_long_slots_f32_cache(handle):
 
 @pytest.mark.parametrize("nt", [3, 40, 1030])
 def test_proj_minimal_hidden(handle, nt):
-    """hidden = 64 (two k sub-tiles, fewer than the LDS ring's depth) on the
+    """hidden = 64 (one 64-deep k stage, fewer than the LDS ring's depth) on the
     GEMV, a small batch (k too short to split) and the data-parallel launch."""
     w = wl.Workload("proj_hidden64", 40, 8, 128, nt=nt, n_ctx=2048, n_slots=1, layers=1,
                     seed=21, pos_mode="arange")

@@ -206,11 +206,20 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  * them in a fixed order and runs the epilogue (see Launches).
  *
  *   x   bf16 [nt][ld_x] activations (device, 16-byte aligned, ld_x % 8 == 0)
- *   w   bf16 [nqt + 2*nkt][hidden] concat weight rows q|k|v (device, aligned)
+ *   w   bf16 [nqt + 2*nkt][hidden] concat weight rows q|k|v (device, aligned),
+ *       or, with w_k and w_v given, the q weight [nqt][hidden] alone
+ *   w_k, w_v  NULL (concat w), or the k and v weights [nkt][hidden] (device,
+ *       aligned): the same page's layers whose q, k, v weights cannot share
+ *       one concat matrix run three matmuls into one epilogue (§2); here the
+ *       three matrices feed the one launch as they are, nothing repacked
  *   hidden  contraction length, a multiple of 64
  *
  * Limits (QKV_ERR_UNSUPPORTED otherwise): NeoX style, head_dim 64 or 128, q
- * and k/v widths multiples of 128; x and w each under 2 GiB.
+ * and k/v widths multiples of 128; x and each weight matrix under 2 GiB
+ * (QKV_ERR_INVALID_ARG).
+ * The weights are read-only and may overlap one another, but none of x and
+ * the weights may overlap an output or a cache (QKV_ERR_ALIAS); w_k and w_v
+ * must be both NULL or both set (QKV_ERR_INVALID_ARG).
  *
  * Launches: 1-4 tokens run one weight-streaming kernel.  More tokens use a
  * workspace held by the handle: a cos/sin table of nt * head_dim * 4 bytes,
@@ -228,10 +237,12 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  */
 typedef struct qkv_proj_args {
     const void *x;          /* bf16 [nt][ld_x] */
-    const void *w;          /* bf16 [nqt + 2*nkt][hidden] */
+    const void *w;          /* bf16 [nqt + 2*nkt][hidden], or [nqt][hidden] with w_k, w_v */
     int hidden;
     int64_t ld_x;           /* 0 = hidden */
     qkv_epilogue_args_t epi;  /* q/k/v are the outputs; biases may be NULL */
+    const void *w_k;        /* NULL, or bf16 [nkt][hidden] */
+    const void *w_v;        /* NULL, or bf16 [nkt][hidden] */
 } qkv_proj_args_t;
 
 int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *a);

@@ -69,7 +69,7 @@ class QkvEpilogueArgs(ctypes.Structure):
 
 class QkvProjArgs(ctypes.Structure):
     _fields_ = [("x", _P), ("w", _P), ("hidden", _I), ("ld_x", _I64),
-                ("epi", QkvEpilogueArgs)]
+                ("epi", QkvEpilogueArgs), ("w_k", _P), ("w_v", _P)]
 
 
 class QkvEpiloguePlan(ctypes.Structure):
@@ -166,12 +166,14 @@ def qkv_epilogue_run_proj(h, args: QkvProjArgs) -> int:
     return lib.qkv_epilogue_run_proj(h, ctypes.byref(args))
 
 
-def make_proj_args(x, w, hidden, epi: QkvEpilogueArgs, ld_x=0) -> QkvProjArgs:
+def make_proj_args(x, w, hidden, epi: QkvEpilogueArgs, ld_x=0, w_k=None, w_v=None) -> QkvProjArgs:
     """Build the run_proj argument block: bf16 activations x and concat weight
-    rows w (tensors of any 2-byte dtype, or raw addresses), the contraction
-    length and the epilogue block whose q/k/v are the outputs."""
+    rows w (tensors of any 2-byte dtype, or raw addresses) -- or, with w_k and
+    w_v, the q, k and v weights as three matrices -- the contraction length
+    and the epilogue block whose q/k/v are the outputs."""
     pa = QkvProjArgs()
     pa.x, pa.w = _addr(x), _addr(w)
+    pa.w_k, pa.w_v = _addr(w_k), _addr(w_v)
     pa.hidden = hidden
     pa.ld_x = ld_x
     pa.epi = epi

@@ -50,7 +50,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct ProjParams {
     const uint16_t *x;       // bf16 [nt][ld_x]
-    const uint16_t *w;       // bf16 [N][K]
+    const uint16_t *wsec[3]; // bf16 weight rows of the q, k, v sections ([nqt|nkt|nkt][K])
+    bool sep;                // the sections are three matrices (else rows of one concat matrix)
     int64_t ld_x;
     int K;                   // hidden
     int N;                   // nqt + 2*nkt
@@ -71,6 +72,20 @@ struct ProjParams {
     int device;              // the handle's device (launch set-up only)
     bool vec;                // sections, biases, caches 16-byte aligned, strides % 4 == 0
 };
+
+// weight row of output n: row n - section base of its section's matrix (SEP:
+// three matrices), or row n of the concat matrix
+template <bool SEP>
+__device__ __forceinline__ const uint16_t *weight_row(const ProjParams &p, int n)
+{
+    if (!SEP)
+        return p.wsec[0] + (int64_t)n * p.K;
+    if (n < p.nqt)
+        return p.wsec[0] + (int64_t)n * p.K;
+    if (n < p.nqt + p.nkt)
+        return p.wsec[1] + (int64_t)(n - p.nqt) * p.K;
+    return p.wsec[2] + (int64_t)(n - p.nqt - p.nkt) * p.K;
+}
 
 // cache row of token t (slot * n_ctx + pos), or -1 when pos or slot is out
 // of range (the caller then sets the error word)
@@ -293,7 +308,9 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
 
     // this wave's load instructions: token rows arow[j] and weight rows
     // brow[j] of the tile, kRpi rows each, lane / kCpr the row within; byte
-    // offsets from x / w (each < 2 GiB); rows past the end repeat the last
+    // offsets from x and from the weight matrix of the load's section (the
+    // kRpi rows of a load lie in one 32-column tile, so in one section: its
+    // base is wave-uniform), each < 2 GiB; rows past the end repeat the last
     // one.  (fixed-size arrays: with a size that depends on the template
     // arguments, captured by the lambda below, hipcc's host pass silently
     // emitted no launch stub)
@@ -301,6 +318,7 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     const bool do_b = S::kInstB >= kWaves || wave >= kWaves - S::kInstB;
     int arow[8] = {0, 0, 0, 0, 0, 0, 0, 0}, brow[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     uint32_t aoff[8], boff[8];
+    const unsigned char *bsec[8];
 #pragma unroll
     for (int j = 0; j < S::kWaveA; ++j) {
         arow[j] = S::kRpi * ((S::kInstA >= kWaves ? wave * S::kWaveA : wave) + j);
@@ -312,10 +330,13 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
         brow[j] = S::kRpi * ((S::kInstB >= kWaves ? wave * S::kWaveB : wave - (kWaves - S::kInstB)) + j);
         const int rb = brow[j] + lrow;
         const int n = group_lo<PT>(tn * GT + rb / 64) * 32 + ((rb >> 5) & 1) * PT * 32 + (rb & 31);
-        boff[j] = (uint32_t)((int64_t)min(n, p.N - 1) * p.K * 2) + (slot ^ swz<S::kCpr>(rb)) * 16;
+        const int nu = group_lo<PT>(tn * GT + brow[j] / 64) * 32 + ((brow[j] >> 5) & 1) * PT * 32;
+        const int sec = nu < p.nqt ? 0 : (nu < p.nqt + p.nkt ? 1 : 2);
+        const int sbase = sec == 0 ? 0 : (sec == 1 ? p.nqt : p.nqt + p.nkt);
+        bsec[j] = reinterpret_cast<const unsigned char *>(p.wsec[sec]);
+        boff[j] = (uint32_t)((int64_t)(min(n, p.N - 1) - sbase) * p.K * 2) + (slot ^ swz<S::kCpr>(rb)) * 16;
     }
     const unsigned char *xb = reinterpret_cast<const unsigned char *>(p.x);
-    const unsigned char *wb = reinterpret_cast<const unsigned char *>(p.w);
     // local stage st (clamped to the last one: the loop stays uniform)
     auto issue = [&](int st) {
         const int stage = st % NSTAGE;
@@ -330,7 +351,8 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
         if (do_b) {
 #pragma unroll
             for (int j = 0; j < S::kWaveB; ++j)
-                __builtin_amdgcn_global_load_lds(wb + boff[j] + kb, (lds_t *)(sb + brow[j] * kRow), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(bsec[j] + boff[j] + kb, (lds_t *)(sb + brow[j] * kRow), 16, 0,
+                                                 0);
         }
     };
 
@@ -678,13 +700,15 @@ constexpr int kGemvSplit = 2;     // waves per NeoX pair, each summing 1/kGemvSp
 // picks U dividing the chunks per lane (hidden/512) when it can, since a
 // partial last step costs as much as a full one.  P: NeoX pairs per wave
 // (1 in every launch; more pairs let one x chunk serve more weight rows).
-template <bool F16, int HD, int NT, int U, int P>
+// SEP: q, k, v weights in three matrices (the concat layout keeps its own
+// instance: the per-section select cost ~1% at 14B).
+template <bool F16, int HD, int NT, int U, int P, bool SEP>
 __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p, InvTable inv)
 {
     constexpr int HALF = HD / 2;
     constexpr int R = 2 * P;                 // weight rows per wave
     const int lane = (int)threadIdx.x & 63;
-    const int wvi = (int)threadIdx.x >> 6;
+    const int wvi = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int kq = wvi % kGemvSplit;         // this wave's share of k
     const int pair0 = ((int)blockIdx.x * (kGemvWaves / kGemvSplit) + wvi / kGemvSplit) * P;
     const bool valid = pair0 < p.N / 2;      // (every wave reaches the barrier below)
@@ -697,8 +721,8 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
     for (int q = 0; q < P; ++q) {
         const int pr = valid ? pair0 + q : 0;
         const int c0 = (pr / HALF) * HD + pr % HALF;
-        wr[2 * q] = p.w + (int64_t)c0 * p.K;
-        wr[2 * q + 1] = p.w + (int64_t)(c0 + HALF) * p.K;
+        wr[2 * q] = weight_row<SEP>(p, c0);
+        wr[2 * q + 1] = weight_row<SEP>(p, c0 + HALF);
     }
     const uint16_t *xr[NT];
 #pragma unroll
@@ -919,18 +943,18 @@ int gemv_step(int K)
     return best;
 }
 
-template <bool F16, int HD, int NT>
+template <bool F16, int HD, int NT, bool SEP>
 hipError_t launch_gemv(const ProjParams &pp, const InvTable &inv, hipStream_t st, int u)
 {
     constexpr int pairs = kGemvWaves / kGemvSplit;   // per block
     const int blocks = (pp.N / 2 + pairs - 1) / pairs;
     const dim3 grid(blocks), block(64 * kGemvWaves);
     switch (u) {
-    case 8: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 8, 1>), grid, block, 0, st, pp, inv); break;
-    case 7: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 7, 1>), grid, block, 0, st, pp, inv); break;
-    case 6: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 6, 1>), grid, block, 0, st, pp, inv); break;
-    case 5: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 5, 1>), grid, block, 0, st, pp, inv); break;
-    default: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 4, 1>), grid, block, 0, st, pp, inv); break;
+    case 8: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 8, 1, SEP>), grid, block, 0, st, pp, inv); break;
+    case 7: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 7, 1, SEP>), grid, block, 0, st, pp, inv); break;
+    case 6: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 6, 1, SEP>), grid, block, 0, st, pp, inv); break;
+    case 5: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 5, 1, SEP>), grid, block, 0, st, pp, inv); break;
+    default: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 4, 1, SEP>), grid, block, 0, st, pp, inv); break;
     }
     return hipGetLastError();
 }
@@ -969,10 +993,13 @@ hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st
     if (pp.M <= kGemvTok) {
         const int u = gemv_step(pp.K);
         if (pp.M == 1)
-            return launch_gemv<F16, HD, 1>(pp, inv, st, u);
+            return pp.sep ? launch_gemv<F16, HD, 1, true>(pp, inv, st, u)
+                          : launch_gemv<F16, HD, 1, false>(pp, inv, st, u);
         if (pp.M == 2)
-            return launch_gemv<F16, HD, 2>(pp, inv, st, u);
-        return launch_gemv<F16, HD, 4>(pp, inv, st, u);
+            return pp.sep ? launch_gemv<F16, HD, 2, true>(pp, inv, st, u)
+                          : launch_gemv<F16, HD, 2, false>(pp, inv, st, u);
+        return pp.sep ? launch_gemv<F16, HD, 4, true>(pp, inv, st, u)
+                      : launch_gemv<F16, HD, 4, false>(pp, inv, st, u);
     }
     // the fused epilogue reads the launch's cos/sin and cache-row tables; the
     // split path's summing kernel computes its own
@@ -1023,34 +1050,48 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
                     (long long)pl.nqt, (long long)pl.nkt);
     if (N > INT32_MAX / 2)
         return fail(h, QKV_ERR_INVALID_ARG, "q|k|v width too large");
-    // the kernels address x and w with 32-bit byte offsets
+    const bool sep = pa->w_k || pa->w_v;            // three weight matrices instead of the concat one
+    // the kernels address x and each weight matrix with 32-bit byte offsets
     if ((int64_t)a->nt * (pa->ld_x ? pa->ld_x : pa->hidden) * 2 > INT32_MAX ||
-        N * pa->hidden * 2 > INT32_MAX)
-        return fail(h, QKV_ERR_INVALID_ARG, "x and w must each span less than 2 GiB");
+        (sep ? pl.nqt : N) * pa->hidden * 2 > INT32_MAX)
+        return fail(h, QKV_ERR_INVALID_ARG, "x and each weight matrix must span less than 2 GiB");
+    if (sep && (!pa->w_k || !pa->w_v))
+        return fail(h, QKV_ERR_INVALID_ARG, "w_k and w_v must be both NULL or both non-NULL");
     const int64_t ld_x = pa->ld_x ? pa->ld_x : pa->hidden;
     if (ld_x < pa->hidden || ld_x % 8 != 0)
         return fail(h, QKV_ERR_INVALID_ARG, "ld_x must be >= hidden and a multiple of 8");
     if (a->nt == 0)
         return QKV_OK;
-    if (!pa->x || !pa->w || (uintptr_t)pa->x % 16 || (uintptr_t)pa->w % 16)
-        return fail(h, QKV_ERR_INVALID_ARG, "x and w must be non-NULL and 16-byte aligned");
+    if (!pa->x || !pa->w || (uintptr_t)pa->x % 16 || (uintptr_t)pa->w % 16 || (uintptr_t)pa->w_k % 16 ||
+        (uintptr_t)pa->w_v % 16)
+        return fail(h, QKV_ERR_INVALID_ARG, "x and the weights must be non-NULL and 16-byte aligned");
+    // the q, k, v weight sections: rows of the concat matrix, or three matrices
+    const uint16_t *const w0 = static_cast<const uint16_t *>(pa->w);
+    const uint16_t *const wsec[3] = {
+        w0, sep ? static_cast<const uint16_t *>(pa->w_k) : w0 + pl.nqt * pa->hidden,
+        sep ? static_cast<const uint16_t *>(pa->w_v) : w0 + (pl.nqt + pl.nkt) * pa->hidden};
     {
-        // x and w are read while the outputs are written: no byte in common
-        // (hull test on each range, conservative for strided rows)
+        // x and the weights are read while the outputs are written: no byte
+        // in common (hull test on each range, conservative for strided rows)
         const int64_t nt = a->nt, cb = a->cache_dtype == QKV_CACHE_F16 ? 2 : 4;
         const int64_t cache_bytes = pl.n_slots * pl.n_ctx * pl.nkt * cb;
-        const uintptr_t ins[2][2] = {
-            {(uintptr_t)pa->x, (uintptr_t)pa->x + (uintptr_t)(((nt - 1) * ld_x + pa->hidden) * 2)},
-            {(uintptr_t)pa->w, (uintptr_t)pa->w + (uintptr_t)(N * pa->hidden * 2)}};
+        const int64_t wrows[3] = {pl.nqt, pl.nkt, pl.nkt};
+        uintptr_t ins[4][2] = {
+            {(uintptr_t)pa->x, (uintptr_t)pa->x + (uintptr_t)(((nt - 1) * ld_x + pa->hidden) * 2)}};
+        for (int s = 0; s < 3; ++s) {
+            ins[1 + s][0] = (uintptr_t)wsec[s];
+            ins[1 + s][1] = (uintptr_t)wsec[s] + (uintptr_t)(wrows[s] * pa->hidden * 2);
+        }
         const uintptr_t outs[5][2] = {
             {(uintptr_t)a->q, (uintptr_t)a->q + (uintptr_t)(((nt - 1) * pl.ld[0] + pl.nqt) * 4)},
             {(uintptr_t)a->k, (uintptr_t)a->k + (uintptr_t)(((nt - 1) * pl.ld[1] + pl.nkt) * 4)},
             {(uintptr_t)a->v, (uintptr_t)a->v + (uintptr_t)(((nt - 1) * pl.ld[2] + pl.nkt) * 4)},
             {(uintptr_t)a->kcache, (uintptr_t)a->kcache + (uintptr_t)cache_bytes},
             {(uintptr_t)a->vcache, (uintptr_t)a->vcache + (uintptr_t)cache_bytes}};
-        const char *in_name[2] = {"x", "w"};
+        const char *in_name[4] = {"x", sep ? "w" : "w (q rows)", sep ? "w_k" : "w (k rows)",
+                                  sep ? "w_v" : "w (v rows)"};
         const char *out_name[5] = {"q", "k", "v", "kcache", "vcache"};
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
             for (int o = 0; o < 5; ++o)
                 if (ins[i][0] < outs[o][1] && outs[o][0] < ins[i][1])
                     return fail(h, QKV_ERR_ALIAS, "read-only %s overlaps output %s", in_name[i],
@@ -1059,7 +1100,9 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
 
     ProjParams pp;
     pp.x = static_cast<const uint16_t *>(pa->x);
-    pp.w = static_cast<const uint16_t *>(pa->w);
+    for (int s = 0; s < 3; ++s)
+        pp.wsec[s] = wsec[s];
+    pp.sep = sep;
     pp.ld_x = ld_x;
     pp.K = pa->hidden;
     pp.N = (int)N;

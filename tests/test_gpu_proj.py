@@ -44,7 +44,7 @@ def handle():
 
 class ProjCase:
     def __init__(self, w, hidden, nt=None, cache_dtype=None, form="separate", bias=True,
-                 pos=None, slot=None, sample=None, ld_x_pad=0, misalign=0):
+                 pos=None, slot=None, sample=None, ld_x_pad=0, misalign=0, weights="concat"):
         self.w, self.hidden = w, hidden
         d = wl.draw_projection(w, hidden, nt=nt)
         if pos is not None:
@@ -57,6 +57,7 @@ class ProjCase:
         self.form, self.bias = form, bias
         self.ld_x_pad = ld_x_pad
         self.misalign = misalign   # shift every output section by this many floats
+        self.weights = weights     # "concat" [N][hidden], or "three" q, k, v matrices
         # tokens the oracle recomputes (all of them unless a sample is given)
         self.sample = np.arange(self.nt) if sample is None else np.asarray(sample)
 
@@ -102,6 +103,13 @@ class ProjCase:
         self.g_x = torch.from_numpy(xp.view(np.int16)).to(DEV)
         self.ld_x = ldx if self.ld_x_pad else 0
         self.g_w = torch.from_numpy(d["w"].view(np.int16)).to(DEV)
+        self.g_wk = self.g_wv = None
+        if self.weights == "three":
+            # three allocations, v first so the sections are not laid out in order
+            wq, wk, wv = (d["w"][a:b] for a, b in ((0, nqt), (nqt, nqt + nkt), (nqt + nkt, nqt + 2 * nkt)))
+            self.g_wv = torch.from_numpy(np.ascontiguousarray(wv).view(np.int16)).to(DEV)
+            self.g_wk = torch.from_numpy(np.ascontiguousarray(wk).view(np.int16)).to(DEV)
+            self.g_w = torch.from_numpy(np.ascontiguousarray(wq).view(np.int16)).to(DEV)
         m = self.misalign
         if self.form == "concat":
             n = nqt + 2 * nkt
@@ -135,7 +143,8 @@ class ProjCase:
                           theta=w.theta, cache_dtype=self.cd, slot=self.g_slot, n_ctx=w.n_ctx,
                           n_slots=w.n_slots, stream=torch.cuda.current_stream(),
                           use_stream=True, nt=self.nt)
-        return B.make_proj_args(self.g_x, self.g_w, self.hidden, epi, ld_x=self.ld_x)
+        return B.make_proj_args(self.g_x, self.g_w, self.hidden, epi, ld_x=self.ld_x, w_k=self.g_wk,
+                                w_v=self.g_wv)
 
     def run_gpu(self, h):
         return B.qkv_epilogue_run_proj(h, self.args())
@@ -365,9 +374,23 @@ def test_proj_rejects_unsupported(handle):
                       cache_dtypes=(wl.CACHE_F32,))
     c96 = ProjCase(w96, hidden=256).upload()
     assert B.qkv_epilogue_run_proj(handle, c96.args()) == B.QKV_ERR_UNSUPPORTED
+    # three weight matrices: both k and v needed; none may overlap an output
+    c3 = ProjCase(SMALL_05B, hidden=512, nt=8, weights="three").upload()
+    a = c3.args()
+    a.w_v = None
+    assert B.qkv_epilogue_run_proj(handle, a) == B.QKV_ERR_INVALID_ARG
+    a = c3.args()
+    a.w_k = c3.g_v.data_ptr()   # the k weights overlapping the v output
+    assert B.qkv_epilogue_run_proj(handle, a) == B.QKV_ERR_ALIAS
+    a = c3.args()
+    a.w_v = c3.vc.data_ptr()    # the v weights overlapping the V cache
+    assert B.qkv_epilogue_run_proj(handle, a) == B.QKV_ERR_ALIAS
+    a = c3.args()
+    a.w_k = c3.g_wk.data_ptr() + 8   # misaligned
+    assert B.qkv_epilogue_run_proj(handle, a) == B.QKV_ERR_INVALID_ARG
     # nothing was launched: the outputs still hold their NaN fill
     torch.cuda.synchronize()
-    assert torch.isnan(c.g_q).all() and torch.isnan(c96.g_q).all()
+    assert torch.isnan(c.g_q).all() and torch.isnan(c96.g_q).all() and torch.isnan(c3.g_q).all()
     assert B.qkv_epilogue_run_proj(handle, base) == B.QKV_OK
     assert B.qkv_epilogue_status(handle) == B.QKV_OK
 
@@ -455,6 +478,18 @@ def test_proj_hd64_256x192(handle):
     c = ProjCase(w, hidden=1024)
     assert _run(handle, c, "hd64_256x192") == B.QKV_OK
     c.check("hd64_256x192")
+
+
+@pytest.mark.parametrize("nt", [1, 3, 40, 1100])
+def test_proj_three_weight_matrices(handle, nt):
+    """The q, k, v weights as three separate matrices (the page's layers that
+    cannot share a concat matrix), in one launch: the GEMV (1 and 3 tokens),
+    the k-split MFMA path (40) and the data-parallel one (1100), 14B widths."""
+    w = wl.Workload("proj_three_w", 40, 8, 128, nt=nt, n_ctx=4096, n_slots=1, layers=1,
+                    seed=29, pos_mode="uniform")
+    c = ProjCase(w, hidden=1024, weights="three")
+    assert _run(handle, c, f"three_w_{nt}") == B.QKV_OK
+    c.check(f"three_w_{nt}")
 
 
 def test_proj_long_slots_f32_cache(handle):

@@ -1053,7 +1053,7 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
     const bool sep = pa->w_k || pa->w_v;            // three weight matrices instead of the concat one
     // the kernels address x and each weight matrix with 32-bit byte offsets
     if ((int64_t)a->nt * (pa->ld_x ? pa->ld_x : pa->hidden) * 2 > INT32_MAX ||
-        (sep ? pl.nqt : N) * pa->hidden * 2 > INT32_MAX)
+        (sep ? std::max(pl.nqt, pl.nkt) : N) * pa->hidden * 2 > INT32_MAX)
         return fail(h, QKV_ERR_INVALID_ARG, "x and each weight matrix must span less than 2 GiB");
     if (sep && (!pa->w_k || !pa->w_v))
         return fail(h, QKV_ERR_INVALID_ARG, "w_k and w_v must be both NULL or both non-NULL");

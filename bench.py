@@ -516,9 +516,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the epilogue needs no collective: each GPU would run its own shard of tokens "
-              "or heads, see the design notes)", file=sys.stderr)
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the epilogue "
+              "needs no collective: each GPU would run the same kernels on its own share of the "
+              "tokens, or of the heads with their biases and cache columns)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -23,8 +23,7 @@
  * against the page by eye.  The per-pair cos/sin are recomputed inside the rope
  * loop exactly as the unfused rope kernel does (nothing is hoisted or blocked).
  *
- * Readings taken where the pages leave a step open (each one is also listed in
- * the design notes of the repository):
+ * Readings taken where the pages leave a step open:
  *   - inverse frequency inv[i] = theta^(-2i/hd) is the correctly rounded f32
  *     of that real number: computed with libm pow in double, rounded once;
  *   - angle a = f32(pos * inv[i]): one f32 multiply, as the page's kernel does;

@@ -233,6 +233,10 @@ struct Shape {
     static_assert((BM * kChunks) % 64 == 0, "table staging");
 };
 
+// Word 3 of a raw buffer resource (32-bit data format, no swizzle, no
+// index stride): untyped loads of the byte range [base, base + num_records).
+constexpr int kRsrcWord3 = 0x00020000;
+
 // s_waitcnt immediate that waits for vmcnt <= v only
 constexpr int vmcnt_wait(int v)
 {
@@ -318,7 +322,7 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     const bool do_b = S::kInstB >= kWaves || wave >= kWaves - S::kInstB;
     int arow[8] = {0, 0, 0, 0, 0, 0, 0, 0}, brow[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     uint32_t aoff[8], boff[8];
-    const unsigned char *bsec[8];
+    int bsec[8];                                  // section of weight load j (wave-uniform)
 #pragma unroll
     for (int j = 0; j < S::kWaveA; ++j) {
         arow[j] = S::kRpi * ((S::kInstA >= kWaves ? wave * S::kWaveA : wave) + j);
@@ -333,10 +337,22 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
         const int nu = group_lo<PT>(tn * GT + brow[j] / 64) * 32 + ((brow[j] >> 5) & 1) * PT * 32;
         const int sec = nu < p.nqt ? 0 : (nu < p.nqt + p.nkt ? 1 : 2);
         const int sbase = sec == 0 ? 0 : (sec == 1 ? p.nqt : p.nqt + p.nkt);
-        bsec[j] = reinterpret_cast<const unsigned char *>(p.wsec[sec]);
+        bsec[j] = sec;
         boff[j] = (uint32_t)((int64_t)(min(n, p.N - 1) - sbase) * p.K * 2) + (slot ^ swz<S::kCpr>(rb)) * 16;
     }
-    const unsigned char *xb = reinterpret_cast<const unsigned char *>(p.x);
+    // buffer resources over x and the three weight matrices: the loads take a
+    // 32-bit offset from a scalar base (as fast as 64-bit per-lane addresses
+    // or up to 2% faster, 256-4096 tokens), and the hardware clamps them to
+    // each buffer's byte range (a load past it would read zeros, never fault)
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(p.x), (short)0,
+                                          (int)(((int64_t)(p.M - 1) * p.ld_x + p.K) * 2), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rw0 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(p.wsec[0]), (short)0, (int)((int64_t)p.nqt * p.K * 2), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rw1 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(p.wsec[1]), (short)0, (int)((int64_t)p.nkt * p.K * 2), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rw2 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(p.wsec[2]), (short)0, (int)((int64_t)p.nkt * p.K * 2), kRsrcWord3);
     // local stage st (clamped to the last one: the loop stays uniform)
     auto issue = [&](int st) {
         const int stage = st % NSTAGE;
@@ -346,13 +362,15 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
         if (do_a) {
 #pragma unroll
             for (int j = 0; j < S::kWaveA; ++j)
-                __builtin_amdgcn_global_load_lds(xb + aoff[j] + kb, (lds_t *)(sa + arow[j] * kRow), 16, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_t *)(sa + arow[j] * kRow), 16, aoff[j] + kb, 0,
+                                                         0, 0);
         }
         if (do_b) {
 #pragma unroll
             for (int j = 0; j < S::kWaveB; ++j)
-                __builtin_amdgcn_global_load_lds(bsec[j] + boff[j] + kb, (lds_t *)(sb + brow[j] * kRow), 16, 0,
-                                                 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(bsec[j] == 0 ? rw0 : (bsec[j] == 1 ? rw1 : rw2),
+                                                         (lds_t *)(sb + brow[j] * kRow), 16, boff[j] + kb, 0, 0,
+                                                         0);
         }
     };
 

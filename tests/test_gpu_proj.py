@@ -492,6 +492,37 @@ def test_proj_three_weight_matrices(handle, nt):
     c.check(f"three_w_{nt}")
 
 
+def _random_shape(seed):
+    """A seeded random projection case inside the path's limits: head_dim 64 or
+    128, q and k/v widths multiples of 128, hidden a multiple of 64, 1-700
+    tokens, either cache type, concat or three weight matrices, biases or none,
+    one sequence or per-token slots."""
+    rng = np.random.default_rng(1000 + seed)
+    hd = int(rng.choice([64, 128]))
+    step = 128 // hd                              # heads per 128 columns
+    n_head = step * int(rng.integers(1, 13))
+    n_kv_head = step * int(rng.integers(1, 5))
+    nt = int(rng.choice([int(rng.integers(1, 5)), int(rng.integers(5, 80)), int(rng.integers(80, 700))]))
+    hidden = 64 * int(rng.integers(1, 25))
+    slots = int(rng.choice([1, 4]))
+    cd = int(rng.choice([wl.CACHE_F32, wl.CACHE_F16]))
+    w = wl.Workload(f"proj_rand_{seed}", n_head, n_kv_head, hd, nt=nt, n_ctx=1024, n_slots=slots,
+                    layers=1, seed=40 + seed, cache_dtypes=(cd,), pos_mode="uniform")
+    return w, dict(hidden=hidden, bias=bool(rng.integers(0, 2)),
+                   weights=str(rng.choice(["concat", "three"])))
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_proj_random_shapes(handle, seed):
+    """Seeded random shapes across the launch plans (GEMV, k-split and
+    data-parallel MFMA tiles of every shape), both head dims, both cache
+    types, both weight layouts, with or without biases and slots."""
+    w, kw = _random_shape(seed)
+    c = ProjCase(w, **kw)
+    assert _run(handle, c, f"rand_{seed}") == B.QKV_OK
+    c.check(f"rand_{seed}")
+
+
 def test_proj_long_slots_f32_cache(handle):
     """The fused long-prompt path with per-token cache slots (32 sequences)
     and an f32 cache; equal (slot, position) pairs are allowed to race."""

@@ -139,6 +139,40 @@ def test_batched_slots_small(handle, nt):
     run_case(handle, Case(w, slot=slot), label=f"slots nt={nt}")
 
 
+# ---- seeded random shapes --------------------------------------------------
+
+def _random_case(seed):
+    """A seeded random launch: head dims from 2 to 256, 1-16 q and 1-8 kv
+    heads, 1-600 tokens at distinct positions, one sequence or three slots,
+    either cache type, separate or concat sections, NeoX or interleaved
+    pairing, a frequency scale or none, and now and then sections shifted
+    by one element (the scalar path)."""
+    rng = np.random.default_rng(2000 + seed)
+    hd = int(rng.choice([2, 4, 6, 8, 16, 18, 32, 64, 96, 128, 256]))
+    nh, nkv = int(rng.integers(1, 17)), int(rng.integers(1, 9))
+    nt = int(rng.choice([1, int(rng.integers(2, 40)), int(rng.integers(40, 600))]))
+    n_slots = int(rng.choice([1, 3]))
+    n_ctx = int(rng.integers(nt, nt + 200))
+    cd = int(rng.choice([wl.CACHE_F32, wl.CACHE_F16]))
+    w = wl.Workload(f"rand{seed}", nh, nkv, hd, nt=nt, n_ctx=n_ctx, n_slots=n_slots, layers=1,
+                    seed=60 + seed, cache_dtypes=(cd,))
+    pos = rng.permutation(n_ctx)[:nt].astype(np.int32)       # distinct rows
+    slot = rng.integers(0, n_slots, nt).astype(np.int32) if n_slots > 1 else None
+    kw = dict(pos=pos, slot=slot, n_ctx=n_ctx, n_slots=n_slots,
+              form=str(rng.choice(["separate", "concat"])), style=int(rng.integers(0, 2)),
+              freq_scale=float(rng.choice([1.0, 1.0, 0.25, 0.5, 2.0])),
+              misalign=int(rng.choice([0, 0, 0, 1])))
+    return w, kw
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_shapes(handle, seed):
+    w, kw = _random_case(seed)
+    c = Case(w, **kw)
+    run_case(handle, c, label=f"rand {seed}: {w.n_head}x{w.n_kv_head}x{w.head_dim} style {kw['style']} "
+                              f"scale {kw['freq_scale']} misalign {kw['misalign']}")
+
+
 # ---- geometry edge cases ----------------------------------------------------
 
 @pytest.mark.parametrize("geom", [(14, 2, 64), (8, 8, 96), (3, 1, 256), (2, 1, 512), (5, 3, 8),

@@ -308,6 +308,51 @@ class Epilogue:
         if rc != QKV_OK:
             raise QkvError(rc, qkv_epilogue_last_error(self.h))
 
+    def run_proj(self, x, w, q, k, v, bq, bk, bv, pos, kcache, vcache, *, n_head, n_kv_head,
+                 head_dim, theta=1.0e6, w_k=None, w_v=None, slot=None, n_ctx=None, n_slots=None,
+                 stream=None):
+        """The projection feeding the epilogue: x [nt][hidden] and the weights
+        (w [nqt+2*nkt][hidden] concat, or w/w_k/w_v per section) as bfloat16
+        device tensors; q, k, v are the float32 outputs; biases may be None."""
+        import torch
+        if kcache.dtype == torch.float32:
+            cd = QKV_CACHE_F32
+        elif kcache.dtype == torch.float16:
+            cd = QKV_CACHE_F16
+        else:
+            raise TypeError(f"cache dtype must be float32 or float16, got {kcache.dtype}")
+        if vcache.dtype != kcache.dtype:
+            raise TypeError("kcache and vcache must share a dtype")
+        if (w_k is None) != (w_v is None):
+            raise TypeError("w_k and w_v go together")
+        for name, t in (("x", x), ("w", w), ("w_k", w_k), ("w_v", w_v)):
+            if t is not None and (t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 2
+                                  or t.stride(1) != 1):
+                raise TypeError(f"{name} must be a 2-D bfloat16 device tensor with unit column stride")
+        for name, t in (("w", w), ("w_k", w_k), ("w_v", w_v)):
+            if t is not None and not t.is_contiguous():
+                raise TypeError(f"{name} must be contiguous")
+        for name, t in (("q", q), ("k", k), ("v", v), ("bq", bq), ("bk", bk), ("bv", bv)):
+            if t is not None and (t.dtype != torch.float32 or not t.is_cuda):
+                raise TypeError(f"{name} must be a float32 device tensor")
+        for name, t in (("pos", pos), ("slot", slot)):
+            if t is not None and (t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous()):
+                raise TypeError(f"{name} must be a contiguous int32 device tensor")
+        hidden = x.shape[1]
+        if w.shape[1] != hidden or any(t is not None and t.shape[1] != hidden for t in (w_k, w_v)):
+            raise ValueError("x and the weights must share the hidden size")
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        epi = make_args(q, k, v, bq, bk, bv, pos, kcache, vcache, n_head=n_head,
+                        n_kv_head=n_kv_head, head_dim=head_dim, theta=theta, cache_dtype=cd,
+                        slot=slot, n_ctx=n_ctx or 0, n_slots=n_slots or 0, stream=stream,
+                        use_stream=True, nt=int(pos.numel()))
+        ld_x = x.stride(0) if x.stride(0) != hidden else 0
+        rc = qkv_epilogue_run_proj(self.h, make_proj_args(x, w, hidden, epi, ld_x=ld_x, w_k=w_k,
+                                                          w_v=w_v))
+        if rc != QKV_OK:
+            raise QkvError(rc, qkv_epilogue_last_error(self.h))
+
     def status(self) -> int:
         return qkv_epilogue_status(self.h)
 

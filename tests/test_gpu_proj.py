@@ -523,6 +523,32 @@ def test_proj_random_shapes(handle, seed):
     c.check(f"rand_{seed}")
 
 
+@pytest.mark.parametrize("weights", ["concat", "three"])
+def test_proj_python_wrapper(weights):
+    """Epilogue.run_proj (the checked torch-tensor wrapper of the same entry
+    point) on a 40-token 14B batch, against the oracle; wrong dtypes raise
+    before any launch."""
+    w = wl.Workload("proj_wrapper", 40, 8, 128, nt=40, n_ctx=1024, n_slots=1, layers=1,
+                    seed=32, pos_mode="uniform")
+    c = ProjCase(w, hidden=512, weights=weights)
+    c.run_oracle().upload()
+    ep = B.Epilogue(0, w.n_ctx)
+    bf = torch.bfloat16
+    wk = None if c.g_wk is None else c.g_wk.view(bf)
+    wv = None if c.g_wv is None else c.g_wv.view(bf)
+    with pytest.raises(TypeError):
+        ep.run_proj(c.g_x.view(bf).float(), c.g_w.view(bf), c.g_q, c.g_k, c.g_v, *c.g_b, c.g_pos, c.kc,
+                    c.vc, n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim, theta=w.theta,
+                    w_k=wk, w_v=wv)
+    ep.run_proj(c.g_x.view(bf), c.g_w.view(bf), c.g_q, c.g_k, c.g_v, *c.g_b, c.g_pos, c.kc, c.vc,
+                n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim, theta=w.theta,
+                w_k=wk, w_v=wv)
+    assert ep.status() == B.QKV_OK, ep.last_error()
+    torch.cuda.synchronize()
+    c.check(f"wrapper_{weights}")
+    ep.close()
+
+
 def test_proj_long_slots_f32_cache(handle):
     """The fused long-prompt path with per-token cache slots (32 sequences)
     and an f32 cache; equal (slot, position) pairs are allowed to race."""

@@ -93,3 +93,25 @@ def test_invalid_requests(handle):
     assert B.qkv_epilogue_run_ex(handle, a) == B.QKV_ERR_INVALID_ARG
     torch.cuda.synchronize()
     assert changed_rows(c.kc, c.cd).size == 0
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes(handle, seed):
+    """Seeded random launches of the q/k-norm variant: head dims 2-256, 1-16 q
+    and 1-8 kv heads, 1-600 tokens at distinct positions, one sequence or
+    three slots, either cache type, separate or concat sections, NeoX or
+    interleaved pairing, biases or none."""
+    rng = np.random.default_rng(3000 + seed)
+    hd = int(rng.choice([2, 4, 8, 16, 18, 32, 64, 96, 128, 256]))
+    nh, nkv = int(rng.integers(1, 17)), int(rng.integers(1, 9))
+    nt = int(rng.choice([1, int(rng.integers(2, 40)), int(rng.integers(40, 600))]))
+    n_slots = int(rng.choice([1, 3]))
+    n_ctx = int(rng.integers(nt, nt + 200))
+    cd = int(rng.choice([wl.CACHE_F32, wl.CACHE_F16]))
+    w = wl.Workload(f"normrand{seed}", nh, nkv, hd, nt=nt, n_ctx=n_ctx, n_slots=n_slots, layers=1,
+                    seed=90 + seed, cache_dtypes=(cd,))
+    pos = rng.permutation(n_ctx)[:nt].astype(np.int32)
+    slot = rng.integers(0, n_slots, nt).astype(np.int32) if n_slots > 1 else None
+    c = Case(w, norm=True, bias=bool(rng.integers(0, 2)), pos=pos, slot=slot, n_ctx=n_ctx,
+             n_slots=n_slots, form=str(rng.choice(["separate", "concat"])), style=int(rng.integers(0, 2)))
+    run_norm(handle, c, f"rand {seed}: {nh}x{nkv}x{hd}")

@@ -34,6 +34,17 @@ def test_exports_every_declared_symbol():
         assert hasattr(B.lib, n)
 
 
+def test_every_kernel_launch_stub_is_defined():
+    """Every kernel the host code launches has its launch stub in the library:
+    some device-code constructs in a kernel template make hipcc's host pass
+    drop the stubs without a diagnostic, leaving undefined symbols that only
+    fail when a launch is resolved."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", B.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    missing = [l for l in out.splitlines() if "device_stub" in l]
+    assert not missing, missing[:5]
+
+
 def test_library_links_no_oracle():
     out = subprocess.run(["nm", "-D", B.LIB_PATH], capture_output=True, text=True).stdout
     assert "oracle" not in out

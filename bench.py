@@ -433,9 +433,15 @@ def cpu_baseline(w, cache_dtype, budget_s=10.0):
         if time.perf_counter() - t0 >= budget_s:
             break
     s_per = spent / n
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
+    except OSError:
+        pass
     return dict(value=algo_bytes(w, w.nt, cb) / s_per / 1e9, unit="GB/s", cores=1, kind="oracle",
                 sample=f"{n} full launch(es) of {w.name} ({w.nt} tokens, f16 cache) on 1 host "
-                       f"thread, {s_per:.3f} s each")
+                       f"thread, {s_per:.3f} s each", cpu=cpu)
 
 
 def hbm_ceiling(steps, stream, nbytes=251703296, sets=8):

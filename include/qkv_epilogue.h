@@ -228,7 +228,8 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  * the 14B shape); those launches are two kernels on the stream (the tables
  * and the GEMM, or the split GEMM and the summing epilogue).  A call that
  * needs more workspace than any before it synchronizes the device and
- * (re)allocates it: make that call outside graph capture.  All other calls
+ * (re)allocates it: make that call outside graph capture (during capture it
+ * returns QKV_ERR_INVALID_ARG and launches nothing).  All other calls
  * allocate nothing and never synchronize.  Calls on one handle share its
  * workspace: calls that may run concurrently (different streams) need
  * different handles.  The f32 sums are taken in a different order than a

@@ -1195,13 +1195,29 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
         const size_t need =
             tab + rows + (pp.ksplit > 1 ? (size_t)pp.ksplit * pp.M * pp.N * sizeof(float) : 0);
         if (h->proj_ws_bytes < need) {
+            // growing synchronizes the device and allocates: refused while the
+            // stream is being captured, where neither is allowed
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            e = hipStreamIsCapturing(st, &cs);
+            if (e != hipSuccess)
+                return fail(h, QKV_ERR_HIP, "stream capture query: %s", hipGetErrorString(e));
+            if (cs != hipStreamCaptureStatusNone)
+                return fail(h, QKV_ERR_INVALID_ARG,
+                            "this call needs %zu bytes of workspace and the handle holds %zu: make one call "
+                            "of this size outside stream capture first",
+                            need, h->proj_ws_bytes);
             e = hipDeviceSynchronize();
-            if (e == hipSuccess && h->proj_ws)
+            if (e != hipSuccess)
+                return fail(h, QKV_ERR_HIP, "device synchronize before growing the workspace: %s",
+                            hipGetErrorString(e));
+            if (h->proj_ws) {
                 e = hipFree(h->proj_ws);
-            h->proj_ws = nullptr;
-            h->proj_ws_bytes = 0;
-            if (e == hipSuccess)
-                e = hipMalloc(&h->proj_ws, need);
+                h->proj_ws = nullptr;
+                h->proj_ws_bytes = 0;
+                if (e != hipSuccess)
+                    return fail(h, QKV_ERR_HIP, "freeing the old workspace: %s", hipGetErrorString(e));
+            }
+            e = hipMalloc(&h->proj_ws, need);
             if (e != hipSuccess) {
                 h->proj_ws = nullptr;
                 return fail(h, QKV_ERR_HIP, "workspace of %zu bytes: %s", need, hipGetErrorString(e));

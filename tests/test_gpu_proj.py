@@ -623,6 +623,34 @@ def test_proj_graph_capture_decode_layers(handle):
     _graph_replays(handle, cases)
 
 
+def test_proj_workspace_growth_refused_in_capture():
+    """On a fresh handle a long-prompt call needs workspace: during stream
+    capture it is refused (INVALID_ARG, nothing launched, the capture stays
+    usable); outside capture the same call grows the workspace and runs."""
+    rc, h = B.qkv_epilogue_create(0, 4096)
+    assert rc == 0
+    try:
+        w = wl.Workload("proj_capture_grow", 40, 8, 128, nt=300, n_ctx=4096, n_slots=1, layers=1,
+                        seed=24, pos_mode="uniform")
+        c = ProjCase(w, hidden=256)
+        c.run_oracle().upload()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            assert B.qkv_epilogue_run_proj(h, c.args()) == B.QKV_ERR_INVALID_ARG
+        assert "outside stream capture" in B.qkv_epilogue_last_error(h)
+        torch.cuda.synchronize()
+        assert torch.isnan(c.g_q).all()
+        assert B.qkv_epilogue_run_proj(h, c.args()) == B.QKV_OK
+        assert B.qkv_epilogue_status(h) == B.QKV_OK
+        torch.cuda.synchronize()
+        c.check("grown outside capture")
+    finally:
+        B.qkv_epilogue_destroy(h)
+
+
 def test_proj_graph_capture_split_and_fused(handle):
     """A k-split call (300 tokens) and a data-parallel call (1100 tokens)
     captured after a warm-up call; no allocation happens in the capture."""

@@ -197,7 +197,8 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  * row, which the epilogue consumes).  Per token t and output n:
  *     y[t][n] = sum_k x[t][k] * w[n][k]      (bf16 inputs, f32 accumulation)
  * then, on y split into its q, k, v sections, exactly the epilogue of
- * qkv_epilogue_run_ex: optional biases, NeoX rotary embedding of q and k, the
+ * qkv_epilogue_run_ex: optional biases, rotary embedding of q and k in the
+ * requested style (NeoX or interleaved) and frequency scale, the
  * sections written to epi.q / epi.k / epi.v (outputs only here) and the K/V
  * cache rows stored.  The GEMM runs on the matrix cores (MFMA) for more than
  * 4 tokens, as a weight-streaming GEMV for 1-4 tokens.  The epilogue runs on
@@ -214,7 +215,7 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  *       three matrices feed the one launch as they are, nothing repacked
  *   hidden  contraction length, a multiple of 64
  *
- * Limits (QKV_ERR_UNSUPPORTED otherwise): NeoX style, head_dim 64 or 128, q
+ * Limits (QKV_ERR_UNSUPPORTED otherwise): head_dim 64 or 128, q
  * and k/v widths multiples of 128; x and each weight matrix under 2 GiB
  * (QKV_ERR_INVALID_ARG).
  * The weights are read-only and may overlap one another, but none of x and

@@ -310,7 +310,7 @@ class Epilogue:
 
     def run_proj(self, x, w, q, k, v, bq, bk, bv, pos, kcache, vcache, *, n_head, n_kv_head,
                  head_dim, theta=1.0e6, w_k=None, w_v=None, slot=None, n_ctx=None, n_slots=None,
-                 stream=None):
+                 rope_style=QKV_ROPE_NEOX, freq_scale=0.0, stream=None):
         """The projection feeding the epilogue: x [nt][hidden] and the weights
         (w [nqt+2*nkt][hidden] concat, or w/w_k/w_v per section) as bfloat16
         device tensors; q, k, v are the float32 outputs; biases may be None."""
@@ -346,7 +346,8 @@ class Epilogue:
         epi = make_args(q, k, v, bq, bk, bv, pos, kcache, vcache, n_head=n_head,
                         n_kv_head=n_kv_head, head_dim=head_dim, theta=theta, cache_dtype=cd,
                         slot=slot, n_ctx=n_ctx or 0, n_slots=n_slots or 0, stream=stream,
-                        use_stream=True, nt=int(pos.numel()))
+                        use_stream=True, nt=int(pos.numel()), rope_style=rope_style,
+                        freq_scale=freq_scale)
         ld_x = x.stride(0) if x.stride(0) != hidden else 0
         rc = qkv_epilogue_run_proj(self.h, make_proj_args(x, w, hidden, epi, ld_x=ld_x, w_k=w_k,
                                                           w_v=w_v))

@@ -70,6 +70,7 @@ struct ProjParams {
     int ksplit;              // k splits of the MFMA path
     float *part;             // [ksplit][M][N] partial sums when ksplit > 1
     int device;              // the handle's device (launch set-up only)
+    int style;               // QKV_ROPE_NEOX (pair j, j + hd/2) or QKV_ROPE_INTERLEAVED (2i, 2i + 1)
     bool vec;                // sections, biases, caches 16-byte aligned, strides % 4 == 0
 };
 
@@ -217,9 +218,9 @@ struct Shape {
     // loads per stage of waves 0-3 and of waves 4-7
     static constexpr int kLoadsLo = kWaveA + (kInstB >= kWaves ? kWaveB : 0);
     static constexpr int kLoadsHi = (kInstA >= kWaves ? kWaveA : 0) + kWaveB;
-    // epilogue: the tile's pair indices (one group of an hd-128 head: 32;
-    // else all hd/2) as cos then sin per token, in 16-byte chunks
-    static constexpr int kPW = (HD == 128 && WN == 1 && G == 1) ? 32 : HD / 2;
+    // epilogue: every pair index of the head (either pairing reads any of
+    // them) as cos then sin per token, in 16-byte chunks
+    static constexpr int kPW = HD / 2;
     static constexpr int kChunks = kPW / 2;
     static constexpr int kTab = BM * kChunks * 16;
     static constexpr int kLds = kRing > kTab ? kRing : kTab;
@@ -278,12 +279,14 @@ __device__ __forceinline__ int group_lo(int g)
 }
 }  // namespace mm
 
-template <bool F16, int HD, int MI, int WN, int BK, int G>
+// IL: interleaved pairs (2i, 2i+1), else NeoX (j, j + hd/2); a template
+// argument so that the NeoX instance carries no code of the other rotation
+template <bool F16, int HD, int MI, int WN, int BK, int G, bool IL>
 __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
 {
     using namespace mm;
     using S = Shape<HD, MI, WN, BK, G>;
-    constexpr int BM = S::BM, BN = S::BN;
+    constexpr int BM = S::BM;
     constexpr int NSTAGE = S::NSTAGE, KS = S::KS, kRow = S::kRow;
     constexpr int HALF = HD / 2;
     constexpr int PT = HALF / 32;                 // tile distance of NeoX partners
@@ -502,10 +505,9 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     }
 
     // ---- epilogue ---------------------------------------------------------
-    // Stage the cos/sin slice of the tile's BM tokens (pair indices ih0 ..
-    // ih0 + kPW) into the LDS ring: chunk c of token r in slot c ^ (r % kChunks),
-    // which keeps the reads below (32 tokens, one chunk) conflict-free.
-    const int ih0 = S::kPW == HALF ? 0 : (group_lo<PT>(tn * GT) * 32) % HD;
+    // Stage the cos/sin table rows of the tile's BM tokens into the LDS ring:
+    // chunk c of token r in slot c ^ (r % kChunks), which keeps the reads
+    // below (32 tokens, one chunk) conflict-free.
     __syncthreads();                              // every wave is done with the ring
     {
         constexpr int kInst = BM * S::kChunks / 64;
@@ -514,7 +516,7 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
             const int r = ca / S::kChunks, sl = ca % S::kChunks;
             const int c = sl ^ (r % S::kChunks);
             const int tokc = min(m0 + r, p.M - 1);
-            const int col = c < S::kChunks / 2 ? ih0 + 4 * c : HALF + ih0 + 4 * (c - S::kChunks / 2);
+            const int col = 4 * c;                    // cos chunks, then sin
             __builtin_amdgcn_global_load_lds(p.rtab + (int64_t)tokc * HD + col, (lds_t *)(lds + u * 1024), 16, 0,
                                              0);
         }
@@ -559,7 +561,7 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
         float *const out = p.out[sec[g]];
         const int64_t ldo = p.ld[sec[g]];
         void *const cache = sec[g] == 1 ? p.cache[0] : p.cache[1];
-        const int cpair = (col0[g] % HD - ih0) / 4 + hi;   // chunk of (gg = 0) in the slice
+        const int cpair = (col0[g] % HD) / 4 + hi;   // cos chunk of (gg = 0)
 #pragma unroll
         for (int ti = 0; ti < MI; ++ti) {
             const int tok = tok0 + ti * 32;
@@ -583,7 +585,7 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
                     y0.e[e] = acc[2 * g * MI + ti][4 * gg + e] + bias0[g][gg].e[e];
                     y1.e[e] = acc[(2 * g + 1) * MI + ti][4 * gg + e] + bias1[g][gg].e[e];
                 }
-                if (sec[g] < 2) {
+                if (sec[g] < 2 && !IL) {
                     const int cc = cpair + 2 * gg;
                     const FVec<4> cv = *reinterpret_cast<const FVec<4> *>(trow + ((cc ^ (r % S::kChunks)) * 16));
                     const FVec<4> sv = *reinterpret_cast<const FVec<4> *>(
@@ -591,6 +593,20 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         rot(y0.e[e], y1.e[e], cv.e[e], sv.e[e]);
+                } else if (sec[g] < 2) {
+                    // interleaved pairs (2i, 2i+1) sit in the lane's own four
+                    // columns: pair indices pi, pi + 1 of one 16-byte chunk
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) {
+                        FVec<4> &y = f ? y1 : y0;
+                        const int pi = ((col0[g] + f * HALF + 8 * gg + 4 * hi) % HD) / 2;
+                        const int cc = pi / 4, e0 = pi % 4;
+                        const FVec<4> cv = *reinterpret_cast<const FVec<4> *>(trow + ((cc ^ (r % S::kChunks)) * 16));
+                        const FVec<4> sv = *reinterpret_cast<const FVec<4> *>(
+                            trow + (((cc + S::kChunks / 2) ^ (r % S::kChunks)) * 16));
+                        rot(y.e[0], y.e[1], cv.e[e0], sv.e[e0]);
+                        rot(y.e[2], y.e[3], cv.e[e0 + 1], sv.e[e0 + 1]);
+                    }
                 }
                 if (!p.vec) {
 #pragma unroll
@@ -673,8 +689,10 @@ __global__ __launch_bounds__(256) void proj_split_epilogue_kernel(ProjParams p, 
     const int64_t row = h1 > qheads ? cache_row(p, t) : -1;
     const int64_t plane = (int64_t)p.M * p.N;
     const float *const srow = p.part + (int64_t)t * p.N;
+    const bool il = p.style == QKV_ROPE_INTERLEAVED;
     for (int h = h0; h < h1; ++h) {
-        const int c0 = h * HD + i, c1 = c0 + HALF;
+        // pair i: columns (i, i + hd/2) of the head, interleaved (2i, 2i + 1)
+        const int c0 = h * HD + (il ? 2 * i : i), c1 = c0 + (il ? 1 : HALF);
         const float *src = srow;
         float y0 = src[c0], y1 = src[c1];
 #pragma unroll 4
@@ -746,14 +764,16 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
     const int nchunk = p.K / 8;              // hidden % 64 == 0: kGemvSplit divides it
     const int c_beg = kq * (nchunk / kGemvSplit);
     const int c_end = valid ? c_beg + nchunk / kGemvSplit : c_beg;
-    // rows 2q and 2q+1 are columns c0 and c0 + hd/2 of pair pair0 + q
+    // rows 2q and 2q+1 are the two columns of pair pair0 + q: c0 and c0 +
+    // hd/2 (NeoX) or c0 + 1 (interleaved)
+    const bool il = p.style == QKV_ROPE_INTERLEAVED;
     const uint16_t *wr[R];
 #pragma unroll
     for (int q = 0; q < P; ++q) {
         const int pr = valid ? pair0 + q : 0;
-        const int c0 = (pr / HALF) * HD + pr % HALF;
+        const int c0 = (pr / HALF) * HD + (il ? 2 * (pr % HALF) : pr % HALF);
         wr[2 * q] = weight_row<SEP>(p, c0);
-        wr[2 * q + 1] = weight_row<SEP>(p, c0 + HALF);
+        wr[2 * q + 1] = weight_row<SEP>(p, c0 + (il ? 1 : HALF));
     }
     const uint16_t *xr[NT];
 #pragma unroll
@@ -854,10 +874,10 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
             }
         const int pr = pair0 + q;
         const int i = pr % HALF;
-        const int c0 = (pr / HALF) * HD + i;     // global output column of the pair's first row
+        const int c0 = (pr / HALF) * HD + (il ? 2 * i : i);   // global output column of the pair's first row
         const int sec = c0 < p.nqt ? 0 : (c0 < p.nqt + p.nkt ? 1 : 2);
         const int sbase = sec == 0 ? 0 : (sec == 1 ? p.nqt : p.nqt + p.nkt);
-        const int s0 = c0 - sbase, s1 = s0 + HALF;   // columns inside the section
+        const int s0 = c0 - sbase, s1 = s0 + (il ? 1 : HALF);   // columns inside the section
         const float *bias = p.b[sec];
         if (bias) {
             y0 = y0 + bias[s0];
@@ -943,14 +963,14 @@ MmPlan mm_plan(int M, int N, int K, int cus)
 
 // Raise the kernel's dynamic-LDS limit to what it uses, once per kernel and
 // device (the caller has made the handle's device current).
-template <bool F16, int HD, int MI, int WN, int BK, int G>
+template <bool F16, int HD, int MI, int WN, int BK, int G, bool IL>
 hipError_t set_mm_lds(int device)
 {
     static std::atomic<unsigned long long> done{0};
     const unsigned long long bit = 1ull << (device & 63);
     if (done.load(std::memory_order_acquire) & bit)
         return hipSuccess;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&proj_mfma_kernel<F16, HD, MI, WN, BK, G>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&proj_mfma_kernel<F16, HD, MI, WN, BK, G, IL>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        mm::Shape<HD, MI, WN, BK, G>::kLds);
     if (e == hipSuccess && device < 64)
@@ -990,32 +1010,39 @@ hipError_t launch_gemv(const ProjParams &pp, const InvTable &inv, hipStream_t st
     return hipGetLastError();
 }
 
-template <bool F16, int HD, int MI, int WN, int BK, int G>
+template <bool F16, int HD, int MI, int WN, int BK, int G, bool IL>
 hipError_t launch_mm(const ProjParams &pp, hipStream_t st)
 {
     using S = mm::Shape<HD, MI, WN, BK, G>;
-    hipError_t e = set_mm_lds<F16, HD, MI, WN, BK, G>(pp.device);
+    hipError_t e = set_mm_lds<F16, HD, MI, WN, BK, G, IL>(pp.device);
     if (e != hipSuccess)
         return e;
     const int gt = WN * G;
     const int tiles = ((pp.M + S::BM - 1) / S::BM) * ((pp.N / 64 + gt - 1) / gt);
     constexpr unsigned lds = S::kLds;
-    hipLaunchKernelGGL((proj_mfma_kernel<F16, HD, MI, WN, BK, G>), dim3(tiles * pp.ksplit), dim3(mm::kThreads),
+    hipLaunchKernelGGL((proj_mfma_kernel<F16, HD, MI, WN, BK, G, IL>), dim3(tiles * pp.ksplit), dim3(mm::kThreads),
                        lds, st, pp);
     return hipGetLastError();
+}
+
+template <bool F16, int HD, bool IL>
+hipError_t launch_mm_shape(const ProjParams &pp, hipStream_t st, const MmPlan &pl)
+{
+    switch (pl.mi * 100 + pl.wn * 10 + pl.g) {
+    case 141: return launch_mm<F16, HD, 1, 4, 64, 1, IL>(pp, st);
+    case 121: return launch_mm<F16, HD, 1, 2, 64, 1, IL>(pp, st);
+    case 221: return launch_mm<F16, HD, 2, 2, 64, 1, IL>(pp, st);
+    case 441: return launch_mm<F16, HD, 4, 4, 64, 1, IL>(pp, st);
+    case 113: return launch_mm<F16, HD, 1, 1, 64, 3, IL>(pp, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <bool F16, int HD>
 hipError_t launch_mm_plan(const ProjParams &pp, hipStream_t st, const MmPlan &pl)
 {
-    switch (pl.mi * 100 + pl.wn * 10 + pl.g) {
-    case 141: return launch_mm<F16, HD, 1, 4, 64, 1>(pp, st);
-    case 121: return launch_mm<F16, HD, 1, 2, 64, 1>(pp, st);
-    case 221: return launch_mm<F16, HD, 2, 2, 64, 1>(pp, st);
-    case 441: return launch_mm<F16, HD, 4, 4, 64, 1>(pp, st);
-    case 113: return launch_mm<F16, HD, 1, 1, 64, 3>(pp, st);
-    default: return hipErrorInvalidValue;
-    }
+    return pp.style == QKV_ROPE_INTERLEAVED ? launch_mm_shape<F16, HD, true>(pp, st, pl)
+                                            : launch_mm_shape<F16, HD, false>(pp, st, pl);
 }
 
 template <bool F16, int HD>
@@ -1065,8 +1092,6 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
     int rc = check_and_plan(a, h->n_ctx, &pl, h->msg, sizeof h->msg, kPlanBiasOptional);
     if (rc != QKV_OK)
         return rc;
-    if (a->rope_style != QKV_ROPE_NEOX)
-        return fail(h, QKV_ERR_UNSUPPORTED, "the projection path implements NeoX pairing only");
     if (a->head_dim != 64 && a->head_dim != 128)
         return fail(h, QKV_ERR_UNSUPPORTED, "the projection path needs head_dim 64 or 128, got %d",
                     a->head_dim);
@@ -1163,6 +1188,7 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
     pp.ksplit = 1;
     pp.part = nullptr;
     pp.device = h->device;
+    pp.style = a->rope_style;
 
     const InvTable &inv = handle_inv(h, a->theta, a->head_dim, a->freq_scale);
     hipStream_t st = (a->stream || a->use_stream) ? static_cast<hipStream_t>(a->stream) : h->stream;

@@ -44,7 +44,8 @@ def handle():
 
 class ProjCase:
     def __init__(self, w, hidden, nt=None, cache_dtype=None, form="separate", bias=True,
-                 pos=None, slot=None, sample=None, ld_x_pad=0, misalign=0, weights="concat"):
+                 pos=None, slot=None, sample=None, ld_x_pad=0, misalign=0, weights="concat",
+                 style=B.QKV_ROPE_NEOX, freq_scale=1.0):
         self.w, self.hidden = w, hidden
         d = wl.draw_projection(w, hidden, nt=nt)
         if pos is not None:
@@ -58,6 +59,7 @@ class ProjCase:
         self.ld_x_pad = ld_x_pad
         self.misalign = misalign   # shift every output section by this many floats
         self.weights = weights     # "concat" [N][hidden], or "three" q, k, v matrices
+        self.style, self.freq_scale = style, freq_scale
         # tokens the oracle recomputes (all of them unless a sample is given)
         self.sample = np.arange(self.nt) if sample is None else np.asarray(sample)
 
@@ -80,7 +82,8 @@ class ProjCase:
         rid, kr, vr, bad = oracle.qkv_epilogue(
             q.ravel(), k.ravel(), v.ravel(), *b, np.ascontiguousarray(d["pos"][s]),
             n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim, theta=w.theta,
-            n_ctx=w.n_ctx, cache_dtype=self.cd, slot=slot, n_slots=w.n_slots)
+            n_ctx=w.n_ctx, cache_dtype=self.cd, slot=slot, n_slots=w.n_slots,
+            rope_style=self.style, freq_scale=self.freq_scale)
         self.o = dict(q=q, k=k, v=v, S=S)
         # the cache rows of every token (addressing only: the chain on zeros)
         zq = np.zeros(self.nt * nqt, np.float32)
@@ -142,7 +145,8 @@ class ProjCase:
                           n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim,
                           theta=w.theta, cache_dtype=self.cd, slot=self.g_slot, n_ctx=w.n_ctx,
                           n_slots=w.n_slots, stream=torch.cuda.current_stream(),
-                          use_stream=True, nt=self.nt)
+                          use_stream=True, nt=self.nt, rope_style=self.style,
+                          freq_scale=self.freq_scale)
         return B.make_proj_args(self.g_x, self.g_w, self.hidden, epi, ld_x=self.ld_x, w_k=self.g_wk,
                                 w_v=self.g_wv)
 
@@ -164,7 +168,11 @@ class ProjCase:
             g = got[name].astype(np.float64)
             o = self.o[name].astype(np.float64)
             b = secs[name]
-            if name != "v":
+            if name != "v" and self.style == B.QKV_ROPE_INTERLEAVED:
+                # partner of column j: j ^ 1
+                bh = b.reshape(b.shape[0], -1, 2)
+                b = (bh + bh[:, :, ::-1]).reshape(b.shape)
+            elif name != "v":
                 # partner of column j inside its head: j +- half
                 bh = b.reshape(b.shape[0], -1, 2, half)
                 b = (bh + bh[:, :, ::-1, :]).reshape(b.shape)
@@ -352,7 +360,7 @@ def test_proj_rejects_unsupported(handle):
     c = ProjCase(SMALL_05B, hidden=512, nt=8).upload()
     base = c.args()
     a = c.args()
-    a.epi.rope_style = B.QKV_ROPE_INTERLEAVED
+    a.epi.rope_style = 2     # no such style
     assert B.qkv_epilogue_run_proj(handle, a) == B.QKV_ERR_UNSUPPORTED
     a = c.args()
     a.hidden = 100
@@ -496,7 +504,8 @@ def _random_shape(seed):
     """A seeded random projection case inside the path's limits: head_dim 64 or
     128, q and k/v widths multiples of 128, hidden a multiple of 64, 1-700
     tokens, either cache type, concat or three weight matrices, biases or none,
-    one sequence or per-token slots."""
+    one sequence or per-token slots, NeoX or interleaved pairing, a frequency
+    scale or none."""
     rng = np.random.default_rng(1000 + seed)
     hd = int(rng.choice([64, 128]))
     step = 128 // hd                              # heads per 128 columns
@@ -508,15 +517,18 @@ def _random_shape(seed):
     cd = int(rng.choice([wl.CACHE_F32, wl.CACHE_F16]))
     w = wl.Workload(f"proj_rand_{seed}", n_head, n_kv_head, hd, nt=nt, n_ctx=1024, n_slots=slots,
                     layers=1, seed=40 + seed, cache_dtypes=(cd,), pos_mode="uniform")
-    return w, dict(hidden=hidden, bias=bool(rng.integers(0, 2)),
-                   weights=str(rng.choice(["concat", "three"])))
+    kw = dict(hidden=hidden, bias=bool(rng.integers(0, 2)), weights=str(rng.choice(["concat", "three"])))
+    kw["style"] = int(rng.integers(0, 2))
+    kw["freq_scale"] = float(rng.choice([1.0, 0.25]))
+    return w, kw
 
 
 @pytest.mark.parametrize("seed", range(40))
 def test_proj_random_shapes(handle, seed):
     """Seeded random shapes across the launch plans (GEMV, k-split and
     data-parallel MFMA tiles of every shape), both head dims, both cache
-    types, both weight layouts, with or without biases and slots."""
+    types, both weight layouts, with or without biases and slots, both
+    pairings."""
     w, kw = _random_shape(seed)
     c = ProjCase(w, **kw)
     assert _run(handle, c, f"rand_{seed}") == B.QKV_OK
@@ -526,11 +538,12 @@ def test_proj_random_shapes(handle, seed):
 @pytest.mark.parametrize("weights", ["concat", "three"])
 def test_proj_python_wrapper(weights):
     """Epilogue.run_proj (the checked torch-tensor wrapper of the same entry
-    point) on a 40-token 14B batch, against the oracle; wrong dtypes raise
-    before any launch."""
+    point) on a 40-token 14B batch, against the oracle (three matrices with
+    interleaved pairing); wrong dtypes raise before any launch."""
     w = wl.Workload("proj_wrapper", 40, 8, 128, nt=40, n_ctx=1024, n_slots=1, layers=1,
                     seed=32, pos_mode="uniform")
-    c = ProjCase(w, hidden=512, weights=weights)
+    style = B.QKV_ROPE_INTERLEAVED if weights == "three" else B.QKV_ROPE_NEOX
+    c = ProjCase(w, hidden=512, weights=weights, style=style)
     c.run_oracle().upload()
     ep = B.Epilogue(0, w.n_ctx)
     bf = torch.bfloat16
@@ -542,7 +555,7 @@ def test_proj_python_wrapper(weights):
                     w_k=wk, w_v=wv)
     ep.run_proj(c.g_x.view(bf), c.g_w.view(bf), c.g_q, c.g_k, c.g_v, *c.g_b, c.g_pos, c.kc, c.vc,
                 n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim, theta=w.theta,
-                w_k=wk, w_v=wv)
+                w_k=wk, w_v=wv, rope_style=style)
     assert ep.status() == B.QKV_OK, ep.last_error()
     torch.cuda.synchronize()
     c.check(f"wrapper_{weights}")
@@ -661,3 +674,33 @@ def test_proj_graph_capture_split_and_fused(handle):
                      seed=23, pos_mode="uniform")
     cases = [ProjCase(w1, hidden=256).upload(), ProjCase(w2, hidden=256).upload()]
     _graph_replays(handle, cases)
+
+
+@pytest.mark.parametrize("geom,nt", [("14b", 1), ("14b", 3), ("14b", 40), ("14b", 300), ("14b", 1030),
+                                     ("0.5b", 2), ("0.5b", 257), ("0.5b", 1100)])
+def test_proj_interleaved(handle, geom, nt):
+    """Interleaved (GPT-J) pairs (2i, 2i+1): the GEMV (1-3 tokens) takes
+    adjacent weight rows as a pair; MFMA launches of 40-1100 tokens, with or
+    without a k split as the plan picks, rotate inside each lane's four
+    consecutive outputs or pair adjacent columns in the summing kernel; hd
+    128, and hd 64 with a frequency scale."""
+    if geom == "14b":
+        w = wl.Workload("proj_il_14b", 40, 8, 128, nt=nt, n_ctx=4096, n_slots=1, layers=1,
+                        seed=60 + nt, pos_mode="uniform")
+        c = ProjCase(w, hidden=512, style=B.QKV_ROPE_INTERLEAVED)
+    else:
+        w = wl.Workload("proj_il_0.5b", 14, 2, 64, nt=nt, n_ctx=2048, n_slots=1, layers=1,
+                        seed=70 + nt, cache_dtypes=(wl.CACHE_F16,), pos_mode="arange")
+        c = ProjCase(w, hidden=896, style=B.QKV_ROPE_INTERLEAVED, freq_scale=0.25)
+    assert _run(handle, c, f"interleaved_{geom}_{nt}") == B.QKV_OK
+    c.check(f"interleaved_{geom}_{nt}")
+
+
+def test_proj_interleaved_full_size_sampled(handle):
+    """4096 tokens x hidden 5120 with interleaved pairing (the largest tile
+    shape), sampled tokens against the oracle."""
+    rng = np.random.default_rng(11)
+    sample = np.unique(np.concatenate([[0, 255, 256, 4095], rng.integers(0, 4096, 28)]))
+    c = ProjCase(wl.PREFILL_14B, hidden=5120, sample=sample, style=B.QKV_ROPE_INTERLEAVED)
+    assert _run(handle, c, "interleaved_full") == B.QKV_OK
+    c.check("interleaved_full")

@@ -70,6 +70,10 @@ def _bind(lib):
     lib.oracle_rope_interleaved.restype = None
     lib.oracle_proj_bf16.argtypes = [P, I64, P, I64, I64, I64, P, I64]
     lib.oracle_proj_bf16.restype = None
+    lib.oracle_e4m3_decode.argtypes = [P, I64, P]
+    lib.oracle_e4m3_decode.restype = None
+    lib.oracle_proj_fp8w.argtypes = [P, I64, P, P, I64, I64, I64, P, I64]
+    lib.oracle_proj_fp8w.restype = None
     lib.oracle_qkv_norm_epilogue.restype = I64
     return lib
 
@@ -303,4 +307,34 @@ def proj_bf16(x_bits, w_bits):
     assert h2 == hidden
     y = np.zeros((nt, n_out), np.float32)
     _load().oracle_proj_bf16(_ptr(x_bits), hidden, _ptr(w_bits), nt, n_out, hidden, _ptr(y), n_out)
+    return y
+
+
+def e4m3_values(codes):
+    """The real value (float64; NaN for 0x7f / 0xff) of each OCP E4M3 code
+    (uint8 array)."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    out = np.zeros(codes.shape, np.float64)
+    _load().oracle_e4m3_decode(_ptr(codes), codes.size, _ptr(out))
+    return out
+
+
+def proj_fp8w(x_bits, w_codes, scale):
+    """Step P with 8-bit float weights: y[t][n] = f32(scale[n] * sum_k x[t][k]
+    * e4m3(w[n][k])), x bfloat16 bits [nt][hidden], w uint8 E4M3 codes
+    [n_out][hidden], scale float32 [n_out]; exact products, double sum."""
+    if not (isinstance(x_bits, np.ndarray) and x_bits.dtype == np.uint16 and x_bits.ndim == 2
+            and x_bits.flags.c_contiguous):
+        raise TypeError("x must be a C-contiguous 2-D uint16 (bfloat16 bits) array")
+    if not (isinstance(w_codes, np.ndarray) and w_codes.dtype == np.uint8 and w_codes.ndim == 2
+            and w_codes.flags.c_contiguous):
+        raise TypeError("w must be a C-contiguous 2-D uint8 (E4M3 codes) array")
+    nt, hidden = x_bits.shape
+    n_out, h2 = w_codes.shape
+    assert h2 == hidden
+    scale = np.ascontiguousarray(scale, np.float32)
+    assert scale.shape == (n_out,)
+    y = np.zeros((nt, n_out), np.float32)
+    _load().oracle_proj_fp8w(_ptr(x_bits), hidden, _ptr(w_codes), _ptr(scale), nt, n_out, hidden,
+                             _ptr(y), n_out)
     return y

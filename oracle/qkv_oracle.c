@@ -173,6 +173,54 @@ void oracle_proj_bf16(const uint16_t *x, int64_t ld_x, const uint16_t *w,
 }
 
 /* ---------------------------------------------------------------------------
+ * Step P with 8-bit float weights (weight-only quantisation of the same
+ * matmul).  Reading, since the page's own weights are block-quantised and it
+ * fixes no 8-bit format: every weight is an OCP 8-bit float in the E4M3
+ * encoding -- sign bit, 4 exponent bits with bias 7, 3 mantissa bits; an
+ * exponent field of 0 holds the subnormals m * 2^-9; the two patterns with
+ * all exponent and mantissa bits set (0x7f, 0xff) are NaN; there is no
+ * infinity -- and each weight row n carries one f32 scale s[n]:
+ *   y[t][n] = f32( s[n] * sum_k x[t][k] * e4m3(w[n][k]) ),
+ * x bfloat16 as above, the products exact in double, the sum in double in k
+ * order, times the scale in double, rounded once to f32.
+ * ------------------------------------------------------------------------- */
+static double oracle_e4m3_to_double(uint8_t b)
+{
+    const int sign = b >> 7;
+    const int e = (b >> 3) & 15;
+    const int m = b & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);               /* m/8 * 2^(1-7) */
+    else
+        v = ldexp((double)(8 + m), e - 10);     /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+void oracle_e4m3_decode(const uint8_t *b, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e4m3_to_double(b[i]);
+}
+
+void oracle_proj_fp8w(const uint16_t *x, int64_t ld_x, const uint8_t *w,
+                      const float *scale, int64_t nt, int64_t n_out,
+                      int64_t hidden, float *y, int64_t ld_y)
+{
+    for (int64_t t = 0; t < nt; ++t) {
+        for (int64_t n = 0; n < n_out; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < hidden; ++k)
+                acc += oracle_bf16_to_double(x[t * ld_x + k]) *
+                       oracle_e4m3_to_double(w[n * hidden + k]);
+            y[t * ld_y + n] = (float)((double)scale[n] * acc);
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
  * Step N -- per-head RMS norm (the q/k norm of the Qwen3-style variant).
  * Page "06 · Assign + fusion" §3.2 lists a per-head q/k norm op (QkNorm) and
  * the fused FusedQkvNorm, "the Qwen3 per-head-norm variant", without a

@@ -15,6 +15,7 @@ import pytest
 import oracle
 import test_oracle_norm_pins as npins
 import test_oracle_pins as pins
+import test_oracle_fp8_pins as fpins
 import test_oracle_proj_pins as ppins
 import test_oracle_rope_variants as rpins
 from qkv_bias_rope_amd import workloads as wl
@@ -95,6 +96,13 @@ MUTATIONS = [
     ("projection bf16 decoded as low half", [("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b;")]),
     ("projection accumulates in f32", [("            double acc = 0.0;\n            for (int64_t k = 0; k < hidden; ++k)",
                                         "            float acc = 0.0f;\n            for (int64_t k = 0; k < hidden; ++k)")]),
+    # 8-bit float weights
+    ("e4m3 exponent bias 8", [("v = ldexp((double)(8 + m), e - 10);", "v = ldexp((double)(8 + m), e - 11);")]),
+    ("e4m3 subnormals read as normals", [("    if (e == 0)\n        v = ldexp((double)m, -9);", "    if (0)\n        v = ldexp((double)m, -9);")]),
+    ("e4m3 sign ignored", [("    return sign ? -v : v;", "    return v;")]),
+    ("e4m3 NaN pattern read as a number", [("    if (e == 15 && m == 7)\n        return NAN;", "    if (0)\n        return NAN;")]),
+    ("fp8 row scale ignored", [("y[t * ld_y + n] = (float)((double)scale[n] * acc);", "y[t * ld_y + n] = (float)acc;")]),
+    ("fp8 scale of the wrong row", [("y[t * ld_y + n] = (float)((double)scale[n] * acc);", "y[t * ld_y + n] = (float)((double)scale[0] * acc);")]),
     ("bias after norm", [("    if (bq)\n        oracle_add_bias(q, bq, nt, nqt, ld_q);\n", ""),
                          ("    oracle_rms_norm_heads(q, nt, ld_q, n_head, head_dim, wq, eps);\n",
                           "    oracle_rms_norm_heads(q, nt, ld_q, n_head, head_dim, wq, eps);\n"
@@ -147,6 +155,12 @@ def _pin_calls():
         ("projection identity", ppins.test_identity_weights_copy_the_input),
         ("projection permutation", ppins.test_row_permutation_permutes_outputs),
         ("projection numpy", ppins.test_matches_numpy_float64_matmul),
+        ("e4m3 table vs torch", fpins.test_code_table_matches_torch),
+        ("e4m3 closed forms", fpins.test_code_table_closed_forms),
+        ("fp8 projection exact rational", fpins.test_exact_rational_small),
+        ("fp8 projection = bf16 of decoded", fpins.test_equals_bf16_projection_of_the_decoded_values),
+        ("fp8 scale once per row", fpins.test_scale_applies_once_per_row),
+        ("fp8 single codes", fpins.test_single_code_rows_decode_exactly),
     ]
 
 

@@ -283,10 +283,11 @@ PEAK_BF16_TFLOPS = 2500.0
 
 class ProjSets:
     """Input sets of the projection-fed epilogue: bf16 activations and concat
-    weights, f32 q/k/v outputs and the caches, R copies rotated so that the
-    weights and activations come from HBM on every launch."""
+    weights (bf16, or E4M3 codes with f32 row scales), f32 q/k/v outputs and
+    the caches, R copies rotated so that the weights and activations come from
+    HBM on every launch."""
 
-    def __init__(self, w, hidden, R, cache_dtype, nt=None):
+    def __init__(self, w, hidden, R, cache_dtype, nt=None, wfmt="bf16"):
         import numpy as np
         import torch
         from qkv_bias_rope_amd import workloads as wl
@@ -296,7 +297,14 @@ class ProjSets:
         self.nt = int(d["pos"].size)
         cdt = torch.float16 if cache_dtype == wl.CACHE_F16 else torch.float32
         x = torch.from_numpy(d["x"].view(np.int16)).to(dev)
-        wt = torch.from_numpy(d["w"].view(np.int16)).to(dev)
+        self.wfmt = wfmt
+        self.scale = None
+        if wfmt == "e4m3":
+            codes, scale = wl.draw_e4m3_weights(w.nqt + 2 * w.nkt, hidden, w.seed)
+            wt = torch.from_numpy(codes).to(dev)
+            self.scale = torch.from_numpy(scale).to(dev)
+        else:
+            wt = torch.from_numpy(d["w"].view(np.int16)).to(dev)
         self.b = [torch.from_numpy(d[n]).to(dev) for n in ("bq", "bk", "bv")]
         pos = torch.from_numpy(d["pos"]).to(dev)
         slot = None if d["slot"] is None else torch.from_numpy(d["slot"]).to(dev)
@@ -320,19 +328,24 @@ class ProjSets:
                           n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim,
                           theta=w.theta, cache_dtype=self.cd, slot=s["slot"], n_ctx=w.n_ctx,
                           n_slots=w.n_slots, stream=stream, use_stream=True, nt=self.nt)
+        if self.wfmt == "e4m3":
+            return B.make_proj_args(s["x"], s["w"], self.hidden, epi, w_format=B.QKV_WEIGHT_E4M3,
+                                    w_scale=self.scale)
         return B.make_proj_args(s["x"], s["w"], self.hidden, epi)
 
 
-def proj_bytes(w, nt, hidden, cb):
-    """Algorithmic HBM bytes of one projection-fed launch: x and W once, the
-    q/k/v rows written, the K/V cache rows, positions and biases."""
+def proj_bytes(w, nt, hidden, cb, wfmt="bf16"):
+    """Algorithmic HBM bytes of one projection-fed launch: x and W once (and
+    the row scales of E4M3 weights), the q/k/v rows written, the K/V cache
+    rows, positions and biases."""
     n = w.nqt + 2 * w.nkt
-    return (nt * hidden * 2 + n * hidden * 2 + nt * n * 4 + 2 * nt * w.nkt * cb + nt * 4
+    wbytes = n * hidden + n * 4 if wfmt == "e4m3" else n * hidden * 2
+    return (nt * hidden * 2 + wbytes + nt * n * 4 + 2 * nt * w.nkt * cb + nt * 4
             + n * 4)
 
 
-def bench_proj(h, w, hidden, steps, warmup, stream, min_set_bytes=1.5e9, nt=None):
-    """Projection-fed epilogue (one launch: bf16 GEMM/GEMV + epilogue)."""
+def bench_proj(h, w, hidden, steps, warmup, stream, min_set_bytes=1.5e9, nt=None, wfmt="bf16"):
+    """Projection-fed epilogue (one launch: GEMM/GEMV + epilogue)."""
     import torch
     from qkv_bias_rope_amd import binding as B
     from qkv_bias_rope_amd import workloads as wl
@@ -340,15 +353,19 @@ def bench_proj(h, w, hidden, steps, warmup, stream, min_set_bytes=1.5e9, nt=None
     cb = 2 if cd == wl.CACHE_F16 else 4
     nt = w.nt if nt is None else nt
     n = w.nqt + 2 * w.nkt
-    per_set = nt * hidden * 2 + n * hidden * 2 + nt * n * 4
+    per_set = nt * hidden * 2 + n * hidden * (1 if wfmt == "e4m3" else 2) + nt * n * 4
     R = max(2, int(-(-min_set_bytes // per_set)))
-    sets = ProjSets(w, hidden, R, cd, nt=nt)
+    sets = ProjSets(w, hidden, R, cd, nt=nt, wfmt=wfmt)
     args = [sets.args(r, stream) for r in range(R)]
     ms = time_launches(h, args, steps, warmup, stream, fn=B.qkv_epilogue_run_proj)
     flops = 2.0 * nt * n * hidden
-    nbytes = proj_bytes(w, nt, hidden, cb)
+    nbytes = proj_bytes(w, nt, hidden, cb, wfmt)
     res = dict(us_per_launch=ms * 1e3, tflops=flops / (ms * 1e-3) / 1e12,
                gbs=nbytes / (ms * 1e-3) / 1e9, flops=flops, bytes=nbytes, sets=R)
+    if wfmt == "e4m3":
+        del sets
+        torch.cuda.empty_cache()
+        return res
     # reference: torch's bf16 matmul of the same shape (library GEMM, bf16 out,
     # no epilogue), event-timed per call over the same rotating input sets so
     # its operands come from HBM too; host overhead included
@@ -372,14 +389,14 @@ def bench_proj(h, w, hidden, steps, warmup, stream, min_set_bytes=1.5e9, nt=None
     return res
 
 
-def bench_proj_decode(h, w, hidden, steps, warmup, stream):
+def bench_proj_decode(h, w, hidden, steps, warmup, stream, wfmt="bf16"):
     """A decode step of the projection-fed epilogue: one token, one launch per
     layer, every layer with its own weights (48 x 73 MB at 14B, so each step
     streams them from HBM).  Microseconds per layer for a stream loop and for a
     HIP-graph replay of the whole step."""
     import torch
     from qkv_bias_rope_amd import binding as B
-    layers = [ProjSets(w, hidden, 1, w.cache_dtypes[0], nt=1) for _ in range(w.layers)]
+    layers = [ProjSets(w, hidden, 1, w.cache_dtypes[0], nt=1, wfmt=wfmt) for _ in range(w.layers)]
     args = [ls.args(0, stream) for ls in layers]
     n_loops = max(1, steps)
     ms_step = time_launches(h, args, n_loops * w.layers, warmup * w.layers, stream,
@@ -670,6 +687,20 @@ def run_all(args, h, stream):
         r = bench_proj_decode(h, wd, hid, max(5, args.steps // 20), 2, stream)
         extra[wd.name + "_proj_step"] = {k: (round(v, 3) if isinstance(v, float) else v)
                                          for k, v in r.items()}
+        log(f"[bench]   {r['us_per_layer_stream']:.2f} us/layer (stream), "
+            f"{r['us_per_layer_graph']:.2f} us/layer (graph)")
+        # the same decode with E4M3 weights and row scales (half the weight bytes)
+        log(f"[bench] {wd.name} projection-fed epilogue, one token, E4M3 weights")
+        r = bench_proj(h, wd, hid, max(50, args.steps // 2), max(5, args.warmup // 2), stream,
+                       min_set_bytes=1.5e9, wfmt="e4m3")
+        extra[wd.name + "_proj_e4m3"] = dict(
+            us_per_layer=round(r["us_per_launch"], 2), gbs=round(r["gbs"], 1),
+            frac_of_peak=round(r["gbs"] / PEAK_HBM_GBS, 4), bytes_per_layer=r["bytes"],
+            hidden=hid, input_sets=r["sets"])
+        log(f"[bench]   {r['us_per_launch']:.1f} us/layer, {r['gbs']:.1f} GB/s")
+        r = bench_proj_decode(h, wd, hid, max(5, args.steps // 20), 2, stream, wfmt="e4m3")
+        extra[wd.name + "_proj_e4m3_step"] = {k: (round(v, 3) if isinstance(v, float) else v)
+                                              for k, v in r.items()}
         log(f"[bench]   {r['us_per_layer_stream']:.2f} us/layer (stream), "
             f"{r['us_per_layer_graph']:.2f} us/layer (graph)")
 

@@ -68,6 +68,10 @@ extern "C" {
 #define QKV_ROPE_NEOX 0         /* pair i with i + head_dim/2 (default) */
 #define QKV_ROPE_INTERLEAVED 1  /* pair 2i with 2i+1 (GPT-J style) */
 
+/* weight formats of qkv_epilogue_run_proj */
+#define QKV_WEIGHT_BF16 0       /* bfloat16 weights (default) */
+#define QKV_WEIGHT_E4M3 1       /* OCP 8-bit float E4M3 weights, one f32 scale per row */
+
 /* Largest supported head_dim (the inverse-frequency table travels with the
  * launch and holds head_dim/2 values). */
 #define QKV_MAX_HEAD_DIM 512
@@ -214,6 +218,20 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  *       one concat matrix run three matmuls into one epilogue (§2); here the
  *       three matrices feed the one launch as they are, nothing repacked
  *   hidden  contraction length, a multiple of 64
+ *   w_format  QKV_WEIGHT_BF16, or QKV_WEIGHT_E4M3: w (and w_k, w_v) then hold
+ *       one byte per weight, an OCP 8-bit float in the E4M3 encoding (sign, 4
+ *       exponent bits with bias 7, 3 mantissa bits, subnormals, 0x7f/0xff NaN,
+ *       no infinity), and row n of the q|k|v rows has the f32 scale
+ *       w_scale[n]: y[t][n] = w_scale[n] * sum_k x[t][k] * w[n][k].  The same
+ *       page's matmul runs on block-quantised weights; this is a weight-only
+ *       8-bit form of it, which halves the bytes a decode step streams.
+ *       E4M3 weights run on the weight-streaming kernel only: 1-4 tokens
+ *       (more is QKV_ERR_UNSUPPORTED); each E4M3 value is converted to bf16
+ *       exactly and the products summed in f32 as for bf16 weights, then
+ *       multiplied by the scale (one more f32 rounding).
+ *   w_scale  E4M3 only: f32 [nqt + 2*nkt] row scales (device, 4-byte
+ *       aligned), indexed by the output's q|k|v column also when the weights
+ *       come as three matrices; read-only, must not overlap an output.
  *
  * Limits (QKV_ERR_UNSUPPORTED otherwise): head_dim 64 or 128, q
  * and k/v widths multiples of 128; x and each weight matrix under 2 GiB
@@ -245,6 +263,8 @@ typedef struct qkv_proj_args {
     qkv_epilogue_args_t epi;  /* q/k/v are the outputs; biases may be NULL */
     const void *w_k;        /* NULL, or bf16 [nkt][hidden] */
     const void *w_v;        /* NULL, or bf16 [nkt][hidden] */
+    int w_format;           /* QKV_WEIGHT_BF16 (0) or QKV_WEIGHT_E4M3 (1) */
+    const float *w_scale;   /* E4M3: f32 [nqt + 2*nkt] row scales (device); else ignored */
 } qkv_proj_args_t;
 
 int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *a);

@@ -33,6 +33,8 @@ QKV_CACHE_F32 = 0
 QKV_CACHE_F16 = 1
 QKV_ROPE_NEOX = 0
 QKV_ROPE_INTERLEAVED = 1
+QKV_WEIGHT_BF16 = 0
+QKV_WEIGHT_E4M3 = 1
 QKV_MAX_HEAD_DIM = 512
 
 EXPORTS = ("qkv_epilogue_create", "qkv_epilogue_run", "qkv_epilogue_run_ex",
@@ -69,7 +71,8 @@ class QkvEpilogueArgs(ctypes.Structure):
 
 class QkvProjArgs(ctypes.Structure):
     _fields_ = [("x", _P), ("w", _P), ("hidden", _I), ("ld_x", _I64),
-                ("epi", QkvEpilogueArgs), ("w_k", _P), ("w_v", _P)]
+                ("epi", QkvEpilogueArgs), ("w_k", _P), ("w_v", _P), ("w_format", _I),
+                ("w_scale", _P)]
 
 
 class QkvEpiloguePlan(ctypes.Structure):
@@ -166,14 +169,17 @@ def qkv_epilogue_run_proj(h, args: QkvProjArgs) -> int:
     return lib.qkv_epilogue_run_proj(h, ctypes.byref(args))
 
 
-def make_proj_args(x, w, hidden, epi: QkvEpilogueArgs, ld_x=0, w_k=None, w_v=None) -> QkvProjArgs:
+def make_proj_args(x, w, hidden, epi: QkvEpilogueArgs, ld_x=0, w_k=None, w_v=None,
+                   w_format=QKV_WEIGHT_BF16, w_scale=None) -> QkvProjArgs:
     """Build the run_proj argument block: bf16 activations x and concat weight
-    rows w (tensors of any 2-byte dtype, or raw addresses) -- or, with w_k and
-    w_v, the q, k and v weights as three matrices -- the contraction length
-    and the epilogue block whose q/k/v are the outputs."""
+    rows w (tensors, or raw addresses) -- or, with w_k and w_v, the q, k and v
+    weights as three matrices -- the contraction length and the epilogue block
+    whose q/k/v are the outputs.  w_format QKV_WEIGHT_E4M3: one-byte E4M3
+    weights with the f32 row scales w_scale."""
     pa = QkvProjArgs()
     pa.x, pa.w = _addr(x), _addr(w)
     pa.w_k, pa.w_v = _addr(w_k), _addr(w_v)
+    pa.w_format, pa.w_scale = w_format, _addr(w_scale)
     pa.hidden = hidden
     pa.ld_x = ld_x
     pa.epi = epi
@@ -310,10 +316,12 @@ class Epilogue:
 
     def run_proj(self, x, w, q, k, v, bq, bk, bv, pos, kcache, vcache, *, n_head, n_kv_head,
                  head_dim, theta=1.0e6, w_k=None, w_v=None, slot=None, n_ctx=None, n_slots=None,
-                 rope_style=QKV_ROPE_NEOX, freq_scale=0.0, stream=None):
-        """The projection feeding the epilogue: x [nt][hidden] and the weights
-        (w [nqt+2*nkt][hidden] concat, or w/w_k/w_v per section) as bfloat16
-        device tensors; q, k, v are the float32 outputs; biases may be None."""
+                 rope_style=QKV_ROPE_NEOX, freq_scale=0.0, w_scale=None, stream=None):
+        """The projection feeding the epilogue: x [nt][hidden] as a bfloat16
+        device tensor, the weights (w [nqt+2*nkt][hidden] concat, or w/w_k/w_v
+        per section) bfloat16 -- or float8_e4m3fn with w_scale, a float32
+        [nqt+2*nkt] tensor of row scales (1-4 tokens); q, k, v are the float32
+        outputs; biases may be None."""
         import torch
         if kcache.dtype == torch.float32:
             cd = QKV_CACHE_F32
@@ -325,10 +333,20 @@ class Epilogue:
             raise TypeError("kcache and vcache must share a dtype")
         if (w_k is None) != (w_v is None):
             raise TypeError("w_k and w_v go together")
-        for name, t in (("x", x), ("w", w), ("w_k", w_k), ("w_v", w_v)):
-            if t is not None and (t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 2
-                                  or t.stride(1) != 1):
-                raise TypeError(f"{name} must be a 2-D bfloat16 device tensor with unit column stride")
+        if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
+            raise TypeError("x must be a 2-D bfloat16 device tensor with unit column stride")
+        wdt = w.dtype
+        if wdt not in (torch.bfloat16, torch.float8_e4m3fn):
+            raise TypeError(f"w must be bfloat16 or float8_e4m3fn, got {wdt}")
+        for name, t in (("w", w), ("w_k", w_k), ("w_v", w_v)):
+            if t is not None and (t.dtype != wdt or not t.is_cuda or t.dim() != 2):
+                raise TypeError(f"{name} must be a 2-D device tensor of the weights' dtype {wdt}")
+        w8 = wdt == torch.float8_e4m3fn
+        if w8 != (w_scale is not None):
+            raise TypeError("w_scale goes with float8_e4m3fn weights, and only with them")
+        if w8 and (w_scale.dtype != torch.float32 or not w_scale.is_cuda or not w_scale.is_contiguous()
+                   or w_scale.numel() != (n_head + 2 * n_kv_head) * head_dim):
+            raise TypeError("w_scale must be a contiguous float32 device tensor of nqt + 2*nkt scales")
         for name, t in (("w", w), ("w_k", w_k), ("w_v", w_v)):
             if t is not None and not t.is_contiguous():
                 raise TypeError(f"{name} must be contiguous")
@@ -349,8 +367,9 @@ class Epilogue:
                         use_stream=True, nt=int(pos.numel()), rope_style=rope_style,
                         freq_scale=freq_scale)
         ld_x = x.stride(0) if x.stride(0) != hidden else 0
-        rc = qkv_epilogue_run_proj(self.h, make_proj_args(x, w, hidden, epi, ld_x=ld_x, w_k=w_k,
-                                                          w_v=w_v))
+        rc = qkv_epilogue_run_proj(self.h, make_proj_args(
+            x, w, hidden, epi, ld_x=ld_x, w_k=w_k, w_v=w_v,
+            w_format=QKV_WEIGHT_E4M3 if w8 else QKV_WEIGHT_BF16, w_scale=w_scale))
         if rc != QKV_OK:
             raise QkvError(rc, qkv_epilogue_last_error(self.h))
 

@@ -50,8 +50,11 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct ProjParams {
     const uint16_t *x;       // bf16 [nt][ld_x]
-    const uint16_t *wsec[3]; // bf16 weight rows of the q, k, v sections ([nqt|nkt|nkt][K])
+    const uint16_t *wsec[3]; // weight rows of the q, k, v sections ([nqt|nkt|nkt][K]): bf16, or
+                             // E4M3 bytes when w8 (then only the GEMV runs)
     bool sep;                // the sections are three matrices (else rows of one concat matrix)
+    bool w8;                 // E4M3 weights with one f32 scale per output row
+    const float *wscale;     // [N] row scales (w8)
     int64_t ld_x;
     int K;                   // hidden
     int N;                   // nqt + 2*nkt
@@ -75,17 +78,21 @@ struct ProjParams {
 };
 
 // weight row of output n: row n - section base of its section's matrix (SEP:
-// three matrices), or row n of the concat matrix
-template <bool SEP>
-__device__ __forceinline__ const uint16_t *weight_row(const ProjParams &p, int n)
+// three matrices), or row n of the concat matrix; rows of K weights of 2
+// bytes (bf16) or 1 byte (W8: E4M3)
+template <bool SEP, bool W8>
+__device__ __forceinline__ const unsigned char *weight_row(const ProjParams &p, int n)
 {
-    if (!SEP)
-        return p.wsec[0] + (int64_t)n * p.K;
-    if (n < p.nqt)
-        return p.wsec[0] + (int64_t)n * p.K;
-    if (n < p.nqt + p.nkt)
-        return p.wsec[1] + (int64_t)(n - p.nqt) * p.K;
-    return p.wsec[2] + (int64_t)(n - p.nqt - p.nkt) * p.K;
+    constexpr int64_t kEl = W8 ? 1 : 2;
+    int s = 0, base = 0;
+    if (SEP && n >= p.nqt + p.nkt) {
+        s = 2;
+        base = p.nqt + p.nkt;
+    } else if (SEP && n >= p.nqt) {
+        s = 1;
+        base = p.nqt;
+    }
+    return reinterpret_cast<const unsigned char *>(p.wsec[s]) + (int64_t)(n - base) * p.K * kEl;
 }
 
 // cache row of token t (slot * n_ctx + pos), or -1 when pos or slot is out
@@ -595,17 +602,19 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
                         rot(y0.e[e], y1.e[e], cv.e[e], sv.e[e]);
                 } else if (sec[g] < 2) {
                     // interleaved pairs (2i, 2i+1) sit in the lane's own four
-                    // columns: pair indices pi, pi + 1 of one 16-byte chunk
+                    // columns: pair indices pi, pi + 1 with pi = 2hi (mod 4),
+                    // so elements 2hi, 2hi + 1 of one 16-byte chunk (chosen
+                    // by select: an indexed register read would go to scratch)
 #pragma unroll
                     for (int f = 0; f < 2; ++f) {
                         FVec<4> &y = f ? y1 : y0;
                         const int pi = ((col0[g] + f * HALF + 8 * gg + 4 * hi) % HD) / 2;
-                        const int cc = pi / 4, e0 = pi % 4;
+                        const int cc = pi / 4;
                         const FVec<4> cv = *reinterpret_cast<const FVec<4> *>(trow + ((cc ^ (r % S::kChunks)) * 16));
                         const FVec<4> sv = *reinterpret_cast<const FVec<4> *>(
                             trow + (((cc + S::kChunks / 2) ^ (r % S::kChunks)) * 16));
-                        rot(y.e[0], y.e[1], cv.e[e0], sv.e[e0]);
-                        rot(y.e[2], y.e[3], cv.e[e0 + 1], sv.e[e0 + 1]);
+                        rot(y.e[0], y.e[1], hi ? cv.e[2] : cv.e[0], hi ? sv.e[2] : sv.e[0]);
+                        rot(y.e[2], y.e[3], hi ? cv.e[3] : cv.e[1], hi ? sv.e[3] : sv.e[1]);
                     }
                 }
                 if (!p.vec) {
@@ -750,30 +759,34 @@ constexpr int kGemvSplit = 2;     // waves per NeoX pair, each summing 1/kGemvSp
 // partial last step costs as much as a full one.  P: NeoX pairs per wave
 // (1 in every launch; more pairs let one x chunk serve more weight rows).
 // SEP: q, k, v weights in three matrices (the concat layout keeps its own
-// instance: the per-section select cost ~1% at 14B).
-template <bool F16, int HD, int NT, int U, int P, bool SEP>
+// instance: the per-section select cost ~1% at 14B).  W8: E4M3 weights, a
+// 16-byte chunk holding 16 of them (two chunks of x); each output is its f32
+// sum times the row's scale.
+template <bool F16, int HD, int NT, int U, int P, bool SEP, bool W8>
 __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p, InvTable inv)
 {
     constexpr int HALF = HD / 2;
+    constexpr int kWpc = W8 ? 16 : 8;        // weights per 16-byte chunk
+    constexpr int XV = kWpc / 8;             // 16-byte chunks of x per weight chunk
     constexpr int R = 2 * P;                 // weight rows per wave
     const int lane = (int)threadIdx.x & 63;
     const int wvi = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int kq = wvi % kGemvSplit;         // this wave's share of k
     const int pair0 = ((int)blockIdx.x * (kGemvWaves / kGemvSplit) + wvi / kGemvSplit) * P;
     const bool valid = pair0 < p.N / 2;      // (every wave reaches the barrier below)
-    const int nchunk = p.K / 8;              // hidden % 64 == 0: kGemvSplit divides it
+    const int nchunk = p.K / kWpc;           // hidden % 64 == 0: kGemvSplit divides it
     const int c_beg = kq * (nchunk / kGemvSplit);
     const int c_end = valid ? c_beg + nchunk / kGemvSplit : c_beg;
     // rows 2q and 2q+1 are the two columns of pair pair0 + q: c0 and c0 +
     // hd/2 (NeoX) or c0 + 1 (interleaved)
     const bool il = p.style == QKV_ROPE_INTERLEAVED;
-    const uint16_t *wr[R];
+    const unsigned char *wr[R];
 #pragma unroll
     for (int q = 0; q < P; ++q) {
         const int pr = valid ? pair0 + q : 0;
         const int c0 = (pr / HALF) * HD + (il ? 2 * (pr % HALF) : pr % HALF);
-        wr[2 * q] = weight_row<SEP>(p, c0);
-        wr[2 * q + 1] = weight_row<SEP>(p, c0 + (il ? 1 : HALF));
+        wr[2 * q] = weight_row<SEP, W8>(p, c0);
+        wr[2 * q + 1] = weight_row<SEP, W8>(p, c0 + (il ? 1 : HALF));
     }
     const uint16_t *xr[NT];
 #pragma unroll
@@ -787,7 +800,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
         for (int t = 0; t < NT; ++t)
             d[r][t] = 0.0f;
     for (int cb = c_beg + lane; cb < c_end; cb += 64 * U) {
-        u32x4 wv[U][R], xv[U][NT];
+        u32x4 wv[U][R], xv[U][NT][XV];
         bool ok[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -797,10 +810,12 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
             // the weights are read once per call: nontemporal
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                wv[u][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wr[r] + cc * 8));
+                wv[u][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wr[r] + cc * 16));
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-                xv[u][t] = *reinterpret_cast<const u32x4 *>(xr[t] + cc * 8);
+#pragma unroll
+                for (int j = 0; j < XV; ++j)
+                    xv[u][t][j] = *reinterpret_cast<const u32x4 *>(xr[t] + cc * kWpc + 8 * j);
         }
         // every load of the step goes out before the first product (left to
         // itself the scheduler interleaved them, waiting on each in turn):
@@ -813,21 +828,46 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
             // taken from the whole 16-byte vector by shuffles: bit-casting
             // single dwords of it compiled to one-dword loads reused for all
             // four pairs (checked in the ISA).
-            bf16x8 xx8[NT];
+            bf16x8 xx8[NT][XV];
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-                xx8[t] = __builtin_bit_cast(bf16x8, xv[u][t]);
+#pragma unroll
+                for (int j = 0; j < XV; ++j)
+                    xx8[t][j] = __builtin_bit_cast(bf16x8, xv[u][t][j]);
 #define QKV_PAIR(v8, e) __builtin_shufflevector(v8, v8, 2 * (e), 2 * (e) + 1)
+            if constexpr (W8) {
+                // dword i of the chunk holds weights 4i..4i+3; each half
+                // converts to two bf16 (exact: every E4M3 value is one) and
+                // meets x elements 4i.. of the chunk's two x chunks
+#define QKV_W8_DWORD(i, j, e)                                                                          \
+    {                                                                                                  \
+        const bf16x2 wlo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wq[i], 1.0f, false);              \
+        const bf16x2 whi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wq[i], 1.0f, true);               \
+        for (int t = 0; t < NT; ++t) {                                                                 \
+            d[r][t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t][j], e), wlo, d[r][t], false);     \
+            d[r][t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t][j], e + 1), whi, d[r][t], false); \
+        }                                                                                              \
+    }
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const bf16x8 w8 = __builtin_bit_cast(
-                    bf16x8, ok[u] ? wv[u][r] : u32x4{0u, 0u, 0u, 0u});
+                for (int r = 0; r < R; ++r) {
+                    const u32x4 wq = ok[u] ? wv[u][r] : u32x4{0u, 0u, 0u, 0u};
+                    QKV_W8_DWORD(0, 0, 0)
+                    QKV_W8_DWORD(1, 0, 2)
+                    QKV_W8_DWORD(2, XV - 1, 0)
+                    QKV_W8_DWORD(3, XV - 1, 2)
+                }
+#undef QKV_W8_DWORD
+            } else {
 #pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    d[r][t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 0), QKV_PAIR(w8, 0), d[r][t], false);
-                    d[r][t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 1), QKV_PAIR(w8, 1), d[r][t], false);
-                    d[r][t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 2), QKV_PAIR(w8, 2), d[r][t], false);
-                    d[r][t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t], 3), QKV_PAIR(w8, 3), d[r][t], false);
+                for (int r = 0; r < R; ++r) {
+                    const bf16x8 w8 = __builtin_bit_cast(bf16x8, ok[u] ? wv[u][r] : u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        d[r][t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t][0], 0), QKV_PAIR(w8, 0), d[r][t], false);
+                        d[r][t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t][0], 1), QKV_PAIR(w8, 1), d[r][t], false);
+                        d[r][t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t][0], 2), QKV_PAIR(w8, 2), d[r][t], false);
+                        d[r][t] = __builtin_amdgcn_fdot2_f32_bf16(QKV_PAIR(xx8[t][0], 3), QKV_PAIR(w8, 3), d[r][t], false);
+                    }
                 }
             }
 #undef QKV_PAIR
@@ -878,6 +918,10 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
         const int sec = c0 < p.nqt ? 0 : (c0 < p.nqt + p.nkt ? 1 : 2);
         const int sbase = sec == 0 ? 0 : (sec == 1 ? p.nqt : p.nqt + p.nkt);
         const int s0 = c0 - sbase, s1 = s0 + (il ? 1 : HALF);   // columns inside the section
+        if (W8) {
+            y0 = y0 * p.wscale[c0];
+            y1 = y1 * p.wscale[c0 + (s1 - s0)];
+        }
         const float *bias = p.b[sec];
         if (bias) {
             y0 = y0 + bias[s0];
@@ -994,18 +1038,43 @@ int gemv_step(int K)
     return best;
 }
 
+// the same for E4M3 weights (16 per chunk): the largest of 4..2 dividing the
+// chunks per lane, else the one wasting the fewest slots (3 at hidden 5120:
+// 160 chunks per wave in one step of 192 slots)
+int gemv_step8(int K)
+{
+    const int c = (K / 16 / kGemvSplit + 63) / 64;
+    int best = 2, waste = 1 << 30;
+    for (int u = 4; u >= 2; --u) {
+        const int w = (c + u - 1) / u * u - c;
+        if (w < waste) {
+            best = u;
+            waste = w;
+        }
+    }
+    return best;
+}
+
 template <bool F16, int HD, int NT, bool SEP>
 hipError_t launch_gemv(const ProjParams &pp, const InvTable &inv, hipStream_t st, int u)
 {
     constexpr int pairs = kGemvWaves / kGemvSplit;   // per block
     const int blocks = (pp.N / 2 + pairs - 1) / pairs;
     const dim3 grid(blocks), block(64 * kGemvWaves);
+    if (pp.w8) {
+        switch (u) {
+        case 4: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 4, 1, SEP, true>), grid, block, 0, st, pp, inv); break;
+        case 3: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 3, 1, SEP, true>), grid, block, 0, st, pp, inv); break;
+        default: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 2, 1, SEP, true>), grid, block, 0, st, pp, inv); break;
+        }
+        return hipGetLastError();
+    }
     switch (u) {
-    case 8: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 8, 1, SEP>), grid, block, 0, st, pp, inv); break;
-    case 7: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 7, 1, SEP>), grid, block, 0, st, pp, inv); break;
-    case 6: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 6, 1, SEP>), grid, block, 0, st, pp, inv); break;
-    case 5: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 5, 1, SEP>), grid, block, 0, st, pp, inv); break;
-    default: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 4, 1, SEP>), grid, block, 0, st, pp, inv); break;
+    case 8: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 8, 1, SEP, false>), grid, block, 0, st, pp, inv); break;
+    case 7: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 7, 1, SEP, false>), grid, block, 0, st, pp, inv); break;
+    case 6: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 6, 1, SEP, false>), grid, block, 0, st, pp, inv); break;
+    case 5: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 5, 1, SEP, false>), grid, block, 0, st, pp, inv); break;
+    default: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 4, 1, SEP, false>), grid, block, 0, st, pp, inv); break;
     }
     return hipGetLastError();
 }
@@ -1049,7 +1118,7 @@ template <bool F16, int HD>
 hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st, MmPlan pl)
 {
     if (pp.M <= kGemvTok) {
-        const int u = gemv_step(pp.K);
+        const int u = pp.w8 ? gemv_step8(pp.K) : gemv_step(pp.K);
         if (pp.M == 1)
             return pp.sep ? launch_gemv<F16, HD, 1, true>(pp, inv, st, u)
                           : launch_gemv<F16, HD, 1, false>(pp, inv, st, u);
@@ -1107,9 +1176,17 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
     if (N > INT32_MAX / 2)
         return fail(h, QKV_ERR_INVALID_ARG, "q|k|v width too large");
     const bool sep = pa->w_k || pa->w_v;            // three weight matrices instead of the concat one
+    if (pa->w_format != QKV_WEIGHT_BF16 && pa->w_format != QKV_WEIGHT_E4M3)
+        return fail(h, QKV_ERR_UNSUPPORTED, "unknown weight format %d", pa->w_format);
+    const bool w8 = pa->w_format == QKV_WEIGHT_E4M3;
+    const int64_t wel = w8 ? 1 : 2;                 // bytes per weight
+    if (w8 && a->nt > kGemvTok)
+        return fail(h, QKV_ERR_UNSUPPORTED,
+                    "E4M3 weights run on the weight-streaming kernel only (1-%d tokens), got %d tokens",
+                    kGemvTok, a->nt);
     // the kernels address x and each weight matrix with 32-bit byte offsets
     if ((int64_t)a->nt * (pa->ld_x ? pa->ld_x : pa->hidden) * 2 > INT32_MAX ||
-        (sep ? std::max(pl.nqt, pl.nkt) : N) * pa->hidden * 2 > INT32_MAX)
+        (sep ? std::max(pl.nqt, pl.nkt) : N) * pa->hidden * wel > INT32_MAX)
         return fail(h, QKV_ERR_INVALID_ARG, "x and each weight matrix must span less than 2 GiB");
     if (sep && (!pa->w_k || !pa->w_v))
         return fail(h, QKV_ERR_INVALID_ARG, "w_k and w_v must be both NULL or both non-NULL");
@@ -1121,33 +1198,38 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
     if (!pa->x || !pa->w || (uintptr_t)pa->x % 16 || (uintptr_t)pa->w % 16 || (uintptr_t)pa->w_k % 16 ||
         (uintptr_t)pa->w_v % 16)
         return fail(h, QKV_ERR_INVALID_ARG, "x and the weights must be non-NULL and 16-byte aligned");
+    if (w8 && (!pa->w_scale || (uintptr_t)pa->w_scale % 4))
+        return fail(h, QKV_ERR_INVALID_ARG, "E4M3 weights need w_scale (non-NULL, 4-byte aligned)");
     // the q, k, v weight sections: rows of the concat matrix, or three matrices
-    const uint16_t *const w0 = static_cast<const uint16_t *>(pa->w);
-    const uint16_t *const wsec[3] = {
-        w0, sep ? static_cast<const uint16_t *>(pa->w_k) : w0 + pl.nqt * pa->hidden,
-        sep ? static_cast<const uint16_t *>(pa->w_v) : w0 + (pl.nqt + pl.nkt) * pa->hidden};
+    const unsigned char *const w0 = static_cast<const unsigned char *>(pa->w);
+    const unsigned char *const wsec[3] = {
+        w0, sep ? static_cast<const unsigned char *>(pa->w_k) : w0 + pl.nqt * pa->hidden * wel,
+        sep ? static_cast<const unsigned char *>(pa->w_v) : w0 + (pl.nqt + pl.nkt) * pa->hidden * wel};
     {
         // x and the weights are read while the outputs are written: no byte
         // in common (hull test on each range, conservative for strided rows)
         const int64_t nt = a->nt, cb = a->cache_dtype == QKV_CACHE_F16 ? 2 : 4;
         const int64_t cache_bytes = pl.n_slots * pl.n_ctx * pl.nkt * cb;
         const int64_t wrows[3] = {pl.nqt, pl.nkt, pl.nkt};
-        uintptr_t ins[4][2] = {
+        uintptr_t ins[5][2] = {
             {(uintptr_t)pa->x, (uintptr_t)pa->x + (uintptr_t)(((nt - 1) * ld_x + pa->hidden) * 2)}};
         for (int s = 0; s < 3; ++s) {
             ins[1 + s][0] = (uintptr_t)wsec[s];
-            ins[1 + s][1] = (uintptr_t)wsec[s] + (uintptr_t)(wrows[s] * pa->hidden * 2);
+            ins[1 + s][1] = (uintptr_t)wsec[s] + (uintptr_t)(wrows[s] * pa->hidden * wel);
         }
+        // the row scales (E4M3 only; else an empty range)
+        ins[4][0] = (uintptr_t)pa->w_scale;
+        ins[4][1] = w8 ? (uintptr_t)pa->w_scale + (uintptr_t)(N * 4) : (uintptr_t)pa->w_scale;
         const uintptr_t outs[5][2] = {
             {(uintptr_t)a->q, (uintptr_t)a->q + (uintptr_t)(((nt - 1) * pl.ld[0] + pl.nqt) * 4)},
             {(uintptr_t)a->k, (uintptr_t)a->k + (uintptr_t)(((nt - 1) * pl.ld[1] + pl.nkt) * 4)},
             {(uintptr_t)a->v, (uintptr_t)a->v + (uintptr_t)(((nt - 1) * pl.ld[2] + pl.nkt) * 4)},
             {(uintptr_t)a->kcache, (uintptr_t)a->kcache + (uintptr_t)cache_bytes},
             {(uintptr_t)a->vcache, (uintptr_t)a->vcache + (uintptr_t)cache_bytes}};
-        const char *in_name[4] = {"x", sep ? "w" : "w (q rows)", sep ? "w_k" : "w (k rows)",
-                                  sep ? "w_v" : "w (v rows)"};
+        const char *in_name[5] = {"x", sep ? "w" : "w (q rows)", sep ? "w_k" : "w (k rows)",
+                                  sep ? "w_v" : "w (v rows)", "w_scale"};
         const char *out_name[5] = {"q", "k", "v", "kcache", "vcache"};
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 5; ++i)
             for (int o = 0; o < 5; ++o)
                 if (ins[i][0] < outs[o][1] && outs[o][0] < ins[i][1])
                     return fail(h, QKV_ERR_ALIAS, "read-only %s overlaps output %s", in_name[i],
@@ -1157,8 +1239,10 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
     ProjParams pp;
     pp.x = static_cast<const uint16_t *>(pa->x);
     for (int s = 0; s < 3; ++s)
-        pp.wsec[s] = wsec[s];
+        pp.wsec[s] = reinterpret_cast<const uint16_t *>(wsec[s]);
     pp.sep = sep;
+    pp.w8 = w8;
+    pp.wscale = w8 ? pa->w_scale : nullptr;
     pp.ld_x = ld_x;
     pp.K = pa->hidden;
     pp.N = (int)N;

@@ -156,5 +156,22 @@ def draw_projection(w: Workload, hidden: int, layer: int = 0, nt: int | None = N
     return dict(x=x, w=wt, bq=d["bq"], bk=d["bk"], bv=d["bv"], pos=d["pos"], slot=d["slot"])
 
 
+def draw_e4m3_weights(n_out: int, hidden: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """Synthetic 8-bit float weights for the projection: OCP E4M3 codes
+    (uint8 [n_out][hidden]) and f32 row scales [n_out].  Codes are drawn
+    directly, never rounded from real values: both signs, the exponent field
+    uniform over 1..11 (magnitudes 2^-6 .. 30) with the mantissa uniform, and
+    one code in 32 from the zero/subnormal patterns; scales log-uniform in
+    [2^-9, 2^-6].  Stream seed*1000 + 800."""
+    rng = np.random.default_rng(seed * 1000 + 800)
+    shape = (n_out, hidden)
+    code = rng.integers(8, 96, shape)                       # exponent field 1..11
+    sub = rng.integers(0, 32, shape) == 0
+    code = np.where(sub, rng.integers(0, 8, shape), code)   # exponent field 0
+    code = code | (rng.integers(0, 2, shape) << 7)
+    scale = np.exp2(rng.uniform(-9.0, -6.0, n_out)).astype(np.float32)
+    return code.astype(np.uint8), scale
+
+
 HIDDEN = {"decode_7b": 3584, "decode_14b": 5120, "prefill_14b_4096": 5120,
           "batched_decode_14b_256seq": 5120, "tiny_decode_0.5b": 896}

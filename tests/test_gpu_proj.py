@@ -45,7 +45,7 @@ def handle():
 class ProjCase:
     def __init__(self, w, hidden, nt=None, cache_dtype=None, form="separate", bias=True,
                  pos=None, slot=None, sample=None, ld_x_pad=0, misalign=0, weights="concat",
-                 style=B.QKV_ROPE_NEOX, freq_scale=1.0):
+                 style=B.QKV_ROPE_NEOX, freq_scale=1.0, wfmt="bf16"):
         self.w, self.hidden = w, hidden
         d = wl.draw_projection(w, hidden, nt=nt)
         if pos is not None:
@@ -60,6 +60,9 @@ class ProjCase:
         self.misalign = misalign   # shift every output section by this many floats
         self.weights = weights     # "concat" [N][hidden], or "three" q, k, v matrices
         self.style, self.freq_scale = style, freq_scale
+        self.wfmt = wfmt           # "bf16", or "e4m3": 8-bit float codes with row scales
+        if wfmt == "e4m3":
+            d["w8"], d["wscale"] = wl.draw_e4m3_weights(w.nqt + 2 * w.nkt, hidden, w.seed)
         # tokens the oracle recomputes (all of them unless a sample is given)
         self.sample = np.arange(self.nt) if sample is None else np.asarray(sample)
 
@@ -68,9 +71,13 @@ class ProjCase:
         w, d, s = self.w, self.d, self.sample
         nqt, nkt = w.nqt, w.nkt
         xs = np.ascontiguousarray(d["x"][s])
-        y = oracle.proj_bf16(xs, d["w"])
-        S = np.abs(wl.bf16_to_f32(xs).astype(np.float64)) @ \
-            np.abs(wl.bf16_to_f32(d["w"]).astype(np.float64)).T
+        ax = np.abs(wl.bf16_to_f32(xs).astype(np.float64))
+        if self.wfmt == "e4m3":
+            y = oracle.proj_fp8w(xs, d["w8"], d["wscale"])
+            S = (ax @ np.abs(oracle.e4m3_values(d["w8"])).T) * np.abs(d["wscale"].astype(np.float64))
+        else:
+            y = oracle.proj_bf16(xs, d["w"])
+            S = ax @ np.abs(wl.bf16_to_f32(d["w"]).astype(np.float64)).T
         q = np.ascontiguousarray(y[:, :nqt])
         k = np.ascontiguousarray(y[:, nqt:nqt + nkt])
         v = np.ascontiguousarray(y[:, nqt + nkt:])
@@ -105,14 +112,16 @@ class ProjCase:
         xp[:, :self.hidden] = d["x"]
         self.g_x = torch.from_numpy(xp.view(np.int16)).to(DEV)
         self.ld_x = ldx if self.ld_x_pad else 0
-        self.g_w = torch.from_numpy(d["w"].view(np.int16)).to(DEV)
+        wsrc = d["w8"] if self.wfmt == "e4m3" else d["w"].view(np.int16)
+        self.g_w = torch.from_numpy(wsrc).to(DEV)
         self.g_wk = self.g_wv = None
+        self.g_scale = torch.from_numpy(d["wscale"]).to(DEV) if self.wfmt == "e4m3" else None
         if self.weights == "three":
             # three allocations, v first so the sections are not laid out in order
-            wq, wk, wv = (d["w"][a:b] for a, b in ((0, nqt), (nqt, nqt + nkt), (nqt + nkt, nqt + 2 * nkt)))
-            self.g_wv = torch.from_numpy(np.ascontiguousarray(wv).view(np.int16)).to(DEV)
-            self.g_wk = torch.from_numpy(np.ascontiguousarray(wk).view(np.int16)).to(DEV)
-            self.g_w = torch.from_numpy(np.ascontiguousarray(wq).view(np.int16)).to(DEV)
+            wq, wk, wv = (wsrc[a:b] for a, b in ((0, nqt), (nqt, nqt + nkt), (nqt + nkt, nqt + 2 * nkt)))
+            self.g_wv = torch.from_numpy(np.ascontiguousarray(wv)).to(DEV)
+            self.g_wk = torch.from_numpy(np.ascontiguousarray(wk)).to(DEV)
+            self.g_w = torch.from_numpy(np.ascontiguousarray(wq)).to(DEV)
         m = self.misalign
         if self.form == "concat":
             n = nqt + 2 * nkt
@@ -147,8 +156,9 @@ class ProjCase:
                           n_slots=w.n_slots, stream=torch.cuda.current_stream(),
                           use_stream=True, nt=self.nt, rope_style=self.style,
                           freq_scale=self.freq_scale)
+        fmt = B.QKV_WEIGHT_E4M3 if self.wfmt == "e4m3" else B.QKV_WEIGHT_BF16
         return B.make_proj_args(self.g_x, self.g_w, self.hidden, epi, ld_x=self.ld_x, w_k=self.g_wk,
-                                w_v=self.g_wv)
+                                w_v=self.g_wv, w_format=fmt, w_scale=self.g_scale)
 
     def run_gpu(self, h):
         return B.qkv_epilogue_run_proj(h, self.args())
@@ -214,7 +224,7 @@ class ProjCase:
 
 def _run(h, c, label):
     say(f"[proj] {label}: nt={c.nt} hidden={c.hidden} N={c.w.nqt + 2 * c.w.nkt} "
-        f"hd={c.w.head_dim} cache={'f16' if c.cd else 'f32'} form={c.form}")
+        f"hd={c.w.head_dim} cache={'f16' if c.cd else 'f32'} form={c.form} weights={c.wfmt}")
     c.run_oracle().upload()
     rc = c.run_gpu(h)
     assert rc == B.QKV_OK, B.qkv_epilogue_last_error(h)
@@ -704,3 +714,104 @@ def test_proj_interleaved_full_size_sampled(handle):
     c = ProjCase(wl.PREFILL_14B, hidden=5120, sample=sample, style=B.QKV_ROPE_INTERLEAVED)
     assert _run(handle, c, "interleaved_full") == B.QKV_OK
     c.check("interleaved_full")
+
+
+# ---- 8-bit float (E4M3) weights: the weight-streaming kernel, 1-4 tokens ----
+
+@pytest.mark.parametrize("nt", [1, 2, 3, 4])
+def test_proj_e4m3_decode_14b(handle, nt):
+    """E4M3 weights with row scales on the 14B decode geometry at its real
+    hidden size (the GEMV streams 36.7 MB of weights)."""
+    c = ProjCase(wl.DECODE_14B, hidden=5120, nt=nt, wfmt="e4m3")
+    assert _run(handle, c, f"e4m3_nt{nt}") == B.QKV_OK
+    c.check(f"e4m3_nt{nt}")
+
+
+@pytest.mark.parametrize("weights,style,nt", [("three", B.QKV_ROPE_NEOX, 1), ("concat", B.QKV_ROPE_INTERLEAVED, 3),
+                                              ("three", B.QKV_ROPE_INTERLEAVED, 4)])
+def test_proj_e4m3_layouts(handle, weights, style, nt):
+    """E4M3 weights as three matrices and with interleaved pairing, 7B
+    geometry (hidden 3584: 112 chunks per wave, two per lane)."""
+    c = ProjCase(wl.DECODE_7B, hidden=3584, nt=nt, wfmt="e4m3", weights=weights, style=style)
+    assert _run(handle, c, f"e4m3_{weights}_{style}_{nt}") == B.QKV_OK
+    c.check(f"e4m3_{weights}_{style}_{nt}")
+
+
+@pytest.mark.parametrize("hidden", [64, 896, 1088])
+def test_proj_e4m3_hd64_ragged_hidden(handle, hidden):
+    """hd 64 with hidden sizes that leave the last step partly masked (64:
+    2 of 64 lanes busy; 896: 28 chunks per wave; 1088: 34), slots, no bias."""
+    w = wl.Workload("proj_e4m3_hd64", 14, 2, 64, nt=3, n_ctx=64, n_slots=8, layers=1, seed=33,
+                    cache_dtypes=(wl.CACHE_F16,))
+    c = ProjCase(w, hidden=hidden, wfmt="e4m3", bias=False)
+    assert _run(handle, c, f"e4m3_hd64_{hidden}") == B.QKV_OK
+    c.check(f"e4m3_hd64_{hidden}")
+
+
+def test_proj_e4m3_every_code_exact(handle):
+    """One-hot activations pick single weights, so every v output is one
+    decoded code times its row's scale plus the bias: bit-equal to the
+    oracle.  The v rows at the picked columns hold every finite E4M3 code."""
+    w = wl.Workload("proj_e4m3_codes", 2, 2, 64, nt=4, n_ctx=64, n_slots=1, layers=1, seed=34,
+                    cache_dtypes=(wl.CACHE_F32,), pos_mode="arange")
+    hidden = 64
+    c = ProjCase(w, hidden=hidden, wfmt="e4m3")
+    cols = np.array([3, 20, 41, 62])
+    x = np.zeros((4, hidden), np.uint16)
+    x[np.arange(4), cols] = 0x3f80                     # bfloat16 1.0
+    c.d["x"] = x
+    finite = np.array([v for v in range(256) if v not in (0x7F, 0xFF)], np.uint8)
+    nqt, nkt = w.nqt, w.nkt
+    vblock = np.resize(finite, (nkt, 4))               # 128 rows x 4 columns = 512 slots
+    c.d["w8"][nqt + nkt:, cols] = vblock
+    assert np.isin(finite, c.d["w8"][nqt + nkt:][:, cols]).all()
+    assert _run(handle, c, "e4m3_codes") == B.QKV_OK
+    c.check("e4m3_codes")
+    got_v = c.g_v.cpu().numpy()
+    assert np.array_equal(got_v.view(np.uint32), c.o["v"].view(np.uint32)), "v differs from the oracle"
+
+
+def test_proj_e4m3_rejections(handle):
+    """E4M3 weights: more than 4 tokens is unsupported, the scales are
+    required, aligned and read-only; an unknown format is unsupported."""
+    c5 = ProjCase(SMALL_05B, hidden=512, nt=5, wfmt="e4m3").upload()
+    assert B.qkv_epilogue_run_proj(handle, c5.args()) == B.QKV_ERR_UNSUPPORTED
+    c = ProjCase(SMALL_05B, hidden=512, nt=4, wfmt="e4m3").upload()
+    a = c.args()
+    a.w_scale = None
+    assert B.qkv_epilogue_run_proj(handle, a) == B.QKV_ERR_INVALID_ARG
+    a = c.args()
+    a.w_scale = c.g_scale.data_ptr() + 2
+    assert B.qkv_epilogue_run_proj(handle, a) == B.QKV_ERR_INVALID_ARG
+    a = c.args()
+    a.w_scale = c.g_k.data_ptr()                    # scales overlapping the k output
+    assert B.qkv_epilogue_run_proj(handle, a) == B.QKV_ERR_ALIAS
+    a = c.args()
+    a.w_format = 7
+    assert B.qkv_epilogue_run_proj(handle, a) == B.QKV_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.isnan(c.g_q).all() and torch.isnan(c5.g_q).all()
+    assert B.qkv_epilogue_run_proj(handle, c.args()) == B.QKV_OK
+    assert B.qkv_epilogue_status(handle) == B.QKV_OK
+
+
+def test_proj_e4m3_python_wrapper():
+    """Epilogue.run_proj with float8_e4m3fn weight tensors and the scale
+    tensor; a missing scale raises before any launch."""
+    w = wl.DECODE_14B
+    c = ProjCase(w, hidden=1024, nt=2, wfmt="e4m3", weights="three")
+    c.run_oracle().upload()
+    ep = B.Epilogue(0, w.n_ctx)
+    f8, bf = torch.float8_e4m3fn, torch.bfloat16
+    ws = [t.view(f8) for t in (c.g_w, c.g_wk, c.g_wv)]
+    with pytest.raises(TypeError):
+        ep.run_proj(c.g_x.view(bf), *ws[:1], c.g_q, c.g_k, c.g_v, *c.g_b, c.g_pos, c.kc, c.vc,
+                    n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim, theta=w.theta,
+                    w_k=ws[1], w_v=ws[2])
+    ep.run_proj(c.g_x.view(bf), ws[0], c.g_q, c.g_k, c.g_v, *c.g_b, c.g_pos, c.kc, c.vc,
+                n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim, theta=w.theta,
+                w_k=ws[1], w_v=ws[2], w_scale=c.g_scale)
+    assert ep.status() == B.QKV_OK, ep.last_error()
+    torch.cuda.synchronize()
+    c.check("e4m3_wrapper")
+    ep.close()

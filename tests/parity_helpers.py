@@ -246,7 +246,9 @@ class Case:
                 gkb = gk.view(np.uint16)
                 ok_k = f16_ulp_diff(gkb, self.o_krows[valid]) <= 1
                 # the f16 K row is also the RNE image of the GPU's own k output
-                ok_k &= gkb == rk.astype(np.float16).view(np.uint16)
+                # (outputs beyond the f16 range round to inf on purpose)
+                with np.errstate(over="ignore"):
+                    ok_k &= gkb == rk.astype(np.float16).view(np.uint16)
                 ok_v = gv.view(np.uint16) == self.o_vrows[valid]
             # Tokens sharing a cache row (duplicate positions) race: each element
             # of the row holds the value of one of the colliding tokens, so per

@@ -56,7 +56,7 @@ extern "C" {
 #define QKV_OK 0
 #define QKV_ERR_INVALID_ARG   (-1) /* bad pointer, size, stride, dtype or theta */
 #define QKV_ERR_ALIAS         (-2) /* output ranges overlap each other or an input */
-#define QKV_ERR_UNSUPPORTED   (-3) /* a rotary style other than NeoX pairing */
+#define QKV_ERR_UNSUPPORTED   (-3) /* a request outside what the kernels implement */
 #define QKV_ERR_HIP           (-4) /* a HIP runtime call or launch failed */
 #define QKV_ERR_POSITION_RANGE (-5) /* (status only) a pos/slot was out of range */
 

@@ -1,9 +1,11 @@
 """The ctypes structures of the binding match the C declarations of
-include/qkv_epilogue.h field by field (offset, and the struct size), checked
-against a small C program that the host compiler builds from the header."""
+include/qkv_epilogue.h field by field (offset, and the struct size), and the
+binding's constants match the header's macros, checked against small C
+programs that the host compiler builds from the header."""
 import ctypes
 import json
 import os
+import re
 import shutil
 import subprocess
 
@@ -50,3 +52,25 @@ def test_struct_layouts_match_header(tmp_path):
         for fname, _ in cls._fields_:
             assert getattr(cls, fname).offset == c[f"{cname}.{fname}"], f"{cname}.{fname}"
         assert ctypes.sizeof(cls) == c[f"{cname}.sizeof"], f"sizeof {cname}"
+
+
+def test_constants_match_header(tmp_path):
+    """Every integer macro QKV_* of the header has a binding constant of the
+    same name and value (the values as the C compiler sees them)."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    hdr = open(os.path.join(ROOT, "include", "qkv_epilogue.h")).read()
+    names = [m for m in re.findall(r"^#define (QKV_\w+)[ \t]+\S", hdr, re.M)]
+    assert len(names) >= 10
+    body = "\n".join(f'    printf("{n} %lld\\n", (long long)({n}));' for n in names)
+    src = tmp_path / "consts.c"
+    src.write_text(f'#include <stdio.h>\n#include "qkv_epilogue.h"\nint main(void) {{\n{body}\n    return 0;\n}}\n')
+    exe = tmp_path / "consts"
+    subprocess.run([cc, "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True, capture_output=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    for line in out.splitlines():
+        name, val = line.split()
+        assert hasattr(B, name), f"binding lacks {name}"
+        assert getattr(B, name) == int(val), f"{name}: binding {getattr(B, name)} != header {val}"

@@ -756,8 +756,10 @@ constexpr int kGemvSplit = 2;     // waves per NeoX pair, each summing 1/kGemvSp
 
 // U: 16-byte chunks of each row in flight per lane and step; the launcher
 // picks U dividing the chunks per lane (hidden/512) when it can, since a
-// partial last step costs as much as a full one.  P: NeoX pairs per wave
-// (1 in every launch; more pairs let one x chunk serve more weight rows).
+// partial last step costs as much as a full one.  P: pairs per wave (1,
+// except 2 for 4 tokens of E4M3 weights at hidden >= 4096; more pairs let
+// one x chunk serve more weight rows; P divides the pair count N/2, a
+// multiple of 64).
 // SEP: q, k, v weights in three matrices (the concat layout keeps its own
 // instance: the per-section select cost ~1% at 14B).  W8: E4M3 weights, a
 // 16-byte chunk holding 16 of them (two chunks of x); each output is its f32
@@ -1062,6 +1064,20 @@ hipError_t launch_gemv(const ProjParams &pp, const InvTable &inv, hipStream_t st
     const int blocks = (pp.N / 2 + pairs - 1) / pairs;
     const dim3 grid(blocks), block(64 * kGemvWaves);
     if (pp.w8) {
+        if constexpr (NT == 4) {
+            // 4 tokens at hidden >= 4096: two pairs per wave, so each x chunk
+            // serves four weight rows (14B: 15.2 against 15.9 us; at hidden
+            // 3584 it measured slower, 9.9 against 9.2)
+            if (pp.K >= 4096) {
+                const dim3 grid2((blocks + 1) / 2);
+                switch (u) {
+                case 4: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 4, 2, SEP, true>), grid2, block, 0, st, pp, inv); break;
+                case 3: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 3, 2, SEP, true>), grid2, block, 0, st, pp, inv); break;
+                default: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 2, 2, SEP, true>), grid2, block, 0, st, pp, inv); break;
+                }
+                return hipGetLastError();
+            }
+        }
         switch (u) {
         case 4: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 4, 1, SEP, true>), grid, block, 0, st, pp, inv); break;
         case 3: hipLaunchKernelGGL((proj_gemv_kernel<F16, HD, NT, 3, 1, SEP, true>), grid, block, 0, st, pp, inv); break;

@@ -154,8 +154,9 @@ typedef struct qkv_epilogue_args {
  *                        or > QKV_MAX_HEAD_DIM; theta <= 0 or not finite; an
  *                        unknown cache_dtype; a stride below its row width;
  *                        n_ctx or n_slots < 0; a cache pointer not aligned to
- *                        its element size; more than 2^28 work units per
- *                        token or 2^31-1 workgroups.
+ *                        its element size; 2^22 or more work units per
+ *                        token (rows of about 2^25 elements) or more than
+ *                        2^31-1 workgroups.
  *   QKV_ERR_ALIAS        two of q, k, v, kcache, vcache share an element, or
  *                        a read-only input (bias, pos, slot) overlaps one.
  *   QKV_ERR_UNSUPPORTED  rope_style is neither QKV_ROPE_NEOX nor

@@ -275,6 +275,54 @@ def make_args(q, k, v, bq, bk, bv, pos, kcache, vcache, *, n_head, n_kv_head, he
     return a
 
 
+def _section_rows(t, width, name, nt):
+    """Raise unless section t holds nt rows of width elements: a contiguous
+    1-D tensor of nt*width elements, or a 2-D [nt][width] view with unit
+    column stride."""
+    if t.dim() == 1:
+        if t.stride(0) != 1 or t.numel() != nt * width:
+            raise ValueError(f"{name}: a 1-D section must be contiguous with nt*width = "
+                             f"{nt}*{width} elements, has {t.numel()}")
+    elif t.dim() == 2:
+        if t.shape[0] != nt or t.shape[1] != width or t.stride(1) != 1:
+            raise ValueError(f"{name}: shape {tuple(t.shape)} (column stride {t.stride(1)}), "
+                             f"expected [{nt}][{width}] with unit column stride")
+    else:
+        raise ValueError(f"{name}: need a 1-D tensor or a 2-D [nt][width] view")
+
+
+def check_extents(q, k, v, bq, bk, bv, pos, slot, kcache, vcache, *, n_head, n_kv_head,
+                  head_dim, n_ctx, n_slots):
+    """Host-side extent checks of one launch (the C ABI takes bare pointers and
+    cannot check them): q/k/v hold nt = pos.numel() rows of their section
+    widths, the biases (when given) one row each, slot nt entries, and each
+    cache is a contiguous tensor of at least n_slots*n_ctx rows of
+    n_kv_head*head_dim elements.  Raises ValueError before anything is
+    launched."""
+    nt = int(pos.numel())
+    nqt, nkt = n_head * head_dim, n_kv_head * head_dim
+    for name, t, width in (("q", q, nqt), ("k", k, nkt), ("v", v, nkt)):
+        _section_rows(t, width, name, nt)
+    for name, t, width in (("bq", bq, nqt), ("bk", bk, nkt), ("bv", bv, nkt)):
+        if t is not None and (t.numel() != width or not t.is_contiguous()):
+            raise ValueError(f"{name}: need {width} contiguous elements, has {t.numel()}")
+    if slot is not None and slot.numel() != nt:
+        raise ValueError(f"slot has {slot.numel()} entries, pos has {nt}")
+    need = n_slots * n_ctx * nkt
+    for name, t in (("kcache", kcache), ("vcache", vcache)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.numel() < need:
+            raise ValueError(f"{name} holds {t.numel()} elements, the launch addresses "
+                             f"n_slots*n_ctx*nkt = {n_slots}*{n_ctx}*{nkt} = {need}")
+
+
+def _check_device(device, **tensors):
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or t.device.index != device):
+            raise TypeError(f"{name} must be a tensor on cuda:{device}, got {t.device}")
+
+
 class Epilogue:
     """A handle bound to one device.  ``run`` launches on torch's current
     stream and raises QkvError on a non-zero return."""
@@ -299,11 +347,16 @@ class Epilogue:
         if vcache.dtype != kcache.dtype:
             raise TypeError("kcache and vcache must share a dtype")
         for name, t in (("q", q), ("k", k), ("v", v), ("bq", bq), ("bk", bk), ("bv", bv)):
-            if t.dtype != torch.float32 or not t.is_cuda:
-                raise TypeError(f"{name} must be a float32 device tensor")
+            if t.dtype != torch.float32:
+                raise TypeError(f"{name} must be float32")
         for name, t in (("pos", pos), ("slot", slot)):
-            if t is not None and (t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous()):
-                raise TypeError(f"{name} must be a contiguous int32 device tensor")
+            if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+                raise TypeError(f"{name} must be a contiguous int32 tensor")
+        check_extents(q, k, v, bq, bk, bv, pos, slot, kcache, vcache, n_head=n_head,
+                      n_kv_head=n_kv_head, head_dim=head_dim, n_ctx=n_ctx or self.n_ctx,
+                      n_slots=n_slots or 1)
+        _check_device(self.device, q=q, k=k, v=v, bq=bq, bk=bk, bv=bv, pos=pos, slot=slot,
+                      kcache=kcache, vcache=vcache)
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
         a = make_args(q, k, v, bq, bk, bv, pos, kcache, vcache, n_head=n_head,
@@ -333,32 +386,49 @@ class Epilogue:
             raise TypeError("kcache and vcache must share a dtype")
         if (w_k is None) != (w_v is None):
             raise TypeError("w_k and w_v go together")
-        if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
-            raise TypeError("x must be a 2-D bfloat16 device tensor with unit column stride")
+        if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+            raise TypeError("x must be a 2-D bfloat16 tensor with unit column stride")
         wdt = w.dtype
         if wdt not in (torch.bfloat16, torch.float8_e4m3fn):
             raise TypeError(f"w must be bfloat16 or float8_e4m3fn, got {wdt}")
         for name, t in (("w", w), ("w_k", w_k), ("w_v", w_v)):
-            if t is not None and (t.dtype != wdt or not t.is_cuda or t.dim() != 2):
-                raise TypeError(f"{name} must be a 2-D device tensor of the weights' dtype {wdt}")
+            if t is not None and (t.dtype != wdt or t.dim() != 2):
+                raise TypeError(f"{name} must be a 2-D tensor of the weights' dtype {wdt}")
         w8 = wdt == torch.float8_e4m3fn
         if w8 != (w_scale is not None):
             raise TypeError("w_scale goes with float8_e4m3fn weights, and only with them")
-        if w8 and (w_scale.dtype != torch.float32 or not w_scale.is_cuda or not w_scale.is_contiguous()
+        if w8 and (w_scale.dtype != torch.float32 or not w_scale.is_contiguous()
                    or w_scale.numel() != (n_head + 2 * n_kv_head) * head_dim):
-            raise TypeError("w_scale must be a contiguous float32 device tensor of nqt + 2*nkt scales")
+            raise TypeError("w_scale must be a contiguous float32 tensor of nqt + 2*nkt scales")
         for name, t in (("w", w), ("w_k", w_k), ("w_v", w_v)):
             if t is not None and not t.is_contiguous():
                 raise TypeError(f"{name} must be contiguous")
         for name, t in (("q", q), ("k", k), ("v", v), ("bq", bq), ("bk", bk), ("bv", bv)):
-            if t is not None and (t.dtype != torch.float32 or not t.is_cuda):
-                raise TypeError(f"{name} must be a float32 device tensor")
+            if t is not None and t.dtype != torch.float32:
+                raise TypeError(f"{name} must be float32")
         for name, t in (("pos", pos), ("slot", slot)):
-            if t is not None and (t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous()):
-                raise TypeError(f"{name} must be a contiguous int32 device tensor")
+            if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+                raise TypeError(f"{name} must be a contiguous int32 tensor")
         hidden = x.shape[1]
         if w.shape[1] != hidden or any(t is not None and t.shape[1] != hidden for t in (w_k, w_v)):
             raise ValueError("x and the weights must share the hidden size")
+        nt = int(pos.numel())
+        nqt, nkt = n_head * head_dim, n_kv_head * head_dim
+        if x.shape[0] != nt:
+            raise ValueError(f"x has {x.shape[0]} rows, pos has {nt} tokens")
+        if w_k is None:
+            if w.shape[0] != nqt + 2 * nkt:
+                raise ValueError(f"w has {w.shape[0]} rows, the concat q|k|v weights need "
+                                 f"nqt + 2*nkt = {nqt + 2 * nkt}")
+        else:
+            for name, t, rows in (("w", w, nqt), ("w_k", w_k, nkt), ("w_v", w_v, nkt)):
+                if t.shape[0] != rows:
+                    raise ValueError(f"{name} has {t.shape[0]} rows, expected {rows}")
+        check_extents(q, k, v, bq, bk, bv, pos, slot, kcache, vcache, n_head=n_head,
+                      n_kv_head=n_kv_head, head_dim=head_dim, n_ctx=n_ctx or self.n_ctx,
+                      n_slots=n_slots or 1)
+        _check_device(self.device, x=x, w=w, w_k=w_k, w_v=w_v, w_scale=w_scale, q=q, k=k, v=v,
+                      bq=bq, bk=bk, bv=bv, pos=pos, slot=slot, kcache=kcache, vcache=vcache)
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
         epi = make_args(q, k, v, bq, bk, bv, pos, kcache, vcache, n_head=n_head,

@@ -1,4 +1,7 @@
-"""Compile the HIP library in-tree: csrc/*.hip -> libqkv_epilogue.so.
+"""Compile the HIP libraries in-tree:
+  csrc/qkv_epilogue.hip, qkv_unfused.hip, qkv_proj.hip -> libqkv_epilogue.so
+  csrc/hbm_probe.hip -> libqkv_probe.so (the benchmark's floor and ceiling
+  kernels; not part of the epilogue library).
 
 hipcc cross-compiles for gfx950 without a GPU.  Flags: -O3, no fast-math
 (denormals and IEEE rounding stay as HIP's defaults), packed FP32 ops off.
@@ -14,6 +17,8 @@ ROOT = os.path.dirname(PKG)
 SRCS = [os.path.join(PKG, "csrc", f) for f in ("qkv_epilogue.hip", "qkv_unfused.hip", "qkv_proj.hip")]
 HDRS = [os.path.join(ROOT, "include", "qkv_epilogue.h"), os.path.join(PKG, "csrc", "qkv_internal.h")]
 LIB = os.path.join(PKG, "libqkv_epilogue.so")
+PROBE_SRC = os.path.join(PKG, "csrc", "hbm_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libqkv_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -23,10 +28,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Always recompile (the build check must compile), atomically replace."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *SRCS, "-o", tmp]
+def _compile(srcs, out, verbose):
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
@@ -34,15 +38,23 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + err)
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompile both libraries (the build check must compile),
+    atomically replacing each."""
+    _compile(SRCS, LIB, verbose)
+    _compile([PROBE_SRC], PROBE_LIB, verbose)
     return LIB
 
 
 def is_stale() -> bool:
-    if not os.path.exists(LIB):
+    if not os.path.exists(LIB) or not os.path.exists(PROBE_LIB):
         return True
-    t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(p) > t for p in (*SRCS, *HDRS))
+    t = min(os.path.getmtime(LIB), os.path.getmtime(PROBE_LIB))
+    return any(os.path.getmtime(p) > t for p in (*SRCS, *HDRS, PROBE_SRC))
 
 
 if __name__ == "__main__":

@@ -70,6 +70,8 @@ struct KParams {
     int64_t n_ctx;
     int64_t n_slots;
     int64_t nkt;
+    uint64_t uph_mul;     // ceil(2^40 / uph): n / uph == (n * uph_mul) >> 40 for n < 2^22
+    uint64_t half_mul;    // ceil(2^40 / half), the same for half
     int nt;
     int hd;
     int half;
@@ -79,16 +81,25 @@ struct KParams {
     int vhalf;            // nkt / 2: distance between the two slots of a v unit
     int U;                // units per token
     int cbu;              // units per column block = blockDim.x
-    int ncb;              // column blocks per token
     int tb;               // tokens per token block
     unsigned has_bias;    // bit s: section s has a bias (all set for run/run_ex)
     const float *nw[2];   // q/k norm weights [hd] (q/k-norm variant only)
     double eps;           // q/k norm epsilon
 };
 
+// n / d for 0 <= n < 2^22 and 1 <= d <= 256 with mul = ceil(2^40 / d): the
+// product overestimates n/d by less than 2^-18, and the fraction of n/d is at
+// most 1 - 1/d, so the floor is exact.  Replaces a runtime integer division
+// (a few dozen instructions) in front of the data loads.
+__device__ __forceinline__ int div_small(int n, uint64_t mul)
+{
+    return (int)(((uint64_t)(uint32_t)n * mul) >> 40);
+}
+
 // Unit r of a token (0 <= r < U): section, column of the first slot, offset
 // of the first slot inside its head (rope units), index of the unit inside
-// its head, and distance from the first slot to the second.
+// its head, and distance from the first slot to the second.  Written with
+// selects only, so that nothing branches before the data loads are issued.
 //  NeoX (STYLE 0):   slots [eo, eo+W) and [eo+half, ...), eo = m*W; element
 //                    eo+e of the first slot pairs with element eo+e+half.
 //  interleaved (1):  W = 4: the same slots, each holding W/2 adjacent pairs
@@ -97,27 +108,17 @@ template <int W, int STYLE>
 __device__ __forceinline__ void decode_unit(const KParams &p, int r, int &sec, int &col, int &eo,
                                             int &m, int &d1)
 {
-    if (r < p.qku) {
-        sec = r < p.qu ? 0 : 1;
-        if (sec)
-            r -= p.qu;
-        const int h = r / p.uph;
-        m = r - h * p.uph;
-        if constexpr (STYLE == 1 && W == 1) {
-            eo = 2 * m;
-            d1 = 1;
-        } else {
-            eo = m * W;
-            d1 = p.half;
-        }
-        col = h * p.hd + eo;
-    } else {
-        sec = 2;
-        eo = 0;
-        m = 0;
-        col = (r - p.qku) * W;
-        d1 = p.vhalf;
-    }
+    const bool rope = r < p.qku;
+    sec = rope ? (r < p.qu ? 0 : 1) : 2;
+    const int rr = r - (sec == 1 ? p.qu : 0);  // unit index inside the q or k section
+    const int h = div_small(rr, p.uph_mul);
+    const int mm = rr - h * p.uph;
+    constexpr bool adj = STYLE == 1 && W == 1;  // scalar interleaved: slots 2m, 2m+1
+    const int e = adj ? 2 * mm : mm * W;
+    eo = rope ? e : 0;
+    m = rope ? mm : 0;
+    col = rope ? h * p.hd + e : (r - p.qku) * W;
+    d1 = rope ? (adj ? 1 : p.half) : p.vhalf;
 }
 
 // (x0, x1) -> (x0*c - x1*s, x0*s + x1*c), evaluated in double: the products of
@@ -128,6 +129,18 @@ __device__ __forceinline__ void rotate_pair(float &x0, float &x1, float c, float
     const double a = (double)x0, b = (double)x1, cd = (double)c, sd = (double)s;
     x0 = (float)(a * cd - b * sd);
     x1 = (float)(a * sd + b * cd);
+}
+
+// Cache row of a token: slot*n_ctx + pos (slot 0 without slots), or -1 with
+// the error bit set when the position or the slot is out of range (the token
+// then writes no cache row).
+__device__ __forceinline__ int64_t cache_row(const KParams &p, int32_t pos, int32_t slot_or_pos)
+{
+    const int64_t sl = p.slot ? (int64_t)slot_or_pos : 0;
+    if (pos >= 0 && (int64_t)pos < p.n_ctx && sl >= 0 && sl < p.n_slots)
+        return sl * p.n_ctx + pos;
+    atomicOr(p.err, 1u);
+    return -1;
 }
 
 // Section operands picked with selects on wave-uniform kernel arguments (an
@@ -160,10 +173,23 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
     float *s_sin = s_cos + TPB * p.half;
     double *s_ss = reinterpret_cast<double *>(s_sin + TPB * p.half);  // NORM: [TPB][nthr]
 
+    // The kernel arguments the data addresses depend on, fetched in one batch
+    // of scalar loads: an empty asm that takes them as scalar-register inputs
+    // keeps the compiler from issuing them in several rounds next to their
+    // first uses, each round a wait on the scalar cache before the data
+    // loads can go out.
+    asm volatile("" ::"s"(p.x[0]), "s"(p.x[1]), "s"(p.x[2]), "s"(p.b[0]), "s"(p.b[1]), "s"(p.b[2]),
+                 "s"(p.pos), "s"(p.slot), "s"(p.ld[0]), "s"(p.ld[1]), "s"(p.ld[2]), "s"(p.uph_mul),
+                 "s"(p.half_mul), "s"(p.nt), "s"(p.hd), "s"(p.half), "s"(p.uph), "s"(p.qu),
+                 "s"(p.qku), "s"(p.vhalf), "s"(p.U), "s"(p.cbu), "s"(p.has_bias), "s"(gridDim.y));
     const int tid = (int)threadIdx.x;
     const int nthr = (int)blockDim.x;
-    const int cb = (int)blockIdx.x % p.ncb;
-    const int t0 = ((int)blockIdx.x / p.ncb) * TPB;
+    // grid: x = column block, (y, z) = token block (z only past 65535 blocks)
+    const int cb = (int)blockIdx.x;
+    const int64_t tb0 = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * TPB;
+    if (tb0 >= p.nt)
+        return;  // the tail of the last z slice (uniform over the workgroup)
+    const int t0 = (int)tb0;
     const int ntok = min(TPB, p.nt - t0);
     const int ent = ntok * p.half;
 
@@ -172,22 +198,25 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
     // loads it needs: the cos/sin inputs are loaded first and their wait does
     // not hold up the data loads issued after them.
 
-    // ---- cos/sin input of this thread's first entry, row input per token ---
+    // ---- cos/sin input of this thread's first entry ------------------------
+    // Entry e = tk*half + i is (token tk, pair index i); the lane of entry
+    // (tk, 0) also forms token tk's cache row, from the position it already
+    // holds.  These loads take per-lane indices, so none of them is turned
+    // into a scalar value the compiler would wait for before the data loads.
     const int ec = min(tid, ent - 1);
-    const int e_tk = ec / p.half;
+    const int e_tk = div_small(ec, p.half_mul);
     const int e_i = ec - e_tk * p.half;
     const int32_t e_pos = p.pos[t0 + e_tk];
+    const int32_t e_slot = (p.slot ? p.slot : p.pos)[t0 + e_tk];
     const float e_inv = inv.v[e_i];
-    const int rc = min(tid, ntok - 1);
-    const int32_t r_pos = p.pos[t0 + rc];
-    const int32_t r_slot = (p.slot ? p.slot : p.pos)[t0 + rc];
 
     // ---- this thread's unit, its biases and its data for every token -------
     const int r = cb * p.cbu + tid;
     const bool live = r < p.U;
     int sec, col, i0, m, d1;
     decode_unit<W, STYLE>(p, min(r, p.U - 1), sec, col, i0, m, d1);
-    float *const xs = pick3(sec, p.x[0], p.x[1], p.x[2]) + col;
+    float *const xsec = pick3(sec, p.x[0], p.x[1], p.x[2]);
+    float *const xs = xsec + col;
     const int64_t ldx = pick3(sec, p.ld[0], p.ld[1], p.ld[2]);
     // A section without a bias reads its own first row instead (a valid
     // address; the values are replaced by zero below) -- no branch, so the
@@ -218,24 +247,20 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
         sincos((double)a, &sd, &cd);
         s_cos[tid] = (float)cd;
         s_sin[tid] = (float)sd;
+        if (e_i == 0)
+            s_row[e_tk] = cache_row(p, e_pos, e_slot);
     }
     for (int e = tid + nthr; e < ent; e += nthr) {  // only when TPB*half > nthr
-        const int tk = e / p.half;
+        const int tk = div_small(e, p.half_mul);
         const int i = e - tk * p.half;
-        const float a = (float)p.pos[t0 + tk] * inv.v[i];
+        const int32_t ps = p.pos[t0 + tk];
+        const float a = (float)ps * inv.v[i];
         double sd, cd;
         sincos((double)a, &sd, &cd);
         s_cos[e] = (float)cd;
         s_sin[e] = (float)sd;
-    }
-    if (tid < ntok) {
-        const int64_t sl = p.slot ? (int64_t)r_slot : 0;
-        int64_t row = -1;
-        if (r_pos >= 0 && (int64_t)r_pos < p.n_ctx && sl >= 0 && sl < p.n_slots)
-            row = sl * p.n_ctx + r_pos;
-        else
-            atomicOr(p.err, 1u);
-        s_row[tid] = row;
+        if (i == 0)
+            s_row[tk] = cache_row(p, ps, (p.slot ? p.slot : p.pos)[t0 + tk]);
     }
 #pragma unroll
     for (int e = 0; e < W; ++e) {
@@ -331,14 +356,27 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
                 }
             }
         }
-        float *xp = xs + (int64_t)(t0 + tt) * ldx;
-        st_data<W, STREAM>(xp, ra);
-        st_data<W, STREAM>(xp + d1, rb);
         const int64_t row = s_row[tt];
-        if (sec > 0 && row >= 0) {
-            const int64_t off = row * p.nkt + col;
-            st_cache<W, F16, STREAM>(cache, off, ra);
-            st_cache<W, F16, STREAM>(cache, off + d1, rb);
+        if constexpr (STREAM) {
+            // the section row and the cache row of this token are the bases,
+            // shared by the lanes of a wave that work on one section
+            float *const xrow = xsec + (int64_t)(t0 + tt) * ldx;
+            st_stream<W>(xrow, (uint32_t)col * 4u, ra);
+            st_stream<W>(xrow, (uint32_t)(col + d1) * 4u, rb);
+            if (sec > 0 && row >= 0) {
+                void *const crow = static_cast<char *>(cache) + row * p.nkt * (F16 ? 2 : 4);
+                st_stream_cache<W, F16>(crow, (uint32_t)col, ra);
+                st_stream_cache<W, F16>(crow, (uint32_t)(col + d1), rb);
+            }
+        } else {
+            float *xp = xs + (int64_t)(t0 + tt) * ldx;
+            st_data<W, false>(xp, ra);
+            st_data<W, false>(xp + d1, rb);
+            if (sec > 0 && row >= 0) {
+                const int64_t off = row * p.nkt + col;
+                st_cache<W, F16, false>(cache, off, ra);
+                st_cache<W, F16, false>(cache, off + d1, rb);
+            }
         }
     }
 }
@@ -346,20 +384,24 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
 template <int W, bool F16, int TPB, bool STREAM, int NORM, int STYLE>
 hipError_t launch_t(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
 {
+    const int64_t ntb = pl.grid / pl.ncb;  // token blocks
+    const unsigned gy = (unsigned)(ntb < 65535 ? ntb : 65535);
+    const unsigned gz = (unsigned)((ntb + gy - 1) / gy);
     hipLaunchKernelGGL((qkv_epilogue_kernel<W, F16, TPB, STREAM, NORM, STYLE>),
-                       dim3((unsigned)pl.grid), dim3((unsigned)pl.nthr), (unsigned)pl.lds, st, kp,
-                       inv);
+                       dim3((unsigned)pl.ncb, gy, gz), dim3((unsigned)pl.nthr), (unsigned)pl.lds, st,
+                       kp, inv);
     return hipGetLastError();
 }
 
+// The planner puts one token in each workgroup: the kernel takes any TPB, but
+// two or four tokens per workgroup measured slower at every launch size.
 template <int W, bool F16, int NORM, int STYLE>
 hipError_t launch_s(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
 {
-    if (pl.tb == 1)
-        return pl.stream ? launch_t<W, F16, 1, true, NORM, STYLE>(kp, inv, pl, st)
-                         : launch_t<W, F16, 1, false, NORM, STYLE>(kp, inv, pl, st);
-    return pl.stream ? launch_t<W, F16, 2, true, NORM, STYLE>(kp, inv, pl, st)
-                     : launch_t<W, F16, 2, false, NORM, STYLE>(kp, inv, pl, st);
+    if (pl.tb != 1)
+        return hipErrorInvalidValue;
+    return pl.stream ? launch_t<W, F16, 1, true, NORM, STYLE>(kp, inv, pl, st)
+                     : launch_t<W, F16, 1, false, NORM, STYLE>(kp, inv, pl, st);
 }
 
 template <int W, bool F16, int NORM>
@@ -392,13 +434,15 @@ int ceil_div(int64_t a, int64_t b)
 }
 
 // Tiling of the (token x unit) space, one unit per thread.  Measured on
-// MI355X (14B shape, 896 units per token):
+// MI355X (14B shape, 896 units per token, kernel time from HIP-graph replays
+// over rotating input sets):
 //  * thousands of tokens (prefill): 128-thread column blocks, one token per
 //    workgroup, nontemporal data (the launch streams far more than the
 //    caches hold) -- the per-workgroup cos/sin (64 values) rides under the
 //    load latency;
-//  * hundreds of tokens (batched decode): wider blocks holding two tokens, so
-//    fewer, fuller workgroups carry the launch;
+//  * hundreds of tokens (batched decode): 256-thread column blocks, one
+//    token per workgroup (256 sequences: 4.6 us, against 4.7-4.9 us for
+//    64-896 threads and 4.9-7.4 us for two or four tokens per workgroup);
 //  * a few tokens (decode): 64-thread blocks spread one token over many
 //    workgroups, default cache policy (the data is cache-resident).
 void choose_tiling(int64_t nt, int U, int uph, Plan *pl)
@@ -408,10 +452,10 @@ void choose_tiling(int64_t nt, int U, int uph, Plan *pl)
         pl->tb = 1;
         pl->stream = true;
     } else if (nt >= 64) {
-        pl->nthr = ceil_div(ceil_div(U, 2), 64) * 64;
-        if (pl->nthr > kMaxBlock)
-            pl->nthr = kMaxBlock;
-        pl->tb = 2;
+        pl->nthr = ceil_div(U, 64) * 64;
+        if (pl->nthr > 256)
+            pl->nthr = 256;
+        pl->tb = 1;
         pl->stream = true;
     } else {
         pl->nthr = 64;
@@ -666,8 +710,9 @@ int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl
     const int W = vec ? 4 : 1;
     const int half = a->head_dim / 2;
     const int64_t U = (int64_t)(a->n_head + a->n_kv_head) * (half / W) + nkt / (2 * W);
-    if (U > (1 << 28)) {
-        set_msg(msg, mlen, "rows too wide: %lld work units per token", (long long)U);
+    if (U >= (1 << 22)) {
+        set_msg(msg, mlen, "rows too wide: %lld work units per token (at most %d)", (long long)U,
+                (1 << 22) - 1);
         return QKV_ERR_INVALID_ARG;
     }
     pl->W = W;
@@ -679,7 +724,7 @@ int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl
         set_msg(msg, mlen, "launch too large: %lld workgroups (split the tokens)", (long long)pl->grid);
         return QKV_ERR_INVALID_ARG;
     }
-    pl->lds = lds_row_bytes(pl->tb) + 2 * pl->tb * half * 4;  // tb <= 2: <= 4 KB + 16
+    pl->lds = lds_row_bytes(pl->tb) + 2 * pl->tb * half * 4;  // <= 2 KB + 16 for one token
     if (pl->norm)
         pl->lds += pl->tb * pl->nthr * 8;  // per-lane partial sums of squares
     return QKV_OK;
@@ -761,8 +806,9 @@ int launch_fused(qkv_epilogue_t *h, const qkv_epilogue_args_t *a, unsigned flags
     kp.vhalf = (int)(pl.nkt / 2);
     kp.U = pl.U;
     kp.cbu = pl.nthr;
-    kp.ncb = pl.ncb;
     kp.tb = pl.tb;
+    kp.uph_mul = ((uint64_t)1 << 40) / (uint64_t)kp.uph + 1;  // ceil: uph never divides 2^40 exactly
+    kp.half_mul = ((uint64_t)1 << 40) / (uint64_t)kp.half + 1;
     kp.has_bias = (a->bq ? 1u : 0u) | (a->bk ? 2u : 0u) | (a->bv ? 4u : 0u);
     kp.nw[0] = wq;
     kp.nw[1] = wk;

@@ -102,6 +102,66 @@ __device__ __forceinline__ void st_cache(void *cache, int64_t off, const FVec<W>
     }
 }
 
+// Stores that reach HBM while the kernel runs.  The L2 of each XCD is
+// write-back: a plain (or merely non-temporal) store leaves its line dirty
+// there, and the release at the end of the kernel writes every dirty line
+// back after the last wave has finished -- a launch that writes a few MB per
+// XCD pays for that writeback on its critical path.  A store at device scope
+// (sc1) is written through the L2 as it is issued; with the non-temporal bit
+// (nt) its line is also marked as streaming.  The global-store builtins carry
+// only the nt bit, so these go through a raw buffer resource.  `base` should
+// be the same for every lane of the wave (a section row, a cache row): the
+// compiler loops over the distinct resources of a wave, once per value.
+constexpr int kStreamStorePolicy = 2 /* nt */ | 16 /* sc1 */;
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const void *base)
+{
+    // raw buffer (stride 0); every offset below 2^31 bytes is in range; the
+    // fourth word selects 32-bit data for untyped access
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
+}
+
+// W floats at byte offset off from base
+template <int W>
+__device__ __forceinline__ void st_stream(float *base, uint32_t off, const FVec<W> &v)
+{
+    const __amdgpu_buffer_rsrc_t r = stream_rsrc(base);
+    if constexpr (W == 4) {
+        const u32x4 u = {__builtin_bit_cast(unsigned, v.e[0]), __builtin_bit_cast(unsigned, v.e[1]),
+                         __builtin_bit_cast(unsigned, v.e[2]), __builtin_bit_cast(unsigned, v.e[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(u, r, (int)off, 0, kStreamStorePolicy);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v.e[0]), r, (int)off, 0,
+                                              kStreamStorePolicy);
+    }
+}
+
+// W values converted to f16 (round to nearest even, per element) or kept f32,
+// at element index idx of the cache row that starts at row_base
+template <int W, bool F16>
+__device__ __forceinline__ void st_stream_cache(void *row_base, uint32_t idx, const FVec<W> &v)
+{
+    if constexpr (F16) {
+        const __amdgpu_buffer_rsrc_t r = stream_rsrc(row_base);
+        HVec<W> h;
+#pragma unroll
+        for (int e = 0; e < W; ++e)
+            h.e[e] = static_cast<_Float16>(v.e[e]);  // v_cvt_f16_f32: RNE
+        if constexpr (W == 4) {
+            const u32x2 u = __builtin_bit_cast(u32x2, h);
+            __builtin_amdgcn_raw_buffer_store_b64(u, r, (int)(idx * 2u), 0, kStreamStorePolicy);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h.e[0]), r,
+                                                  (int)(idx * 2u), 0, kStreamStorePolicy);
+        }
+    } else {
+        st_stream<W>(static_cast<float *>(row_base), idx * 4u, v);
+    }
+}
+
 // LDS layout: int64 row[tb] | float cos[tb*half] | float sin[tb*half]
 __host__ __device__ inline int lds_row_bytes(int tb)
 {
@@ -113,7 +173,7 @@ struct Plan {
     int U;        // units per token
     int nthr;     // threads per workgroup (one unit each)
     int ncb;      // column blocks per token
-    int tb;       // tokens per workgroup (1 or 2)
+    int tb;       // tokens per workgroup (the planner uses 1)
     bool stream;  // nontemporal hints on the data
     bool norm;    // q/k-norm variant (column blocks hold whole heads)
     int style;    // QKV_ROPE_NEOX or QKV_ROPE_INTERLEAVED

@@ -34,6 +34,22 @@ def test_exports_every_declared_symbol():
         assert hasattr(B.lib, n)
 
 
+def test_probe_library_exports_and_stands_apart():
+    """The benchmark's reference kernels live in their own library: it exports
+    its entry points, defines its launch stubs, and the epilogue library
+    carries none of them."""
+    from qkv_bias_rope_amd import probe as P
+    out = subprocess.run(["nm", "-D", "--defined-only", P.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (qkv_probe_\w+)", out))
+    assert exported == set(P.EXPORTS), exported
+    und = subprocess.run(["nm", "-D", "--undefined-only", P.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert "device_stub" not in und
+    epi = subprocess.run(["nm", "-D", B.LIB_PATH], capture_output=True, text=True).stdout
+    assert "qkv_probe" not in epi
+
+
 def test_every_kernel_launch_stub_is_defined():
     """Every kernel the host code launches has its launch stub in the library:
     some device-code constructs in a kernel template make hipcc's host pass

@@ -18,17 +18,27 @@ Timing: HIP events on the launch stream around the timed launches.  Beside
 that figure the line carries the p10/p50/p90 of single launches and the warm
 figure (one input set reused).
 
-Extra figures in the same line: the 256-sequence batched decode (f16 and f32
-caches) in GB/s, decode microseconds per layer for the 7B and 14B decode steps
-(stream loop and HIP-graph replay), the unfused seven-launch chain, the q/k-norm
-variant, and the projection-fed epilogue (bf16 GEMM / GEMV with the epilogue in
-its output stage) on the 14B prefill (TFLOP/s), the 14B one-token decode
-(us per layer, GB/s of weight streaming) and a 48-layer decode step of it
-(stream loop and HIP graph).  The CPU baseline is the oracle of
-the unfused chain, single-threaded, timed on a bounded sample of the headline
-workload.
+Reference points measured in the same run with the probe library
+(libqkv_probe.so, not part of the epilogue):
+  * ceiling: the best bare in-place add and copy of the prefill launch's bytes
+    over rotating buffers (swept over store policy and vectors per thread) --
+    "frac_of_achievable" is the epilogue's rate over the better of the two;
+  * the 256-sequence decode (f16 and f32 caches) is timed on the GPU side: 256
+    launches over 64 rotating input sets captured in one HIP graph and
+    replayed, beside a bare row pass that moves the same bytes from the same
+    sets into the same caches, and an empty kernel of the same launch shape;
+  * the empty-kernel floor of each decode launch shape, beside the decode
+    microseconds per layer (7B, 14B and the tiny decode; stream loop and
+    HIP-graph replay of a whole step).
+Also: the unfused seven-launch chain, the q/k-norm variant, the rope variants,
+and the projection-fed epilogue (bf16 GEMM / GEMV with the epilogue in its
+output stage) on the 14B prefill (TFLOP/s), the 14B one-token decode and a
+48-layer decode step of it.  The CPU baseline is the oracle of the unfused
+chain on the host cores, every configuration, one thread and a thread pool over
+token chunks; the headline's pool figure is `cpu_baseline`.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+       python bench.py --batched-only | --copy-calib | --proj-sweep
 """
 from __future__ import annotations
 
@@ -197,6 +207,38 @@ def launch_percentiles(h, arg_list, n, stream, fn=None):
     return dict(p10=round(q(0.1), 3), p50=round(q(0.5), 3), p90=round(q(0.9), 3), launches=n)
 
 
+def time_graph(launch, n_launch, replays, stream, warm_replays=2):
+    """Microseconds per launch of `launch(i)` (i = 0..n_launch-1) captured
+    into one HIP graph on `stream` and replayed `replays` times between two
+    events on the same stream: the GPU-side rate of back-to-back launches,
+    with no host issue in the timed region (each launch still waits for the
+    previous one, as consecutive layers do)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(n_launch):
+            rc = launch(i)
+            assert rc == 0, rc
+    with torch.cuda.stream(stream):
+        t_end = time.perf_counter() + 0.2
+        while time.perf_counter() < t_end:
+            g.replay()
+            torch.cuda.synchronize()
+        for _ in range(warm_replays):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
+        e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (n_launch * replays)
+    del g
+    return us
+
+
 def bench_bandwidth(h, w, cache_dtype, steps, warmup, stream, min_set_bytes=1.5e9, slot=False,
                     fn=None, norm=False, rope_style=0, freq_scale=0.0):
     from qkv_bias_rope_amd import workloads as wl
@@ -217,6 +259,66 @@ def bench_bandwidth(h, w, cache_dtype, steps, warmup, stream, min_set_bytes=1.5e
         fn = norm_runner(sets)
     ms = time_launches(h, args, steps, warmup, stream, fn=fn)
     return dict(ms=ms, bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9, sets=R), sets
+
+
+def bench_batched(h, w, cache_dtype, stream, n_launch=256, replays=4, R=64):
+    """The 256-sequence decode, GPU side: `n_launch` launches over R rotating
+    input sets (~470 MB of q/k/v, beyond the 256 MB last-level cache; one
+    shared cache pair, written at fresh random rows by every set) captured in
+    a HIP graph and replayed.  Beside it, on the same sets, positions and
+    caches: the probe library's row pass that moves the same bytes (the bare
+    pass; best over tokens per workgroup and store policy), the in-place add
+    of the q/k/v alone, and an empty kernel of the epilogue's launch shape."""
+    import torch
+    from qkv_bias_rope_amd import binding as B
+    from qkv_bias_rope_amd import probe as P
+    from qkv_bias_rope_amd import workloads as wl
+    cb = 2 if cache_dtype == wl.CACHE_F16 else 4
+    nbytes = algo_bytes(w, w.nt, cb, slot=True)
+    sets = Sets(w, R, cache_dtype, share_cache=True)
+    args = [sets.args(r, stream) for r in range(R)]
+    run = B.qkv_epilogue_run_ex
+    ep_us = time_graph(lambda i: run(h, args[i % R]), n_launch, replays, stream)
+    loop_ms = time_launches(h, args, n_launch, 32, stream)
+    assert B.qkv_epilogue_status(h) == 0, B.qkv_epilogue_last_error(h)
+    rc, plan = B.qkv_epilogue_plan(args[0])
+    assert rc == 0
+    # the same bytes through the bare row pass: concat copies of the sets' rows
+    xs = [torch.cat([st["q"], st["k"], st["v"]], dim=1).contiguous() for st in sets.sets]
+    bcat = torch.cat([sets.bq, sets.bk, sets.bv]).contiguous()
+    kc, vc = sets.sets[0]["kc"], sets.sets[0]["vc"]
+    rows = []
+    for tpb in (1, 2, 4):
+        for pol in (1, 2):
+            us = time_graph(lambda i, tpb=tpb, pol=pol: P.rows(
+                xs[i % R], bcat, w.nqt, w.nkt, sets.sets[i % R]["pos"], sets.sets[i % R]["slot"],
+                w.n_ctx, kc, vc, block=256, tpb=tpb, policy=pol, stream=stream), n_launch, replays, stream)
+            rows.append(dict(tokens_per_workgroup=tpb, policy=pol, us=round(us, 3),
+                             gbs=round(nbytes / us / 1e3, 1)))
+    adds = []
+    for pol in (1, 2):
+        us = time_graph(lambda i, pol=pol: P.add(xs[i % R], 256, 1, pol, stream), n_launch, replays,
+                        stream)
+        adds.append(dict(policy=pol, us=round(us, 3)))
+    empty_us = time_graph(lambda i: P.empty(int(plan.grid), int(plan.block), stream), n_launch,
+                          replays, stream)
+    bare = _best(rows)
+    bare1 = _best([r for r in rows if r["tokens_per_workgroup"] == 1])
+    gbs = nbytes / ep_us / 1e3
+    res = dict(us_per_launch=round(ep_us, 3), gbs=round(gbs, 1),
+               frac_of_peak=round(gbs / PEAK_HBM_GBS, 4),
+               bare_pass_us=bare["us"], bare_pass_gbs=bare["gbs"],
+               frac_of_achievable=round(bare["us"] / ep_us, 4),
+               bare_pass_one_token_per_workgroup_us=bare1["us"],
+               inplace_add_qkv_only_us=_best(adds)["us"],
+               empty_kernel_same_launch_us=round(empty_us, 3),
+               stream_loop_us_per_launch=round(loop_ms * 1e3, 3),
+               launch=dict(grid=int(plan.grid), block=int(plan.block)),
+               bytes_per_launch=nbytes, input_sets=R, graph_launches=n_launch,
+               graph_replays=replays, bare_pass_sweep=rows)
+    del sets, args, xs
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_decode(h, w, steps, warmup, stream, unfused=False):
@@ -425,77 +527,181 @@ def bench_proj_decode(h, w, hidden, steps, warmup, stream, wfmt="bf16"):
                 us_per_layer_graph=ms_graph * 1e3 / w.layers, layers=w.layers)
 
 
-def cpu_baseline(w, cache_dtype, budget_s=10.0):
-    """The oracle (single-threaded C, unfused chain) on the headline workload,
-    repeated over whole launches until about budget_s seconds have passed."""
-    import numpy as np
+def cpu_threads():
+    """Host threads for the oracle's parallel leg: the cores this process may
+    run on, capped by OMP_NUM_THREADS when set (the share of a shared host)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
+                        "unknown")
+    except OSError:
+        return "unknown"
+
+
+def oracle_launch_s(w, d, cache_dtype, threads, budget_s):
+    """Seconds per launch of the oracle's unfused chain on one launch's inputs
+    (q/k/v copied fresh before each timed call), repeated for about budget_s.
+    With threads > 1 the tokens are split into contiguous chunks, one oracle
+    call each, run by a thread pool: the chain is unchanged (tokens are
+    independent and ctypes releases the interpreter lock during the call)."""
     import oracle
-    from qkv_bias_rope_amd import workloads as wl
-    d = wl.draw_layer(w, 0)
-    cb = 2 if cache_dtype == wl.CACHE_F16 else 4
-    n = 0
-    t0 = time.perf_counter()
+    from concurrent.futures import ThreadPoolExecutor
+    nt = int(d["pos"].size)
+    chunks = [(a, min(nt, a + -(-nt // threads))) for a in range(0, nt, -(-nt // threads))]
+
+    def one(q, k, v, a, b):
+        oracle.qkv_epilogue(q[a:b].ravel(), k[a:b].ravel(), v[a:b].ravel(), d["bq"], d["bk"],
+                            d["bv"], d["pos"][a:b], n_head=w.n_head, n_kv_head=w.n_kv_head,
+                            head_dim=w.head_dim, theta=w.theta, n_ctx=w.n_ctx,
+                            cache_dtype=cache_dtype,
+                            slot=None if d["slot"] is None else d["slot"][a:b],
+                            n_slots=w.n_slots)
+
+    pool = ThreadPoolExecutor(threads) if len(chunks) > 1 else None
+    n, spent = 0, 0.0
+    t_end = time.perf_counter() + budget_s
     while True:
         q, k, v = (d[x].copy() for x in ("q", "k", "v"))
         ts = time.perf_counter()
-        oracle.qkv_epilogue(q.ravel(), k.ravel(), v.ravel(), d["bq"], d["bk"], d["bv"], d["pos"],
-                            n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim,
-                            theta=w.theta, n_ctx=w.n_ctx, cache_dtype=cache_dtype,
-                            slot=d["slot"], n_slots=w.n_slots)
-        n += 1
-        if n == 1:
-            spent = time.perf_counter() - ts
+        if pool is None:
+            one(q, k, v, 0, nt)
         else:
-            spent += time.perf_counter() - ts
-        if time.perf_counter() - t0 >= budget_s:
+            list(pool.map(lambda c: one(q, k, v, *c), chunks))
+        spent += time.perf_counter() - ts
+        n += 1
+        if time.perf_counter() >= t_end and n >= 3:
             break
-    s_per = spent / n
-    cpu = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
-    except OSError:
-        pass
-    return dict(value=algo_bytes(w, w.nt, cb) / s_per / 1e9, unit="GB/s", cores=1, kind="oracle",
-                sample=f"{n} full launch(es) of {w.name} ({w.nt} tokens, f16 cache) on 1 host "
-                       f"thread, {s_per:.3f} s each", cpu=cpu)
+    if pool is not None:
+        pool.shutdown()
+    return spent / n, n
 
 
-def hbm_ceiling(steps, stream, nbytes=251703296, sets=8):
-    """A practical HBM ceiling on the same box: torch's in-place add over
-    buffers that move the headline launch's bytes (half read, half written),
-    rotated over `sets` buffers so they come from HBM.  Event-timed per call."""
+def cpu_oracle_all(budget_s=3.0):
+    """The oracle on the host cores, every configuration: one thread, and a
+    thread pool over token chunks (batched launches only).  Microseconds per
+    launch (per layer for the decode shapes) and GB/s by the same byte count
+    as the GPU.  The 256-sequence decode keeps only the 256 written rows
+    (the oracle returns the rows; no cache is allocated)."""
+    from qkv_bias_rope_amd import workloads as wl
+    nthr = cpu_threads()
+    out = {"cpu": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0)),
+           "threads_parallel": nthr}
+    for w in wl.ALL:
+        for cd in w.cache_dtypes:
+            cb = 2 if cd == wl.CACHE_F16 else 4
+            nbytes = algo_bytes(w, w.nt, cb, slot=w.n_slots > 1)
+            d = wl.draw_layer(w, 0)
+            tag = w.name + ("" if len(w.cache_dtypes) == 1 else ("_f16" if cd == wl.CACHE_F16 else "_f32"))
+            s1, n1 = oracle_launch_s(w, d, cd, 1, budget_s)
+            r = dict(us_per_launch_1thread=round(s1 * 1e6, 2), gbs_1thread=round(nbytes / s1 / 1e9, 4),
+                     launches_1thread=n1, bytes_per_launch=nbytes)
+            if w.nt > 1:
+                sn, nn = oracle_launch_s(w, d, cd, nthr, budget_s)
+                r.update(us_per_launch_nthread=round(sn * 1e6, 2),
+                         gbs_nthread=round(nbytes / sn / 1e9, 4), launches_nthread=nn)
+            out[tag] = r
+            log(f"[bench]   oracle {tag}: {r}")
+    return out
+
+
+def _best(results, key="us"):
+    return min(results, key=lambda r: r[key])
+
+
+def ceilings_prefill(steps, stream, nbytes=251703296, sets=8):
+    """What a bare streaming pass achieves for the prefill launch's bytes on
+    this device: the probe library's in-place add (half read, half written,
+    like the epilogue's q/k/v) and copy, each over `sets` rotating buffers so
+    every launch comes from HBM, swept over store policy and vectors per
+    thread; event-timed over a stream loop like the headline."""
     import torch
-    n = nbytes // 8                                   # float32 elements per buffer
+    from qkv_bias_rope_amd import probe as P
+    n = nbytes // 8 // 4 * 4                        # float32 elements per buffer
     bufs = [torch.ones(n, dtype=torch.float32, device="cuda:0") for _ in range(sets)]
-    with torch.cuda.stream(stream):
-        for i in range(2 * sets):
-            bufs[i % sets].add_(1.0)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(steps):
-            bufs[i % sets].add_(1.0)
-        e1.record(stream)
-        e1.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    del bufs
+    dsts = [torch.empty_like(b) for b in bufs]
+    out = {"bytes": n * 8, "rotating_buffers": sets, "block": 256}
+    k = max(20, min(steps, 100))
+    for name in ("inplace_add", "copy"):
+        res = []
+        for pol in (1, 2):
+            for vpt in (1, 2):
+                if name == "inplace_add":
+                    fn = lambda i, pol=pol, vpt=vpt: P.add(bufs[i % sets], 256, vpt, pol, stream)
+                else:
+                    fn = lambda i, pol=pol, vpt=vpt: P.copy(dsts[i % sets], bufs[i % sets], 256, vpt,
+                                                            pol, stream)
+                with torch.cuda.stream(stream):
+                    for i in range(2 * sets):
+                        assert fn(i) == 0
+                    torch.cuda.synchronize()
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for i in range(k):
+                        fn(i)
+                    e1.record(stream)
+                    e1.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / k
+                res.append(dict(policy=pol, vpt=vpt, us=round(us, 3), gbs=round(n * 8 / us / 1e3, 1)))
+        b = _best(res)
+        out[name] = dict(best_us=b["us"], best_gbs=b["gbs"], best_policy=b["policy"],
+                         best_vpt=b["vpt"], sweep=res)
+    out["achievable_gbs"] = max(out["inplace_add"]["best_gbs"], out["copy"]["best_gbs"])
+    del bufs, dsts
     torch.cuda.empty_cache()
-    return dict(us_per_call=round(ms * 1e3, 3), gbs=round(n * 8 / (ms * 1e-3) / 1e9, 1), bytes=n * 8)
+    return out
+
+
+def floors(stream, shapes):
+    """Per-launch floor of an empty kernel at the given (grid, block) launch
+    shapes: back-to-back in a HIP-graph replay (GPU side) and in a stream
+    loop issued from this process (host issue included)."""
+    import torch
+    from qkv_bias_rope_amd import probe as P
+    out = {}
+    for g_, b_ in shapes:
+        gu = time_graph(lambda i: P.empty(g_, b_, stream), 256, 4, stream)
+        with torch.cuda.stream(stream):
+            for _ in range(64):
+                P.empty(g_, b_, stream)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(512):
+                P.empty(g_, b_, stream)
+            e1.record(stream)
+            e1.synchronize()
+        out[f"grid{g_}x{b_}"] = dict(graph_us=round(gu, 3),
+                                     stream_loop_us=round(e0.elapsed_time(e1) * 1e3 / 512, 3))
+    return out
 
 
 def copy_calibration(steps):
-    """A plain device copy of known size (for scaling FETCH_SIZE/WRITE_SIZE)."""
+    """Known traffic for scaling FETCH_SIZE / WRITE_SIZE: the probe library's
+    copy of 1 GiB (1 GiB read, 1 GiB written) under the non-temporal policy,
+    then under the write-through policy the epilogue's streaming stores use;
+    `steps` launches each."""
     import torch
+    from qkv_bias_rope_amd import probe as P
     n = 256 * 1024 * 1024  # float32 elements = 1 GiB
     src = torch.ones(n, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
-    for _ in range(steps):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
-                      "launches": steps}))
+    s = torch.cuda.current_stream()
+    for pol in (1, 2):
+        for _ in range(steps):
+            assert P.copy(dst, src, 256, 1, pol, s) == 0
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_policy": pol, "bytes_read": n * 4, "bytes_written": n * 4,
+                          "launches": steps}), flush=True)
 
 
 PROJ_SWEEP_TOKENS = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096)
@@ -533,6 +739,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--batched-only", action="store_true",
+                    help="run only the 256-sequence decode (f16 and f32 caches), one JSON line")
     ap.add_argument("--proj-sweep", action="store_true",
                     help="run only the projection-fed epilogue at 1..4096 tokens (14B width, "
                          "hidden 5120), one JSON line per token count")
@@ -559,6 +767,19 @@ def main():
         return
     if args.proj_sweep:
         proj_sweep(args)
+        return
+    if args.batched_only:
+        rc, h = B.qkv_epilogue_create(0, 4096)
+        assert rc == 0, rc
+        stream = torch.cuda.Stream()
+        out = {}
+        with torch.cuda.stream(stream):
+            for cd, tag in ((wl.CACHE_F16, "f16"), (wl.CACHE_F32, "f32")):
+                r = bench_batched(h, wl.BATCHED_DECODE_14B, cd, stream)
+                out[f"{wl.BATCHED_DECODE_14B.name}_{tag}"] = r
+                log(f"[bench] {tag}: {r['us_per_launch']} us/launch, bare pass {r['bare_pass_us']} us")
+        B.qkv_epilogue_destroy(h)
+        print(json.dumps(out), flush=True)
         return
 
     rc, h = B.qkv_epilogue_create(0, 4096)
@@ -594,26 +815,34 @@ def run_all(args, h, stream):
             f"{extra[w.name + '_warm']}")
     del sets
     torch.cuda.empty_cache()
+    ceil = None
     if not args.no_extra:
-        extra["hbm_ceiling_inplace_add"] = hbm_ceiling(args.steps, stream)
-        log(f"[bench] HBM ceiling (in-place add of the same bytes): {extra['hbm_ceiling_inplace_add']}")
+        log("[bench] ceilings: bare passes of the prefill launch's bytes")
+        ceil = ceilings_prefill(args.steps, stream)
+        extra["ceiling_prefill_14b_4096"] = ceil
+        extra[w.name + "_frac_of_achievable"] = round(main_res["gbs"] / ceil["achievable_gbs"], 4)
+        log(f"[bench]   achievable {ceil['achievable_gbs']} GB/s (add {ceil['inplace_add']['best_gbs']}, "
+            f"copy {ceil['copy']['best_gbs']}); epilogue at "
+            f"{extra[w.name + '_frac_of_achievable']:.3f} of it")
 
     if not args.no_extra:
         wb = wl.BATCHED_DECODE_14B
         for cd, tag in ((wl.CACHE_F16, "f16"), (wl.CACHE_F32, "f32")):
-            log(f"[bench] {wb.name} {tag}")
-            r, sets = bench_bandwidth(h, wb, cd, args.steps, args.warmup, stream,
-                                      min_set_bytes=1.0e9, slot=True)
-            del sets
-            torch.cuda.empty_cache()
-            extra[f"{wb.name}_{tag}"] = dict(
-                gbs=round(r["gbs"], 1), us_per_launch=round(r["ms"] * 1e3, 3),
-                bytes_per_launch=r["bytes"], frac_of_peak=round(r["gbs"] / PEAK_HBM_GBS, 4),
-                input_sets=r["sets"])
-            log(f"[bench]   {r['ms'] * 1e3:.2f} us/launch, {r['gbs']:.1f} GB/s")
+            log(f"[bench] {wb.name} {tag} (HIP-graph replay)")
+            r = bench_batched(h, wb, cd, stream)
+            extra[f"{wb.name}_{tag}"] = r
+            log(f"[bench]   {r['us_per_launch']:.3f} us/launch, {r['gbs']:.1f} GB/s; bare pass "
+                f"{r['bare_pass_us']:.3f} us ({r['frac_of_achievable']:.3f} of achievable); empty "
+                f"kernel {r['empty_kernel_same_launch_us']:.3f} us")
+        fl = floors(stream, [(3, 64), (9, 64), (14, 64)])
+        extra["empty_kernel_floor"] = fl
+        log(f"[bench] empty-kernel floor: {fl}")
+        shape = {wl.TINY_DECODE.name: "grid3x64", wl.DECODE_7B.name: "grid9x64",
+                 wl.DECODE_14B.name: "grid14x64"}
         for wd in (wl.TINY_DECODE, wl.DECODE_7B, wl.DECODE_14B):
             log(f"[bench] {wd.name}")
             r = bench_decode(h, wd, max(10, args.steps // 10), max(2, args.warmup // 10), stream)
+            r["empty_kernel_same_launch"] = fl[shape[wd.name]]
             extra[wd.name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
             log(f"[bench]   {r['us_per_layer_stream']:.2f} us/layer (stream), "
                 f"{r.get('us_per_layer_graph', float('nan')):.2f} us/layer (graph)")
@@ -706,10 +935,19 @@ def run_all(args, h, stream):
 
     cpu = None
     if not args.no_cpu:
-        log("[bench] CPU oracle baseline")
-        cpu = cpu_baseline(w, wl.CACHE_F16)
-        cpu["value"] = round(cpu["value"], 4)
-        log(f"[bench]   {cpu['value']} GB/s")
+        log("[bench] CPU oracle on the host cores, every configuration")
+        co = cpu_oracle_all()
+        extra["cpu_oracle"] = co
+        c4 = co[w.name]
+        cpu = {"value": c4["gbs_nthread"], "unit": "GB/s", "cores": co["threads_parallel"],
+               "kind": "oracle",
+               "sample": (f"{c4['launches_nthread']} full launches of {w.name} ({w.nt} tokens, f16 "
+                          f"cache), tokens split over {co['threads_parallel']} host threads; "
+                          f"{c4['us_per_launch_nthread'] / 1e3:.1f} ms per launch"),
+               "single_thread": {"value": c4["gbs_1thread"], "cores": 1,
+                                 "ms_per_launch": round(c4["us_per_launch_1thread"] / 1e3, 2),
+                                 "launches": c4["launches_1thread"]},
+               "cpu": co["cpu"]}
 
     traffic = read_traffic(w.name)
     achieved = main_res["gbs"]

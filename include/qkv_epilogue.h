@@ -271,6 +271,31 @@ typedef struct qkv_proj_args {
 int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *a);
 
 /*
+ * qkv_epilogue_run_proj for callers that cannot allocate device memory: code
+ * being captured into a HIP graph, serving loops that must not call the
+ * allocator, harnesses that forbid it.  Same arguments, results and errors as
+ * qkv_epilogue_run_proj, and the same kernels; the launches of more than 4
+ * tokens take their workspace (cos/sin table, cache rows, k-split partial
+ * sums) from a static device array of 32 MiB (33554432 bytes) instead of the
+ * handle's.  It never allocates, frees or synchronizes.
+ *   - Limit: a call whose workspace exceeds 32 MiB returns
+ *     QKV_ERR_UNSUPPORTED and launches nothing.  The workspace is nt *
+ *     head_dim * 4 bytes plus nt * 8, each rounded up to 256, plus splits * nt
+ *     * (nqt + 2*nkt) * 4 when the planner splits k (256 tokens of the 14B
+ *     shape split four ways: 29.5 MB, within the limit; 4096 unsplit tokens:
+ *     2.1 MB).  Use qkv_epilogue_run_proj beyond it.
+ *   - The array exists once per GPU, for the life of the process; its
+ *     address is looked up when a handle is created on that device
+ *     (QKV_ERR_HIP here if that lookup failed).  Every call on one GPU, from
+ *     any handle, uses the same array and leaves its contents behind: calls
+ *     whose launches can overlap on one GPU (different streams, different
+ *     threads) race on it and must be ordered by the caller.  Nothing in it
+ *     needs clearing between calls: every element a launch reads was written
+ *     earlier in the same call.
+ */
+int qkv_epilogue_run_proj_noalloc(qkv_epilogue_t *h, const qkv_proj_args_t *a);
+
+/*
  * The same operation as qkv_epilogue_run_ex, computed by the UNFUSED chain the
  * fused kernel replaces: three bias-add launches (q, k, v), two rope launches
  * (q, k) and two store launches (K, V), seven kernels in that order (page "73 ·

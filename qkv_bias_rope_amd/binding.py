@@ -41,7 +41,7 @@ EXPORTS = ("qkv_epilogue_create", "qkv_epilogue_run", "qkv_epilogue_run_ex",
            "qkv_epilogue_run_unfused", "qkv_epilogue_run_qk_norm",
            "qkv_epilogue_status", "qkv_epilogue_last_error", "qkv_epilogue_destroy",
            "qkv_epilogue_inv_freq", "qkv_epilogue_inv_freq_scaled", "qkv_epilogue_check_args",
-           "qkv_epilogue_plan", "qkv_epilogue_run_proj")
+           "qkv_epilogue_plan", "qkv_epilogue_run_proj", "qkv_epilogue_run_proj_noalloc")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -121,6 +121,8 @@ def _load():
     lib.qkv_epilogue_plan.restype = _I
     lib.qkv_epilogue_run_proj.argtypes = [_P, ctypes.POINTER(QkvProjArgs)]
     lib.qkv_epilogue_run_proj.restype = _I
+    lib.qkv_epilogue_run_proj_noalloc.argtypes = [_P, ctypes.POINTER(QkvProjArgs)]
+    lib.qkv_epilogue_run_proj_noalloc.restype = _I
     return lib
 
 
@@ -167,6 +169,10 @@ def qkv_epilogue_run_qk_norm(h, args: QkvEpilogueArgs, w_q, w_k, eps: float) -> 
 
 def qkv_epilogue_run_proj(h, args: QkvProjArgs) -> int:
     return lib.qkv_epilogue_run_proj(h, ctypes.byref(args))
+
+
+def qkv_epilogue_run_proj_noalloc(h, args: QkvProjArgs) -> int:
+    return lib.qkv_epilogue_run_proj_noalloc(h, ctypes.byref(args))
 
 
 def make_proj_args(x, w, hidden, epi: QkvEpilogueArgs, ld_x=0, w_k=None, w_v=None,

@@ -860,6 +860,10 @@ int qkv_epilogue_create(qkv_epilogue_t **out, const qkv_epilogue_config_t *cfg)
         e = hipMalloc(reinterpret_cast<void **>(&h->d_err), 16);
     if (e == hipSuccess)
         e = hipMemset(h->d_err, 0, 16);
+    // the static workspace's address on this device (the allocation-free
+    // projection reports an error if the lookup failed)
+    if (e == hipSuccess)
+        (void)proj_scratch_setup(h->device);
     if (e != hipSuccess) {
         if (h->d_err)
             (void)hipFree(h->d_err);

@@ -248,6 +248,10 @@ namespace qkv_detail {
 
 int fail(qkv_epilogue *h, int code, const char *fmt, ...);
 
+// Look up, once per device (that device current), the device address of the
+// allocation-free projection's static workspace.  Called by create.
+int proj_scratch_setup(int device);
+
 // The handle's table for (theta, head_dim, freq_scale; 0 means 1), recomputed
 // only when they change.
 const InvTable &handle_inv(qkv_epilogue *h, float theta, int head_dim, float freq_scale);

@@ -34,6 +34,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <cmath>
 #include <cstring>
 
@@ -1164,7 +1165,52 @@ hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st
 
 }  // namespace
 
-extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *pa)
+// ---- the workspace of the allocation-free entry point -----------------------
+// A file-scope device array, one copy per GPU the library runs on, held until
+// the process ends.  Its device address is taken once per device at handle
+// creation (proj_scratch_setup) with that device current; host code uses only
+// that address, never the array's name (which names a host-side stand-in).
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+void *g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+namespace qkv_detail {
+
+int proj_scratch_setup(int device)
+{
+    if (device < 0 || device >= kMaxScratchDevices)
+        return QKV_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[device])
+        return QKV_OK;
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+        return QKV_ERR_HIP;
+    g_scratch_ptr[device] = ptr;
+    return QKV_OK;
+}
+
+}  // namespace qkv_detail
+
+namespace {
+
+void *scratch_ptr(int device)
+{
+    if (device < 0 || device >= kMaxScratchDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    return g_scratch_ptr[device];
+}
+
+// run_proj and run_proj_noalloc: identical but for where the MFMA path's
+// workspace lives (the handle's, grown with hipMalloc; or the static scratch)
+int run_proj_impl(qkv_epilogue_t *h, const qkv_proj_args_t *pa, bool static_ws)
 {
     if (!h)
         return QKV_ERR_INVALID_ARG;
@@ -1320,7 +1366,21 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
         const size_t rows = ((size_t)pp.M * sizeof(int64_t) + 255) / 256 * 256;
         const size_t need =
             tab + rows + (pp.ksplit > 1 ? (size_t)pp.ksplit * pp.M * pp.N * sizeof(float) : 0);
-        if (h->proj_ws_bytes < need) {
+        if (static_ws) {
+            void *const sp = scratch_ptr(h->device);
+            if (!sp)
+                return fail(h, QKV_ERR_HIP, "the static workspace of device %d has no address "
+                            "(handle creation could not look it up)", h->device);
+            if (need > kScratchBytes)
+                return fail(h, QKV_ERR_UNSUPPORTED,
+                            "this call needs %zu bytes of workspace; the allocation-free entry point "
+                            "has %zu (use qkv_epilogue_run_proj, or fewer tokens per call)",
+                            need, kScratchBytes);
+            char *ws = static_cast<char *>(sp);
+            pp.rtab = reinterpret_cast<const float *>(ws);
+            pp.rows = reinterpret_cast<const int64_t *>(ws + tab);
+            pp.part = reinterpret_cast<float *>(ws + tab + rows);
+        } else if (h->proj_ws_bytes < need) {
             // growing synchronizes the device and allocates: refused while the
             // stream is being captured, where neither is allowed
             hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -1350,10 +1410,12 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
             }
             h->proj_ws_bytes = need;
         }
-        char *ws = static_cast<char *>(h->proj_ws);
-        pp.rtab = reinterpret_cast<const float *>(ws);
-        pp.rows = reinterpret_cast<const int64_t *>(ws + tab);
-        pp.part = reinterpret_cast<float *>(ws + tab + rows);
+        if (!static_ws) {
+            char *ws = static_cast<char *>(h->proj_ws);
+            pp.rtab = reinterpret_cast<const float *>(ws);
+            pp.rows = reinterpret_cast<const int64_t *>(ws + tab);
+            pp.part = reinterpret_cast<float *>(ws + tab + rows);
+        }
     }
     const bool f16 = a->cache_dtype == QKV_CACHE_F16;
     if (a->head_dim == 128)
@@ -1364,4 +1426,16 @@ extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *p
         return fail(h, QKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     h->last_stream = st;
     return QKV_OK;
+}
+
+}  // namespace
+
+extern "C" int qkv_epilogue_run_proj(qkv_epilogue_t *h, const qkv_proj_args_t *pa)
+{
+    return run_proj_impl(h, pa, false);
+}
+
+extern "C" int qkv_epilogue_run_proj_noalloc(qkv_epilogue_t *h, const qkv_proj_args_t *pa)
+{
+    return run_proj_impl(h, pa, true);
 }

@@ -1,5 +1,6 @@
 """Compile the HIP libraries in-tree:
-  csrc/qkv_epilogue.hip, qkv_unfused.hip, qkv_proj.hip -> libqkv_epilogue.so
+  csrc/qkv_epilogue.hip, qkv_unfused.hip, qkv_proj.hip, qkv_host.cpp
+    -> libqkv_epilogue.so
   csrc/hbm_probe.hip -> libqkv_probe.so (the benchmark's floor and ceiling
   kernels; not part of the epilogue library).
 
@@ -14,8 +15,11 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", f) for f in ("qkv_epilogue.hip", "qkv_unfused.hip", "qkv_proj.hip")]
-HDRS = [os.path.join(ROOT, "include", "qkv_epilogue.h"), os.path.join(PKG, "csrc", "qkv_internal.h")]
+SRCS = [os.path.join(PKG, "csrc", f)
+        for f in ("qkv_epilogue.hip", "qkv_unfused.hip", "qkv_proj.hip", "qkv_host.cpp")]
+HOST_SRC = os.path.join(PKG, "csrc", "qkv_host.cpp")   # the host-only part (no HIP)
+HDRS = [os.path.join(ROOT, "include", "qkv_epilogue.h"), os.path.join(PKG, "csrc", "qkv_internal.h"),
+        os.path.join(PKG, "csrc", "qkv_plan.h")]
 LIB = os.path.join(PKG, "libqkv_epilogue.so")
 PROBE_SRC = os.path.join(PKG, "csrc", "hbm_probe.hip")
 PROBE_LIB = os.path.join(PKG, "libqkv_probe.so")

@@ -1,6 +1,7 @@
-// qkv_internal.h -- internals shared by the translation units of
-// libqkv_epilogue.so (fused kernel, unfused chain): vector slot types, the
-// load/store policies, argument validation and planning, the handle.
+// qkv_internal.h -- internals shared by the HIP translation units of
+// libqkv_epilogue.so (fused kernel, unfused chain, projection): vector slot
+// types, the load/store policies and the handle.  Argument validation and
+// planning are host-only and declared in qkv_plan.h.
 // Not part of the public interface (that is include/qkv_epilogue.h).
 #ifndef QKV_INTERNAL_H
 #define QKV_INTERNAL_H
@@ -12,11 +13,9 @@
 #include <cstdio>
 
 #include "qkv_epilogue.h"
+#include "qkv_plan.h"
 
 namespace qkv_detail {
-
-constexpr int kMaxHalf = QKV_MAX_HEAD_DIM / 2;
-constexpr int kMaxBlock = 1024;
 
 // Inverse-frequency table passed by value in the kernel arguments.
 struct InvTable {
@@ -161,47 +160,6 @@ __device__ __forceinline__ void st_stream_cache(void *row_base, uint32_t idx, co
         st_stream<W>(static_cast<float *>(row_base), idx * 4u, v);
     }
 }
-
-// LDS layout: int64 row[tb] | float cos[tb*half] | float sin[tb*half]
-__host__ __device__ inline int lds_row_bytes(int tb)
-{
-    return ((tb * 8) + 15) & ~15;
-}
-
-struct Plan {
-    int W;        // vector width: 4 (16-byte slots) or 1 (scalar slots)
-    int U;        // units per token
-    int nthr;     // threads per workgroup (one unit each)
-    int ncb;      // column blocks per token
-    int tb;       // tokens per workgroup (the planner uses 1)
-    bool stream;  // nontemporal hints on the data
-    bool norm;    // q/k-norm variant (column blocks hold whole heads)
-    int style;    // QKV_ROPE_NEOX or QKV_ROPE_INTERLEAVED
-    int64_t grid;
-    int lds;
-    int half;
-    int64_t nqt, nkt;
-    int64_t ld[3];
-    int64_t n_ctx, n_slots;
-};
-
-int ceil_div(int64_t a, int64_t b);
-void set_msg(char *msg, size_t len, const char *fmt, ...);
-
-// check_and_plan flags
-constexpr unsigned kPlanBiasOptional = 1u;  // NULL biases mean "no bias"
-constexpr unsigned kPlanNorm = 2u;          // plan the q/k-norm variant
-
-// Validate a request (the checks run_ex documents) and plan the fused launch.
-// With kPlanNorm, wq/wk are the [head_dim] norm weights (checked for NULL,
-// alignment and overlap with the outputs) and eps the norm epsilon.
-int check_and_plan(const qkv_epilogue_args_t *a, int64_t n_ctx_default, Plan *pl, char *msg,
-                   size_t mlen, unsigned flags = 0, const float *wq = nullptr,
-                   const float *wk = nullptr, float eps = 0.0f);
-
-// inv[i] = f32(freq_scale * theta^(-2i/head_dim)), computed in double and
-// rounded once.
-void host_inv_freq(float theta, int head_dim, float freq_scale, float *out);
 
 struct DeviceGuard {
     int prev = -1;

@@ -266,9 +266,11 @@ def bench_batched(h, w, cache_dtype, stream, n_launch=256, replays=4, R=64):
     input sets (~470 MB of q/k/v, beyond the 256 MB last-level cache; one
     shared cache pair, written at fresh random rows by every set) captured in
     a HIP graph and replayed.  Beside it, on the same sets, positions and
-    caches: the probe library's row pass that moves the same bytes (the bare
-    pass; best over tokens per workgroup and store policy), the in-place add
-    of the q/k/v alone, and an empty kernel of the epilogue's launch shape."""
+    caches: the probe library's row pass that moves the same bytes from
+    concat [nt][nqt+2nkt] copies of the rows (the bare pass; best over tokens
+    per workgroup and store policy, and at one token per workgroup like the
+    epilogue), the epilogue itself on those concat rows, the in-place add of
+    the q/k/v alone, and an empty kernel of the epilogue's launch shape."""
     import torch
     from qkv_bias_rope_amd import binding as B
     from qkv_bias_rope_amd import probe as P
@@ -287,6 +289,17 @@ def bench_batched(h, w, cache_dtype, stream, n_launch=256, replays=4, R=64):
     xs = [torch.cat([st["q"], st["k"], st["v"]], dim=1).contiguous() for st in sets.sets]
     bcat = torch.cat([sets.bq, sets.bk, sets.bv]).contiguous()
     kc, vc = sets.sets[0]["kc"], sets.sets[0]["vc"]
+    # the epilogue on that concat layout too (q|k|v sections of one row)
+    cargs = []
+    for r in range(R):
+        x, st = xs[r], sets.sets[r]
+        cargs.append(B.make_args(x[:, :w.nqt], x[:, w.nqt:w.nqt + w.nkt], x[:, w.nqt + w.nkt:], sets.bq,
+                                 sets.bk, sets.bv, st["pos"], kc, vc, n_head=w.n_head,
+                                 n_kv_head=w.n_kv_head, head_dim=w.head_dim, theta=w.theta,
+                                 cache_dtype=cache_dtype, slot=st["slot"], n_ctx=w.n_ctx,
+                                 n_slots=w.n_slots, stream=stream, use_stream=True))
+    cat_us = time_graph(lambda i: run(h, cargs[i % R]), n_launch, replays, stream)
+    assert B.qkv_epilogue_status(h) == 0, B.qkv_epilogue_last_error(h)
     rows = []
     for tpb in (1, 2, 4):
         for pol in (1, 2):
@@ -310,13 +323,15 @@ def bench_batched(h, w, cache_dtype, stream, n_launch=256, replays=4, R=64):
                bare_pass_us=bare["us"], bare_pass_gbs=bare["gbs"],
                frac_of_achievable=round(bare["us"] / ep_us, 4),
                bare_pass_one_token_per_workgroup_us=bare1["us"],
+               concat_layout_us_per_launch=round(cat_us, 3),
+               concat_layout_frac_of_bare_pass_one_token=round(bare1["us"] / cat_us, 4),
                inplace_add_qkv_only_us=_best(adds)["us"],
                empty_kernel_same_launch_us=round(empty_us, 3),
                stream_loop_us_per_launch=round(loop_ms * 1e3, 3),
                launch=dict(grid=int(plan.grid), block=int(plan.block)),
                bytes_per_launch=nbytes, input_sets=R, graph_launches=n_launch,
                graph_replays=replays, bare_pass_sweep=rows)
-    del sets, args, xs
+    del sets, args, xs, cargs
     torch.cuda.empty_cache()
     return res
 

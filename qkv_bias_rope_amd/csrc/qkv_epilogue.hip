@@ -131,6 +131,14 @@ __device__ __forceinline__ void rotate_pair(float &x0, float &x1, float c, float
     x1 = (float)(a * sd + b * cd);
 }
 
+// A 64-bit value that is the same in every active lane, as a scalar.
+__device__ __forceinline__ int64_t readfirstlane64(int64_t v)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Cache row of a token: slot*n_ctx + pos (slot 0 without slots), or -1 with
 // the error bit set when the position or the slot is out of range (the token
 // then writes no cache row).
@@ -358,15 +366,36 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
         }
         const int64_t row = s_row[tt];
         if constexpr (STREAM) {
-            // the section row and the cache row of this token are the bases,
-            // shared by the lanes of a wave that work on one section
-            float *const xrow = xsec + (int64_t)(t0 + tt) * ldx;
-            st_stream<W>(xrow, (uint32_t)col * 4u, ra);
-            st_stream<W>(xrow, (uint32_t)(col + d1) * 4u, rb);
-            if (sec > 0 && row >= 0) {
-                void *const crow = static_cast<char *>(cache) + row * p.nkt * (F16 ? 2 : 4);
-                st_stream_cache<W, F16>(crow, (uint32_t)col, ra);
-                st_stream_cache<W, F16>(crow, (uint32_t)(col + d1), rb);
+            // The bases of the stores are this token's row of the lane's
+            // section and its cache row.  When every lane of the wave works on
+            // one section (always, when the sections' unit counts are
+            // multiples of 64), they are taken from the first lane: the buffer
+            // resource is then a scalar value and each store one instruction.
+            // A wave spanning two sections takes the per-lane bases, and the
+            // compiler loops over their distinct values.
+            const int sec0 = __builtin_amdgcn_readfirstlane(sec);
+            if (__builtin_amdgcn_ballot_w64(sec != sec0) == 0) {
+                const int64_t tok = t0 + tt;
+                float *const xrow = pick3(sec0, p.x[0], p.x[1], p.x[2]) +
+                                    tok * pick3(sec0, p.ld[0], p.ld[1], p.ld[2]);
+                st_stream<W>(xrow, (uint32_t)col * 4u, ra);
+                st_stream<W>(xrow, (uint32_t)(col + d1) * 4u, rb);
+                const int64_t row0 = readfirstlane64(row);
+                if (sec0 > 0 && row0 >= 0) {
+                    void *const crow = static_cast<char *>(sec0 == 1 ? p.cache[0] : p.cache[1]) +
+                                       row0 * p.nkt * (F16 ? 2 : 4);
+                    st_stream_cache<W, F16>(crow, (uint32_t)col, ra);
+                    st_stream_cache<W, F16>(crow, (uint32_t)(col + d1), rb);
+                }
+            } else {
+                float *const xrow = xsec + (int64_t)(t0 + tt) * ldx;
+                st_stream<W>(xrow, (uint32_t)col * 4u, ra);
+                st_stream<W>(xrow, (uint32_t)(col + d1) * 4u, rb);
+                if (sec > 0 && row >= 0) {
+                    void *const crow = static_cast<char *>(cache) + row * p.nkt * (F16 ? 2 : 4);
+                    st_stream_cache<W, F16>(crow, (uint32_t)col, ra);
+                    st_stream_cache<W, F16>(crow, (uint32_t)(col + d1), rb);
+                }
             }
         } else {
             float *xp = xs + (int64_t)(t0 + tt) * ldx;

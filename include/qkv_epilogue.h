@@ -33,14 +33,25 @@
  * Conventions common to every call:
  *   - All tensor pointers are caller-owned DEVICE pointers on the handle's
  *     device.  The library never allocates, frees or copies tensor memory.
- *   - Calls that launch work are asynchronous on the given HIP stream: they
- *     never synchronize and may be captured into a HIP graph.
+ *     The device memory it owns: each handle's 16-byte error word (create),
+ *     each handle's projection workspace (grown by qkv_epilogue_run_proj,
+ *     freed by destroy) and one static projection array per GPU
+ *     (qkv_epilogue_run_proj_noalloc).
+ *   - Calls that launch work are asynchronous on the given HIP stream and
+ *     may be captured into a HIP graph.  Two calls block: qkv_epilogue_status
+ *     (by design) and a qkv_epilogue_run_proj call that has to grow the
+ *     handle's workspace (it synchronizes the device first; not allowed
+ *     during capture).
  *   - Every function returns 0 on success or a negative QKV_ERR_* code; the
  *     text of the last failure is available from qkv_epilogue_last_error.
  *     There is no fallback path: an unsupported request is an error (page
  *     "06 · Assign + fusion", §2.1: a violated kernel invariant aborts rather
  *     than falling back).
- *   - A handle is not thread-safe: use one handle per host thread.
+ *   - A handle is not thread-safe: use one handle per host thread.  Launches
+ *     of one handle on several streams may overlap, except the projection
+ *     calls, which share the handle's workspace (or the GPU's static array):
+ *     overlapping projection calls need separate handles (or, for the
+ *     allocation-free entry point, ordering by the caller).
  */
 #ifndef QKV_EPILOGUE_H
 #define QKV_EPILOGUE_H
@@ -86,7 +97,9 @@ typedef struct qkv_epilogue_config {
 
 /*
  * Create a handle.  Allocates the handle and a 16-byte device error word on
- * cfg->device (that word is the only device memory the library owns).
+ * cfg->device, and looks up the address of that device's static projection
+ * array (the projection workspace itself is allocated later, by the first
+ * qkv_epilogue_run_proj call that needs it).
  * Returns QKV_ERR_INVALID_ARG for a NULL out/cfg, n_ctx < 1 or a bad device
  * ordinal, QKV_ERR_HIP if the device cannot be used.  *out is NULL on error.
  */
@@ -308,10 +321,13 @@ int qkv_epilogue_run_proj_noalloc(qkv_epilogue_t *h, const qkv_proj_args_t *a);
 int qkv_epilogue_run_unfused(qkv_epilogue_t *h, const qkv_epilogue_args_t *a);
 
 /*
- * Blocking: synchronize the stream of the handle's last launch, read and
- * clear the device error word.  Returns QKV_ERR_POSITION_RANGE if any token
- * launched since the last status call had pos outside [0, n_ctx) or slot
- * outside [0, n_slots), QKV_ERR_HIP on a runtime failure, else 0.
+ * Blocking: wait for every stream the handle has launched on since the last
+ * status call (up to 8 distinct streams; past that, for the whole device),
+ * then read and clear the device error word.  Returns QKV_ERR_POSITION_RANGE
+ * if any token launched since the last status call had pos outside
+ * [0, n_ctx) or slot outside [0, n_slots), QKV_ERR_HIP on a runtime failure,
+ * else 0.  Replays of a captured HIP graph are not launches the handle sees:
+ * synchronize the replay stream before calling status to cover them.
  */
 int qkv_epilogue_status(qkv_epilogue_t *h);
 
@@ -319,7 +335,8 @@ int qkv_epilogue_status(qkv_epilogue_t *h);
  * stays valid until the next call on the handle. */
 const char *qkv_epilogue_last_error(const qkv_epilogue_t *h);
 
-/* Free the handle and its error word.  NULL is a no-op. */
+/* Free the handle, its error word and its projection workspace (no launch
+ * of the handle may still be running).  NULL is a no-op. */
 void qkv_epilogue_destroy(qkv_epilogue_t *h);
 
 /* ---- host-only helpers (no device needed) ------------------------------- */

@@ -212,6 +212,6 @@ extern "C" int qkv_epilogue_run_unfused(qkv_epilogue_t *h, const qkv_epilogue_ar
                   : launch_chain_w<1>(a, pl, inv, h->d_err, st);
     if (e != hipSuccess)
         return fail(h, QKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    h->last_stream = st;
+    note_stream(h, st);
     return QKV_OK;
 }

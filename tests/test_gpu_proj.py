@@ -743,6 +743,33 @@ def test_proj_e4m3_layouts(handle, weights, style, nt):
     c.check(f"e4m3_{weights}_{style}_{nt}")
 
 
+@pytest.mark.parametrize("geom,weights,style,hidden", [
+    ("7b", "three", B.QKV_ROPE_NEOX, 4096),          # two chunks per lane
+    ("7b", "three", B.QKV_ROPE_INTERLEAVED, 4160),   # three, last step partly masked
+    ("14b", "concat", B.QKV_ROPE_INTERLEAVED, 8192),  # four
+])
+def test_proj_e4m3_two_pairs_per_wave_layouts(handle, geom, weights, style, hidden):
+    """4 tokens at hidden >= 4096 run the GEMV with two NeoX/interleaved pairs
+    per wave: the three-matrix layout, interleaved pairing and each unroll
+    depth of that instance."""
+    w = wl.DECODE_7B if geom == "7b" else wl.DECODE_14B
+    c = ProjCase(w, hidden=hidden, nt=4, wfmt="e4m3", weights=weights, style=style)
+    label = f"e4m3_p2_{geom}_{weights}_{style}_{hidden}"
+    assert _run(handle, c, label) == B.QKV_OK
+    c.check(label)
+
+
+@pytest.mark.parametrize("hidden", [4096, 4160])
+def test_proj_e4m3_two_pairs_per_wave_hd64(handle, hidden):
+    """head_dim 64 at 4 tokens and hidden >= 4096 (two pairs per wave), slots,
+    no bias; 4160 leaves the last step partly masked."""
+    w = wl.Workload("proj_e4m3_hd64_p2", 14, 2, 64, nt=4, n_ctx=64, n_slots=8, layers=1, seed=35,
+                    cache_dtypes=(wl.CACHE_F16,))
+    c = ProjCase(w, hidden=hidden, wfmt="e4m3", bias=False)
+    assert _run(handle, c, f"e4m3_p2_hd64_{hidden}") == B.QKV_OK
+    c.check(f"e4m3_p2_hd64_{hidden}")
+
+
 @pytest.mark.parametrize("hidden", [64, 896, 1088])
 def test_proj_e4m3_hd64_ragged_hidden(handle, hidden):
     """hd 64 with hidden sizes that leave the last step partly masked (64:

@@ -25,9 +25,8 @@
 //    pick few, wide column blocks and several tokens per block; a one-token
 //    decode spreads the token over many small column blocks.
 //  * cos/sin are computed once per (token, pair index) per workgroup, in double
-//    precision (qkv_sincos.h), rounded to f32 and kept in LDS; the inverse
-//    frequencies ride in the kernel arguments (computed on the host once per
-//    theta/head_dim).
+//    precision, rounded to f32 and kept in LDS; the inverse frequencies ride in
+//    the kernel arguments (computed on the host once per theta/head_dim).
 //  * The rotation is evaluated in double: the products of two f32 values are
 //    exact in double, so x0*c - x1*s is rounded once there and once to f32
 //    whether or not the compiler fuses it into an FMA.
@@ -252,10 +251,10 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
     // ---- cos/sin per (token, pair index) and cache row per token -----------
     if (tid < ent) {
         const float a = (float)e_pos * e_inv;   // f32 angle
-        float cv, sv;
-        rope_cos_sin(a, cv, sv);
-        s_cos[tid] = cv;
-        s_sin[tid] = sv;
+        double sd, cd;
+        sincos((double)a, &sd, &cd);
+        s_cos[tid] = (float)cd;
+        s_sin[tid] = (float)sd;
         if (e_i == 0)
             s_row[e_tk] = cache_row(p, e_pos, e_slot);
     }
@@ -264,10 +263,10 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
         const int i = e - tk * p.half;
         const int32_t ps = p.pos[t0 + tk];
         const float a = (float)ps * inv.v[i];
-        float cv, sv;
-        rope_cos_sin(a, cv, sv);
-        s_cos[e] = cv;
-        s_sin[e] = sv;
+        double sd, cd;
+        sincos((double)a, &sd, &cd);
+        s_cos[e] = (float)cd;
+        s_sin[e] = (float)sd;
         if (i == 0)
             s_row[tk] = cache_row(p, ps, (p.slot ? p.slot : p.pos)[t0 + tk]);
     }

@@ -14,7 +14,6 @@
 
 #include "qkv_epilogue.h"
 #include "qkv_plan.h"
-#include "qkv_sincos.h"
 
 namespace qkv_detail {
 
@@ -99,32 +98,6 @@ __device__ __forceinline__ void st_cache(void *cache, int64_t off, const FVec<W>
         }
     } else {
         st_data<W, STREAM>(static_cast<float *>(cache) + off, v);
-    }
-}
-
-// The library's double sincos for angles beyond 2^20, out of line: its long
-// general-purpose body (large-argument reduction included) stays out of the
-// kernels' instruction stream, which a short launch fetches cold on every CU.
-// Returns (cos, sin) in registers.
-static __device__ __noinline__ float2 rope_cos_sin_far(float a)
-{
-    double sd, cd;
-    sincos((double)a, &sd, &cd);
-    return make_float2((float)cd, (float)sd);
-}
-
-// cos and sin of a rope angle, each the f32 rounding of a double-precision
-// value: the short evaluation of qkv_sincos.h for |a| < 2^20, the library's
-// double sincos beyond it (the branch diverges only in waves holding such
-// angles).
-__device__ __forceinline__ void rope_cos_sin(float a, float &c, float &s)
-{
-    if (sincos_rope_in_range(a))
-        sincos_rope(a, s, c);
-    else {
-        const float2 cs = rope_cos_sin_far(a);
-        c = cs.x;
-        s = cs.y;
     }
 }
 

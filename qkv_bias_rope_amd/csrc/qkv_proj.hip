@@ -138,10 +138,10 @@ __global__ __launch_bounds__(256) void rope_table_kernel(ProjParams p, InvTable 
         return;
     const int t = (int)(idx / half), i = (int)(idx - (int64_t)t * half);
     const float ang = (float)p.pos[t] * inv.v[i];
-    float cv, sv;
-    rope_cos_sin(ang, cv, sv);
-    tab[(int64_t)t * 2 * half + i] = cv;
-    tab[(int64_t)t * 2 * half + half + i] = sv;
+    double sd, cd;
+    sincos((double)ang, &sd, &cd);
+    tab[(int64_t)t * 2 * half + i] = (float)cd;
+    tab[(int64_t)t * 2 * half + half + i] = (float)sd;
     if (i == 0)
         rows[t] = cache_row(p, t);
 }
@@ -691,7 +691,10 @@ __global__ __launch_bounds__(256) void proj_split_epilogue_kernel(ProjParams p, 
     float cv = 1.0f, sv = 0.0f;
     if (h0 < qheads + kheads) {
         const float ang = (float)p.pos[t] * inv.v[i];
-        rope_cos_sin(ang, cv, sv);
+        double sd, cd;
+        sincos((double)ang, &sd, &cd);
+        cv = (float)cd;
+        sv = (float)sd;
     }
     const int64_t row = h1 > qheads ? cache_row(p, t) : -1;
     const int64_t plane = (int64_t)p.M * p.N;
@@ -929,9 +932,9 @@ __global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p
         }
         if (sec < 2) {
             const float ang = (float)p.pos[t] * inv.v[i];
-            float cv, sv;
-            rope_cos_sin(ang, cv, sv);
-            rot(y0, y1, cv, sv);
+            double sd, cd;
+            sincos((double)ang, &sd, &cd);
+            rot(y0, y1, (float)cd, (float)sd);
         }
         float *out = p.out[sec];
         out[(int64_t)t * p.ld[sec] + s0] = y0;

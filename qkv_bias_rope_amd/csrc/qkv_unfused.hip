@@ -49,10 +49,10 @@ __global__ __launch_bounds__(kBlockU) void add_bias_kernel(float *x, int64_t ld,
 // rotation in double.
 __device__ __forceinline__ void turn(float &x0, float &x1, float a)
 {
-    float cv, sv;
-    rope_cos_sin(a, cv, sv);
-    const double c = (double)cv;
-    const double s = (double)sv;
+    double sd, cd;
+    sincos((double)a, &sd, &cd);
+    const double c = (double)(float)cd;
+    const double s = (double)(float)sd;
     const double u = (double)x0, w = (double)x1;
     x0 = (float)(u * c - w * s);
     x1 = (float)(u * s + w * c);

@@ -745,6 +745,28 @@ def proj_sweep(args):
     B.qkv_epilogue_destroy(h)
 
 
+def decode_all(h, args, stream):
+    """The one-token decode workloads (tiny, 7B, 14B) beside the empty kernel
+    of each one's launch shape."""
+    import torch
+    from qkv_bias_rope_amd import workloads as wl
+    out = {}
+    fl = floors(stream, [(3, 64), (9, 64), (14, 64)])
+    out["empty_kernel_floor"] = fl
+    log(f"[bench] empty-kernel floor: {fl}")
+    shape = {wl.TINY_DECODE.name: "grid3x64", wl.DECODE_7B.name: "grid9x64",
+             wl.DECODE_14B.name: "grid14x64"}
+    for wd in (wl.TINY_DECODE, wl.DECODE_7B, wl.DECODE_14B):
+        log(f"[bench] {wd.name}")
+        r = bench_decode(h, wd, max(10, args.steps // 10), max(2, args.warmup // 10), stream)
+        r["empty_kernel_same_launch"] = fl[shape[wd.name]]
+        out[wd.name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
+        log(f"[bench]   {r['us_per_layer_stream']:.2f} us/layer (stream), "
+            f"{r.get('us_per_layer_graph', float('nan')):.2f} us/layer (graph)")
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -756,6 +778,9 @@ def main():
                     help="run only a 1 GiB device copy (counter calibration)")
     ap.add_argument("--batched-only", action="store_true",
                     help="run only the 256-sequence decode (f16 and f32 caches), one JSON line")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="run only the one-token decode workloads and the empty-kernel floor, "
+                         "one JSON line")
     ap.add_argument("--proj-sweep", action="store_true",
                     help="run only the projection-fed epilogue at 1..4096 tokens (14B width, "
                          "hidden 5120), one JSON line per token count")
@@ -782,6 +807,15 @@ def main():
         return
     if args.proj_sweep:
         proj_sweep(args)
+        return
+    if args.decode_only:
+        rc, h = B.qkv_epilogue_create(0, 4096)
+        assert rc == 0, rc
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            out = decode_all(h, args, stream)
+        B.qkv_epilogue_destroy(h)
+        print(json.dumps(out), flush=True)
         return
     if args.batched_only:
         rc, h = B.qkv_epilogue_create(0, 4096)
@@ -849,19 +883,7 @@ def run_all(args, h, stream):
             log(f"[bench]   {r['us_per_launch']:.3f} us/launch, {r['gbs']:.1f} GB/s; bare pass "
                 f"{r['bare_pass_us']:.3f} us ({r['frac_of_achievable']:.3f} of achievable); empty "
                 f"kernel {r['empty_kernel_same_launch_us']:.3f} us")
-        fl = floors(stream, [(3, 64), (9, 64), (14, 64)])
-        extra["empty_kernel_floor"] = fl
-        log(f"[bench] empty-kernel floor: {fl}")
-        shape = {wl.TINY_DECODE.name: "grid3x64", wl.DECODE_7B.name: "grid9x64",
-                 wl.DECODE_14B.name: "grid14x64"}
-        for wd in (wl.TINY_DECODE, wl.DECODE_7B, wl.DECODE_14B):
-            log(f"[bench] {wd.name}")
-            r = bench_decode(h, wd, max(10, args.steps // 10), max(2, args.warmup // 10), stream)
-            r["empty_kernel_same_launch"] = fl[shape[wd.name]]
-            extra[wd.name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
-            log(f"[bench]   {r['us_per_layer_stream']:.2f} us/layer (stream), "
-                f"{r.get('us_per_layer_graph', float('nan')):.2f} us/layer (graph)")
-            torch.cuda.empty_cache()
+        extra.update(decode_all(h, args, stream))
         # same-binary A/B of the fusion: the unfused seven-launch chain
         wd = wl.DECODE_14B
         log(f"[bench] {wd.name} unfused chain")

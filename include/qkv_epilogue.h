@@ -321,13 +321,12 @@ int qkv_epilogue_run_proj_noalloc(qkv_epilogue_t *h, const qkv_proj_args_t *a);
 int qkv_epilogue_run_unfused(qkv_epilogue_t *h, const qkv_epilogue_args_t *a);
 
 /*
- * Blocking: wait for every stream the handle has launched on since the last
- * status call (up to 8 distinct streams; past that, for the whole device),
- * then read and clear the device error word.  Returns QKV_ERR_POSITION_RANGE
- * if any token launched since the last status call had pos outside
- * [0, n_ctx) or slot outside [0, n_slots), QKV_ERR_HIP on a runtime failure,
- * else 0.  Replays of a captured HIP graph are not launches the handle sees:
- * synchronize the replay stream before calling status to cover them.
+ * Blocking: synchronize the handle's device (every stream, so launches on any
+ * stream and replays of captured graphs are all finished), then read and
+ * clear the handle's device error word.  Returns QKV_ERR_POSITION_RANGE if
+ * any token launched with this handle since the last status call had pos
+ * outside [0, n_ctx) or slot outside [0, n_slots), QKV_ERR_HIP on a runtime
+ * failure, else 0.  It also waits for unrelated work queued on the device.
  */
 int qkv_epilogue_status(qkv_epilogue_t *h);
 

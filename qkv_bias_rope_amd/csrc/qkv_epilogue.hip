@@ -541,7 +541,6 @@ int launch_fused(qkv_epilogue_t *h, const qkv_epilogue_args_t *a, unsigned flags
     e = pl.W == 4 ? launch_w<4>(kp, inv, pl, f16, st) : launch_w<1>(kp, inv, pl, f16, st);
     if (e != hipSuccess)
         return fail(h, QKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    note_stream(h, st);
     return QKV_OK;
 }
 
@@ -567,8 +566,6 @@ int qkv_epilogue_create(qkv_epilogue_t **out, const qkv_epilogue_config_t *cfg)
     h->device = cfg->device;
     h->n_ctx = cfg->n_ctx;
     h->stream = static_cast<hipStream_t>(cfg->stream);
-    h->n_used = 0;
-    h->used_overflow = false;
     h->inv_theta = 0.0f;
     h->inv_hd = 0;
     h->inv_scale = 0.0f;
@@ -637,16 +634,15 @@ int qkv_epilogue_status(qkv_epilogue_t *h)
     DeviceGuard g;
     hipError_t e = g.set(h->device);
     unsigned int word = 0;
-    // every launch since the last call has finished before the word is read
-    if (e == hipSuccess && h->used_overflow)
+    // Every launch made before this call, on any stream and from any graph
+    // replay, has finished before the word is read.  The device is waited
+    // for, not a list of the handle's streams: a caller may have destroyed a
+    // stream it launched on since, and graph replays are launches the handle
+    // never sees.
+    if (e == hipSuccess)
         e = hipDeviceSynchronize();
-    for (int i = 0; e == hipSuccess && !h->used_overflow && i < h->n_used; ++i)
-        e = hipStreamSynchronize(h->used[i]);
-    if (e == hipSuccess) {
-        h->n_used = 0;
-        h->used_overflow = false;
+    if (e == hipSuccess)
         e = hipMemcpy(&word, h->d_err, sizeof word, hipMemcpyDeviceToHost);
-    }
     // cleared before any later launch can run (the null stream is waited for)
     if (e == hipSuccess && word)
         e = hipMemsetAsync(h->d_err, 0, sizeof word, nullptr);

@@ -189,12 +189,6 @@ struct qkv_epilogue {
     int device;
     int64_t n_ctx;
     hipStream_t stream;
-    // the distinct streams launched on since the last status call (status
-    // waits for all of them; past kMaxTracked it waits for the device)
-    static constexpr int kMaxTracked = 8;
-    hipStream_t used[kMaxTracked];
-    int n_used;
-    bool used_overflow;
     unsigned int *d_err;
     float inv_theta;
     int inv_hd;
@@ -210,18 +204,6 @@ struct qkv_epilogue {
 namespace qkv_detail {
 
 int fail(qkv_epilogue *h, int code, const char *fmt, ...);
-
-// Note that a launch went to stream st (status waits for it).
-inline void note_stream(qkv_epilogue *h, hipStream_t st)
-{
-    for (int i = 0; i < h->n_used; ++i)
-        if (h->used[i] == st)
-            return;
-    if (h->n_used < qkv_epilogue::kMaxTracked)
-        h->used[h->n_used++] = st;
-    else
-        h->used_overflow = true;
-}
 
 // Look up, once per device (that device current), the device address of the
 // allocation-free projection's static workspace.  Called by create.

@@ -1424,7 +1424,6 @@ int run_proj_impl(qkv_epilogue_t *h, const qkv_proj_args_t *pa, bool static_ws)
         e = f16 ? launch_proj<true, 64>(pp, inv, st, plan) : launch_proj<false, 64>(pp, inv, st, plan);
     if (e != hipSuccess)
         return fail(h, QKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    note_stream(h, st);
     return QKV_OK;
 }
 

@@ -212,6 +212,5 @@ extern "C" int qkv_epilogue_run_unfused(qkv_epilogue_t *h, const qkv_epilogue_ar
                   : launch_chain_w<1>(a, pl, inv, h->d_err, st);
     if (e != hipSuccess)
         return fail(h, QKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    note_stream(h, st);
     return QKV_OK;
 }

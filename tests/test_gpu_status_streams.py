@@ -2,10 +2,10 @@
 call, not only the stream of the last launch.
 
 A token with an out-of-range position is launched on one stream behind a few
-large matrix products (so that it finishes late), then a valid launch goes to
-another stream; status must still report the range error, and a second status
-call must find the word cleared.  The same with nine streams, past the eight
-the handle tracks one by one (status then waits for the device).
+large matrix products (so that it finishes late), then valid launches go to
+other streams; status must still report the range error, and a second status
+call must find the word cleared.  Also after the streams of those launches
+are destroyed, and for a range error that only a graph replay produces.
 """
 import pytest
 import torch
@@ -62,3 +62,45 @@ def test_status_waits_for_every_stream(handle, n_streams):
     for c in good:
         c.download()
         c.check(label="status streams")
+
+
+def test_status_after_the_streams_are_gone(handle):
+    """Launches on streams the caller has destroyed (after synchronizing them)
+    before calling status: status neither fails nor misses the error."""
+    say("[case] status after the launch streams were destroyed")
+    w = wl.TINY_DECODE
+    bad = Case(w, pos=[w.n_ctx]).run_oracle().upload()
+    good = Case(w, pos=[2]).run_oracle().upload()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    _launch(handle, bad, s1)
+    _launch(handle, good, s2)
+    s1.synchronize()
+    s2.synchronize()
+    del s1, s2
+    import gc
+    gc.collect()
+    assert B.qkv_epilogue_status(handle) == B.QKV_ERR_POSITION_RANGE, B.qkv_epilogue_last_error(handle)
+    assert B.qkv_epilogue_status(handle) == B.QKV_OK
+
+
+def test_status_covers_graph_replays(handle):
+    """A range error produced only by a replay of a captured graph (the
+    captured launch itself is the library's only sight of it)."""
+    say("[case] status after a graph replay")
+    w = wl.TINY_DECODE
+    c = Case(w, pos=[3]).run_oracle().upload()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        assert c.run_gpu(handle, stream=torch.cuda.current_stream()) == 0
+    assert B.qkv_epilogue_status(handle) == B.QKV_OK
+    # the captured launch reads pos from device memory: an out-of-range value
+    # written there now is seen only by the replays
+    c.g_pos.fill_(w.n_ctx + 1)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        g.replay()
+    assert B.qkv_epilogue_status(handle) == B.QKV_ERR_POSITION_RANGE
+    assert B.qkv_epilogue_status(handle) == B.QKV_OK

@@ -675,6 +675,43 @@ def ceilings_prefill(steps, stream, nbytes=251703296, sets=8):
     return out
 
 
+def ceiling_read(nbytes, steps, stream, min_set_bytes=1.5e9):
+    """What a bare read of `nbytes` (a decode step's weight matrix) takes on
+    this device: the probe library's read-only pass over rotating buffers (as
+    many as the projection's own timing rotates, so every launch comes from
+    HBM), swept over load policy and vectors per thread; event-timed over a
+    stream loop."""
+    import torch
+    from qkv_bias_rope_amd import probe as P
+    n = nbytes // 4 // 4 * 4
+    sets = max(2, int(-(-min_set_bytes // (n * 4))))
+    bufs = [torch.ones(n, dtype=torch.float32, device="cuda:0") for _ in range(sets)]
+    out = torch.empty(P.read_out_numel(n // 4, 256, 1), dtype=torch.float32, device="cuda:0")
+    k = max(50, min(steps, 200))
+    res = []
+    for pol in (0, 1):
+        for vpt in (1, 2, 4, 8):
+            fn = lambda i, pol=pol, vpt=vpt: P.read(bufs[i % sets], out, 256, vpt, pol, stream)
+            with torch.cuda.stream(stream):
+                for i in range(2 * sets):
+                    assert fn(i) == 0
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for i in range(k):
+                    fn(i)
+                e1.record(stream)
+                e1.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / k
+            res.append(dict(policy=pol, vpt=vpt, us=round(us, 3), gbs=round(n * 4 / us / 1e3, 1)))
+    b = _best(res)
+    del bufs, out
+    torch.cuda.empty_cache()
+    return dict(bytes=n * 4, rotating_buffers=sets, block=256, best_us=b["us"], best_gbs=b["gbs"],
+                best_policy=b["policy"], best_vpt=b["vpt"], sweep=res)
+
+
 def floors(stream, shapes):
     """Per-launch floor of an empty kernel at the given (grid, block) launch
     shapes: back-to-back in a HIP-graph replay (GPU side) and in a stream
@@ -949,6 +986,13 @@ def run_all(args, h, stream):
             input_sets=r["sets"])
         log(f"[bench]   {r['us_per_launch']:.1f} us/layer, {r['gbs']:.1f} GB/s "
             f"(library bf16 matmul call {r['library_bf16_matmul_call_us']:.1f} us)")
+        # the GEMV streams the weights once: a bare read of the same bytes
+        cr = ceiling_read((wd.nqt + 2 * wd.nkt) * hid * 2, args.steps, stream)
+        extra["ceiling_decode_14b_proj_weights_bf16"] = cr
+        extra[wd.name + "_proj"]["bare_read_of_weights_us"] = cr["best_us"]
+        extra[wd.name + "_proj"]["frac_of_bare_read"] = round(cr["best_us"] / r["us_per_launch"], 4)
+        log(f"[bench]   bare read of the {cr['bytes']} weight bytes: {cr['best_us']} us "
+            f"({cr['best_gbs']} GB/s)")
         log(f"[bench] {wd.name} projection-fed epilogue, {wd.layers}-layer decode step")
         r = bench_proj_decode(h, wd, hid, max(5, args.steps // 20), 2, stream)
         extra[wd.name + "_proj_step"] = {k: (round(v, 3) if isinstance(v, float) else v)
@@ -964,6 +1008,11 @@ def run_all(args, h, stream):
             frac_of_peak=round(r["gbs"] / PEAK_HBM_GBS, 4), bytes_per_layer=r["bytes"],
             hidden=hid, input_sets=r["sets"])
         log(f"[bench]   {r['us_per_launch']:.1f} us/layer, {r['gbs']:.1f} GB/s")
+        cr = ceiling_read((wd.nqt + 2 * wd.nkt) * hid, args.steps, stream)
+        extra["ceiling_decode_14b_proj_weights_e4m3"] = cr
+        extra[wd.name + "_proj_e4m3"]["bare_read_of_weights_us"] = cr["best_us"]
+        extra[wd.name + "_proj_e4m3"]["frac_of_bare_read"] = round(cr["best_us"] / r["us_per_launch"], 4)
+        log(f"[bench]   bare read of the {cr['bytes']} weight bytes: {cr['best_us']} us")
         r = bench_proj_decode(h, wd, hid, max(5, args.steps // 20), 2, stream, wfmt="e4m3")
         extra[wd.name + "_proj_e4m3_step"] = {k: (round(v, 3) if isinstance(v, float) else v)
                                               for k, v in r.items()}

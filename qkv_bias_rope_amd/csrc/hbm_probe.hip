@@ -8,6 +8,10 @@
 //            loads before its stores.
 //  * add:    buf += 1 in place over 16-byte vectors (the read/write mix of an
 //            in-place elementwise pass).
+//  * read:   a pass that only reads: every thread sums its 16-byte vectors
+//            and each wave writes one float of the sum (4 bytes per 1 KB
+//            times the vectors per thread), the traffic of a kernel that
+//            streams a weight matrix once.
 //  * rows:   the byte pattern of a batched decode step without any of its
 //            arithmetic beyond one add: every element of a [nt][width] f32
 //            matrix gets b[col] added in place, and the columns
@@ -120,6 +124,29 @@ __global__ __launch_bounds__(1024) void add_kernel(f32x4 *__restrict__ buf, int6
     }
 }
 
+// Workgroup g reads vectors [g*blockDim*VPT, (g+1)*blockDim*VPT) as copy does
+// and wave w of it writes the sum of its lanes' vectors to out[g*waves + w].
+template <int VPT, int POL>
+__global__ __launch_bounds__(1024) void read_kernel(const f32x4 *__restrict__ src, int64_t n,
+                                                    float *__restrict__ out)
+{
+    const int64_t g0 = (int64_t)blockIdx.x * blockDim.x * VPT;
+    f32x4 r[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+        r[j] = ld<POL>(src + min(g0 + (int64_t)j * blockDim.x + threadIdx.x, n - 1));
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const bool in = g0 + (int64_t)j * blockDim.x + threadIdx.x < n;
+        acc += in ? (r[j].x + r[j].y) + (r[j].z + r[j].w) : 0.0f;
+    }
+    for (int m = 32; m >= 1; m >>= 1)
+        acc += __shfl_xor(acc, m, 64);
+    if ((threadIdx.x & 63) == 0)
+        out[(int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64] = acc;
+}
+
 // One thread per 16-byte vector of a row, TPB rows per workgroup row of the
 // grid (blockIdx.y); blockIdx.x walks the column vectors.
 template <int TPB, bool F16, int POL>
@@ -186,6 +213,25 @@ template <int VPT, int POL>
 void launch_add(long long g, int block, hipStream_t st, f32x4 *p, long long n16)
 {
     hipLaunchKernelGGL((add_kernel<VPT, POL>), dim3((unsigned)g), dim3(block), 0, st, p, (int64_t)n16);
+}
+
+template <int VPT, int POL>
+void launch_read(long long g, int block, hipStream_t st, const f32x4 *s, long long n16, float *out)
+{
+    hipLaunchKernelGGL((read_kernel<VPT, POL>), dim3((unsigned)g), dim3(block), 0, st, s, (int64_t)n16,
+                       out);
+}
+
+template <int POL>
+bool dispatch_read(int vpt, long long g, int block, hipStream_t st, const f32x4 *s, long long n, float *out)
+{
+    switch (vpt) {
+    case 1: launch_read<1, POL>(g, block, st, s, n, out); return true;
+    case 2: launch_read<2, POL>(g, block, st, s, n, out); return true;
+    case 4: launch_read<4, POL>(g, block, st, s, n, out); return true;
+    case 8: launch_read<8, POL>(g, block, st, s, n, out); return true;
+    default: return false;
+    }
 }
 
 template <int POL>
@@ -271,6 +317,24 @@ int qkv_probe_copy(void *dst, const void *src, long long n16, int block, int vpt
     const bool ok = policy == 0   ? dispatch_copy<0>(vpt, g, block, st, d, s, n16)
                     : policy == 1 ? dispatch_copy<1>(vpt, g, block, st, d, s, n16)
                                   : dispatch_copy<2>(vpt, g, block, st, d, s, n16);
+    return ok ? rc_of(hipGetLastError()) : -1;
+}
+
+// src: n16 16-byte vectors, 16-byte aligned; out: at least
+// qkv_probe_grid(n16, block, vpt) * block / 64 floats, the per-wave sums;
+// policy 0 plain or 1 non-temporal loads.
+int qkv_probe_read(const void *src, long long n16, float *out, int block, int vpt, int policy,
+                   hipStream_t st)
+{
+    if (!src || !out || n16 < 1 || bad_block(block) || ((uintptr_t)src & 15u) || policy < 0 ||
+        policy > 1)
+        return -1;
+    const long long g = qkv_probe_grid(n16, block, vpt);
+    if (g > 0x7fffffffLL)
+        return -1;
+    auto *p = static_cast<const f32x4 *>(src);
+    const bool ok = policy == 0 ? dispatch_read<0>(vpt, g, block, st, p, n16, out)
+                                : dispatch_read<1>(vpt, g, block, st, p, n16, out);
     return ok ? rc_of(hipGetLastError()) : -1;
 }
 

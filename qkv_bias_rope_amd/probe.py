@@ -1,7 +1,8 @@
 """ctypes binding of libqkv_probe.so: the benchmark's reference kernels.
 
 These set the floor (an empty kernel) and the ceilings (a streaming copy, an
-in-place add, and a row-scatter pass that moves the batched decode's bytes)
+in-place add, a read-only pass, and a row-scatter pass that moves the batched
+decode's bytes)
 that the epilogue's timings are read against on the same device.  They are
 measurement tools, not part of the epilogue; only the benchmark and its tests
 load them.  Argument marshalling only; every entry point returns 0 or a
@@ -38,6 +39,8 @@ def _load():
     lib.qkv_probe_copy.restype = _I
     lib.qkv_probe_add.argtypes = [_P, _LL, _I, _I, _I, _P]
     lib.qkv_probe_add.restype = _I
+    lib.qkv_probe_read.argtypes = [_P, _LL, _P, _I, _I, _I, _P]
+    lib.qkv_probe_read.restype = _I
     lib.qkv_probe_rows.argtypes = [_P, _P, _LL, _LL, _LL, _LL, _P, _P, _LL, _P, _P, _I, _I, _I, _I,
                                    _P]
     lib.qkv_probe_rows.restype = _I
@@ -45,7 +48,8 @@ def _load():
 
 
 lib = _load()
-EXPORTS = ("qkv_probe_grid", "qkv_probe_empty", "qkv_probe_copy", "qkv_probe_add", "qkv_probe_rows")
+EXPORTS = ("qkv_probe_grid", "qkv_probe_empty", "qkv_probe_copy", "qkv_probe_add", "qkv_probe_read",
+           "qkv_probe_rows")
 
 
 def _s(stream):
@@ -76,6 +80,22 @@ def add(buf, block=256, vpt=1, policy=2, stream=None) -> int:
     """buf += 1 in place for a float32 device tensor (numel a multiple of 4)."""
     assert buf.numel() % 4 == 0
     return lib.qkv_probe_add(buf.data_ptr(), buf.numel() // 4, block, vpt, policy, _s(stream))
+
+
+def read_out_numel(n16: int, block: int, vpt: int) -> int:
+    """Floats the per-wave sums of a read launch take."""
+    return grid(n16, block, vpt) * block // 64
+
+
+def read(src, out, block=256, vpt=1, policy=1, stream=None) -> int:
+    """Read every element of a float32 device tensor (numel a multiple of 4);
+    out (float32, at least read_out_numel(src.numel() // 4, block, vpt)
+    elements) receives the per-wave sums.  Policy 0 plain or 1 non-temporal
+    loads."""
+    assert src.numel() % 4 == 0 and src.dtype == torch.float32 and out.dtype == torch.float32
+    n16 = src.numel() // 4
+    assert out.numel() >= read_out_numel(n16, block, vpt)
+    return lib.qkv_probe_read(src.data_ptr(), n16, out.data_ptr(), block, vpt, policy, _s(stream))
 
 
 def rows(x, b, kv_col, nkt, pos, slot, n_ctx, kc, vc, block=256, tpb=1, policy=2,

@@ -67,3 +67,37 @@ def test_rows(cache, policy, tpb):
     untouched = torch.ones(n_slots * n_ctx, dtype=torch.bool, device=DEV)
     untouched[rows] = False
     assert bool((kc[untouched] == 9.0).all()) and bool((vc[untouched] == 9.0).all())
+
+
+@pytest.mark.parametrize("policy", (0, 1))
+@pytest.mark.parametrize("vpt", (1, 2, 4, 8))
+@pytest.mark.parametrize("block", (128, 256))
+def test_read(policy, vpt, block):
+    """Every wave's sum of the vectors it reads, exact with small integers
+    (any summation order gives the same f32 value)."""
+    rng = np.random.default_rng(vpt * 10 + policy)
+    n16 = 3 * block * vpt + 37          # a ragged last workgroup
+    src_np = rng.integers(-3, 4, 4 * n16).astype(np.float32)
+    src = torch.from_numpy(src_np).to(DEV)
+    n_out = P.read_out_numel(n16, block, vpt)
+    out = torch.full((n_out,), -1.0, device=DEV)
+    assert P.read(src, out, block=block, vpt=vpt, policy=policy,
+                  stream=torch.cuda.current_stream()) == 0
+    torch.cuda.synchronize()
+    vec = src_np.reshape(n16, 4).sum(axis=1).astype(np.int64)
+    groups = P.grid(n16, block, vpt)
+    want = np.zeros(n_out, np.int64)
+    for g in range(groups):
+        for t in range(block):
+            for j in range(vpt):
+                k = g * block * vpt + j * block + t
+                if k < n16:
+                    want[g * (block // 64) + t // 64] += vec[k]
+    assert np.array_equal(out.cpu().numpy().astype(np.int64), want)
+
+
+def test_read_rejects_bad_arguments():
+    x = torch.zeros(256, device=DEV)
+    out = torch.zeros(64, device=DEV)
+    assert P.read(x, out, policy=2) == -1        # loads have two policies only
+    assert P.read(x, out, vpt=3) == -1

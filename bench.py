@@ -675,6 +675,66 @@ def ceilings_prefill(steps, stream, nbytes=251703296, sets=8):
     return out
 
 
+def ceiling_prefill_rows(h, steps, stream, R=8):
+    """The prefill's own byte pattern without its arithmetic: the probe
+    library's row pass over concat [4096][nqt+2nkt] copies of the rows (read
+    and written back in place, the bias read once, the k/v columns stored to
+    the f16 cache rows at the tokens' positions), rotating R buffers, swept
+    over tokens per workgroup and store policy; beside it the epilogue itself
+    on the same concat rows.  Event-timed stream loops, as the headline."""
+    import torch
+    from qkv_bias_rope_amd import binding as B
+    from qkv_bias_rope_amd import probe as P
+    from qkv_bias_rope_amd import workloads as wl
+    w = wl.PREFILL_14B
+    nbytes = algo_bytes(w, w.nt, 2)
+    sets = Sets(w, R, wl.CACHE_F16, share_cache=True)
+    xs = [torch.cat([st["q"], st["k"], st["v"]], dim=1).contiguous() for st in sets.sets]
+    for st in sets.sets:
+        st["q"] = st["k"] = st["v"] = None
+    torch.cuda.empty_cache()
+    bcat = torch.cat([sets.bq, sets.bk, sets.bv]).contiguous()
+    kc, vc = sets.sets[0]["kc"], sets.sets[0]["vc"]
+    pos = sets.sets[0]["pos"]
+    k = max(20, min(steps, 100))
+
+    def loop(fn):
+        with torch.cuda.stream(stream):
+            for i in range(2 * R):
+                assert fn(i) == 0
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(k):
+                fn(i)
+            e1.record(stream)
+            e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / k
+
+    res = []
+    for tpb in (1, 2, 4):
+        for pol in (1, 2):
+            us = loop(lambda i, tpb=tpb, pol=pol: P.rows(xs[i % R], bcat, w.nqt, w.nkt, pos, None, w.n_ctx,
+                                                         kc, vc, block=256, tpb=tpb, policy=pol,
+                                                         stream=stream))
+            res.append(dict(tokens_per_workgroup=tpb, policy=pol, us=round(us, 3),
+                            gbs=round(nbytes / us / 1e3, 1)))
+    cargs = [B.make_args(x[:, :w.nqt], x[:, w.nqt:w.nqt + w.nkt], x[:, w.nqt + w.nkt:], sets.bq, sets.bk,
+                         sets.bv, pos, kc, vc, n_head=w.n_head, n_kv_head=w.n_kv_head,
+                         head_dim=w.head_dim, theta=w.theta, cache_dtype=wl.CACHE_F16, n_ctx=w.n_ctx,
+                         stream=stream, use_stream=True) for x in xs]
+    cat_us = loop(lambda i: B.qkv_epilogue_run_ex(h, cargs[i % R]))
+    assert B.qkv_epilogue_status(h) == 0, B.qkv_epilogue_last_error(h)
+    b = _best(res)
+    del sets, xs, cargs
+    torch.cuda.empty_cache()
+    return dict(bytes=nbytes, rotating_buffers=R, block=256, best_us=b["us"], best_gbs=b["gbs"],
+                best_tokens_per_workgroup=b["tokens_per_workgroup"], best_policy=b["policy"],
+                epilogue_concat_layout_us=round(cat_us, 3),
+                epilogue_concat_layout_frac_of_row_pass=round(b["us"] / cat_us, 4), sweep=res)
+
+
 def ceiling_read(nbytes, steps, stream, min_set_bytes=1.5e9):
     """What a bare read of `nbytes` (a decode step's weight matrix) takes on
     this device: the probe library's read-only pass over rotating buffers (as
@@ -907,6 +967,11 @@ def run_all(args, h, stream):
         ceil = ceilings_prefill(args.steps, stream)
         extra["ceiling_prefill_14b_4096"] = ceil
         extra[w.name + "_frac_of_achievable"] = round(main_res["gbs"] / ceil["achievable_gbs"], 4)
+        rp = ceiling_prefill_rows(h, args.steps, stream)
+        ceil["row_pass"] = rp
+        extra[w.name + "_frac_of_row_pass"] = round(rp["best_us"] / (main_res["ms"] * 1e3), 4)
+        log(f"[bench]   row pass of the same byte pattern {rp['best_us']} us ({rp['best_gbs']} GB/s); "
+            f"epilogue on concat rows {rp['epilogue_concat_layout_us']} us")
         log(f"[bench]   achievable {ceil['achievable_gbs']} GB/s (add {ceil['inplace_add']['best_gbs']}, "
             f"copy {ceil['copy']['best_gbs']}); epilogue at "
             f"{extra[w.name + '_frac_of_achievable']:.3f} of it")

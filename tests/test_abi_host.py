@@ -301,3 +301,13 @@ def test_create_without_device_fails_loudly():
     assert rc == B.QKV_ERR_INVALID_ARG
     assert B.qkv_epilogue_last_error(None) == "NULL handle"
     B.qkv_epilogue_destroy(None)   # no-op
+
+
+def test_rows_too_wide_rejected():
+    """The kernel decodes units with a reciprocal multiply exact below 2^22
+    units per token: one more head past that is refused, one less is not."""
+    # hd 128 on the vector path: 16 units per head, nkt/8 for v
+    under = base_args(nt=1, n_head=(1 << 18) - 20)
+    assert rc_of(under) == (0, "")
+    rc, msg = rc_of(base_args(nt=1, n_head=1 << 18))
+    assert rc == B.QKV_ERR_INVALID_ARG and "rows too wide" in msg

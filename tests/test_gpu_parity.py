@@ -369,3 +369,20 @@ def test_graph_capture_replay_48_layers(handle):
             c.run_oracle()
             c.download()
             c.check(check_untouched=False, label=f"graph replay {rep} layer {li}")
+
+
+@pytest.mark.parametrize("norm", [False, True])
+def test_token_blocks_past_the_y_grid_limit(handle, norm):
+    """More than 65535 token blocks in one launch: the grid's z dimension,
+    and the early return of the last z slice's tail (one 8-dim q head and one
+    kv head, 70001 tokens at positions 0..70000)."""
+    w = wl.Workload("z_grid_70001", 1, 1, 8, nt=70001, n_ctx=70001, n_slots=1, layers=1, seed=41,
+                    pos_mode="arange", cache_dtypes=(wl.CACHE_F16,))
+    c = Case(w, norm=norm)
+    rc, plan = B.qkv_epilogue_plan(c.run_oracle().upload().args())
+    assert rc == 0 and plan.grid // plan.col_blocks > 65535, (rc, plan.grid)
+    say(f"[case] z grid, {plan.grid} workgroups, norm={norm}")
+    assert c.run_gpu(handle) == 0, B.qkv_epilogue_last_error(handle)
+    assert B.qkv_epilogue_status(handle) == 0
+    c.download()
+    c.check(label="z grid")

@@ -792,8 +792,21 @@ def floors(stream, shapes):
                 P.empty(g_, b_, stream)
             e1.record(stream)
             e1.synchronize()
-        out[f"grid{g_}x{b_}"] = dict(graph_us=round(gu, 3),
-                                     stream_loop_us=round(e0.elapsed_time(e1) * 1e3 / 512, 3))
+        loop_us = e0.elapsed_time(e1) * 1e3 / 512
+        # the same empty kernel taking 1280 bytes of arguments, as a launch of
+        # the epilogue does: HIP's host path for a launch that carries them
+        with torch.cuda.stream(stream):
+            for _ in range(64):
+                P.empty_args(g_, b_, stream)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(512):
+                P.empty_args(g_, b_, stream)
+            e1.record(stream)
+            e1.synchronize()
+        out[f"grid{g_}x{b_}"] = dict(graph_us=round(gu, 3), stream_loop_us=round(loop_us, 3),
+                                     stream_loop_us_with_1280_byte_args=round(
+                                         e0.elapsed_time(e1) * 1e3 / 512, 3))
     return out
 
 
@@ -842,6 +855,24 @@ def proj_sweep(args):
     B.qkv_epilogue_destroy(h)
 
 
+def decode_loop_c(w, steps, warmup):
+    """The decode step issued from C with no Python in the process
+    (tests/c/decode_loop, built by __graft_entry__.build()): microseconds per
+    layer of an event-timed stream loop and host microseconds per call.  None
+    when the program is not built."""
+    import subprocess
+    exe = os.path.join(ROOT, "tests", "c", "decode_loop")
+    if not os.path.exists(exe):
+        log("[bench]   tests/c/decode_loop not built; skipped")
+        return None
+    r = subprocess.run([exe, str(w.n_head), str(w.n_kv_head), str(w.head_dim), str(w.layers), str(steps),
+                        str(warmup)], capture_output=True, text=True, timeout=120)
+    if r.returncode != 0:
+        log(f"[bench]   decode_loop failed: {r.stderr.strip()}")
+        return None
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
 def decode_all(h, args, stream):
     """The one-token decode workloads (tiny, 7B, 14B) beside the empty kernel
     of each one's launch shape."""
@@ -857,6 +888,12 @@ def decode_all(h, args, stream):
         log(f"[bench] {wd.name}")
         r = bench_decode(h, wd, max(10, args.steps // 10), max(2, args.warmup // 10), stream)
         r["empty_kernel_same_launch"] = fl[shape[wd.name]]
+        if wd.layers > 1:
+            # the same step issued from C (separate section buffers on every layer)
+            c = decode_loop_c(wd, max(50, args.steps // 2), 5)
+            if c is not None:
+                r["us_per_layer_stream_from_c"] = round(c["us_per_layer"], 3)
+                r["host_issue_us_per_call_from_c"] = round(c["host_issue_us_per_call"], 3)
         out[wd.name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
         log(f"[bench]   {r['us_per_layer_stream']:.2f} us/layer (stream), "
             f"{r.get('us_per_layer_graph', float('nan')):.2f} us/layer (graph)")

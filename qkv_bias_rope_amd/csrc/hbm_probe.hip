@@ -4,6 +4,10 @@
 //
 //  * empty:  a kernel that does nothing -- the per-launch floor of a grid of
 //            a given size (dispatch, wave launch, end-of-kernel).
+//  * empty_args: the same with 1280 bytes of kernel arguments, about what an
+//            epilogue launch passes (its parameters and the 1 KB
+//            inverse-frequency table): HIP's host path for a launch that
+//            carries arguments.
 //  * copy:   dst = src over 16-byte vectors, each thread issuing all its
 //            loads before its stores.
 //  * add:    buf += 1 in place over 16-byte vectors (the read/write mix of an
@@ -50,6 +54,13 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kNtDevice = 2 /* nt */ | 16 /* sc1 */;
 
 __global__ void empty_kernel() {}
+
+// kernel arguments of the size an epilogue launch passes (unused: the
+// argument segment keeps its size, and the host copies every byte of it)
+struct ArgBlock {
+    float v[320];
+};
+__global__ void empty_args_kernel(ArgBlock) {}
 
 template <int POL, typename T>
 __device__ __forceinline__ T ld(const T *p)
@@ -297,6 +308,17 @@ int qkv_probe_empty(int grid, int block, hipStream_t st)
     if (grid < 1 || bad_block(block))
         return -1;
     hipLaunchKernelGGL(empty_kernel, dim3(grid), dim3(block), 0, st);
+    return rc_of(hipGetLastError());
+}
+
+int qkv_probe_empty_args(int grid, int block, hipStream_t st)
+{
+    if (grid < 1 || bad_block(block))
+        return -1;
+    ArgBlock a;
+    for (int i = 0; i < 320; ++i)
+        a.v[i] = (float)i;
+    hipLaunchKernelGGL(empty_args_kernel, dim3(grid), dim3(block), 0, st, a);
     return rc_of(hipGetLastError());
 }
 

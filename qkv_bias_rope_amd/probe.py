@@ -35,6 +35,8 @@ def _load():
     lib.qkv_probe_grid.restype = _LL
     lib.qkv_probe_empty.argtypes = [_I, _I, _P]
     lib.qkv_probe_empty.restype = _I
+    lib.qkv_probe_empty_args.argtypes = [_I, _I, _P]
+    lib.qkv_probe_empty_args.restype = _I
     lib.qkv_probe_copy.argtypes = [_P, _P, _LL, _I, _I, _I, _P]
     lib.qkv_probe_copy.restype = _I
     lib.qkv_probe_add.argtypes = [_P, _LL, _I, _I, _I, _P]
@@ -48,8 +50,8 @@ def _load():
 
 
 lib = _load()
-EXPORTS = ("qkv_probe_grid", "qkv_probe_empty", "qkv_probe_copy", "qkv_probe_add", "qkv_probe_read",
-           "qkv_probe_rows")
+EXPORTS = ("qkv_probe_grid", "qkv_probe_empty", "qkv_probe_empty_args", "qkv_probe_copy", "qkv_probe_add",
+           "qkv_probe_read", "qkv_probe_rows")
 
 
 def _s(stream):
@@ -64,6 +66,12 @@ def grid(n16: int, block: int, vpt: int) -> int:
 
 def empty(grid_: int, block: int, stream=None) -> int:
     return lib.qkv_probe_empty(grid_, block, _s(stream))
+
+
+def empty_args(grid_: int, block: int, stream=None) -> int:
+    """An empty kernel that takes 1280 bytes of arguments (about an epilogue
+    launch's)."""
+    return lib.qkv_probe_empty_args(grid_, block, _s(stream))
 
 
 POLICIES = (0, 1, 2)

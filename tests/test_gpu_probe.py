@@ -37,6 +37,15 @@ def test_rejects_bad_arguments():
     assert P.add(x, vpt=3) == -1                  # no such instance
     assert P.add(x, policy=3) == -1
     assert P.empty(0, 64) == -1
+    assert P.empty_args(0, 64) == -1
+    assert P.empty_args(3, 100) == -1
+
+
+def test_empty_kernels_launch():
+    s = torch.cuda.current_stream()
+    assert P.empty(14, 64, s) == 0
+    assert P.empty_args(14, 64, s) == 0
+    torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("cache", (torch.float16, torch.float32))

@@ -172,8 +172,8 @@ __device__ __forceinline__ T pick3(int s, T a, T b, T c)
 //              with no LDS and no wait at the barrier.
 // Column blocks hold whole heads (the planner makes blockDim a multiple of the
 // units per head).
-template <int W, bool F16, int TPB, bool STREAM, int NORM, int STYLE>
-__global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvTable inv)
+template <int W, bool F16, int TPB, bool STREAM, int NORM, int STYLE, typename TAB>
+__global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, TAB inv)
 {
     extern __shared__ __align__(16) unsigned char lds_raw[];
     int64_t *s_row = reinterpret_cast<int64_t *>(lds_raw);
@@ -410,13 +410,13 @@ __global__ __launch_bounds__(kMaxBlock) void qkv_epilogue_kernel(KParams p, InvT
     }
 }
 
-template <int W, bool F16, int TPB, bool STREAM, int NORM, int STYLE>
-hipError_t launch_t(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
+template <int W, bool F16, int TPB, bool STREAM, int NORM, int STYLE, typename TAB>
+hipError_t launch_t(const KParams &kp, const TAB &inv, const Plan &pl, hipStream_t st)
 {
     const int64_t ntb = pl.grid / pl.ncb;  // token blocks
     const unsigned gy = (unsigned)(ntb < 65535 ? ntb : 65535);
     const unsigned gz = (unsigned)((ntb + gy - 1) / gy);
-    hipLaunchKernelGGL((qkv_epilogue_kernel<W, F16, TPB, STREAM, NORM, STYLE>),
+    hipLaunchKernelGGL((qkv_epilogue_kernel<W, F16, TPB, STREAM, NORM, STYLE, TAB>),
                        dim3((unsigned)pl.ncb, gy, gz), dim3((unsigned)pl.nthr), (unsigned)pl.lds, st,
                        kp, inv);
     return hipGetLastError();
@@ -424,8 +424,8 @@ hipError_t launch_t(const KParams &kp, const InvTable &inv, const Plan &pl, hipS
 
 // The planner puts one token in each workgroup: the kernel takes any TPB, but
 // two or four tokens per workgroup measured slower at every launch size.
-template <int W, bool F16, int NORM, int STYLE>
-hipError_t launch_s(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
+template <int W, bool F16, int NORM, int STYLE, typename TAB>
+hipError_t launch_s(const KParams &kp, const TAB &inv, const Plan &pl, hipStream_t st)
 {
     if (pl.tb != 1)
         return hipErrorInvalidValue;
@@ -433,15 +433,15 @@ hipError_t launch_s(const KParams &kp, const InvTable &inv, const Plan &pl, hipS
                      : launch_t<W, F16, 1, false, NORM, STYLE>(kp, inv, pl, st);
 }
 
-template <int W, bool F16, int NORM>
-hipError_t launch_n(const KParams &kp, const InvTable &inv, const Plan &pl, hipStream_t st)
+template <int W, bool F16, int NORM, typename TAB>
+hipError_t launch_n(const KParams &kp, const TAB &inv, const Plan &pl, hipStream_t st)
 {
     return pl.style == QKV_ROPE_INTERLEAVED ? launch_s<W, F16, NORM, 1>(kp, inv, pl, st)
                                             : launch_s<W, F16, NORM, 0>(kp, inv, pl, st);
 }
 
-template <int W>
-hipError_t launch_w(const KParams &kp, const InvTable &inv, const Plan &pl, bool f16,
+template <int W, typename TAB>
+hipError_t launch_w(const KParams &kp, const TAB &inv, const Plan &pl, bool f16,
                     hipStream_t st)
 {
     const int uph = pl.half / W;
@@ -538,7 +538,12 @@ int launch_fused(qkv_epilogue_t *h, const qkv_epilogue_args_t *a, unsigned flags
     if (e != hipSuccess)
         return fail(h, QKV_ERR_HIP, "hipSetDevice(%d): %s", h->device, hipGetErrorString(e));
     const bool f16 = a->cache_dtype == QKV_CACHE_F16;
-    e = pl.W == 4 ? launch_w<4>(kp, inv, pl, f16, st) : launch_w<1>(kp, inv, pl, f16, st);
+    if (pl.half <= kSmallHalf) {
+        const InvTableSmall sm = small_table(inv);
+        e = pl.W == 4 ? launch_w<4>(kp, sm, pl, f16, st) : launch_w<1>(kp, sm, pl, f16, st);
+    } else {
+        e = pl.W == 4 ? launch_w<4>(kp, inv, pl, f16, st) : launch_w<1>(kp, inv, pl, f16, st);
+    }
     if (e != hipSuccess)
         return fail(h, QKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return QKV_OK;

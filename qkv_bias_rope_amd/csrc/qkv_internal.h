@@ -18,9 +18,26 @@
 namespace qkv_detail {
 
 // Inverse-frequency table passed by value in the kernel arguments.
-struct InvTable {
-    float v[kMaxHalf];
+// The inverse-frequency table a launch passes by value in its kernel
+// arguments.  HIP's host time for issuing a launch grows with the bytes of its
+// arguments, so a launch whose head_dim/2 fits kSmallHalf (head_dim <= 128)
+// passes only that many entries.
+template <int N>
+struct InvTableN {
+    float v[N];
 };
+constexpr int kSmallHalf = 64;
+using InvTable = InvTableN<kMaxHalf>;
+using InvTableSmall = InvTableN<kSmallHalf>;
+
+// The first kSmallHalf entries of a full table.
+inline InvTableSmall small_table(const InvTable &t)
+{
+    InvTableSmall s;
+    for (int i = 0; i < kSmallHalf; ++i)
+        s.v[i] = t.v[i];
+    return s;
+}
 
 template <int W>
 struct alignas(4 * W) FVec {

@@ -129,7 +129,7 @@ __device__ __forceinline__ void put_cache(void *cache, int64_t off, float v)
 // rows[t] is token t's cache row (slot * n_ctx + pos, or -1 when out of
 // range).  Every column block reads them instead of recomputing them.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void rope_table_kernel(ProjParams p, InvTable inv, float *tab,
+__global__ __launch_bounds__(256) void rope_table_kernel(ProjParams p, InvTableSmall inv, float *tab,
                                                          int64_t *rows)
 {
     const int half = p.half;
@@ -673,7 +673,7 @@ int split_heads_per_thread(int M, int N, int hd)
 }
 
 template <bool F16, int HD>
-__global__ __launch_bounds__(256) void proj_split_epilogue_kernel(ProjParams p, InvTable inv, int hpt)
+__global__ __launch_bounds__(256) void proj_split_epilogue_kernel(ProjParams p, InvTableSmall inv, int hpt)
 {
     constexpr int HALF = HD / 2;
     const int heads = p.N / HD;
@@ -766,7 +766,7 @@ constexpr int kGemvSplit = 2;     // waves per NeoX pair, each summing 1/kGemvSp
 // 16-byte chunk holding 16 of them (two chunks of x); each output is its f32
 // sum times the row's scale.
 template <bool F16, int HD, int NT, int U, int P, bool SEP, bool W8>
-__global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p, InvTable inv)
+__global__ __launch_bounds__(64 * kGemvWaves) void proj_gemv_kernel(ProjParams p, InvTableSmall inv)
 {
     constexpr int HALF = HD / 2;
     constexpr int kWpc = W8 ? 16 : 8;        // weights per 16-byte chunk
@@ -1059,7 +1059,7 @@ int gemv_step8(int K)
 }
 
 template <bool F16, int HD, int NT, bool SEP>
-hipError_t launch_gemv(const ProjParams &pp, const InvTable &inv, hipStream_t st, int u)
+hipError_t launch_gemv(const ProjParams &pp, const InvTableSmall &inv, hipStream_t st, int u)
 {
     constexpr int pairs = kGemvWaves / kGemvSplit;   // per block
     const int blocks = (pp.N / 2 + pairs - 1) / pairs;
@@ -1132,7 +1132,7 @@ hipError_t launch_mm_plan(const ProjParams &pp, hipStream_t st, const MmPlan &pl
 }
 
 template <bool F16, int HD>
-hipError_t launch_proj(const ProjParams &pp, const InvTable &inv, hipStream_t st, MmPlan pl)
+hipError_t launch_proj(const ProjParams &pp, const InvTableSmall &inv, hipStream_t st, MmPlan pl)
 {
     if (pp.M <= kGemvTok) {
         const int u = pp.w8 ? gemv_step8(pp.K) : gemv_step(pp.K);
@@ -1336,7 +1336,8 @@ int run_proj_impl(qkv_epilogue_t *h, const qkv_proj_args_t *pa, bool static_ws)
     pp.device = h->device;
     pp.style = a->rope_style;
 
-    const InvTable &inv = handle_inv(h, a->theta, a->head_dim, a->freq_scale);
+    // head_dim is 64 or 128 here: the short table holds every entry
+    const InvTableSmall inv = small_table(handle_inv(h, a->theta, a->head_dim, a->freq_scale));
     hipStream_t st = (a->stream || a->use_stream) ? static_cast<hipStream_t>(a->stream) : h->stream;
     DeviceGuard g;
     hipError_t e = g.set(h->device);

@@ -65,10 +65,10 @@ __device__ __forceinline__ void turn(float &x0, float &x1, float a)
 //  interleaved (STYLE 1): W = 4: d = half, each slot holds W/2 adjacent pairs
 //    (pair indices eo/2 + j and (eo+half)/2 + j); W = 1: the slots are
 //    x[2m] and x[2m+1], pair index m.
-template <int W, bool STREAM, int STYLE>
+template <int W, bool STREAM, int STYLE, typename TAB>
 __global__ __launch_bounds__(kBlockU) void rope_kernel(float *x, int64_t ld, int n_heads,
                                                        int hd, const int32_t *pos,
-                                                       InvTable inv, int64_t n_items)
+                                                       TAB inv, int64_t n_items)
 {
     const int64_t g = (int64_t)blockIdx.x * kBlockU + threadIdx.x;
     if (g >= n_items)
@@ -136,8 +136,8 @@ unsigned grid_of(int64_t n_items)
     return (unsigned)((n_items + kBlockU - 1) / kBlockU);
 }
 
-template <int W, bool F16, bool STREAM, int STYLE>
-hipError_t launch_chain(const qkv_epilogue_args_t *a, const Plan &pl, const InvTable &inv,
+template <int W, bool F16, bool STREAM, int STYLE, typename TAB>
+hipError_t launch_chain(const qkv_epilogue_args_t *a, const Plan &pl, const TAB &inv,
                         unsigned int *err, hipStream_t st)
 {
     const int64_t nt = a->nt;
@@ -155,7 +155,7 @@ hipError_t launch_chain(const qkv_epilogue_args_t *a, const Plan &pl, const InvT
     const int heads[2] = {a->n_head, a->n_kv_head};
     for (int s = 0; s < 2; ++s) {
         const int64_t n = nt * heads[s] * (pl.half / W);
-        hipLaunchKernelGGL((rope_kernel<W, STREAM, STYLE>), dim3(grid_of(n)), dim3(kBlockU), 0, st,
+        hipLaunchKernelGGL((rope_kernel<W, STREAM, STYLE, TAB>), dim3(grid_of(n)), dim3(kBlockU), 0, st,
                            xs[s], pl.ld[s], heads[s], a->head_dim, a->pos, inv, n);
     }
     // store x2 (K from the k section, V from the v section)
@@ -169,8 +169,8 @@ hipError_t launch_chain(const qkv_epilogue_args_t *a, const Plan &pl, const InvT
     return hipGetLastError();
 }
 
-template <int W>
-hipError_t launch_chain_w(const qkv_epilogue_args_t *a, const Plan &pl, const InvTable &inv,
+template <int W, typename TAB>
+hipError_t launch_chain_w(const qkv_epilogue_args_t *a, const Plan &pl, const TAB &inv,
                           unsigned int *err, hipStream_t st)
 {
     const bool f16 = a->cache_dtype == QKV_CACHE_F16;
@@ -208,8 +208,14 @@ extern "C" int qkv_epilogue_run_unfused(qkv_epilogue_t *h, const qkv_epilogue_ar
     hipError_t e = g.set(h->device);
     if (e != hipSuccess)
         return fail(h, QKV_ERR_HIP, "hipSetDevice(%d): %s", h->device, hipGetErrorString(e));
-    e = pl.W == 4 ? launch_chain_w<4>(a, pl, inv, h->d_err, st)
-                  : launch_chain_w<1>(a, pl, inv, h->d_err, st);
+    if (pl.half <= kSmallHalf) {
+        const InvTableSmall sm = small_table(inv);
+        e = pl.W == 4 ? launch_chain_w<4>(a, pl, sm, h->d_err, st)
+                      : launch_chain_w<1>(a, pl, sm, h->d_err, st);
+    } else {
+        e = pl.W == 4 ? launch_chain_w<4>(a, pl, inv, h->d_err, st)
+                      : launch_chain_w<1>(a, pl, inv, h->d_err, st);
+    }
     if (e != hipSuccess)
         return fail(h, QKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return QKV_OK;

@@ -74,3 +74,20 @@ def test_c_program_matches_oracle(tmp_path, w, cd):
     for t in range(nt):
         assert np.array_equal(gkc[pos[t]].view(bits), gk[t].astype(cdt).view(bits))
         assert np.array_equal(gvc[pos[t]].view(bits), vr[t].view(bits))
+
+
+def test_c_decode_loop_runs():
+    """tests/c/decode_loop, the decode step the benchmark issues from C: a few
+    steps of the 7B shape end with the status call clean and a JSON line of
+    positive timings; bad arguments are refused."""
+    exe = os.path.join(ROOT, "tests", "c", "decode_loop")
+    if not os.path.exists(exe):
+        pytest.fail("tests/c/decode_loop is not built: run __graft_entry__.build()")
+    import json
+    r = subprocess.run([exe, "28", "4", "128", "28", "5", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    assert d["layers"] == 28 and d["steps"] == 5
+    assert d["us_per_layer"] > 0 and d["host_issue_us_per_call"] > 0
+    bad = subprocess.run([exe, "28", "4", "128", "0", "5", "2"], capture_output=True, text=True, timeout=60)
+    assert bad.returncode != 0 and "bad arguments" in bad.stderr

@@ -239,10 +239,11 @@ int qkv_epilogue_run_qk_norm(qkv_epilogue_t *h, const qkv_epilogue_args_t *a,
  *       w_scale[n]: y[t][n] = w_scale[n] * sum_k x[t][k] * w[n][k].  The same
  *       page's matmul runs on block-quantised weights; this is a weight-only
  *       8-bit form of it, which halves the bytes a decode step streams.
- *       E4M3 weights run on the weight-streaming kernel only: 1-4 tokens
- *       (more is QKV_ERR_UNSUPPORTED); each E4M3 value is converted to bf16
- *       exactly and the products summed in f32 as for bf16 weights, then
- *       multiplied by the scale (one more f32 rounding).
+ *       E4M3 weights run on both kernels, at any token count: each E4M3
+ *       value is converted to bf16 exactly and the products summed in f32 as
+ *       for bf16 weights (the activations stay bf16: the matrix cores'
+ *       8-bit forms take 8-bit floats on both sides), then multiplied by
+ *       the scale (one more f32 rounding).
  *   w_scale  E4M3 only: f32 [nqt + 2*nkt] row scales (device, 4-byte
  *       aligned), indexed by the output's q|k|v column also when the weights
  *       come as three matrices; read-only, must not overlap an output.

@@ -202,25 +202,30 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kLdsMax = 160 * 1024;           // per workgroup on gfx950
 
 // HD, the tile shape (MI token tiles and G pair groups per wave, WN waves
-// along the outputs) and the k depth BK of a stage (32, 64 or 128)
-template <int HD, int MI, int WN, int BK, int G>
+// along the outputs), the k depth BK of a stage (32, 64 or 128) and the
+// weight format (W8: one-byte E4M3 weights, so a weight row of a stage is
+// half as long as a token row)
+template <int HD, int MI, int WN, int BK, int G, bool W8>
 struct Shape {
     static constexpr int WM = kWaves / WN;
     static constexpr int BM = WM * MI * 32;
     static constexpr int BN = WN * G * 64;
-    static constexpr int kRow = BK * 2;           // bytes per row and stage
-    static constexpr int kCpr = BK / 8;           // 16-byte chunks per row
-    static constexpr int kRpi = 1024 / kRow;      // rows per load instruction
+    static constexpr int kRow = BK * 2;           // bytes per token row and stage
+    static constexpr int kCpr = BK / 8;           // 16-byte chunks per token row
+    static constexpr int kRpi = 1024 / kRow;      // token rows per load instruction
+    static constexpr int kRowB = W8 ? BK : BK * 2;  // the same for the weight rows
+    static constexpr int kCprB = kRowB / 16;
+    static constexpr int kRpiB = 1024 / kRowB;
     static constexpr int KS = BK / 16;            // k steps of 16 per stage
     static constexpr int kRegionA = BM * kRow;
-    static constexpr int kStage = kRegionA + BN * kRow;
+    static constexpr int kStage = kRegionA + BN * kRowB;
     // ring depth: as many stages as the LDS holds, at most 4
     static constexpr int NSTAGE = kLdsMax / kStage >= 4 ? 4 : kLdsMax / kStage;
     static constexpr int kRing = NSTAGE * kStage;
     // load instructions per stage: an equal share per wave when there are 8
     // or more, else (4 of them) token rows on waves 0-3 and weight rows on
     // waves 4-7
-    static constexpr int kInstA = BM / kRpi, kInstB = BN / kRpi;
+    static constexpr int kInstA = BM / kRpi, kInstB = BN / kRpiB;
     static constexpr int kWaveA = kInstA >= kWaves ? kInstA / kWaves : 1;
     static constexpr int kWaveB = kInstB >= kWaves ? kInstB / kWaves : 1;
     // loads per stage of waves 0-3 and of waves 4-7
@@ -231,8 +236,11 @@ struct Shape {
     static constexpr int kPW = HD / 2;
     static constexpr int kChunks = kPW / 2;
     static constexpr int kTab = BM * kChunks * 16;
-    static constexpr int kLds = kRing > kTab ? kRing : kTab;
+    // W8: the tile's row scales after the table, [pair group][lo | partner][32]
+    static constexpr int kScl = W8 ? BN * 4 : 0;
+    static constexpr int kLds = kRing > kTab + kScl ? kRing : kTab + kScl;
     static_assert(BK == 32 || BK == 64 || BK == 128, "stage depth");
+    static_assert(!W8 || BK >= 64, "E4M3 weights: stages 64 or 128 deep");
     static_assert(NSTAGE >= 2, "the LDS holds two stages");
     static_assert(kInstA % kWaves == 0 || kInstA == 4, "token-row loads");
     static_assert(kInstB % kWaves == 0 || kInstB == 4, "weight-row loads");
@@ -240,6 +248,7 @@ struct Shape {
     static_assert(kWaveA <= 8 && kWaveB <= 8, "load slots");
     static_assert((NSTAGE - 1) * (kLoadsLo > kLoadsHi ? kLoadsLo : kLoadsHi) <= 63, "vmcnt range");
     static_assert((BM * kChunks) % 64 == 0, "table staging");
+    static_assert(kLds <= kLdsMax, "LDS");
 };
 
 // Word 3 of a raw buffer resource (32-bit data format, no swizzle, no
@@ -288,14 +297,20 @@ __device__ __forceinline__ int group_lo(int g)
 }  // namespace mm
 
 // IL: interleaved pairs (2i, 2i+1), else NeoX (j, j + hd/2); a template
-// argument so that the NeoX instance carries no code of the other rotation
-template <bool F16, int HD, int MI, int WN, int BK, int G, bool IL>
+// argument so that the NeoX instance carries no code of the other rotation.
+// W8: E4M3 weights.  Their bytes go to LDS as they are (a stage's weight row
+// is BK bytes); each fragment read takes the lane's 8 codes and turns them
+// into 8 bf16 (exact: every E4M3 value is a bf16 value), so the products and
+// the f32 sums are those of bf16 weights; the epilogue multiplies each sum by
+// its row's scale before the bias.
+template <bool F16, int HD, int MI, int WN, int BK, int G, bool IL, bool W8>
 __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
 {
     using namespace mm;
-    using S = Shape<HD, MI, WN, BK, G>;
+    using S = Shape<HD, MI, WN, BK, G, W8>;
     constexpr int BM = S::BM;
-    constexpr int NSTAGE = S::NSTAGE, KS = S::KS, kRow = S::kRow;
+    constexpr int NSTAGE = S::NSTAGE, KS = S::KS, kRow = S::kRow, kRowB = S::kRowB;
+    constexpr int64_t kWel = W8 ? 1 : 2;          // bytes per weight
     constexpr int HALF = HD / 2;
     constexpr int PT = HALF / 32;                 // tile distance of NeoX partners
     extern __shared__ __align__(16) unsigned char lds[];
@@ -306,6 +321,7 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int lrow = lane / S::kCpr, slot = lane % S::kCpr;
+    const int lrowb = lane / S::kCprB, slotb = lane % S::kCprB;
     const int lr = lane & 31, hi = lane >> 5;
 
     constexpr int GT = WN * G;                    // pair groups per tile
@@ -321,12 +337,12 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     const int kbeg = (int)((int64_t)split * KTall / p.ksplit);
     const int len = (int)((int64_t)(split + 1) * KTall / p.ksplit) - kbeg;
 
-    // this wave's load instructions: token rows arow[j] and weight rows
-    // brow[j] of the tile, kRpi rows each, lane / kCpr the row within; byte
-    // offsets from x and from the weight matrix of the load's section (the
-    // kRpi rows of a load lie in one 32-column tile, so in one section: its
-    // base is wave-uniform), each < 2 GiB; rows past the end repeat the last
-    // one.  (fixed-size arrays: with a size that depends on the template
+    // this wave's load instructions: token rows arow[j] (kRpi rows each,
+    // lane / kCpr the row within) and weight rows brow[j] (kRpiB rows, lane /
+    // kCprB) of the tile; byte offsets from x and from the weight matrix of
+    // the load's section (the rows of a load lie in one 32-column tile, so in
+    // one section: its base is wave-uniform), each < 2 GiB; rows past the end
+    // repeat the last one.  (fixed-size arrays: with a size that depends on the template
     // arguments, captured by the lambda below, hipcc's host pass silently
     // emitted no launch stub)
     const bool do_a = S::kInstA >= kWaves || wave < S::kInstA;
@@ -342,14 +358,14 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     }
 #pragma unroll
     for (int j = 0; j < S::kWaveB; ++j) {
-        brow[j] = S::kRpi * ((S::kInstB >= kWaves ? wave * S::kWaveB : wave - (kWaves - S::kInstB)) + j);
-        const int rb = brow[j] + lrow;
+        brow[j] = S::kRpiB * ((S::kInstB >= kWaves ? wave * S::kWaveB : wave - (kWaves - S::kInstB)) + j);
+        const int rb = brow[j] + lrowb;
         const int n = group_lo<PT>(tn * GT + rb / 64) * 32 + ((rb >> 5) & 1) * PT * 32 + (rb & 31);
         const int nu = group_lo<PT>(tn * GT + brow[j] / 64) * 32 + ((brow[j] >> 5) & 1) * PT * 32;
         const int sec = nu < p.nqt ? 0 : (nu < p.nqt + p.nkt ? 1 : 2);
         const int sbase = sec == 0 ? 0 : (sec == 1 ? p.nqt : p.nqt + p.nkt);
         bsec[j] = sec;
-        boff[j] = (uint32_t)((int64_t)(min(n, p.N - 1) - sbase) * p.K * 2) + (slot ^ swz<S::kCpr>(rb)) * 16;
+        boff[j] = (uint32_t)((int64_t)(min(n, p.N - 1) - sbase) * p.K * kWel) + (slotb ^ swz<S::kCprB>(rb)) * 16;
     }
     // buffer resources over x and the three weight matrices: the loads take a
     // 32-bit offset from a scalar base (as fast as 64-bit per-lane addresses
@@ -359,15 +375,16 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(p.x), (short)0,
                                           (int)(((int64_t)(p.M - 1) * p.ld_x + p.K) * 2), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rw0 = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(p.wsec[0]), (short)0, (int)((int64_t)p.nqt * p.K * 2), kRsrcWord3);
+        const_cast<uint16_t *>(p.wsec[0]), (short)0, (int)((int64_t)p.nqt * p.K * kWel), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rw1 = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(p.wsec[1]), (short)0, (int)((int64_t)p.nkt * p.K * 2), kRsrcWord3);
+        const_cast<uint16_t *>(p.wsec[1]), (short)0, (int)((int64_t)p.nkt * p.K * kWel), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rw2 = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(p.wsec[2]), (short)0, (int)((int64_t)p.nkt * p.K * 2), kRsrcWord3);
+        const_cast<uint16_t *>(p.wsec[2]), (short)0, (int)((int64_t)p.nkt * p.K * kWel), kRsrcWord3);
     // local stage st (clamped to the last one: the loop stays uniform)
     auto issue = [&](int st) {
         const int stage = st % NSTAGE;
-        const uint32_t kb = (uint32_t)(kbeg + min(st, len - 1)) * kRow;
+        const uint32_t kst = (uint32_t)(kbeg + min(st, len - 1));
+        const uint32_t kb = kst * kRow, kbb = kst * kRowB;
         unsigned char *sa = lds + stage * S::kStage;
         unsigned char *sb = sa + S::kRegionA;
         if (do_a) {
@@ -380,7 +397,7 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
 #pragma unroll
             for (int j = 0; j < S::kWaveB; ++j)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(bsec[j] == 0 ? rw0 : (bsec[j] == 1 ? rw1 : rw2),
-                                                         (lds_t *)(sb + brow[j] * kRow), 16, boff[j] + kb, 0, 0,
+                                                         (lds_t *)(sb + brow[j] * kRowB), 16, boff[j] + kbb, 0, 0,
                                                          0);
         }
     };
@@ -395,24 +412,40 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
             acc[q][v] = 0.0f;
 
     // fragment reads: lane reads row lr of each 32-row tile, chunk 2j + hi
-    // for k step j of the stage
+    // for k step j of the stage; an E4M3 weight row holds step j in chunk j,
+    // the lane's 8 codes in its half hi
     const int g = swz<S::kCpr>(lr);               // tiles start at multiples of 32
+    const int gb = swz<S::kCprB>(lr);
     const int abase = (wm * MI * 32 + lr) * kRow;
-    const int bbase = S::kRegionA + (wn * G * 64 + lr) * kRow;
-    int koff[8];
+    const int bbase = S::kRegionA + (wn * G * 64 + lr) * kRowB;
+    int koff[8], koffb[8];
 #pragma unroll
-    for (int j = 0; j < KS; ++j)
+    for (int j = 0; j < KS; ++j) {
         koff[j] = ((2 * j + hi) ^ g) * 16;
+        koffb[j] = W8 ? (j ^ gb) * 16 + 8 * hi : koff[j];
+    }
     // two fragment buffers: step j uses buffer j % 2
     static_assert(KS % 2 == 0, "steps per stage");
     bf16x8 a0[MI], b0[2 * G], a1[MI], b1[2 * G];
-    auto read_frags = [&](const unsigned char *s, int ko, bf16x8 (&fa)[MI], bf16x8 (&fb)[2 * G]) {
+    auto read_frags = [&](const unsigned char *s, int j, bf16x8 (&fa)[MI], bf16x8 (&fb)[2 * G]) {
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
-            fa[mi] = *reinterpret_cast<const bf16x8 *>(s + abase + mi * 32 * kRow + ko);
+            fa[mi] = *reinterpret_cast<const bf16x8 *>(s + abase + mi * 32 * kRow + koff[j]);
 #pragma unroll
-        for (int t = 0; t < 2 * G; ++t)
-            fb[t] = *reinterpret_cast<const bf16x8 *>(s + bbase + t * 32 * kRow + ko);
+        for (int t = 0; t < 2 * G; ++t) {
+            if constexpr (W8) {
+                typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                const u32x2 c8 = *reinterpret_cast<const u32x2 *>(s + bbase + t * 32 * kRowB + koffb[j]);
+                const bf16x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.x, 1.0f, false);
+                const bf16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.x, 1.0f, true);
+                const bf16x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.y, 1.0f, false);
+                const bf16x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.y, 1.0f, true);
+                fb[t] = __builtin_shufflevector(__builtin_shufflevector(w0, w1, 0, 1, 2, 3),
+                                                __builtin_shufflevector(w2, w3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+            } else {
+                fb[t] = *reinterpret_cast<const bf16x8 *>(s + bbase + t * 32 * kRowB + koff[j]);
+            }
+        }
     };
     // half h takes products q = (2g + f)*MI + ti in [h*G*MI, (h+1)*G*MI)
     auto mfma_half = [&](int h, const bf16x8 (&fa)[MI], const bf16x8 (&fb)[2 * G]) {
@@ -430,7 +463,7 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     else
         __builtin_amdgcn_s_waitcnt(vmcnt_wait((NSTAGE - 1) * S::kLoadsHi));
     ring_barrier();
-    read_frags(lds, koff[0], a0, b0);
+    read_frags(lds, 0, a0, b0);
 
     // Per pair of k steps: step j's products, first half; the next step's
     // fragments; step j's second half; step j + 1's first half; the
@@ -449,14 +482,14 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
             __builtin_amdgcn_sched_barrier(0);
             mfma_half(0, a0, b0);
             __builtin_amdgcn_sched_barrier(0);
-            read_frags(s, koff[jj + 1], a1, b1);
+            read_frags(s, jj + 1, a1, b1);
             __builtin_amdgcn_sched_barrier(0);
             mfma_half(1, a0, b0);
             __builtin_amdgcn_sched_barrier(0);
             mfma_half(0, a1, b1);
             __builtin_amdgcn_sched_barrier(0);
             if (jj + 2 < KS) {
-                read_frags(s, koff[jj + 2], a0, b0);
+                read_frags(s, jj + 2, a0, b0);
             } else {
                 if (S::kLoadsLo == S::kLoadsHi || wave < 4)
                     __builtin_amdgcn_s_waitcnt(vmcnt_wait((NSTAGE - 2) * S::kLoadsLo));
@@ -464,7 +497,7 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
                     __builtin_amdgcn_s_waitcnt(vmcnt_wait((NSTAGE - 2) * S::kLoadsHi));
                 ring_barrier();
                 issue(kt + NSTAGE);
-                read_frags(lds + ((kt + 1) % NSTAGE) * S::kStage, koff[0], a0, b0);
+                read_frags(lds + ((kt + 1) % NSTAGE) * S::kStage, 0, a0, b0);
             }
             __builtin_amdgcn_sched_barrier(0);
             mfma_half(1, a1, b1);
@@ -528,6 +561,20 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
             __builtin_amdgcn_global_load_lds(p.rtab + (int64_t)tokc * HD + col, (lds_t *)(lds + u * 1024), 16, 0,
                                              0);
         }
+        if constexpr (W8) {
+            // thread u < GT*16 copies 16 bytes: pair group q = u / 16, its lo
+            // (f = 0) or partner (f = 1) columns, four of them; a group past
+            // the last output is not read below
+            const int u = tid;
+            const int q = u >> 4, f = (u >> 3) & 1, c4 = (u & 7) * 4;
+            if (u < GT * 16 && tn * GT + q < ng) {
+                const float *const src = p.wscale + group_lo<PT>(tn * GT + q) * 32 + f * HALF + c4;
+                float *const dst = reinterpret_cast<float *>(lds + S::kTab) + q * 64 + f * 32 + c4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dst[e] = src[e];
+            }
+        }
     }
     // per pair group: its section, the lane's 32 bias values; the tokens'
     // cache rows when any group is in k or v
@@ -588,10 +635,27 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
             for (int gg = 0; gg < 4; ++gg) {
                 const int c0 = cs[g] + 8 * gg, c1 = c0 + HALF;
                 FVec<4> &y0 = Y0[gg], &y1 = Y1[gg];
+                if constexpr (W8) {
+                    // each sum times its row's scale, rounded, then the bias
+                    // (two roundings, as the weight-streaming kernel: no FMA)
+#pragma clang fp contract(off)
+                    const float *const sl = reinterpret_cast<const float *>(lds + S::kTab) +
+                                            (wn * G + g) * 64 + 8 * gg + 4 * hi;
+                    const FVec<4> sc0 = *reinterpret_cast<const FVec<4> *>(sl);
+                    const FVec<4> sc1 = *reinterpret_cast<const FVec<4> *>(sl + 32);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    y0.e[e] = acc[2 * g * MI + ti][4 * gg + e] + bias0[g][gg].e[e];
-                    y1.e[e] = acc[(2 * g + 1) * MI + ti][4 * gg + e] + bias1[g][gg].e[e];
+                    for (int e = 0; e < 4; ++e) {
+                        const float m0 = acc[2 * g * MI + ti][4 * gg + e] * sc0.e[e];
+                        const float m1 = acc[(2 * g + 1) * MI + ti][4 * gg + e] * sc1.e[e];
+                        y0.e[e] = m0 + bias0[g][gg].e[e];
+                        y1.e[e] = m1 + bias1[g][gg].e[e];
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        y0.e[e] = acc[2 * g * MI + ti][4 * gg + e] + bias0[g][gg].e[e];
+                        y1.e[e] = acc[(2 * g + 1) * MI + ti][4 * gg + e] + bias1[g][gg].e[e];
+                    }
                 }
                 if (sec[g] < 2 && !IL) {
                     const int cc = cpair + 2 * gg;
@@ -710,6 +774,10 @@ __global__ __launch_bounds__(256) void proj_split_epilogue_kernel(ProjParams p, 
             src += plane;
             y0 = y0 + src[c0];
             y1 = y1 + src[c1];
+        }
+        if (p.w8) {
+            y0 = y0 * p.wscale[c0];
+            y1 = y1 * p.wscale[c1];
         }
         const int sec = h < qheads ? 0 : (h < qheads + kheads ? 1 : 2);
         const int sbase = sec == 0 ? 0 : (sec == 1 ? p.nqt : p.nqt + p.nkt);
@@ -975,7 +1043,7 @@ int mm_bm(int mi, int wn)
 // of its S*M*N f32 partials (~5 TB/s) and a summing kernel (~3 us), no split
 // the cos/sin table kernel (~4 us).  Against sweeps of every shape and split
 // at 16-4096 tokens it picks the fastest measured plan or one within 3%.
-MmPlan mm_plan(int M, int N, int K, int cus)
+MmPlan mm_plan(int M, int N, int K, int cus, bool w8)
 {
     struct Cand {
         int mi, wn, g;
@@ -985,10 +1053,12 @@ MmPlan mm_plan(int M, int N, int K, int cus)
         {4, 4, 1, 1.90}, {2, 2, 1, 1.13}, {1, 2, 1, 0.72}, {1, 4, 1, 0.90}, {1, 1, 3, 1.58}};
     const int KT = K / 64;
     const int NG = N / 64;
-    const double w_us = (double)N * K * 2 / 5.5e6;
+    const double w_us = (double)N * K * (w8 ? 1 : 2) / 5.5e6;
     MmPlan best = {4, 4, 1, 1};
     double best_t = 1e300;
     for (const Cand &c : cands) {
+        if (w8 && c.g == 3)
+            continue;   // 12 weight-row loads per E4M3 stage do not share out over 8 waves
         const int64_t bm = mm_bm(c.mi, c.wn), gt = c.wn * c.g;
         const int64_t tiles = ((M + bm - 1) / bm) * ((NG + gt - 1) / gt);
         const int smax = KT / 4 < 1 ? 1 : (KT / 4 > 64 ? 64 : KT / 4);   // >= 4 stages per split
@@ -1010,16 +1080,16 @@ MmPlan mm_plan(int M, int N, int K, int cus)
 
 // Raise the kernel's dynamic-LDS limit to what it uses, once per kernel and
 // device (the caller has made the handle's device current).
-template <bool F16, int HD, int MI, int WN, int BK, int G, bool IL>
+template <bool F16, int HD, int MI, int WN, int BK, int G, bool IL, bool W8>
 hipError_t set_mm_lds(int device)
 {
     static std::atomic<unsigned long long> done{0};
     const unsigned long long bit = 1ull << (device & 63);
     if (done.load(std::memory_order_acquire) & bit)
         return hipSuccess;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&proj_mfma_kernel<F16, HD, MI, WN, BK, G, IL>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&proj_mfma_kernel<F16, HD, MI, WN, BK, G, IL, W8>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       mm::Shape<HD, MI, WN, BK, G>::kLds);
+                                       mm::Shape<HD, MI, WN, BK, G, W8>::kLds);
     if (e == hipSuccess && device < 64)
         done.fetch_or(bit, std::memory_order_release);
     return e;
@@ -1096,30 +1166,34 @@ hipError_t launch_gemv(const ProjParams &pp, const InvTableSmall &inv, hipStream
     return hipGetLastError();
 }
 
-template <bool F16, int HD, int MI, int WN, int BK, int G, bool IL>
+template <bool F16, int HD, int MI, int WN, int BK, int G, bool IL, bool W8>
 hipError_t launch_mm(const ProjParams &pp, hipStream_t st)
 {
-    using S = mm::Shape<HD, MI, WN, BK, G>;
-    hipError_t e = set_mm_lds<F16, HD, MI, WN, BK, G, IL>(pp.device);
+    using S = mm::Shape<HD, MI, WN, BK, G, W8>;
+    hipError_t e = set_mm_lds<F16, HD, MI, WN, BK, G, IL, W8>(pp.device);
     if (e != hipSuccess)
         return e;
     const int gt = WN * G;
     const int tiles = ((pp.M + S::BM - 1) / S::BM) * ((pp.N / 64 + gt - 1) / gt);
     constexpr unsigned lds = S::kLds;
-    hipLaunchKernelGGL((proj_mfma_kernel<F16, HD, MI, WN, BK, G, IL>), dim3(tiles * pp.ksplit), dim3(mm::kThreads),
-                       lds, st, pp);
+    hipLaunchKernelGGL((proj_mfma_kernel<F16, HD, MI, WN, BK, G, IL, W8>), dim3(tiles * pp.ksplit),
+                       dim3(mm::kThreads), lds, st, pp);
     return hipGetLastError();
 }
 
-template <bool F16, int HD, bool IL>
+template <bool F16, int HD, bool IL, bool W8>
 hipError_t launch_mm_shape(const ProjParams &pp, hipStream_t st, const MmPlan &pl)
 {
     switch (pl.mi * 100 + pl.wn * 10 + pl.g) {
-    case 141: return launch_mm<F16, HD, 1, 4, 64, 1, IL>(pp, st);
-    case 121: return launch_mm<F16, HD, 1, 2, 64, 1, IL>(pp, st);
-    case 221: return launch_mm<F16, HD, 2, 2, 64, 1, IL>(pp, st);
-    case 441: return launch_mm<F16, HD, 4, 4, 64, 1, IL>(pp, st);
-    case 113: return launch_mm<F16, HD, 1, 1, 64, 3, IL>(pp, st);
+    case 141: return launch_mm<F16, HD, 1, 4, 64, 1, IL, W8>(pp, st);
+    case 121: return launch_mm<F16, HD, 1, 2, 64, 1, IL, W8>(pp, st);
+    case 221: return launch_mm<F16, HD, 2, 2, 64, 1, IL, W8>(pp, st);
+    case 441: return launch_mm<F16, HD, 4, 4, 64, 1, IL, W8>(pp, st);
+    case 113:
+        if constexpr (W8)
+            return hipErrorInvalidValue;    // the planner never picks it for E4M3 weights
+        else
+            return launch_mm<F16, HD, 1, 1, 64, 3, IL, W8>(pp, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1127,8 +1201,12 @@ hipError_t launch_mm_shape(const ProjParams &pp, hipStream_t st, const MmPlan &p
 template <bool F16, int HD>
 hipError_t launch_mm_plan(const ProjParams &pp, hipStream_t st, const MmPlan &pl)
 {
-    return pp.style == QKV_ROPE_INTERLEAVED ? launch_mm_shape<F16, HD, true>(pp, st, pl)
-                                            : launch_mm_shape<F16, HD, false>(pp, st, pl);
+    const bool il = pp.style == QKV_ROPE_INTERLEAVED;
+    if (pp.w8)
+        return il ? launch_mm_shape<F16, HD, true, true>(pp, st, pl)
+                  : launch_mm_shape<F16, HD, false, true>(pp, st, pl);
+    return il ? launch_mm_shape<F16, HD, true, false>(pp, st, pl)
+              : launch_mm_shape<F16, HD, false, false>(pp, st, pl);
 }
 
 template <bool F16, int HD>
@@ -1242,10 +1320,6 @@ int run_proj_impl(qkv_epilogue_t *h, const qkv_proj_args_t *pa, bool static_ws)
         return fail(h, QKV_ERR_UNSUPPORTED, "unknown weight format %d", pa->w_format);
     const bool w8 = pa->w_format == QKV_WEIGHT_E4M3;
     const int64_t wel = w8 ? 1 : 2;                 // bytes per weight
-    if (w8 && a->nt > kGemvTok)
-        return fail(h, QKV_ERR_UNSUPPORTED,
-                    "E4M3 weights run on the weight-streaming kernel only (1-%d tokens), got %d tokens",
-                    kGemvTok, a->nt);
     // the kernels address x and each weight matrix with 32-bit byte offsets
     if ((int64_t)a->nt * (pa->ld_x ? pa->ld_x : pa->hidden) * 2 > INT32_MAX ||
         (sep ? std::max(pl.nqt, pl.nkt) : N) * pa->hidden * wel > INT32_MAX)
@@ -1349,7 +1423,7 @@ int run_proj_impl(qkv_epilogue_t *h, const qkv_proj_args_t *pa, bool static_ws)
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device);
         if (e != hipSuccess || cus <= 0)
             return fail(h, QKV_ERR_HIP, "compute-unit count: %s", hipGetErrorString(e));
-        plan = mm_plan(pp.M, pp.N, pp.K, cus);
+        plan = mm_plan(pp.M, pp.N, pp.K, cus, pp.w8);
         pp.ksplit = plan.ksplit;
         {
             // the grid (tiles x splits) and the kernels' tile indices are 32-bit

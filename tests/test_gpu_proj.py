@@ -804,12 +804,12 @@ def test_proj_e4m3_every_code_exact(handle):
     assert np.array_equal(got_v.view(np.uint32), c.o["v"].view(np.uint32)), "v differs from the oracle"
 
 
-def test_proj_e4m3_rejections(handle):
-    """E4M3 weights: more than 4 tokens is unsupported, the scales are
-    required, aligned and read-only; an unknown format is unsupported."""
-    c5 = ProjCase(SMALL_05B, hidden=512, nt=5, wfmt="e4m3").upload()
-    assert B.qkv_epilogue_run_proj(handle, c5.args()) == B.QKV_ERR_UNSUPPORTED
-    c = ProjCase(SMALL_05B, hidden=512, nt=4, wfmt="e4m3").upload()
+@pytest.mark.parametrize("nt", [4, 5])
+def test_proj_e4m3_rejections(handle, nt):
+    """E4M3 weights, on the GEMV (4 tokens) and the MFMA path (5): the
+    scales are required, aligned and read-only; an unknown format is
+    unsupported.  Nothing is launched for a rejected call."""
+    c = ProjCase(SMALL_05B, hidden=512, nt=nt, wfmt="e4m3").upload()
     a = c.args()
     a.w_scale = None
     assert B.qkv_epilogue_run_proj(handle, a) == B.QKV_ERR_INVALID_ARG
@@ -823,9 +823,107 @@ def test_proj_e4m3_rejections(handle):
     a.w_format = 7
     assert B.qkv_epilogue_run_proj(handle, a) == B.QKV_ERR_UNSUPPORTED
     torch.cuda.synchronize()
-    assert torch.isnan(c.g_q).all() and torch.isnan(c5.g_q).all()
+    assert torch.isnan(c.g_q).all()
     assert B.qkv_epilogue_run_proj(handle, c.args()) == B.QKV_OK
     assert B.qkv_epilogue_status(handle) == B.QKV_OK
+
+
+# ---- E4M3 weights on the MFMA kernel, 5+ tokens -------------------------------
+
+@pytest.mark.parametrize("nt", [5, 64, 150, 258, 400, 520, 1000, 1300, 1800])
+def test_proj_e4m3_mfma_plan_switches(handle, nt):
+    """E4M3 weights through every tile shape the plan picks for them, k
+    split and data-parallel, at the 14B width with hidden 2048: the codes
+    land in LDS as bytes, each fragment read turns 8 of them into bf16, the
+    epilogue (or the split path's summing kernel) applies the row scales.
+    The oracle recomputes both ends of every 256-token block and a random
+    sample (its E4M3 decode costs ~0.1 s per token at this width); the cache
+    addressing is checked for all tokens.  Distinct positions, so that every
+    sampled token's cache row is its own."""
+    w = wl.Workload("proj_plan_e4m3", 40, 8, 128, nt=nt, n_ctx=4096, n_slots=1, layers=1,
+                    seed=36, pos_mode="uniform")
+    rng = np.random.default_rng(nt)
+    ends = np.r_[np.arange(0, nt, 256), np.arange(255, nt, 256), nt - 1]
+    sample = np.unique(np.r_[ends, rng.integers(0, nt, 16)]) if nt > 40 else None
+    c = ProjCase(w, hidden=2048, wfmt="e4m3", sample=sample,
+                 pos=rng.permutation(w.n_ctx)[:nt].astype(np.int32))
+    assert _run(handle, c, f"e4m3_plan_{nt}") == B.QKV_OK
+    c.check(f"e4m3_plan_{nt}")
+
+
+@pytest.mark.parametrize("weights,style,nt", [("three", B.QKV_ROPE_NEOX, 40), ("three", B.QKV_ROPE_NEOX, 1030),
+                                              ("concat", B.QKV_ROPE_INTERLEAVED, 40),
+                                              ("three", B.QKV_ROPE_INTERLEAVED, 1030)])
+def test_proj_e4m3_mfma_layouts(handle, weights, style, nt):
+    """Three weight matrices and interleaved pairing on the MFMA kernel with
+    E4M3 weights, split (40 tokens) and data-parallel (1030), 7B geometry."""
+    rng = np.random.default_rng(nt)
+    c = ProjCase(wl.DECODE_7B, hidden=3584, nt=nt, wfmt="e4m3", weights=weights, style=style,
+                 sample=np.unique(np.r_[0, nt - 1, rng.integers(0, nt, 30)]),
+                 pos=rng.permutation(wl.DECODE_7B.n_ctx)[:nt].astype(np.int32))
+    assert _run(handle, c, f"e4m3_mfma_{weights}_{style}_{nt}") == B.QKV_OK
+    c.check(f"e4m3_mfma_{weights}_{style}_{nt}")
+
+
+@pytest.mark.parametrize("nt", [40, 1030])
+def test_proj_e4m3_mfma_hd64(handle, nt):
+    """head_dim 64 with slots and no bias on the MFMA kernel, E4M3 weights."""
+    w = wl.Workload("proj_e4m3_hd64_mm", 14, 2, 64, nt=nt, n_ctx=512, n_slots=4, layers=1, seed=37,
+                    cache_dtypes=(wl.CACHE_F16,))
+    rng = np.random.default_rng(nt + 1)
+    sample = np.unique(np.r_[0, nt - 1, rng.integers(0, nt, 30)])
+    rows = rng.permutation(w.n_slots * w.n_ctx)[:nt]         # distinct (slot, position) rows
+    c = ProjCase(w, hidden=896, wfmt="e4m3", bias=False, sample=sample,
+                 pos=(rows % w.n_ctx).astype(np.int32), slot=(rows // w.n_ctx).astype(np.int32))
+    assert _run(handle, c, f"e4m3_mfma_hd64_{nt}") == B.QKV_OK
+    c.check(f"e4m3_mfma_hd64_{nt}")
+
+
+def test_proj_e4m3_prefill_full_size_sampled(handle):
+    """4096 tokens x hidden 5120 with E4M3 weights: the data-parallel
+    256 x 256 tiles, three stages of LDS; sampled tokens, every row address."""
+    rng = np.random.default_rng(38)
+    sample = np.unique(np.concatenate([[0, 1, 255, 256, 2047, 4095], rng.integers(0, 4096, 42)]))
+    c = ProjCase(wl.PREFILL_14B, hidden=5120, sample=sample, wfmt="e4m3")
+    assert _run(handle, c, "e4m3_prefill_full") == B.QKV_OK
+    c.check("e4m3_prefill_full")
+
+
+def test_proj_e4m3_batched_full_size_sampled(handle):
+    """256 sequences, one token each, slot per sequence, hidden 5120, E4M3
+    weights: the k-split path, row scales applied after the partials' sum."""
+    rng = np.random.default_rng(39)
+    sample = np.unique(np.concatenate([[0, 127, 128, 255], rng.integers(0, 256, 28)]))
+    c = ProjCase(wl.BATCHED_DECODE_14B, hidden=5120, sample=sample, wfmt="e4m3")
+    assert _run(handle, c, "e4m3_batched_full") == B.QKV_OK
+    c.check("e4m3_batched_full")
+
+
+@pytest.mark.parametrize("nt,hidden", [(40, 64), (64, 1024)])
+def test_proj_e4m3_every_code_exact_mfma(handle, nt, hidden):
+    """The one-hot test on the MFMA kernel: fused epilogue (40 tokens,
+    hidden 64, no split) and the k-split path (64 tokens, hidden 1024).  Each
+    v output is one decoded code times its row's scale plus the bias, equal
+    to the oracle bit for bit; the picked columns of the v rows hold every
+    finite E4M3 code."""
+    w = wl.Workload(f"proj_e4m3_codes_mm{nt}", 2, 2, 64, nt=nt, n_ctx=128, n_slots=1, layers=1, seed=40,
+                    cache_dtypes=(wl.CACHE_F32,), pos_mode="arange")
+    c = ProjCase(w, hidden=hidden, wfmt="e4m3")
+    rng = np.random.default_rng(41)
+    cols = rng.integers(0, hidden, nt)
+    x = np.zeros((nt, hidden), np.uint16)
+    x[np.arange(nt), cols] = 0x3f80                    # bfloat16 1.0
+    c.d["x"] = x
+    finite = np.array([v for v in range(256) if v not in (0x7F, 0xFF)], np.uint8)
+    nqt, nkt = w.nqt, w.nkt
+    ucols = np.unique(cols)
+    vblock = np.resize(finite, (nkt, ucols.size))
+    c.d["w8"][nqt + nkt:, ucols] = vblock
+    assert np.isin(finite, c.d["w8"][nqt + nkt:][:, ucols]).all()
+    assert _run(handle, c, f"e4m3_codes_mm{nt}") == B.QKV_OK
+    c.check(f"e4m3_codes_mm{nt}")
+    got_v = c.g_v.cpu().numpy()
+    assert np.array_equal(got_v.view(np.uint32), c.o["v"].view(np.uint32)), "v differs from the oracle"
 
 
 def test_proj_e4m3_python_wrapper():

@@ -6,10 +6,11 @@ product is an integer of magnitude <= 9, and every partial sum over hidden =
 5120 terms is an integer below 2^16, so each f32 addition is exact and the
 GPU's sums equal the oracle's (exact double sums rounded once) bit for bit, on
 every launch form: the weight-streaming kernel (1-4 tokens), the MFMA kernel
-with k split (256 tokens) and data-parallel (4096 tokens).  At position 0
-(cos 1, sin 0) with no bias the epilogue passes those values through, so
-q/k/v and the cache rows must equal the oracle's bit for bit; this pins the
-indexing of x, of the q|k|v weight rows and of the outputs exactly.
+with k split (256 tokens) and data-parallel (4096 tokens), with bf16 and with
+E4M3 weights.  At position 0 (cos 1, sin 0) with no bias the epilogue passes
+those values through, so q/k/v and the cache rows must equal the oracle's bit
+for bit; this pins the indexing of x, of the q|k|v weight rows and of the
+outputs exactly.
 
 Page "73 · D3-8 — G4 FusedQKV ported to CUDA", §2 and §4 (i), shows the concat
 matmul equal bit for bit to three separate matmuls; here the same holds for
@@ -129,6 +130,28 @@ def test_exact_data_parallel_4096(handle):
     assert _run(handle, c, "exact_dp_4096") == B.QKV_OK
     _check_exact(c, "exact_dp_4096")
     c.check("exact_dp_4096")
+
+
+@pytest.mark.parametrize("weights", ["concat", "three"])
+def test_exact_e4m3_ksplit_256(handle, weights):
+    """E4M3 weights (codes of -3..3, scales 1) on the k-split MFMA path: the
+    codes converted to bf16 in the fragment reads, the partials summed, then
+    scaled -- bit-equal to the oracle."""
+    sample = np.unique(np.r_[0, 1, 127, 128, 255, np.random.default_rng(7).integers(0, 256, 27)])
+    c = _exact_case(256, 5120, 160, wl.CACHE_F16, weights=weights, wfmt="e4m3", sample=sample)
+    assert _run(handle, c, f"exact_e4m3_ksplit_{weights}") == B.QKV_OK
+    _check_exact(c, f"exact_e4m3_ksplit_{weights}")
+    c.check(f"exact_e4m3_ksplit_{weights}")
+
+
+def test_exact_e4m3_data_parallel_4096(handle):
+    """E4M3 weights on the data-parallel MFMA kernel (4096 tokens, hidden
+    5120): sampled tokens bit-equal to the oracle, every cache row's address."""
+    sample = np.unique(np.r_[0, 255, 256, 4095, np.random.default_rng(8).integers(0, 4096, 44)])
+    c = _exact_case(4096, 5120, 170, wl.CACHE_F32, wfmt="e4m3", sample=sample)
+    assert _run(handle, c, "exact_e4m3_dp_4096") == B.QKV_OK
+    _check_exact(c, "exact_e4m3_dp_4096")
+    c.check("exact_e4m3_dp_4096")
 
 
 @pytest.mark.parametrize("nt", [4, 256])

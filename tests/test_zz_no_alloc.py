@@ -41,26 +41,27 @@ def _same(a, b):
             assert torch.equal(x.view(torch.int32), y.view(torch.int32))
 
 
-def _case(nt, hidden, seed, sample=None):
+def _case(nt, hidden, seed, sample=None, wfmt="bf16"):
     """Distinct random positions: tokens sharing a cache row race for it (a
     caller error), which would make the two entry points' rows differ."""
     w = wl.Workload(f"noalloc_{nt}", 40, 8, 128, nt=nt, n_ctx=4096, n_slots=1, layers=1,
                     seed=seed, pos_mode="uniform")
     pos = np.random.default_rng(seed).permutation(w.n_ctx)[:nt].astype(np.int32)
-    return ProjCase(w, hidden=hidden, sample=sample, pos=pos)
+    return ProjCase(w, hidden=hidden, sample=sample, pos=pos, wfmt=wfmt)
 
 
 @pytest.mark.parametrize("sizes", [((256, 5120), (40, 1024)), ((1030, 1024), (300, 512))])
-def test_noalloc_matches_run_proj_two_calls(handle, sizes):
+@pytest.mark.parametrize("wfmt", ["bf16", "e4m3"])
+def test_noalloc_matches_run_proj_two_calls(handle, sizes, wfmt):
     """First pair: 256 tokens at hidden 5120 (k split four ways: table, rows
     and 29 MB of partial sums in the workspace), then 40 tokens at hidden 1024.
     Second pair: 1030 tokens (data-parallel: table and rows only), then 300
-    tokens split at hidden 512."""
+    tokens split at hidden 512.  With bf16 and with E4M3 weights."""
     cases = []
     for i, (nt, hid) in enumerate(sizes):
         sample = None if nt <= 300 else np.unique(np.r_[0, nt - 1, np.arange(0, nt, 37)])
-        c = _case(nt, hid, 40 + i, sample)
-        say(f"[noalloc] nt={nt} hidden={hid}: run_proj")
+        c = _case(nt, hid, 40 + i, sample, wfmt=wfmt)
+        say(f"[noalloc] nt={nt} hidden={hid} weights={wfmt}: run_proj")
         c.run_oracle().upload()
         assert c.run_gpu(handle) == B.QKV_OK, B.qkv_epilogue_last_error(handle)
         assert B.qkv_epilogue_status(handle) == B.QKV_OK

@@ -847,10 +847,14 @@ def proj_sweep(args):
         for nt in PROJ_SWEEP_TOKENS:
             steps = args.steps if nt <= 512 else max(10, args.steps // 5)
             r = bench_proj(h, w, hidden, steps, args.warmup, stream, min_set_bytes=1.0e9, nt=nt)
+            r8 = bench_proj(h, w, hidden, steps, args.warmup, stream, min_set_bytes=1.0e9, nt=nt,
+                            wfmt="e4m3")
             print(json.dumps({"proj_sweep_tokens": nt, "hidden": hidden,
                               "us_per_launch": round(r["us_per_launch"], 2),
                               "tflops": round(r["tflops"], 1), "gbs": round(r["gbs"], 1),
-                              "library_bf16_matmul_call_us": round(r["library_bf16_matmul_call_us"], 2)}),
+                              "library_bf16_matmul_call_us": round(r["library_bf16_matmul_call_us"], 2),
+                              "e4m3_us_per_launch": round(r8["us_per_launch"], 2),
+                              "e4m3_gbs": round(r8["gbs"], 1)}),
                   flush=True)
     B.qkv_epilogue_destroy(h)
 
@@ -1076,6 +1080,14 @@ def run_all(args, h, stream):
             input_sets=r["sets"])
         log(f"[bench]   {r['us_per_launch']:.1f} us/launch, {r['tflops']:.1f} TFLOP/s "
             f"(library bf16 matmul call {r['library_bf16_matmul_call_us']:.1f} us)")
+        # the same launch with E4M3 weights (bf16 products on the matrix cores)
+        log(f"[bench] {w.name} projection-fed epilogue, E4M3 weights")
+        r = bench_proj(h, w, hid, max(20, args.steps // 2), max(2, args.warmup // 4), stream,
+                       min_set_bytes=1.0e9, wfmt="e4m3")
+        extra[w.name + "_proj_e4m3"] = dict(
+            us_per_launch=round(r["us_per_launch"], 2), tflops=round(r["tflops"], 1),
+            frac_of_bf16_peak=round(r["tflops"] / PEAK_BF16_TFLOPS, 4), hidden=hid, input_sets=r["sets"])
+        log(f"[bench]   {r['us_per_launch']:.1f} us/launch, {r['tflops']:.1f} TFLOP/s")
         wd = wl.DECODE_14B
         hid = wl.HIDDEN[wd.name]
         log(f"[bench] {wd.name} projection-fed epilogue, one token (hidden {hid})")

@@ -412,18 +412,24 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
             acc[q][v] = 0.0f;
 
     // fragment reads: lane reads row lr of each 32-row tile, chunk 2j + hi
-    // for k step j of the stage; an E4M3 weight row holds step j in chunk j,
-    // the lane's 8 codes in its half hi
+    // for k step j of the stage.  W8: the k values inside a stage are taken
+    // in another order (the same for both operands, so only the order of
+    // the f32 sums changes): lane (lr, hi) of steps 2p and 2p + 1 takes the
+    // 16 codes of weight chunk 2p + hi, one 16-byte read for the step pair
+    // (8-byte reads of the 64-byte E4M3 rows reach only half the banks per
+    // half-wave), and its token chunks 4p + 2hi and 4p + 2hi + 1.
     const int g = swz<S::kCpr>(lr);               // tiles start at multiples of 32
     const int gb = swz<S::kCprB>(lr);
     const int abase = (wm * MI * 32 + lr) * kRow;
     const int bbase = S::kRegionA + (wn * G * 64 + lr) * kRowB;
-    int koff[8], koffb[8];
+    int koff[8], koffb[4];
 #pragma unroll
-    for (int j = 0; j < KS; ++j) {
-        koff[j] = ((2 * j + hi) ^ g) * 16;
-        koffb[j] = W8 ? (j ^ gb) * 16 + 8 * hi : koff[j];
-    }
+    for (int j = 0; j < KS; ++j)
+        koff[j] = ((W8 ? 4 * (j >> 1) + 2 * hi + (j & 1) : 2 * j + hi) ^ g) * 16;
+#pragma unroll
+    for (int q = 0; q < KS / 2; ++q)
+        koffb[q] = ((2 * q + hi) ^ gb) * 16;
+    u32x4 braw[6];                                // W8: a step pair's codes, per weight tile
     // two fragment buffers: step j uses buffer j % 2
     static_assert(KS % 2 == 0, "steps per stage");
     bf16x8 a0[MI], b0[2 * G], a1[MI], b1[2 * G];
@@ -434,12 +440,16 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
 #pragma unroll
         for (int t = 0; t < 2 * G; ++t) {
             if constexpr (W8) {
-                typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-                const u32x2 c8 = *reinterpret_cast<const u32x2 *>(s + bbase + t * 32 * kRowB + koffb[j]);
-                const bf16x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.x, 1.0f, false);
-                const bf16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.x, 1.0f, true);
-                const bf16x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.y, 1.0f, false);
-                const bf16x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.y, 1.0f, true);
+                // even step: read the pair's 16 codes, convert the first 8;
+                // odd step: convert the other 8 (no LDS read)
+                if ((j & 1) == 0)
+                    braw[t] = *reinterpret_cast<const u32x4 *>(s + bbase + t * 32 * kRowB + koffb[j >> 1]);
+                const unsigned int c0 = (j & 1) ? braw[t].z : braw[t].x;
+                const unsigned int c1 = (j & 1) ? braw[t].w : braw[t].y;
+                const bf16x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, 1.0f, false);
+                const bf16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, 1.0f, true);
+                const bf16x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, 1.0f, false);
+                const bf16x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, 1.0f, true);
                 fb[t] = __builtin_shufflevector(__builtin_shufflevector(w0, w1, 0, 1, 2, 3),
                                                 __builtin_shufflevector(w2, w3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
             } else {

@@ -52,7 +52,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 struct ProjParams {
     const uint16_t *x;       // bf16 [nt][ld_x]
     const uint16_t *wsec[3]; // weight rows of the q, k, v sections ([nqt|nkt|nkt][K]): bf16, or
-                             // E4M3 bytes when w8 (then only the GEMV runs)
+                             // E4M3 bytes when w8
     bool sep;                // the sections are three matrices (else rows of one concat matrix)
     bool w8;                 // E4M3 weights with one f32 scale per output row
     const float *wscale;     // [N] row scales (w8)

@@ -209,12 +209,16 @@ void oracle_proj_fp8w(const uint16_t *x, int64_t ld_x, const uint8_t *w,
                       const float *scale, int64_t nt, int64_t n_out,
                       int64_t hidden, float *y, int64_t ld_y)
 {
+    /* the value of each of the 256 codes, decoded once per call (a code's
+     * value depends on nothing else) */
+    double val[256];
+    for (int c = 0; c < 256; ++c)
+        val[c] = oracle_e4m3_to_double((uint8_t)c);
     for (int64_t t = 0; t < nt; ++t) {
         for (int64_t n = 0; n < n_out; ++n) {
             double acc = 0.0;
             for (int64_t k = 0; k < hidden; ++k)
-                acc += oracle_bf16_to_double(x[t * ld_x + k]) *
-                       oracle_e4m3_to_double(w[n * hidden + k]);
+                acc += oracle_bf16_to_double(x[t * ld_x + k]) * val[w[n * hidden + k]];
             y[t * ld_y + n] = (float)((double)scale[n] * acc);
         }
     }

@@ -461,10 +461,16 @@ def test_proj_plan_switches(handle, nt):
     on 256 x 128 split 2 ways, 400 data-parallel 128 x 128, 520 data-
     parallel 64 x 256, 1000 data-parallel 256 x 128, 1300 data-parallel
     256 x 192 (three pair groups per wave; 112 groups leave the last tile
-    one group), 1800 data-parallel 256 x 256."""
+    one group), 1800 data-parallel 256 x 256.  The oracle recomputes both
+    ends of every 256-token block and a random sample; the cache addressing
+    is checked for all tokens (distinct positions: each sampled token's
+    cache row is its own)."""
     w = wl.Workload("proj_plan", 40, 8, 128, nt=nt, n_ctx=4096, n_slots=1, layers=1,
                     seed=19, pos_mode="uniform")
-    c = ProjCase(w, hidden=2048)
+    rng = np.random.default_rng(nt + 19)
+    ends = np.r_[np.arange(0, nt, 256), np.arange(255, nt, 256), nt - 1]
+    c = ProjCase(w, hidden=2048, sample=np.unique(np.r_[ends, rng.integers(0, nt, 24)]),
+                 pos=rng.permutation(w.n_ctx)[:nt].astype(np.int32))
     assert _run(handle, c, f"plan_{nt}") == B.QKV_OK
     c.check(f"plan_{nt}")
 

@@ -194,8 +194,8 @@ class Epilogue:
         """The projection feeding the epilogue: x [nt][hidden] as a bfloat16
         device tensor, the weights (w [nqt+2*nkt][hidden] concat, or w/w_k/w_v
         per section) bfloat16 -- or float8_e4m3fn with w_scale, a float32
-        [nqt+2*nkt] tensor of row scales (1-4 tokens); q, k, v are the float32
-        outputs; biases may be None."""
+        [nqt+2*nkt] tensor of row scales; q, k, v are the float32 outputs;
+        biases may be None."""
         import torch
         if kcache.dtype == torch.float32:
             cd = QKV_CACHE_F32

@@ -435,14 +435,15 @@ def test_proj_split_head_groups_ragged(handle):
 
 
 @pytest.mark.parametrize("nt", [40, 300, 1030])
-def test_proj_repeat_is_bitwise_identical(handle, nt):
+@pytest.mark.parametrize("wfmt", ["bf16", "e4m3"])
+def test_proj_repeat_is_bitwise_identical(handle, nt, wfmt):
     """The k-split partials are added in split order and every tile sums its
     k steps in one order, so a repeated launch reproduces q/k/v bit for bit
-    (40 and 300 tokens split k, 1030 run data-parallel); the first result is
-    also checked against the oracle."""
+    (40 and 300 tokens split k, 1030 run data-parallel), with bf16 and with
+    E4M3 weights; the first result is also checked against the oracle."""
     w = wl.Workload("proj_repeat", 40, 8, 128, nt=nt, n_ctx=4096, n_slots=1, layers=1,
                     seed=25, pos_mode="arange")
-    c = ProjCase(w, hidden=1024)
+    c = ProjCase(w, hidden=1024, wfmt=wfmt)
     assert _run(handle, c, f"repeat_{nt}") == B.QKV_OK
     first = [t.clone() for t in (c.g_q, c.g_k, c.g_v)]
     for _ in range(3):
@@ -646,12 +647,14 @@ def _graph_replays(handle, cases, reps=2):
             c.check(f"graph replay {rep} call {i}")
 
 
-def test_proj_graph_capture_decode_layers(handle):
+@pytest.mark.parametrize("wfmt", ["bf16", "e4m3"])
+def test_proj_graph_capture_decode_layers(handle, wfmt):
     """Six one-token layers (alternating concat and separate outputs) captured
-    into one HIP graph and replayed with new activations and positions."""
+    into one HIP graph and replayed with new activations and positions, with
+    bf16 and with E4M3 weights."""
     cases = []
     for layer in range(6):
-        c = ProjCase(wl.DECODE_14B, hidden=5120, nt=1,
+        c = ProjCase(wl.DECODE_14B, hidden=5120, nt=1, wfmt=wfmt,
                      form="concat" if layer % 2 == 0 else "separate")
         c.upload()
         cases.append(c)
@@ -687,14 +690,16 @@ def test_proj_workspace_growth_refused_in_capture():
         B.qkv_epilogue_destroy(h)
 
 
-def test_proj_graph_capture_split_and_fused(handle):
+@pytest.mark.parametrize("wfmt", ["bf16", "e4m3"])
+def test_proj_graph_capture_split_and_fused(handle, wfmt):
     """A k-split call (300 tokens) and a data-parallel call (1100 tokens)
-    captured after a warm-up call; no allocation happens in the capture."""
+    captured after a warm-up call; no allocation happens in the capture.
+    With bf16 and with E4M3 weights."""
     w1 = wl.Workload("proj_graph_split", 40, 8, 128, nt=300, n_ctx=4096, n_slots=1, layers=1,
                      seed=22, pos_mode="uniform")
     w2 = wl.Workload("proj_graph_long", 40, 8, 128, nt=1100, n_ctx=4096, n_slots=1, layers=1,
                      seed=23, pos_mode="uniform")
-    cases = [ProjCase(w1, hidden=256).upload(), ProjCase(w2, hidden=256).upload()]
+    cases = [ProjCase(w1, hidden=256, wfmt=wfmt).upload(), ProjCase(w2, hidden=256, wfmt=wfmt).upload()]
     _graph_replays(handle, cases)
 
 

@@ -299,10 +299,10 @@ __device__ __forceinline__ int group_lo(int g)
 // IL: interleaved pairs (2i, 2i+1), else NeoX (j, j + hd/2); a template
 // argument so that the NeoX instance carries no code of the other rotation.
 // W8: E4M3 weights.  Their bytes go to LDS as they are (a stage's weight row
-// is BK bytes); each fragment read takes the lane's 8 codes and turns them
-// into 8 bf16 (exact: every E4M3 value is a bf16 value), so the products and
-// the f32 sums are those of bf16 weights; the epilogue multiplies each sum by
-// its row's scale before the bias.
+// is BK bytes); each k step turns the lane's 8 codes into 8 bf16 (exact:
+// every E4M3 value is a bf16 value; one 16-byte LDS read serves two steps),
+// so the products and the f32 sums are those of bf16 weights; the epilogue
+// multiplies each sum by its row's scale before the bias.
 template <bool F16, int HD, int MI, int WN, int BK, int G, bool IL, bool W8>
 __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
 {
@@ -342,9 +342,9 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     // kCprB) of the tile; byte offsets from x and from the weight matrix of
     // the load's section (the rows of a load lie in one 32-column tile, so in
     // one section: its base is wave-uniform), each < 2 GiB; rows past the end
-    // repeat the last one.  (fixed-size arrays: with a size that depends on the template
-    // arguments, captured by the lambda below, hipcc's host pass silently
-    // emitted no launch stub)
+    // repeat the last one.  (fixed-size arrays: with a size that depends on
+    // the template arguments, captured by the lambda below, hipcc's host pass
+    // silently emitted no launch stub)
     const bool do_a = S::kInstA >= kWaves || wave < S::kInstA;
     const bool do_b = S::kInstB >= kWaves || wave >= kWaves - S::kInstB;
     int arow[8] = {0, 0, 0, 0, 0, 0, 0, 0}, brow[8] = {0, 0, 0, 0, 0, 0, 0, 0};

@@ -302,7 +302,7 @@ def bench_batched(h, w, cache_dtype, stream, n_launch=256, replays=4, R=64):
     assert B.qkv_epilogue_status(h) == 0, B.qkv_epilogue_last_error(h)
     rows = []
     for tpb in (1, 2, 4):
-        for pol in (1, 2):
+        for pol in (1, 2, 3):
             us = time_graph(lambda i, tpb=tpb, pol=pol: P.rows(
                 xs[i % R], bcat, w.nqt, w.nkt, sets.sets[i % R]["pos"], sets.sets[i % R]["slot"],
                 w.n_ctx, kc, vc, block=256, tpb=tpb, policy=pol, stream=stream), n_launch, replays, stream)
@@ -714,7 +714,7 @@ def ceiling_prefill_rows(h, steps, stream, R=8):
 
     res = []
     for tpb in (1, 2, 4):
-        for pol in (1, 2):
+        for pol in (1, 2, 3):
             us = loop(lambda i, tpb=tpb, pol=pol: P.rows(xs[i % R], bcat, w.nqt, w.nkt, pos, None, w.n_ctx,
                                                          kc, vc, block=256, tpb=tpb, policy=pol,
                                                          stream=stream))

@@ -31,7 +31,9 @@
 //   1  non-temporal loads and stores (the nt bit);
 //   2  non-temporal loads, stores non-temporal at device scope (nt sc1),
 //      which are written through the XCD's L2 as they are issued instead of
-//      being written back by the end-of-kernel release.
+//      being written back by the end-of-kernel release;
+//   3  (row pass only) as 2, but the cache rows stored at device scope
+//      without the non-temporal bit (sc1), the epilogue's combination.
 // Policy 2 stores go through a raw buffer resource whose base is the same
 // for a whole workgroup (a block of the buffer, or a row), with offsets
 // below 2^31.
@@ -52,6 +54,7 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kNtDevice = 2 /* nt */ | 16 /* sc1 */;
+constexpr int kDevice = 16 /* sc1 */;
 
 __global__ void empty_kernel() {}
 
@@ -82,7 +85,8 @@ __device__ __forceinline__ void st16(void *base, uint32_t off, f32x4 v)
         __builtin_nontemporal_store(v, p);
     } else {
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kNtDevice);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0,
+                                               POL == 3 ? kDevice : kNtDevice);
     }
 }
 
@@ -96,7 +100,8 @@ __device__ __forceinline__ void st8(void *base, uint32_t off, f16x4 v)
         __builtin_nontemporal_store(v, p);
     } else {
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)off, 0, kNtDevice);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)off, 0,
+                                              POL == 3 ? kDevice : kNtDevice);
     }
 }
 
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(1024) void rows_kernel(float *__restrict__ x, const
         if (t0 + j >= nt)
             break;
         const f32x4 r = v[j] + bv;
-        st16<POL>(x + (t0 + j) * width4 * 4, (uint32_t)(c * 16), r);
+        st16<POL == 3 ? 2 : POL>(x + (t0 + j) * width4 * 4, (uint32_t)(c * 16), r);
         if (to_cache) {
             void *const crow = static_cast<char *>(cache) + row[j] * nkt4 * cvec;
             if constexpr (F16) {
@@ -387,7 +392,7 @@ int qkv_probe_rows(float *x, const float *b, long long nt, long long width, long
 {
     if (!x || !b || !pos || !kc || !vc || nt < 1 || width < 4 || (width & 3) || (kv_col & 3) ||
         (nkt & 3) || nkt < 4 || kv_col < 0 || kv_col + 2 * nkt > width || n_ctx < 1 ||
-        bad_block(block) || policy < 0 || policy > 2 || width * 4 >= 0x7fffffffLL)
+        bad_block(block) || policy < 0 || policy > 3 || width * 4 >= 0x7fffffffLL)
         return -1;
     if (((uintptr_t)x | (uintptr_t)b | (uintptr_t)kc | (uintptr_t)vc) & 15u)
         return -1;
@@ -401,11 +406,13 @@ int qkv_probe_rows(float *x, const float *b, long long nt, long long width, long
     if (f16)
         ok = policy == 0   ? dispatch_rows<true, 0>(tpb, grid, block, st, x, b, nt, w4, kv_col / 4, nkt / 4, pos, slot, n_ctx, kc, vc)
              : policy == 1 ? dispatch_rows<true, 1>(tpb, grid, block, st, x, b, nt, w4, kv_col / 4, nkt / 4, pos, slot, n_ctx, kc, vc)
-                           : dispatch_rows<true, 2>(tpb, grid, block, st, x, b, nt, w4, kv_col / 4, nkt / 4, pos, slot, n_ctx, kc, vc);
+             : policy == 2 ? dispatch_rows<true, 2>(tpb, grid, block, st, x, b, nt, w4, kv_col / 4, nkt / 4, pos, slot, n_ctx, kc, vc)
+                           : dispatch_rows<true, 3>(tpb, grid, block, st, x, b, nt, w4, kv_col / 4, nkt / 4, pos, slot, n_ctx, kc, vc);
     else
         ok = policy == 0   ? dispatch_rows<false, 0>(tpb, grid, block, st, x, b, nt, w4, kv_col / 4, nkt / 4, pos, slot, n_ctx, kc, vc)
              : policy == 1 ? dispatch_rows<false, 1>(tpb, grid, block, st, x, b, nt, w4, kv_col / 4, nkt / 4, pos, slot, n_ctx, kc, vc)
-                           : dispatch_rows<false, 2>(tpb, grid, block, st, x, b, nt, w4, kv_col / 4, nkt / 4, pos, slot, n_ctx, kc, vc);
+             : policy == 2 ? dispatch_rows<false, 2>(tpb, grid, block, st, x, b, nt, w4, kv_col / 4, nkt / 4, pos, slot, n_ctx, kc, vc)
+                           : dispatch_rows<false, 3>(tpb, grid, block, st, x, b, nt, w4, kv_col / 4, nkt / 4, pos, slot, n_ctx, kc, vc);
     return ok ? rc_of(hipGetLastError()) : -1;
 }
 

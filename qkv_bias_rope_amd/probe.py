@@ -10,7 +10,9 @@ negative code.
 
 Memory policy of the copy/add/rows kernels: 0 plain loads and stores, 1
 non-temporal loads and stores, 2 non-temporal loads and non-temporal
-device-scope stores (written through the L2 as they are issued).
+device-scope stores (written through the L2 as they are issued); the row
+pass also takes 3: as 2, but the cache rows stored at device scope without
+the non-temporal bit (the epilogue's combination).
 """
 from __future__ import annotations
 

@@ -35,7 +35,7 @@ def test_rejects_bad_arguments():
     x = torch.zeros(64, device=DEV)
     assert P.copy(x, x, block=100) == -1          # block not a multiple of 64
     assert P.add(x, vpt=3) == -1                  # no such instance
-    assert P.add(x, policy=3) == -1
+    assert P.add(x, policy=3) == -1               # policy 3 is the row pass's only
     assert P.empty(0, 64) == -1
     assert P.empty_args(0, 64) == -1
     assert P.empty_args(3, 100) == -1
@@ -49,7 +49,7 @@ def test_empty_kernels_launch():
 
 
 @pytest.mark.parametrize("cache", (torch.float16, torch.float32))
-@pytest.mark.parametrize("policy", (0, 1, 2))
+@pytest.mark.parametrize("policy", (0, 1, 2, 3))
 @pytest.mark.parametrize("tpb", (1, 2, 4))
 def test_rows(cache, policy, tpb):
     rng = np.random.default_rng(5)

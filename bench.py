@@ -309,7 +309,7 @@ def bench_batched(h, w, cache_dtype, stream, n_launch=256, replays=4, R=64):
             rows.append(dict(tokens_per_workgroup=tpb, policy=pol, us=round(us, 3),
                              gbs=round(nbytes / us / 1e3, 1)))
     adds = []
-    for pol in (1, 2):
+    for pol in (1, 2, 3):
         us = time_graph(lambda i, pol=pol: P.add(xs[i % R], 256, 1, pol, stream), n_launch, replays,
                         stream)
         adds.append(dict(policy=pol, us=round(us, 3)))
@@ -646,7 +646,7 @@ def ceilings_prefill(steps, stream, nbytes=251703296, sets=8):
     k = max(20, min(steps, 100))
     for name in ("inplace_add", "copy"):
         res = []
-        for pol in (1, 2):
+        for pol in (1, 2, 3):
             for vpt in (1, 2):
                 if name == "inplace_add":
                     fn = lambda i, pol=pol, vpt=vpt: P.add(bufs[i % sets], 256, vpt, pol, stream)

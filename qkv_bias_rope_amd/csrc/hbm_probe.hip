@@ -32,8 +32,9 @@
 //   2  non-temporal loads, stores non-temporal at device scope (nt sc1),
 //      which are written through the XCD's L2 as they are issued instead of
 //      being written back by the end-of-kernel release;
-//   3  (row pass only) as 2, but the cache rows stored at device scope
-//      without the non-temporal bit (sc1), the epilogue's combination.
+//   3  non-temporal loads, stores at device scope without the non-temporal
+//      bit (sc1); in the row pass only the cache rows take these stores and
+//      the rows keep policy 2's (the epilogue's combination).
 // Policy 2 stores go through a raw buffer resource whose base is the same
 // for a whole workgroup (a block of the buffer, or a row), with offsets
 // below 2^31.
@@ -332,7 +333,7 @@ int qkv_probe_empty_args(int grid, int block, hipStream_t st)
 int qkv_probe_copy(void *dst, const void *src, long long n16, int block, int vpt, int policy,
                    hipStream_t st)
 {
-    if (!dst || !src || n16 < 1 || bad_block(block) || policy < 0 || policy > 2)
+    if (!dst || !src || n16 < 1 || bad_block(block) || policy < 0 || policy > 3)
         return -1;
     if (((uintptr_t)dst | (uintptr_t)src) & 15u)
         return -1;
@@ -343,7 +344,8 @@ int qkv_probe_copy(void *dst, const void *src, long long n16, int block, int vpt
     auto *s = static_cast<const f32x4 *>(src);
     const bool ok = policy == 0   ? dispatch_copy<0>(vpt, g, block, st, d, s, n16)
                     : policy == 1 ? dispatch_copy<1>(vpt, g, block, st, d, s, n16)
-                                  : dispatch_copy<2>(vpt, g, block, st, d, s, n16);
+                    : policy == 2 ? dispatch_copy<2>(vpt, g, block, st, d, s, n16)
+                                  : dispatch_copy<3>(vpt, g, block, st, d, s, n16);
     return ok ? rc_of(hipGetLastError()) : -1;
 }
 
@@ -368,7 +370,7 @@ int qkv_probe_read(const void *src, long long n16, float *out, int block, int vp
 // buf: n16 16-byte vectors, 16-byte aligned; every float gets 1 added.
 int qkv_probe_add(void *buf, long long n16, int block, int vpt, int policy, hipStream_t st)
 {
-    if (!buf || n16 < 1 || bad_block(block) || ((uintptr_t)buf & 15u) || policy < 0 || policy > 2)
+    if (!buf || n16 < 1 || bad_block(block) || ((uintptr_t)buf & 15u) || policy < 0 || policy > 3)
         return -1;
     const long long g = qkv_probe_grid(n16, block, vpt);
     if (g > 0x7fffffffLL)
@@ -376,7 +378,8 @@ int qkv_probe_add(void *buf, long long n16, int block, int vpt, int policy, hipS
     auto *p = static_cast<f32x4 *>(buf);
     const bool ok = policy == 0   ? dispatch_add<0>(vpt, g, block, st, p, n16)
                     : policy == 1 ? dispatch_add<1>(vpt, g, block, st, p, n16)
-                                  : dispatch_add<2>(vpt, g, block, st, p, n16);
+                    : policy == 2 ? dispatch_add<2>(vpt, g, block, st, p, n16)
+                                  : dispatch_add<3>(vpt, g, block, st, p, n16);
     return ok ? rc_of(hipGetLastError()) : -1;
 }
 

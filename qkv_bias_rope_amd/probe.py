@@ -10,9 +10,10 @@ negative code.
 
 Memory policy of the copy/add/rows kernels: 0 plain loads and stores, 1
 non-temporal loads and stores, 2 non-temporal loads and non-temporal
-device-scope stores (written through the L2 as they are issued); the row
-pass also takes 3: as 2, but the cache rows stored at device scope without
-the non-temporal bit (the epilogue's combination).
+device-scope stores (written through the L2 as they are issued), 3
+non-temporal loads and device-scope stores without the non-temporal bit (in
+the row pass only the cache rows take these; the rows keep 2's: the
+epilogue's combination).
 """
 from __future__ import annotations
 

@@ -16,7 +16,7 @@ P = pytest.importorskip("qkv_bias_rope_amd.probe")
 DEV = "cuda:0"
 
 
-@pytest.mark.parametrize("policy", (0, 1, 2))
+@pytest.mark.parametrize("policy", (0, 1, 2, 3))
 @pytest.mark.parametrize("vpt", (1, 2, 4, 8))
 def test_copy_and_add(policy, vpt):
     n = 4 * (3 * 256 * vpt + 37)   # a ragged last workgroup
@@ -35,7 +35,7 @@ def test_rejects_bad_arguments():
     x = torch.zeros(64, device=DEV)
     assert P.copy(x, x, block=100) == -1          # block not a multiple of 64
     assert P.add(x, vpt=3) == -1                  # no such instance
-    assert P.add(x, policy=3) == -1               # policy 3 is the row pass's only
+    assert P.add(x, policy=4) == -1               # no such policy
     assert P.empty(0, 64) == -1
     assert P.empty_args(0, 64) == -1
     assert P.empty_args(3, 100) == -1

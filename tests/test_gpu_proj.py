@@ -558,6 +558,18 @@ def test_proj_random_shapes(handle, seed):
     c.check(f"rand_{seed}")
 
 
+@pytest.mark.parametrize("seed", range(40, 64))
+def test_proj_random_shapes_e4m3(handle, seed):
+    """The same seeded random shapes with E4M3 weights and row scales: the
+    GEMV for 1-4 tokens, the k-split and data-parallel MFMA tiles (E4M3
+    stages, converted fragments, scales in the fused epilogue or in the
+    summing kernel) for more."""
+    w, kw = _random_shape(seed)
+    c = ProjCase(w, wfmt="e4m3", **kw)
+    assert _run(handle, c, f"rand_e4m3_{seed}") == B.QKV_OK
+    c.check(f"rand_e4m3_{seed}")
+
+
 @pytest.mark.parametrize("weights", ["concat", "three"])
 def test_proj_python_wrapper(weights):
     """Epilogue.run_proj (the checked torch-tensor wrapper of the same entry

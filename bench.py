@@ -844,7 +844,10 @@ def proj_sweep(args):
     rc, h = B.qkv_epilogue_create(0, 4096)
     assert rc == 0, rc
     stream = torch.cuda.Stream()
-    w = wl.Workload("proj_sweep_14b", 40, 8, 128, nt=1, n_ctx=4096, n_slots=1, layers=1, seed=30)
+    # each launch is a prompt of nt tokens at positions 0..nt-1 (distinct
+    # cache rows, as in a real prefill)
+    w = wl.Workload("proj_sweep_14b", 40, 8, 128, nt=1, n_ctx=4096, n_slots=1, layers=1, seed=30,
+                    pos_mode="arange")
     hidden = 5120
     with torch.cuda.stream(stream):
         for nt in PROJ_SWEEP_TOKENS:

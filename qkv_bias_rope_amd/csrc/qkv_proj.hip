@@ -177,12 +177,15 @@ __global__ __launch_bounds__(256) void rope_table_kernel(ProjParams p, InvTableS
 // 64 four-byte banks serving 16 lanes at a time -- takes 8.  The fragments
 // of a stage's k steps are double-buffered in registers; per pair of steps
 // j, j + 1:
-//   products of step j (first half); read step-(j+1) fragments; products of
-//   step j (second half); products of step j+1 (first half); read step-(j+2)
-//   fragments -- or, after the stage's last step: wait for this wave's loads
-//   of the next stage and meet the other waves (after which this stage is
-//   free and the next visible), refill this stage NSTAGE ahead and read the
-//   next stage's first fragments; products of step j+1 (second half).
+//   products of step j, with the step-(j+1) fragment reads spread among
+//   them (one read after each MFMA); products of step j+1, with the
+//   step-(j+2) reads spread among them -- or, after the stage's last step:
+//   its first half; wait for this wave's loads of the next stage and meet
+//   the other waves (after which this stage is free and the next visible),
+//   refill this stage NSTAGE ahead and read the next stage's first
+//   fragments; its second half.  Bunched after a step's first half, as
+//   before, the reads had four MFMAs in front of their first use and the
+//   4096-token launch ran 1-2% (bf16) and 1-4% (E4M3) slower.
 //
 // The grid is tiles x S: with S = 1 each workgroup finishes its tile (the
 // epilogue below); when the tiles are too few to fill the chip, k is split S
@@ -433,12 +436,16 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     // two fragment buffers: step j uses buffer j % 2
     static_assert(KS % 2 == 0, "steps per stage");
     bf16x8 a0[MI], b0[2 * G], a1[MI], b1[2 * G];
+    // bf16: the reads go out in the order the products first use them (the
+    // first weight fragment, the token fragments, the other weight fragments)
     auto read_frags = [&](const unsigned char *s, int j, bf16x8 (&fa)[MI], bf16x8 (&fb)[2 * G]) {
+        if constexpr (!W8)
+            fb[0] = *reinterpret_cast<const bf16x8 *>(s + bbase + koff[j]);
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
             fa[mi] = *reinterpret_cast<const bf16x8 *>(s + abase + mi * 32 * kRow + koff[j]);
 #pragma unroll
-        for (int t = 0; t < 2 * G; ++t) {
+        for (int t = W8 ? 0 : 1; t < 2 * G; ++t) {
             if constexpr (W8) {
                 // even step: read the pair's 16 codes, convert the first 8;
                 // odd step: convert the other 8 (no LDS read)
@@ -464,6 +471,22 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
             acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[q / MI], fa[q % MI], acc[q], 0, 0, 0);
     };
 
+    // The next step's fragment reads, spread over this step's products: one
+    // LDS read after each MFMA while both last (sched_group_barrier masks:
+    // 0x008 MFMA, 0x100 LDS read).  Every read then has about seven MFMAs in
+    // front of its first use, and the eight waves' reads reach the LDS spread
+    // over the step instead of in one burst after its first half.
+    auto spread_reads = [&]() {
+        constexpr int kM = 2 * G * MI, kR = W8 ? MI : MI + 2 * G;
+#pragma unroll
+        for (int i = 0; i < (kR < kM ? kR : kM); ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if constexpr (kM > kR)
+            __builtin_amdgcn_sched_group_barrier(0x008, kM - kR, 0);
+    };
+
     // prologue: stages 0..NSTAGE-1 in flight, stage 0 landed everywhere
 #pragma unroll
     for (int st = 0; st < NSTAGE; ++st)
@@ -475,12 +498,12 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
     ring_barrier();
     read_frags(lds, 0, a0, b0);
 
-    // Per pair of k steps: step j's products, first half; the next step's
-    // fragments; step j's second half; step j + 1's first half; the
-    // fragments of step j + 2 -- or, after the stage's last step: wait for
-    // this wave's loads of the next stage, meet the other waves (after which
-    // this stage is free and the next visible), refill this stage NSTAGE
-    // ahead and read the next stage's first fragments; step j + 1's second
+    // Per pair of k steps: step j's products with the fragment reads of step
+    // j + 1 spread among them; then step j + 1's products with those of step
+    // j + 2 -- or, after the stage's last step: its first half, then wait
+    // for this wave's loads of the next stage, meet the other waves (after
+    // which this stage is free and the next visible), refill this stage
+    // NSTAGE ahead, read the next stage's first fragments, and the second
     // half.  The refill goes out right after the barrier: with two stages
     // (256 x 256) it has one stage's time to land, and issuing it later,
     // even spread between the products, measured slower.
@@ -491,16 +514,19 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
         for (int jj = 0; jj < KS; jj += 2) {
             __builtin_amdgcn_sched_barrier(0);
             mfma_half(0, a0, b0);
-            __builtin_amdgcn_sched_barrier(0);
             read_frags(s, jj + 1, a1, b1);
-            __builtin_amdgcn_sched_barrier(0);
             mfma_half(1, a0, b0);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_half(0, a1, b1);
+            spread_reads();
             __builtin_amdgcn_sched_barrier(0);
             if (jj + 2 < KS) {
+                mfma_half(0, a1, b1);
                 read_frags(s, jj + 2, a0, b0);
+                mfma_half(1, a1, b1);
+                spread_reads();
+                __builtin_amdgcn_sched_barrier(0);
             } else {
+                mfma_half(0, a1, b1);
+                __builtin_amdgcn_sched_barrier(0);
                 if (S::kLoadsLo == S::kLoadsHi || wave < 4)
                     __builtin_amdgcn_s_waitcnt(vmcnt_wait((NSTAGE - 2) * S::kLoadsLo));
                 else
@@ -508,9 +534,9 @@ __global__ __launch_bounds__(mm::kThreads) void proj_mfma_kernel(ProjParams p)
                 ring_barrier();
                 issue(kt + NSTAGE);
                 read_frags(lds + ((kt + 1) % NSTAGE) * S::kStage, 0, a0, b0);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_half(1, a1, b1);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_half(1, a1, b1);
         }
     }
     // the clamped reloads of the last iterations land before the ring is

@@ -183,9 +183,9 @@ __global__ __launch_bounds__(256) void rope_table_kernel(ProjParams p, InvTableS
 //   its first half; wait for this wave's loads of the next stage and meet
 //   the other waves (after which this stage is free and the next visible),
 //   refill this stage NSTAGE ahead and read the next stage's first
-//   fragments; its second half.  Bunched after a step's first half, as
-//   before, the reads had four MFMAs in front of their first use and the
-//   4096-token launch ran 1-2% (bf16) and 1-4% (E4M3) slower.
+//   fragments; its second half.  Bunched after a step's first half
+//   instead, the reads have four MFMAs in front of their first use, and the
+//   4096-token launch measured 1-2% (bf16) and 1-4% (E4M3) slower.
 //
 // The grid is tiles x S: with S = 1 each workgroup finishes its tile (the
 // epilogue below); when the tiles are too few to fill the chip, k is split S
